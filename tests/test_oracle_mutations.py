@@ -1,0 +1,71 @@
+"""The oracle pins must catch plausible mistakes.
+
+Each case plants one mistake in a temporary copy of the C oracle (on the CPU),
+builds it, and runs the pin suite against it in a subprocess: the suite must
+fail.  The shipped oracle is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+from oracle import build as obuild
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "kvq_oracle.c")
+
+MUTANTS = {
+    # rounding: half away from zero instead of half to even
+    "round_half_away": ("float y = rintf(ratio);", "float y = roundf(ratio);"),
+    # offset added before rounding (the literal reading rejected by the spec)
+    "offset_first": ("float y = rintf(ratio);", "float y = rintf(ratio + (float)(-(1 << (bits - 1)))) + (float)(1 << (bits - 1));"),
+    # eps guard dropped
+    "no_eps": ("if (s < KVO_EPS) s = KVO_EPS;", ""),
+    # codes against the fp32 scale instead of the stored fp16 scale
+    "unrounded_scale": ("*scale16 = kvo_f32_to_f16(s);", "*scale16 = kvo_f32_to_f16(s * 1.0009765625f);"),
+    # fp16 conversion truncates instead of rounding
+    "f16_truncate": ("double n = nearbyint(a / quantum);", "double n = floor(a / quantum);"),
+    # symmetric quantizer divides by 8 instead of 7
+    "sym4_qmax": ("float dd = amax / 7.0f;", "float dd = amax / 8.0f;"),
+    # centering bias added instead of subtracted
+    "bias_sign": ("if (bias) v = v - bias[d];", "if (bias) v = v + bias[d];"),
+    # dequantization drops the zero point
+    "dequant_no_zero": ("return (double)v->u[(int64_t)t * D + d] * s + z;\n    }\n    case KVO_SYM4",
+                        "return (double)v->u[(int64_t)t * D + d] * s;\n    }\n    case KVO_SYM4"),
+    # softmax scale applied twice
+    "scale_twice": ("logit[t] = scale * acc;", "logit[t] = scale * scale * acc;"),
+    # SnapKV mean over S instead of the clamped window
+    "mean_over_S": ("score[j] /= (double)wc;", "score[j] /= (double)S;"),
+    # SnapKV window taken from the front
+    "window_front": ("for (int i = S - wc; i < S; ++i) {", "for (int i = 0; i < wc; ++i) {"),
+    # tie-break prefers the higher position
+    "tie_high": ("return (x->i > y->i) - (x->i < y->i);", "return (x->i < y->i) - (x->i > y->i);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mut = tmp_path / "kvq_oracle.c"
+    mut.write_text(src.replace(old, new))
+    lib = str(tmp_path / "libmut.so")
+    obuild.build(src=str(mut), out=lib)
+    env = dict(os.environ, KVQ_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(HERE, "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+
+
+def test_control_unmutated_copy_passes(tmp_path):
+    """The same harness with an unmodified copy passes (the mutants fail for their mistake)."""
+    lib = str(tmp_path / "libctl.so")
+    obuild.build(src=SRC, out=lib)
+    env = dict(os.environ, KVQ_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(HERE, "test_oracle_pins.py")],
+                       env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]
