@@ -1,0 +1,368 @@
+// api.hip -- host side of the libkvq C ABI: validation, buffer sizing,
+// host counters and kernel dispatch.  No call allocates, frees or
+// synchronizes; every argument is checked before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+using namespace kvq;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+kvq_status hip_status(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_HIP; }
+
+int esize(int dt) { return dt == KVQ_F32 ? 4 : 2; }
+bool valid_dtype(int dt) { return dt == KVQ_F32 || dt == KVQ_F16 || dt == KVQ_BF16; }
+
+// Layout checks shared by every call.  Returns KVQ_OK or an error.
+kvq_status check_layout(const kvq_layout* L) {
+    if (!L) return KVQ_ERR_INVALID_ARG;
+    if (L->batch < 1 || L->n_kv_heads < 1 || L->capacity < 1) return KVQ_ERR_INVALID_ARG;
+    if (!valid_dtype(L->in_dtype)) return KVQ_ERR_INVALID_ARG;
+    if (L->flags & ~(KVQ_CENTER_K | KVQ_TEST_CENTER_ANY)) return KVQ_ERR_INVALID_ARG;
+    const int D = L->head_dim;
+    if (D != 32 && D != 64 && D != 128) return D > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
+    switch (L->k_kind) {
+        case KVQ_PLAIN: break;
+        case KVQ_KIVI_CH:
+            if (L->k_bits != 4 && L->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
+            if (!is_pow2(L->k_group) || L->k_group < 8 || L->k_group > 128) return KVQ_ERR_UNSUPPORTED;
+            break;
+        case KVQ_TOK_AFFINE:
+            if (L->k_bits != 4 && L->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
+            if ((L->k_group != 32 && L->k_group != 64 && L->k_group != 128) || L->k_group > D)
+                return KVQ_ERR_UNSUPPORTED;
+            break;
+        case KVQ_TOK_SYM4:
+            if (L->k_bits != 4 || L->k_group != 32) return KVQ_ERR_UNSUPPORTED;
+            break;
+        default: return KVQ_ERR_INVALID_ARG;
+    }
+    switch (L->v_kind) {
+        case KVQ_PLAIN: break;
+        case KVQ_TOK_AFFINE:
+            if (L->v_bits != 4 && L->v_bits != 8) return KVQ_ERR_UNSUPPORTED;
+            if ((L->v_group != 32 && L->v_group != 64 && L->v_group != 128) || L->v_group > D)
+                return KVQ_ERR_UNSUPPORTED;
+            break;
+        case KVQ_KIVI_CH: case KVQ_TOK_SYM4: return KVQ_ERR_UNSUPPORTED;   // K-only kinds
+        default: return KVQ_ERR_INVALID_ARG;
+    }
+    if (L->flags & KVQ_CENTER_K) {
+        // Mean-centering is gated to the symmetric 4-bit K format (the
+        // zero-point formats already absorb a static mean); PLAIN keys are
+        // allowed only through the test seam.
+        const bool ok = L->k_kind == KVQ_TOK_SYM4 ||
+                        (L->k_kind == KVQ_PLAIN && (L->flags & KVQ_TEST_CENTER_ANY));
+        if (!ok) return KVQ_ERR_UNSUPPORTED;
+        // the seam stores centered keys at full precision: fp32 only
+        if (L->k_kind == KVQ_PLAIN && L->in_dtype != KVQ_F32) return KVQ_ERR_UNSUPPORTED;
+    }
+    return KVQ_OK;
+}
+
+int table_rows(const kvq_layout* L) {
+    return L->k_kind == KVQ_KIVI_CH ? L->capacity / L->k_group + 3 : 0;
+}
+
+void sizes_of(const kvq_layout* L, kvq_sizes* s) {
+    memset(s, 0, sizeof *s);
+    const size_t BH = (size_t)L->batch * L->n_kv_heads;
+    const size_t C = (size_t)L->capacity, D = (size_t)L->head_dim;
+    switch (L->k_kind) {
+        case KVQ_PLAIN: s->k_codes = BH * C * D * esize(L->in_dtype); break;
+        case KVQ_KIVI_CH:
+            s->k_codes = BH * C * D * L->k_bits / 8;
+            s->k_table_rows = table_rows(L);
+            s->k_meta = BH * (size_t)s->k_table_rows * D * 2 * 2;
+            s->k_resid = BH * (size_t)L->k_group * D * esize(L->in_dtype);
+            s->k_row = C * 4;
+            break;
+        case KVQ_TOK_AFFINE:
+            s->k_codes = BH * C * D * L->k_bits / 8;
+            s->k_meta = BH * C * (D / L->k_group) * 2 * 2;
+            break;
+        case KVQ_TOK_SYM4:
+            s->k_codes = BH * C * D / 2;
+            s->k_meta = BH * C * (D / 32) * 2;
+            break;
+    }
+    if (L->v_kind == KVQ_PLAIN) {
+        s->v_codes = BH * C * D * esize(L->in_dtype);
+    } else {
+        s->v_codes = BH * C * D * L->v_bits / 8;
+        s->v_meta = BH * C * (D / L->v_group) * 2 * 2;
+    }
+    s->pos = C * 4;
+}
+
+// Device buffers a layout needs must be present and aligned.
+kvq_status check_cache(const kvq_layout* L, const kvq_cache* c) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    if (c->n_stored < 0 || c->n_stored > L->capacity || c->n_quant < 0 || c->n_quant > c->n_stored ||
+        c->next_pos < c->n_stored || c->n_head < 0 || c->n_head > c->n_stored)
+        return KVQ_ERR_INVALID_ARG;
+    if (L->k_kind != KVQ_KIVI_CH && c->n_quant != c->n_stored) return KVQ_ERR_INVALID_ARG;
+    if (L->k_kind == KVQ_KIVI_CH && c->n_stored - c->n_quant >= L->k_group)
+        return KVQ_ERR_INVALID_ARG;
+    const void* need[8] = {c->k_codes, c->v_codes, c->pos, nullptr, nullptr, nullptr, nullptr, nullptr};
+    int n = 3;
+    if (L->k_kind != KVQ_PLAIN) need[n++] = c->k_meta;
+    if (L->k_kind == KVQ_KIVI_CH) { need[n++] = c->k_resid; need[n++] = c->k_row; }
+    if (L->v_kind != KVQ_PLAIN) need[n++] = c->v_meta;
+    for (int i = 0; i < n; ++i) if (!need[i]) return KVQ_ERR_INVALID_ARG;
+    for (int i = 0; i < n; ++i) if (!aligned16(need[i])) return KVQ_ERR_ALIGNMENT;
+    if (L->flags & KVQ_CENTER_K) {
+        if (!c->k_bias) return KVQ_ERR_INVALID_ARG;
+        if (!aligned16(c->k_bias)) return KVQ_ERR_ALIGNMENT;
+    }
+    return KVQ_OK;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_version(void) { return KVQ_VERSION; }
+
+const char* kvq_status_string(kvq_status s) {
+    switch (s) {
+        case KVQ_OK: return "ok";
+        case KVQ_NOOP: return "nothing to do";
+        case KVQ_ERR_INVALID_ARG: return "invalid argument";
+        case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KVQ_ERR_CAPACITY: return "cache capacity exceeded";
+        case KVQ_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+        case KVQ_ERR_HIP: return "HIP runtime or launch error";
+    }
+    return "unknown status";
+}
+
+kvq_status kvq_cache_sizes(const kvq_layout* L, kvq_sizes* out) {
+    if (!out) return KVQ_ERR_INVALID_ARG;
+    const kvq_status st = check_layout(L);
+    if (st != KVQ_OK) return st;
+    sizes_of(L, out);
+    return KVQ_OK;
+}
+
+kvq_status kvq_cache_reset(kvq_cache* c) {
+    if (!c) return KVQ_ERR_INVALID_ARG;
+    c->n_stored = c->n_quant = c->next_pos = c->n_head = 0;
+    return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(const kvq_layout* L, kvq_cache* c, const void* k_new,
+                               const void* v_new, int32_t n_new, void* stream) {
+    kvq_status st = check_layout(L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, c)) != KVQ_OK) return st;
+    if (n_new < 1 || !k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
+    if ((int64_t)c->n_stored + n_new > L->capacity) return KVQ_ERR_CAPACITY;
+    if ((int64_t)c->next_pos + n_new > INT32_MAX) return KVQ_ERR_CAPACITY;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int B = L->batch, H = L->n_kv_heads, D = L->head_dim;
+
+    // V (and per-token K) rows: quantized once, at write time.
+    RowQuantArgs v{};
+    v.src = v_new; v.codes = c->v_codes; v.meta = c->v_meta; v.bias = nullptr;
+    v.B = B; v.H = H; v.n = n_new; v.D = D; v.cap = L->capacity; v.slot0 = c->n_stored;
+    v.kind = L->v_kind; v.bits = L->v_bits; v.group = L->v_group; v.in_dtype = L->in_dtype;
+    hipError_t e = launch_row_quant(v, s);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+
+    int new_quant = c->n_stored + n_new;
+    if (L->k_kind == KVQ_KIVI_CH) {
+        ChannelQuantArgs k{};
+        k.k_new = k_new; k.resid = c->k_resid; k.codes = c->k_codes; k.table = c->k_meta;
+        k.k_row = c->k_row;
+        k.B = B; k.H = H; k.D = D; k.cap = L->capacity; k.rows = table_rows(L);
+        k.Gt = L->k_group; k.bits = L->k_bits; k.in_dtype = L->in_dtype;
+        k.r0 = c->n_stored - c->n_quant;
+        k.n_new = n_new;
+        k.n_quant = c->n_quant;
+        k.n_groups = (k.r0 + n_new) / L->k_group;
+        e = launch_channel_quant(k, s);
+        new_quant = c->n_quant + k.n_groups * L->k_group;
+    } else {
+        RowQuantArgs k{};
+        k.src = k_new; k.codes = c->k_codes; k.meta = c->k_meta;
+        k.bias = (L->flags & KVQ_CENTER_K) ? c->k_bias : nullptr;
+        k.B = B; k.H = H; k.n = n_new; k.D = D; k.cap = L->capacity; k.slot0 = c->n_stored;
+        k.kind = L->k_kind; k.bits = L->k_bits; k.group = L->k_group; k.in_dtype = L->in_dtype;
+        e = launch_row_quant(k, s);
+    }
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+    e = launch_fill_pos(c->pos, c->n_stored, c->next_pos, n_new, s);
+    if (e != hipSuccess) return KVQ_ERR_HIP;
+
+    if (c->n_head == c->n_stored) c->n_head += n_new;   // never evicted: positions == slots
+    c->n_stored += n_new;
+    c->next_pos += n_new;
+    c->n_quant = new_quant;
+    return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_q_heads) {
+    if (check_layout(L) != KVQ_OK || n_q_heads < 1) return 0;
+    return decode_workspace_bytes(L->batch, n_q_heads, L->head_dim, L->capacity);
+}
+
+kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* c, const void* q,
+                                int32_t q_dtype, int32_t n_q_heads, float sm_scale, float* out,
+                                void* ws, size_t ws_bytes, void* stream) {
+    kvq_status st = check_layout(L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, c)) != KVQ_OK) return st;
+    if (!q || !out || !valid_dtype(q_dtype)) return KVQ_ERR_INVALID_ARG;
+    if (n_q_heads < 1 || n_q_heads % L->n_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+    if (n_q_heads / L->n_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
+    if (!(sm_scale == sm_scale) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGNMENT;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = L->head_dim;
+    if (c->n_stored == 0)
+        return hip_status(launch_zero_f32(out, (size_t)L->batch * n_q_heads * D, s));
+    const size_t need = decode_workspace_bytes(L->batch, n_q_heads, D, L->capacity);
+    if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(ws)) return KVQ_ERR_ALIGNMENT;
+
+    DecodeArgs a{};
+    a.k_codes = c->k_codes; a.k_meta = c->k_meta; a.k_resid = c->k_resid;
+    a.v_codes = c->v_codes; a.v_meta = c->v_meta; a.k_row = c->k_row;
+    a.q = q; a.out = out;
+    a.B = L->batch; a.Hkv = L->n_kv_heads; a.Hq = n_q_heads; a.D = D; a.cap = L->capacity;
+    a.T = c->n_stored; a.n_quant = c->n_quant; a.Gt = L->k_group;
+    a.k_kind = L->k_kind; a.k_bits = L->k_bits; a.k_group = L->k_group;
+    a.v_kind = L->v_kind; a.v_bits = L->v_bits; a.v_group = L->v_group;
+    a.in_dtype = L->in_dtype; a.q_dtype = q_dtype;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    decode_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = a.ws_o + (size_t)a.B * a.Hq * a.n_splits * D;
+    return hip_status(launch_decode(a, s));
+}
+
+kvq_status kvq_evict_streaming(const kvq_layout* L, const kvq_cache* src, kvq_cache* dst,
+                               int32_t sink, int32_t window, void* stream) {
+    kvq_status st = check_layout(L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, src)) != KVQ_OK) return st;
+    if (!dst) return KVQ_ERR_INVALID_ARG;
+    if (sink < 0 || window < 1) return KVQ_ERR_INVALID_ARG;
+    const int n = src->n_stored;
+    if ((int64_t)sink + window >= n) return KVQ_NOOP;
+    // dst buffers: present, aligned, disjoint from src
+    kvq_cache probe = *dst;
+    probe.n_stored = probe.n_quant = probe.next_pos = probe.n_head = 0;
+    if ((st = check_cache(L, &probe)) != KVQ_OK) return st;
+    kvq_sizes sz;
+    sizes_of(L, &sz);
+    const void* sp[7] = {src->k_codes, src->k_meta, src->k_resid, src->v_codes, src->v_meta, src->pos, src->k_row};
+    const void* dp[7] = {dst->k_codes, dst->k_meta, dst->k_resid, dst->v_codes, dst->v_meta, dst->pos, dst->k_row};
+    const size_t nb[7] = {sz.k_codes, sz.k_meta, sz.k_resid, sz.v_codes, sz.v_meta, sz.pos, sz.k_row};
+    for (int i = 0; i < 7; ++i)
+        for (int j = 0; j < 7; ++j)
+            if (overlaps(sp[i], nb[i], dp[j], nb[j])) return KVQ_ERR_INVALID_ARG;
+    const int r = n - src->n_quant;                    // open K group (KIVI_CH)
+    if (L->k_kind == KVQ_KIVI_CH) {
+        if (window < L->k_group) return KVQ_ERR_INVALID_ARG;
+        // kept positions must stay two runs: the sink prefix (positions ==
+        // slots) and one run of consecutive positions
+        const int h = src->n_head;
+        const bool fresh = (h == n);
+        if (!fresh && (sink > h || n - window < h)) return KVQ_ERR_UNSUPPORTED;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = L->head_dim;
+    EvictArgs a{};
+    int nbuf = 0;
+    auto add = [&](const void* sptr, void* dptr, size_t row_bytes) {
+        a.src[nbuf] = sptr; a.dst[nbuf] = dptr; a.row_bytes[nbuf] = (int)row_bytes; ++nbuf;
+    };
+    if (L->k_kind == KVQ_PLAIN) add(src->k_codes, dst->k_codes, (size_t)D * esize(L->in_dtype));
+    else add(src->k_codes, dst->k_codes, (size_t)D * L->k_bits / 8);
+    if (L->k_kind == KVQ_TOK_AFFINE) add(src->k_meta, dst->k_meta, (size_t)(D / L->k_group) * 4);
+    if (L->k_kind == KVQ_TOK_SYM4) add(src->k_meta, dst->k_meta, (size_t)(D / 32) * 2);
+    if (L->v_kind == KVQ_PLAIN) add(src->v_codes, dst->v_codes, (size_t)D * esize(L->in_dtype));
+    else {
+        add(src->v_codes, dst->v_codes, (size_t)D * L->v_bits / 8);
+        add(src->v_meta, dst->v_meta, (size_t)(D / L->v_group) * 4);
+    }
+    a.n_buf = nbuf;
+    a.src_pos = src->pos; a.dst_pos = dst->pos;
+    a.BH = L->batch * L->n_kv_heads; a.cap = L->capacity; a.n = n; a.sink = sink; a.window = window;
+    a.n_quant_new = sink + window - (L->k_kind == KVQ_KIVI_CH ? r : 0);
+    if (L->k_kind == KVQ_KIVI_CH) {
+        a.src_row = src->k_row; a.dst_row = dst->k_row;
+        a.src_table = src->k_meta; a.dst_table = dst->k_meta;
+        a.table_row_bytes = D * 4; a.rows = table_rows(L);
+        a.src_resid = src->k_resid; a.dst_resid = dst->k_resid; a.resid_bytes = sz.k_resid;
+    }
+    if (launch_evict(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    dst->n_stored = sink + window;
+    dst->n_quant = a.n_quant_new;
+    dst->next_pos = src->next_pos;
+    dst->n_head = sink < src->n_head ? sink : src->n_head;
+    return KVQ_OK;
+}
+
+size_t kvq_snapkv_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t w) {
+    if (B < 1 || H < 1 || S < 1 || w < 1 || (D != 32 && D != 64 && D != 128)) return 0;
+    return snapkv_ws_bytes(B, H, S, D, w);
+}
+
+kvq_status kvq_snapkv_select(const void* k, const void* v, int32_t B, int32_t H, int32_t S,
+                             int32_t D, int32_t w, int32_t n_sink, int32_t budget, float* scores,
+                             int32_t* kept, void* k_out, void* v_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+    if (!k || !v || !kept || !k_out || !v_out) return KVQ_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || S < 1 || w < 1 || budget < 1 || n_sink < 0) return KVQ_ERR_INVALID_ARG;
+    if (D != 32 && D != 64 && D != 128) return D > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
+    if ((w < S ? w : S) > 128) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * S > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    const void* ptrs[7] = {k, v, scores, kept, k_out, v_out, ws};
+    for (const void* p : ptrs) if (p && !aligned16(p)) return KVQ_ERR_ALIGNMENT;
+    const size_t need = snapkv_ws_bytes(B, H, S, D, w);
+    if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    SnapArgs a{};
+    a.k = static_cast<const uint16_t*>(k); a.v = static_cast<const uint16_t*>(v);
+    a.kept = kept; a.k_out = static_cast<uint16_t*>(k_out); a.v_out = static_cast<uint16_t*>(v_out);
+    a.B = B; a.H = H; a.S = S; a.D = D; a.w = w; a.n_sink = n_sink; a.budget = budget;
+    a.n_chunks = (S + 127) / 128;
+    const int wc = w < S ? w : S;
+    size_t stats = (size_t)B * H * a.n_chunks * wc * 2 * sizeof(float);
+    stats = (stats + 255) & ~(size_t)255;
+    a.stats = static_cast<float*>(ws);
+    a.scores = scores ? scores : reinterpret_cast<float*>(static_cast<char*>(ws) + stats);
+    if (launch_snapkv_scores(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    if (launch_snapkv_select(a.scores, B, H, S, n_sink, budget, kept, s) != hipSuccess) return KVQ_ERR_HIP;
+    if (launch_snapkv_gather(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    return KVQ_OK;
+}
+
+kvq_status kvq_snapkv_select_from_scores(const float* scores, int32_t B, int32_t H, int32_t S,
+                                         int32_t n_sink, int32_t budget, int32_t* kept, void* stream) {
+    if (!scores || !kept) return KVQ_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || S < 1 || budget < 1 || n_sink < 0) return KVQ_ERR_INVALID_ARG;
+    if ((int64_t)B * H * S > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    if (!aligned16(scores) || !aligned16(kept)) return KVQ_ERR_ALIGNMENT;
+    return hip_status(launch_snapkv_select(scores, B, H, S, n_sink, budget, kept,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

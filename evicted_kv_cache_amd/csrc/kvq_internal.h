@@ -1,0 +1,137 @@
+// kvq_internal.h -- shared device helpers and kernel launch interfaces of
+// libkvq (gfx950).  Not part of the public ABI (include/kvq.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// ---------------------------------------------------------------- dtypes
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+    return __uint_as_float(b << 16);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+// fp32 -> fp16, round to nearest even, subnormals kept (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Load element i of an array of dtype DT as fp32 (exact widening).
+template <int DT>
+__device__ __forceinline__ float load_as_f32(const void* p, int64_t i) {
+    if constexpr (DT == KVQ_F32) {
+        return static_cast<const float*>(p)[i];
+    } else if constexpr (DT == KVQ_F16) {
+        return f16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+    } else {
+        return bf16_bits_to_f32(static_cast<const uint16_t*>(p)[i]);
+    }
+}
+
+// Load 4 consecutive elements (index i is a multiple of 4).
+template <int DT>
+__device__ __forceinline__ void load4_as_f32(const void* p, int64_t i, float v[4]) {
+    if constexpr (DT == KVQ_F32) {
+        float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+        v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else {
+        uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+        if constexpr (DT == KVQ_F16) {
+            v[0] = f16_bits_to_f32(x.x & 0xFFFFu); v[1] = f16_bits_to_f32(x.x >> 16);
+            v[2] = f16_bits_to_f32(x.y & 0xFFFFu); v[3] = f16_bits_to_f32(x.y >> 16);
+        } else {
+            v[0] = bf16_bits_to_f32(x.x & 0xFFFFu); v[1] = bf16_bits_to_f32(x.x >> 16);
+            v[2] = bf16_bits_to_f32(x.y & 0xFFFFu); v[3] = bf16_bits_to_f32(x.y >> 16);
+        }
+    }
+}
+
+__host__ __device__ constexpr int dtype_bytes(int dt) { return dt == KVQ_F32 ? 4 : 2; }
+
+// Quantization constants of the specification (kvq.h): eps = 1e-5.
+constexpr float kEps = 1e-5f;
+
+// ---------------------------------------------------------------- launch args
+
+// Per-token group quantization (TOK_AFFINE / TOK_SYM4) or plain copy of rows
+// src [B][H][n][D] into slots [slot0, slot0 + n) of dst [B][H][cap][...].
+struct RowQuantArgs {
+    const void* src;
+    void* codes;
+    void* meta;
+    const float* bias;     // TOK_SYM4 centering [H][D] or nullptr
+    int B, H, n, D, cap, slot0;
+    int kind, bits, group, in_dtype;
+};
+hipError_t launch_row_quant(const RowQuantArgs& a, hipStream_t s);
+
+// KIVI per-channel: close `n_groups` groups made of the current residual
+// (r0 keys) followed by new keys, then store the remaining new keys in the
+// residual.
+struct ChannelQuantArgs {
+    const void* k_new;     // [B][H][n_new][D]
+    void* resid;           // [B][H][Gt][D]
+    void* codes;           // [B][H][cap][D*bits/8]
+    void* table;           // [B][H][rows][D][2] fp16
+    int32_t* k_row;        // [cap]
+    int B, H, D, cap, rows, Gt, bits, in_dtype;
+    int r0;                // residual fill before the append
+    int n_new;
+    int n_quant;           // coded slots before the append
+    int n_groups;          // groups closed by this append
+};
+hipError_t launch_channel_quant(const ChannelQuantArgs& a, hipStream_t s);
+
+hipError_t launch_fill_pos(int32_t* pos, int slot0, int first_pos, int n, hipStream_t s);
+
+// Decode attention.
+struct DecodeArgs {
+    const void* k_codes; const void* k_meta; const void* k_resid;
+    const void* v_codes; const void* v_meta;
+    const int32_t* k_row;
+    const void* q; float* out;
+    float* ws_o;           // [B][Hq][ns][D]
+    float* ws_ml;          // [B][Hq][ns][2]
+    int B, Hkv, Hq, D, cap, T, n_quant, Gt;
+    int k_kind, k_bits, k_group, v_kind, v_bits, v_group;
+    int in_dtype, q_dtype;
+    float scale_log2;      // sm_scale * log2(e)
+    int n_splits, split_len;
+};
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+size_t decode_workspace_bytes(int B, int Hq, int D, int cap);
+void decode_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
+
+// StreamingLLM compaction.
+struct EvictArgs {
+    // row buffers: src/dst base, bytes per slot row
+    const void* src[4]; void* dst[4]; int row_bytes[4]; int n_buf;
+    const int32_t* src_pos; int32_t* dst_pos;
+    const int32_t* src_row; int32_t* dst_row;      // KIVI_CH only (else nullptr)
+    const void* src_table; void* dst_table; int table_row_bytes; int rows;
+    const void* src_resid; void* dst_resid; size_t resid_bytes;
+    int BH, cap, n, sink, window, n_quant_new;
+};
+hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
+
+// SnapKV.
+struct SnapArgs {
+    const uint16_t* k; const uint16_t* v;
+    float* scores; int32_t* kept; uint16_t* k_out; uint16_t* v_out;
+    float* stats;          // [B][H][n_chunks][w][2]
+    int B, H, S, D, w, n_sink, budget, n_chunks;
+};
+size_t snapkv_ws_bytes(int B, int H, int S, int D, int w);
+hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s);
+hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_sink, int budget,
+                                int32_t* kept, hipStream_t s);
+hipError_t launch_snapkv_gather(const SnapArgs& a, hipStream_t s);
+
+hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
+
+}  // namespace kvq

@@ -1,0 +1,294 @@
+// snapkv.hip -- SnapKV prefill scoring, selection and gather (gfx950).
+//
+// "SnapKV -- Prefill Observation-Window Token Eviction", section "How it
+// works": the last w key rows act as queries; scores are the window mean of
+// softmax(K_w K^T / sqrt(D)) rows; the first n_sink positions are always
+// kept; the top (budget - n_sink) of the rest are added; kept rows are
+// gathered in their original order.
+//
+// The w x S logit block is a dense fp16 contraction, computed with
+// v_mfma_f32_32x32x16_f16 in two passes over the keys: pass 1 (stats) gives
+// each window row's max and exp-sum per chunk of 128 keys (keys as MFMA rows,
+// so the per-window-row reductions stay inside a lane), pass 2 (scores)
+// merges the chunk stats and recomputes the logits with window rows as MFMA
+// rows, so each key's sum over window rows stays inside a lane.  Recomputing
+// the block is cheaper than storing the w x S fp32 logits.
+//
+// Selection is a deterministic MSB-first radix select over order-preserving
+// 32-bit keys of the fp32 scores (4 passes of 8 bits, LDS histograms), then
+// ties at the threshold are resolved by ascending position with a block
+// prefix scan, and the kept set is emitted in ascending order by a second
+// scan.  No floating-point atomics are used, so results are reproducible.
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kChunk = 128;          // keys per block (4 waves x 32)
+constexpr int kMaxWindow = 128;
+
+__device__ __forceinline__ half8 load_half8(const uint16_t* p) {
+    return __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(p));
+}
+
+// acc row index (within a 32-row tile) of accumulator element v for lane half kh.
+__device__ __forceinline__ int acc_row(int v, int kh) { return 8 * (v >> 2) + 4 * kh + (v & 3); }
+
+__global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
+    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int kh = lane >> 5, l32 = lane & 31;
+    const int S = a.S, D = a.D;
+    const int wc = min(a.w, S);
+    const int row0 = S - wc;
+    const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
+    const float c = 1.4426950408889634f / sqrtf((float)D);
+    const int key_base = chunk * kChunk + wave * 32;
+    __shared__ float sm[4][kMaxWindow], sl[4][kMaxWindow];
+
+    const int key = key_base + l32;
+    for (int nt = 0; nt * 32 < wc; ++nt) {
+        const int wr = nt * 32 + l32;
+        floatx16 acc = {};
+        for (int ks = 0; ks < D; ks += 16) {
+            const int d0 = ks + kh * 8;
+            half8 A = {}, Bv = {};
+            if (key < S) A = load_half8(K + (int64_t)key * D + d0);
+            if (wr < wc) Bv = load_half8(K + (int64_t)(row0 + wr) * D + d0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bv, acc, 0, 0, 0);
+        }
+        // acc[v] = logit(key_base + acc_row(v, kh), window row wr)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            if (key_base + acc_row(v, kh) < S) mx = fmaxf(mx, acc[v] * c);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        float sum = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            if (key_base + acc_row(v, kh) < S) sum += exp2f(acc[v] * c - mx);
+        sum += __shfl_xor(sum, 32);
+        if (kh == 0 && wr < wc) { sm[wave][wr] = mx; sl[wave][wr] = sum; }
+    }
+    __syncthreads();
+    if (tid < wc) {
+        float M = -INFINITY;
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][tid]);
+        float L = 0.0f;
+        for (int w = 0; w < 4; ++w)
+            if (sm[w][tid] > -INFINITY) L += sl[w][tid] * exp2f(sm[w][tid] - M);
+        float* st = a.stats + ((((int64_t)b * a.H + h) * a.n_chunks + chunk) * wc + tid) * 2;
+        st[0] = M;
+        st[1] = L;
+    }
+}
+
+__global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
+    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int kh = lane >> 5, l32 = lane & 31;
+    const int S = a.S, D = a.D;
+    const int wc = min(a.w, S);
+    const int row0 = S - wc;
+    const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
+    const float c = 1.4426950408889634f / sqrtf((float)D);
+    __shared__ float Mrow[kMaxWindow], invL[kMaxWindow];
+    if (tid < wc) {
+        const float* st = a.stats + (((int64_t)b * a.H + h) * a.n_chunks * wc + tid) * 2;
+        float M = -INFINITY;
+        for (int ch = 0; ch < a.n_chunks; ++ch) M = fmaxf(M, st[(int64_t)ch * wc * 2]);
+        float L = 0.0f;
+        for (int ch = 0; ch < a.n_chunks; ++ch)
+            L += st[(int64_t)ch * wc * 2 + 1] * exp2f(st[(int64_t)ch * wc * 2] - M);
+        Mrow[tid] = M;
+        invL[tid] = 1.0f / L;
+    }
+    __syncthreads();
+    const int key = chunk * kChunk + wave * 32 + l32;
+    float score = 0.0f;
+    for (int mt = 0; mt * 32 < wc; ++mt) {
+        const int wr = mt * 32 + l32;
+        floatx16 acc = {};
+        for (int ks = 0; ks < D; ks += 16) {
+            const int d0 = ks + kh * 8;
+            half8 A = {}, Bv = {};
+            if (wr < wc) A = load_half8(K + (int64_t)(row0 + wr) * D + d0);
+            if (key < S) Bv = load_half8(K + (int64_t)key * D + d0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bv, acc, 0, 0, 0);
+        }
+        // acc[v] = logit(window row mt*32 + acc_row(v, kh), key)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = mt * 32 + acc_row(v, kh);
+            if (i < wc) score += exp2f(acc[v] * c - Mrow[i]) * invL[i];
+        }
+    }
+    score += __shfl_xor(score, 32);
+    if (kh == 0 && key < S)
+        a.scores[((int64_t)b * a.H + h) * S + key] = score / (float)wc;
+}
+
+// ---------------------------------------------------------------- selection
+
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;                 // -0 ranks as +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive scan of one value per thread over a block of nthreads (<= 1024)
+// threads; returns the inclusive prefix, and *total the block sum.
+__device__ uint32_t block_scan(uint32_t v, uint32_t* lds16, uint32_t* total) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) lds16[wave] = x;
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t run = 0;
+        for (int w = 0; w < nw; ++w) { const uint32_t t = lds16[w]; lds16[w] = run; run += t; }
+        lds16[16] = run;
+    }
+    __syncthreads();
+    const uint32_t res = x + lds16[wave];
+    *total = lds16[16];
+    __syncthreads();
+    return res;
+}
+
+__global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, int S, int n_sink,
+                                                           int budget, int32_t* kept_all) {
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int n_keep = min(budget, S);
+    const int n_s = min(n_sink, n_keep);
+    const int k = n_keep - n_s;
+    const int C = S - n_s;
+    const float* sc = scores + bh * S;
+    int32_t* kept = kept_all + bh * n_keep;
+    if (k == C || k == 0) {                       // all candidates, or sinks only
+        for (int i = tid; i < n_keep; i += blockDim.x) kept[i] = i;
+        return;
+    }
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t lds16[17];
+    __shared__ uint32_t s_prefix, s_krem;
+    uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) hist[tid] = 0;
+        __syncthreads();
+        for (int j = n_s + tid; j < S; j += blockDim.x) {
+            const uint32_t key = order_key(sc[j]);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        // bins from the top: thread t holds bin 255 - t
+        const uint32_t cnt = tid < 256 ? hist[255 - tid] : 0u;
+        uint32_t tot;
+        const uint32_t incl = block_scan(cnt, lds16, &tot);
+        if (tid < 256 && incl - cnt < krem && incl >= krem) {
+            s_prefix = prefix | ((uint32_t)(255 - tid) << shift);
+            s_krem = krem - (incl - cnt);
+        }
+        __syncthreads();
+        prefix = s_prefix;
+        krem = s_krem;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    const uint32_t tau = prefix;   // k-th largest key; krem of the keys equal to tau are taken
+    const int per = (S + (int)blockDim.x - 1) / (int)blockDim.x;
+    const int j0 = min(S, tid * per), j1 = min(S, j0 + per);
+    uint32_t nties = 0;
+    for (int j = max(j0, n_s); j < j1; ++j) nties += (order_key(sc[j]) == tau);
+    uint32_t tot;
+    uint32_t tie_rank = block_scan(nties, lds16, &tot) - nties;
+    uint32_t nsel = 0;
+    for (int j = j0; j < j1; ++j) {
+        bool sel;
+        if (j < n_s) sel = true;
+        else {
+            const uint32_t key = order_key(sc[j]);
+            if (key > tau) sel = true;
+            else if (key == tau) sel = (tie_rank++ < krem);
+            else sel = false;
+        }
+        nsel += sel;
+    }
+    uint32_t out = block_scan(nsel, lds16, &tot) - nsel;
+    tie_rank -= nties;
+    for (int j = j0; j < j1; ++j) {
+        bool sel;
+        if (j < n_s) sel = true;
+        else {
+            const uint32_t key = order_key(sc[j]);
+            if (key > tau) sel = true;
+            else if (key == tau) sel = (tie_rank++ < krem);
+            else sel = false;
+        }
+        if (sel && out < (uint32_t)n_keep) kept[out++] = j;
+    }
+}
+
+__global__ __launch_bounds__(256) void snap_gather_kernel(SnapArgs a, int n_keep) {
+    const int upr = a.D / 8;                      // 16-byte units per fp16 row
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rows = (int64_t)a.B * a.H * n_keep;
+    if (idx >= rows * upr) return;
+    const int64_t r = idx / upr;
+    const int u = (int)(idx - r * upr);
+    const int64_t bh = r / n_keep;
+    const int j = a.kept[r];
+    if (j < 0 || j >= a.S) return;
+    const int64_t src = bh * a.S + j;
+    const uint4* ks = reinterpret_cast<const uint4*>(a.k);
+    const uint4* vs = reinterpret_cast<const uint4*>(a.v);
+    reinterpret_cast<uint4*>(a.k_out)[r * upr + u] = ks[src * upr + u];
+    reinterpret_cast<uint4*>(a.v_out)[r * upr + u] = vs[src * upr + u];
+}
+
+}  // namespace
+
+size_t snapkv_ws_bytes(int B, int H, int S, int D, int w) {
+    (void)D;
+    const int wc = w < S ? w : S;
+    const int n_chunks = (S + kChunk - 1) / kChunk;
+    size_t stats = (size_t)B * H * n_chunks * wc * 2 * sizeof(float);
+    stats = (stats + 255) & ~(size_t)255;
+    return stats + (size_t)B * H * S * sizeof(float);
+}
+
+hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_chunks, (unsigned)a.H, (unsigned)a.B);
+    hipLaunchKernelGGL(snap_stats_kernel, grid, dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(snap_scores_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_sink, int budget,
+                                int32_t* kept, hipStream_t s) {
+    hipLaunchKernelGGL(snap_select_kernel, dim3((unsigned)(B * H)), dim3(1024), 0, s,
+                       scores, S, n_sink, budget, kept);
+    return hipGetLastError();
+}
+
+hipError_t launch_snapkv_gather(const SnapArgs& a, hipStream_t s) {
+    const int n_keep = a.budget < a.S ? a.budget : a.S;
+    const int64_t total = (int64_t)a.B * a.H * n_keep * (a.D / 8);
+    hipLaunchKernelGGL(snap_gather_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a, n_keep);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,256 @@
+/*
+ * kvq.h -- C ABI of libkvq: decode-time attention over a compressed KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Four operations make up the path:
+ *   kvq_quantize_append   quantize-on-write of new K/V rows
+ *   kvq_decode_attention  fused dequantize + QK^T + softmax + PV for one query
+ *                         token per sequence, reading the packed cache
+ *   kvq_evict_streaming   StreamingLLM sink + window compaction
+ *   kvq_snapkv_select     SnapKV prefill scoring, selection and gather
+ *
+ * Sources the operations follow (cited by page title and section):
+ *   [P1] "StreamingLLM + KIVI -- long-context decode without growing the KV
+ *        cache" (posttrainllm.com).
+ *   [P2] "SnapKV -- Prefill Observation-Window Token Eviction" (veloxquant-mlx).
+ *   [P3] "kv-cache: optional per-channel K-cache mean-centering for Q4_0"
+ *        (llama.cpp pull request #51).
+ *   [P4] "Low-bit KV caches on MLX: what exists and what is missing".
+ *
+ * Conventions for every call:
+ *   - Pointers named in a layout comment as device memory are device pointers
+ *     on the current HIP device; the layout/cache/size structs themselves are
+ *     host memory.  The caller owns all memory; the library allocates nothing
+ *     and keeps no state besides cached device properties.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and never synchronized; outputs are valid once the stream reaches them.
+ *   - Arguments are validated on the host before anything is enqueued.  On an
+ *     error nothing is launched and caches are left unchanged.  Launch
+ *     failures are reported as KVQ_ERR_HIP.
+ *   - Every device pointer must be 16-byte aligned (KVQ_ERR_ALIGNMENT).
+ *   - Lengths are uniform over the batch and follow from the calls, so no
+ *     device-to-host read-back is ever needed: the cache struct's counters
+ *     are host-side and updated when work is enqueued.
+ *   - Calls on one cache must be ordered (same stream or explicit events).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_VERSION 1
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_NOOP = 1,               /* nothing to do (eviction below the cap) */
+    KVQ_ERR_INVALID_ARG = -1,
+    KVQ_ERR_UNSUPPORTED = -2,   /* valid request outside what the kernels implement */
+    KVQ_ERR_CAPACITY = -3,      /* append past the cache capacity */
+    KVQ_ERR_ALIGNMENT = -4,
+    KVQ_ERR_WORKSPACE = -5,     /* workspace missing or too small */
+    KVQ_ERR_HIP = -6            /* a HIP launch or runtime call failed */
+} kvq_status;
+
+/* Element types of K/V inputs, queries and PLAIN storage. */
+typedef enum { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 } kvq_dtype;
+
+/* Storage kinds.
+ *
+ * KVQ_PLAIN      values stored as given, in the layout's in_dtype.
+ * KVQ_KIVI_CH    (K only) KIVI per-channel keys ([P1] "KIVI"; [P4] s.3):
+ *                one (scale, zero) per (batch, kv-head, channel) for each
+ *                closed group of k_group consecutive tokens (group = append
+ *                index / k_group).  Keys of the open group wait in a
+ *                full-precision residual buffer and are attended from it.
+ * KVQ_TOK_AFFINE per-token asymmetric groups of `group` channels along
+ *                head_dim ([P1] "Affine quantisation formula" per token for V;
+ *                [P4] s.1 mx.quantize group layout for K and V).
+ * KVQ_TOK_SYM4   (K only) symmetric 4-bit blocks of 32 channels with one fp16
+ *                scale (the Q4_0 shape, [P3] "The idea"), optionally after
+ *                subtracting a fixed per-(kv-head, channel) mean.
+ */
+typedef enum { KVQ_PLAIN = 0, KVQ_KIVI_CH = 1, KVQ_TOK_AFFINE = 2, KVQ_TOK_SYM4 = 3 } kvq_kind;
+
+/* layout.flags */
+#define KVQ_CENTER_K         0x1  /* subtract cache.k_bias before quantizing K (TOK_SYM4 only) */
+#define KVQ_TEST_CENTER_ANY  0x2  /* test seam: also allow KVQ_CENTER_K with PLAIN keys */
+
+/* Quantization arithmetic (bit-exact specification, fp32, IEEE round to
+ * nearest even, no fused multiply-add):
+ *   affine slice x[0..n):  range = max - min;  s = max(1e-5, range / (2^bits - 1));
+ *       scale = fp16(s), zero = fp16(min);  code u = clamp(rint((x - zero) / scale), 0, 2^bits-1)
+ *       where zero and scale are the stored fp16 values widened to fp32.
+ *       Dequantized value: u * scale + zero.            ([P1] formula, eps 1e-5)
+ *   symmetric block of 32: x' = x - bias; d = fp16(max(1e-5, max|x'| / 7));
+ *       code u = clamp(rint(x' / d), -8, 7) + 8;  value (u - 8) * d.
+ * Codes are stored packed: 8-bit codes one per byte; 4-bit codes two per
+ * byte with element 2i in the low nibble of byte i.
+ */
+typedef struct kvq_layout {
+    int32_t batch;        /* B >= 1 */
+    int32_t n_kv_heads;   /* Hkv >= 1 */
+    int32_t head_dim;     /* D in {32, 64, 128} */
+    int32_t capacity;     /* slots per (batch, kv-head), >= 1 */
+    int32_t k_kind;       /* kvq_kind */
+    int32_t k_bits;       /* 4 or 8 (KIVI_CH, TOK_AFFINE); 4 (TOK_SYM4); ignored for PLAIN */
+    int32_t k_group;      /* KIVI_CH: tokens per group (8..128, power of two);
+                             TOK_AFFINE: channels per group (32, 64 or 128, dividing D);
+                             TOK_SYM4: must be 32; PLAIN: ignored */
+    int32_t v_kind;       /* KVQ_PLAIN or KVQ_TOK_AFFINE */
+    int32_t v_bits;       /* 4 or 8 (TOK_AFFINE) */
+    int32_t v_group;      /* channels per group (32, 64 or 128, dividing D) */
+    int32_t in_dtype;     /* kvq_dtype of appended K/V, PLAIN storage and the KIVI residual */
+    int32_t flags;        /* KVQ_CENTER_K | KVQ_TEST_CENTER_ANY */
+} kvq_layout;
+
+/* One layer's cache.  Device buffers (sizes from kvq_cache_sizes):
+ *   k_codes  coded K:  [B][Hkv][capacity][D*k_bits/8] bytes
+ *            PLAIN K:  [B][Hkv][capacity][D] in_dtype
+ *   k_meta   TOK_AFFINE: [B][Hkv][capacity][D/k_group][2] fp16 (scale, zero)
+ *            TOK_SYM4:   [B][Hkv][capacity][D/32] fp16 scales
+ *            KIVI_CH:    [B][Hkv][k_table_rows][D][2] fp16 (scale, zero) table,
+ *                        one row per live token group, rows in group order
+ *            PLAIN: unused (may be NULL)
+ *   k_resid  KIVI_CH only: [B][Hkv][k_group][D] in_dtype; residual row i holds
+ *            the key of slot n_quant + i
+ *   v_codes, v_meta  as for K with v_kind / v_bits / v_group
+ *   pos      [capacity] int32 absolute position of each slot (shared over
+ *            batch and heads; [P2]: positions stay the true positions)
+ *   k_row    KIVI_CH only: [capacity] int32 table row of each coded slot
+ *   k_bias   [Hkv][D] fp32 mean subtracted from K before TOK_SYM4
+ *            quantization when layout.flags has KVQ_CENTER_K ([P3]); else NULL
+ * Host counters (maintained by the library; zero them for an empty cache):
+ *   n_stored  slots in use, n_quant  slots whose K is coded (KIVI_CH: the
+ *   rest are in the residual; other kinds: == n_stored), next_pos  position
+ *   of the next appended token (generation counter, [P1] "stored count" vs
+ *   current length), n_head  length of the slot prefix whose positions equal
+ *   their slot index.
+ */
+typedef struct kvq_cache {
+    void* k_codes;
+    void* k_meta;
+    void* k_resid;
+    void* v_codes;
+    void* v_meta;
+    int32_t* pos;
+    int32_t* k_row;
+    const float* k_bias;
+    int32_t n_stored;
+    int32_t n_quant;
+    int32_t next_pos;
+    int32_t n_head;
+} kvq_cache;
+
+typedef struct kvq_sizes {
+    size_t k_codes, k_meta, k_resid, v_codes, v_meta, pos, k_row;  /* bytes */
+    int32_t k_table_rows;   /* KIVI_CH table rows (capacity / k_group + 3), else 0 */
+    int32_t reserved;
+} kvq_sizes;
+
+/* Validate a layout and report the byte size of every cache buffer (host only). */
+kvq_status kvq_cache_sizes(const kvq_layout* layout, kvq_sizes* out);
+
+/* Zero the host counters of a cache (host only). */
+kvq_status kvq_cache_reset(kvq_cache* cache);
+
+/* Quantize-on-write ([P1] "KIVI": K per channel, V per token; [P4] s.1 and
+ * s.3).  Appends n_new tokens per (batch, kv-head) at slots n_stored ..
+ * n_stored+n_new-1 with positions next_pos ...  V rows (and TOK_AFFINE /
+ * TOK_SYM4 / PLAIN K rows) are quantized immediately and never change.
+ * KIVI_CH keys enter the residual; every time the residual reaches k_group
+ * keys the group closes: per channel its min/max over exactly those keys
+ * gives (scale, zero), its codes are written to k_codes and one table row is
+ * appended.  Appending in chunks gives the same bytes as appending one token
+ * at a time.
+ *   k_new, v_new: device [B][Hkv][n_new][D] in_dtype.  n_new >= 1.
+ * Errors: KVQ_ERR_CAPACITY if n_stored + n_new > capacity (nothing evicts
+ * automatically; [P1] "Implementation": append, then evict);
+ * KVQ_ERR_UNSUPPORTED for KVQ_CENTER_K on a kind other than TOK_SYM4 (or
+ * PLAIN with KVQ_TEST_CENTER_ANY) -- the Q4_0-only gate of [P3].           */
+kvq_status kvq_quantize_append(const kvq_layout* layout, kvq_cache* cache,
+                               const void* k_new, const void* v_new,
+                               int32_t n_new, void* stream);
+
+/* Workspace bytes kvq_decode_attention needs for this layout (any fill). */
+size_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t n_q_heads);
+
+/* Decode attention for one query token per sequence ([P4] s.1: scores
+ * against the packed keys, softmax, weighted sum of the packed values; no
+ * full-precision copy of the cache is made; [P4] s.5: split over the token
+ * axis for long caches).
+ *   out[b][hq][:] = sum_t softmax_t(sm_scale * q[b][hq] . k_t) v_t
+ * over the n_stored slots of kv-head hk = hq / (n_q_heads / Hkv), where k_t,
+ * v_t are the dequantized entries (KIVI_CH residual keys as stored).
+ * Centered keys are attended as stored: the per-row constant q.k_bar does not
+ * change the softmax ([P3] "Why this is safe").
+ *   q: device [B][n_q_heads][D] of q_dtype; out: device [B][n_q_heads][D] fp32.
+ *   sm_scale <= 0 selects 1/sqrt(D).  n_q_heads must be a multiple of Hkv with
+ *   at most 8 query heads per kv-head.
+ *   ws: device workspace of at least kvq_decode_workspace_bytes bytes.
+ * An empty cache (n_stored == 0) writes zeros.                              */
+kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache,
+                                const void* q, int32_t q_dtype, int32_t n_q_heads,
+                                float sm_scale, float* out,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* StreamingLLM compaction ([P1] "Implementation", "StreamingLLM"): when
+ * n_stored > sink + window, copy slots [0, sink) and the last `window` slots,
+ * in order, from src into dst (out-of-place; dst has the same layout and its
+ * own buffers, which must not overlap src's).  Codes, metadata, positions and
+ * residual keys are copied bit-for-bit; nothing is re-quantized.  KIVI_CH
+ * table rows no kept slot refers to are dropped and k_row is renumbered
+ * ([P1]: per-channel K scales are not sliced by eviction).
+ * Returns KVQ_NOOP (nothing enqueued, dst untouched) when n_stored <= sink +
+ * window.  KIVI_CH requires window >= k_group (the open group is never
+ * evicted) and that the kept positions form at most two runs (the sink
+ * prefix and one run of consecutive positions): KVQ_ERR_UNSUPPORTED otherwise.
+ * On success dst's counters are set (n_stored = sink + window).            */
+kvq_status kvq_evict_streaming(const kvq_layout* layout, const kvq_cache* src,
+                               kvq_cache* dst, int32_t sink, int32_t window,
+                               void* stream);
+
+/* Workspace bytes for kvq_snapkv_select / kvq_snapkv_select_from_scores. */
+size_t kvq_snapkv_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t seq_len,
+                                  int32_t head_dim, int32_t obs_window);
+
+/* SnapKV prefill selection ([P2] "How it works"):
+ *   1. scores[j] = mean over the last w' = min(obs_window, S) key rows i of
+ *      softmax_j(K[i] . K[j] / sqrt(D))  (keys stand in for queries; no mask)
+ *   2. the first n_s = min(n_sink, n_keep) positions are always kept
+ *   3. the top n_keep - n_s of the other positions by score are added
+ *      (equal scores: lower position first), n_keep = min(budget, S)
+ *   4. kept positions in ascending order; K/V rows gathered in that order.
+ *   k, v:        device [B][Hkv][S][D] fp16
+ *   scores:      device [B][Hkv][S] fp32 output, or NULL (kept in workspace)
+ *   kept:        device [B][Hkv][n_keep] int32 output
+ *   k_out,v_out: device [B][Hkv][n_keep][D] fp16 outputs
+ * obs_window and budget >= 1, n_sink >= 0; D in {32, 64, 128}; obs_window <= 128.
+ * Clamps (obs_window > S, budget >= S, n_sink > budget) are not errors.     */
+kvq_status kvq_snapkv_select(const void* k, const void* v, int32_t batch,
+                             int32_t n_kv_heads, int32_t seq_len, int32_t head_dim,
+                             int32_t obs_window, int32_t n_sink, int32_t budget,
+                             float* scores, int32_t* kept, void* k_out, void* v_out,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* Steps 2-4 of kvq_snapkv_select without the gather, from given scores
+ * [B][Hkv][S] fp32 (finite; -0 ranks as +0).  kept: [B][Hkv][n_keep].     */
+kvq_status kvq_snapkv_select_from_scores(const float* scores, int32_t batch,
+                                         int32_t n_kv_heads, int32_t seq_len,
+                                         int32_t n_sink, int32_t budget,
+                                         int32_t* kept, void* stream);
+
+/* Static description of a status code. */
+const char* kvq_status_string(kvq_status status);
+
+/* KVQ_VERSION of the built library. */
+int32_t kvq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,220 @@
+"""Host-side tests of the libkvq C ABI (no GPU needed).
+
+Validation runs before anything is enqueued, so invalid calls can be made
+with fake (never dereferenced) device pointers on a machine without a GPU.
+"""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+import evicted_kv_cache_amd as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # 16-byte aligned, never dereferenced by validation
+MIS = 0x10004           # misaligned
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"kvq_quantize_append", "kvq_decode_attention", "kvq_evict_streaming",
+            "kvq_snapkv_select"} <= set(names)
+    lib = K.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(K.EXPORTS)
+    assert lib.kvq_version() == 1
+
+
+def test_status_strings():
+    for code in (0, 1, -1, -2, -3, -4, -5, -6):
+        assert K.status_string(code) and K.status_string(code) != "unknown status"
+    assert K.status_string(-99) == "unknown status"
+
+
+def c5_layout(**kw):
+    base = dict(batch=64, n_kv_heads=8, head_dim=128, capacity=32768, k_kind="tok_affine",
+                k_bits=4, k_group=64, v_kind="tok_affine", v_bits=4, v_group=64, in_dtype="bf16")
+    base.update(kw)
+    return K.Layout(**base)
+
+
+def test_cache_sizes_headline_layout():
+    s = K.kvq_cache_sizes(c5_layout())
+    # 4-bit codes: 64 B per token-head; g64 fp16 (scale, zero): 8 B per token-head
+    assert s.k_codes == s.v_codes == 64 * 8 * 32768 * 64 == 2 ** 30
+    assert s.k_meta == s.v_meta == 64 * 8 * 32768 * 8 == 2 ** 27
+    elems = 64 * 8 * 32768 * 128
+    assert (s.k_codes + s.k_meta) * 8 / elems == 4.5        # P4: 4.5 bits/elt at g64
+    s32 = K.kvq_cache_sizes(c5_layout(k_group=32))
+    assert (s32.k_codes + s32.k_meta) * 8 / elems == 5.0    # P4: 5.0 bits/elt at g32
+
+
+def test_cache_sizes_match_tinygpt_int8_value_bytes():
+    """P1 cache-bytes table at T=500 (12 layers x 8 heads x 32 dim): int8 values
+    cost 1 B/element and per-token fp16 scale+zero 2 x 2 B per token-head;
+    with layers laid out as batch, kvq's per-token int8 V has exactly those bytes."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "p1_streaming_kivi.json")))
+    t, b = g["tinygpt"], g["int8_kivi_bytes"]
+    L = K.Layout(batch=t["layers"], n_kv_heads=t["heads"], head_dim=t["head_dim"],
+                 capacity=t["T"], k_kind="kivi_ch", k_bits=8, k_group=32,
+                 v_kind="tok_affine", v_bits=8, v_group=t["head_dim"], in_dtype="f32")
+    s = K.kvq_cache_sizes(L)
+    assert s.v_codes == b["v_codes"]
+    assert s.v_meta == 2 * b["v_scales_each"]
+    assert s.k_codes == b["k_codes"]
+    # P1's K keeps one (scale, zero) per channel over all of T; kvq freezes one
+    # per 32-token group: table rows = capacity / 32 + 3 (two runs of slots)
+    assert s.k_table_rows == 500 // 32 + 3
+    # P1's printed total for its own layout (whole-T K scales) is consistent
+    assert b["k_codes"] + b["v_codes"] + 2 * b["k_scales_each"] + 2 * b["v_scales_each"] == b["total"]
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), K.KVQ_ERR_UNSUPPORTED),
+    (dict(head_dim=0), K.KVQ_ERR_INVALID_ARG),
+    (dict(batch=0), K.KVQ_ERR_INVALID_ARG),
+    (dict(k_bits=3), K.KVQ_ERR_UNSUPPORTED),
+    (dict(k_group=48), K.KVQ_ERR_UNSUPPORTED),
+    (dict(v_kind="tok_sym4"), K.KVQ_ERR_UNSUPPORTED),
+    (dict(k_kind="kivi_ch", k_group=12), K.KVQ_ERR_UNSUPPORTED),
+    (dict(k_kind="tok_sym4", k_group=64), K.KVQ_ERR_UNSUPPORTED),
+    # P3 gate: centering only for the symmetric 4-bit K format
+    (dict(flags=K.KVQ_CENTER_K), K.KVQ_ERR_UNSUPPORTED),
+    (dict(k_kind="plain", flags=K.KVQ_CENTER_K), K.KVQ_ERR_UNSUPPORTED),
+    (dict(k_kind="plain", flags=K.KVQ_CENTER_K | K.KVQ_TEST_CENTER_ANY), K.KVQ_ERR_UNSUPPORTED),
+    (dict(flags=0x100), K.KVQ_ERR_INVALID_ARG),
+])
+def test_layout_validation(kw, code):
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_cache_sizes(c5_layout(**kw))
+    assert e.value.status == code
+
+
+def test_centering_gate_accepts_sym4_and_test_seam():
+    K.kvq_cache_sizes(c5_layout(k_kind="tok_sym4", k_group=32, flags=K.KVQ_CENTER_K))
+    K.kvq_cache_sizes(c5_layout(k_kind="plain", in_dtype="f32",
+                                flags=K.KVQ_CENTER_K | K.KVQ_TEST_CENTER_ANY))
+
+
+def fake_cache(L, n_stored=0, n_quant=None, misalign=None, base=FAKE):
+    s = K.kvq_cache_sizes(L)
+    ptr = {n: (base + (1 << 32) * i if getattr(s, n) else None)
+           for i, n in enumerate(("k_codes", "k_meta", "k_resid", "v_codes", "v_meta", "pos", "k_row"))}
+    if misalign:
+        ptr[misalign] = MIS
+    c = K.c_cache(ptr["k_codes"], ptr["k_meta"], ptr["k_resid"], ptr["v_codes"], ptr["v_meta"],
+                  ptr["pos"], ptr["k_row"], None, n_stored,
+                  n_stored if n_quant is None else n_quant, n_stored, n_stored)
+    return c
+
+
+def call_append(L, c, n_new, k=FAKE, v=FAKE):
+    cl = L.c()
+    return K.lib().kvq_quantize_append(ctypes.byref(cl), ctypes.byref(c), k, v, n_new, None)
+
+
+def test_append_validation_without_gpu():
+    L = c5_layout(batch=1, capacity=100)
+    c = fake_cache(L, n_stored=90)
+    assert call_append(L, c, 11) == K.KVQ_ERR_CAPACITY          # nothing auto-evicts
+    assert c.n_stored == 90                                      # cache unchanged on error
+    assert call_append(L, c, 0) == K.KVQ_ERR_INVALID_ARG
+    assert call_append(L, c, 1, k=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert call_append(L, c, 1, k=0) == K.KVQ_ERR_INVALID_ARG
+    bad = fake_cache(L, n_stored=5, misalign="v_meta")
+    assert call_append(L, bad, 1) == K.KVQ_ERR_ALIGNMENT
+    missing = fake_cache(L, n_stored=5)
+    missing.k_meta = None
+    assert call_append(L, missing, 1) == K.KVQ_ERR_INVALID_ARG
+    # counters must be consistent
+    inc = fake_cache(L, n_stored=5, n_quant=3)
+    assert call_append(L, inc, 1) == K.KVQ_ERR_INVALID_ARG
+    # centering without a bias pointer
+    Ls = c5_layout(batch=1, capacity=100, k_kind="tok_sym4", k_group=32, flags=K.KVQ_CENTER_K)
+    assert call_append(Ls, fake_cache(Ls), 1) == K.KVQ_ERR_INVALID_ARG
+
+
+def test_kivi_residual_counter_validation():
+    L = c5_layout(batch=1, capacity=100, k_kind="kivi_ch", k_group=32)
+    assert call_append(L, fake_cache(L, n_stored=40, n_quant=0), 1) == K.KVQ_ERR_INVALID_ARG
+
+
+def call_decode(L, c, hq, ws=FAKE, ws_bytes=1 << 30, q=FAKE, out=FAKE, qdt=K.KVQ_BF16, scale=0.0):
+    cl = L.c()
+    return K.lib().kvq_decode_attention(ctypes.byref(cl), ctypes.byref(c), q, qdt, hq,
+                                        ctypes.c_float(scale), out, ws, ws_bytes, None)
+
+
+def test_decode_validation_without_gpu():
+    L = c5_layout(batch=2, capacity=1000)
+    c = fake_cache(L, n_stored=500)
+    assert call_decode(L, c, 12) == K.KVQ_ERR_INVALID_ARG        # not a multiple of Hkv
+    assert call_decode(L, c, 8 * 9) == K.KVQ_ERR_UNSUPPORTED     # > 8 q-heads per kv-head
+    assert call_decode(L, c, 32, ws=0) == K.KVQ_ERR_WORKSPACE
+    need = K.kvq_decode_workspace_bytes(L, 32)
+    assert need > 0
+    assert call_decode(L, c, 32, ws_bytes=need - 1) == K.KVQ_ERR_WORKSPACE
+    assert call_decode(L, c, 32, q=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert call_decode(L, c, 32, qdt=7) == K.KVQ_ERR_INVALID_ARG
+    assert call_decode(L, c, 32, scale=float("nan")) == K.KVQ_ERR_INVALID_ARG
+
+
+def call_evict(L, src, dst, sink, window):
+    cl = L.c()
+    return K.lib().kvq_evict_streaming(ctypes.byref(cl), ctypes.byref(src), ctypes.byref(dst),
+                                       sink, window, None)
+
+
+def test_evict_validation_without_gpu():
+    L = c5_layout(batch=1, capacity=300, k_kind="kivi_ch", k_group=32)
+    src = fake_cache(L, n_stored=280, n_quant=256)
+    dst = fake_cache(L, base=FAKE + (1 << 40))
+    # below the cap: NOOP, nothing enqueued (no GPU call happens)
+    assert call_evict(L, src, dst, 4, 276) == K.KVQ_NOOP
+    assert dst.n_stored == 0
+    # out-of-place: dst must not alias src
+    assert call_evict(L, src, src, 4, 256) == K.KVQ_ERR_INVALID_ARG
+    # the open K group must stay: window >= k_group
+    assert call_evict(L, src, dst, 4, 16) == K.KVQ_ERR_INVALID_ARG
+    assert call_evict(L, src, dst, -1, 256) == K.KVQ_ERR_INVALID_ARG
+    # kept positions may not form a third run: after a first eviction the
+    # sink prefix can only shrink and the window must stay past it
+    src.n_head = 4
+    assert call_evict(L, src, dst, 8, 200) == K.KVQ_ERR_UNSUPPORTED
+    assert call_evict(L, src, dst, 2, 277) == K.KVQ_ERR_UNSUPPORTED   # window reaches slot 3 < n_head
+
+
+def test_snapkv_validation_without_gpu():
+    lib = K.lib()
+    ws = K.kvq_snapkv_workspace_bytes(1, 8, 8192, 128, 32)
+    assert ws > 8 * 8192 * 4
+
+    def call(B=1, H=8, S=8192, D=128, w=32, sink=4, budget=512, ws_bytes=ws, k=FAKE):
+        return lib.kvq_snapkv_select(k, FAKE, B, H, S, D, w, sink, budget, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, ws_bytes, None)
+    assert call(D=96) == K.KVQ_ERR_UNSUPPORTED
+    assert call(w=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(budget=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(sink=-1) == K.KVQ_ERR_INVALID_ARG
+    assert call(w=200) == K.KVQ_ERR_UNSUPPORTED
+    assert call(S=100, w=200, ws_bytes=0) == K.KVQ_ERR_WORKSPACE  # w clamps to S: allowed, ws checked
+    assert call(ws_bytes=ws - 1) == K.KVQ_ERR_WORKSPACE
+    assert call(k=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert lib.kvq_snapkv_select_from_scores(MIS, 1, 8, 100, 4, 10, FAKE, None) == K.KVQ_ERR_ALIGNMENT
+    assert lib.kvq_snapkv_select_from_scores(FAKE, 1, 8, 0, 4, 10, FAKE, None) == K.KVQ_ERR_INVALID_ARG
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(K, "_lib", None)
+    with pytest.raises(ImportError):
+        K.lib()

@@ -1,0 +1,301 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Codes, scales, zeros, positions, table rows and residual keys must match
+bit-for-bit; attention outputs within 2e-3 of the fp64 oracle, measured as
+max |o - o_ref| / max_d |o_ref| per (batch, query-head) row over the same
+dequantized cache.  Sizes span several tiles and splits with ragged tails.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import evicted_kv_cache_amd as K
+import synth
+from oracle.cache import OracleCache
+
+from _gpu import (DEV, assert_same_state, attn_err, layouts, say, to_dev)
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def gen(w, B, H, T, Hq=None):
+    """Seeded K, V [B][H][T][D] and q [B][Hq][D] in the workload dtype."""
+    Hq = Hq or w.n_q_heads
+    D = w.head_dim
+    np_dt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+    k = np.empty((B, H, T, D), np_dt)
+    v = np.empty((B, H, T, D), np_dt)
+    q = np.empty((B, Hq, D), np_dt)
+    g = Hq // H
+    ww = dataclasses.replace(w, n_q_heads=Hq, n_kv_heads=H)
+    for b in range(B):
+        for h in range(H):
+            kk, vv, qq = synth.slice_cast(ww, b, h, T)
+            k[b, h], v[b, h], q[b, h * g:(h + 1) * g] = kk, vv, qq
+    return k, v, q
+
+
+def build_pair(pl, ol, k, v, dtype, chunks=None, k_bias=None):
+    """Append the same chunks to a product and an oracle cache."""
+    c = K.Cache(pl, k_bias=None if k_bias is None else torch.from_numpy(k_bias))
+    o = OracleCache(ol, k_bias=k_bias)
+    T = k.shape[2]
+    chunks = chunks or [(0, T)]
+    for s, e in chunks:
+        kd = to_dev(np.ascontiguousarray(k[:, :, s:e]), dtype)
+        vd = to_dev(np.ascontiguousarray(v[:, :, s:e]), dtype)
+        K.kvq_quantize_append(pl, c, kd, vd)
+        o.append(k[:, :, s:e], v[:, :, s:e])
+    torch.cuda.synchronize()
+    return c, o
+
+
+def check_decode(pl, c, o, q, qdt, sm_scale=0.0, tol=TOL):
+    out = K.kvq_decode_attention(pl, c, to_dev(q, qdt), sm_scale=sm_scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = o.decode(q, qdt, sm_scale)
+    err = attn_err(got, ref)
+    assert np.all(np.isfinite(got))
+    assert err <= tol, err
+    return got, err
+
+
+# ---------------------------------------------------------------- per format
+
+CASES = {
+    # mlx-style 4-bit affine g64 K and V, bf16 (headline format), 2 x 8 heads
+    "affine4_g64_bf16": dict(w="affine4_g64", B=2, H=8, T=1500,
+                             lay=dict(k_kind="tok_affine", k_bits=4, k_group=64, v_kind="tok_affine",
+                                      v_bits=4, v_group=64, in_dtype="bf16"),
+                             chunks=[(0, 1), (1, 700), (700, 1500)]),
+    # KIVI int4, per-channel K over 32-token groups + residual, outlier channels
+    "kivi4_llama3b": dict(w="llama3b_kivi_int4", B=1, H=8, T=1000,
+                          lay=dict(k_kind="kivi_ch", k_bits=4, k_group=32, v_kind="tok_affine",
+                                   v_bits=4, v_group=32, in_dtype="f16"),
+                          chunks=[(0, 1), (1, 300), (300, 1000)]),
+    # KIVI int8, tinygpt shape, fp32
+    "kivi8_tiny": dict(w="kivi_int8_tiny", B=1, H=8, T=450,
+                       lay=dict(k_kind="kivi_ch", k_bits=8, k_group=32, v_kind="tok_affine",
+                                v_bits=8, v_group=32, in_dtype="f32"),
+                       chunks=[(0, 17), (17, 450)]),
+    # symmetric 4-bit K with mean-centering, int8 per-token V
+    "sym4_centered": dict(w="q4_0_centered", B=2, H=8, T=777,
+                          lay=dict(k_kind="tok_sym4", k_bits=4, k_group=32, v_kind="tok_affine",
+                                   v_bits=8, v_group=128, in_dtype="f16"),
+                          center=True, chunks=[(0, 400), (400, 777)]),
+    # 8-bit affine K g32 with 4-bit V g32 at head_dim 64, GQA 2
+    "affine8_d64": dict(w="affine4_g64", B=3, H=2, T=600, Hq=4, D=64,
+                        lay=dict(k_kind="tok_affine", k_bits=8, k_group=32, v_kind="tok_affine",
+                                 v_bits=4, v_group=32, in_dtype="bf16")),
+    # full-precision cache
+    "plain_f32": dict(w="kivi_int8_tiny", B=1, H=8, T=300,
+                      lay=dict(k_kind="plain", k_bits=4, k_group=32, v_kind="plain", v_bits=4,
+                               v_group=32, in_dtype="f32")),
+}
+
+
+def make_case(name):
+    cfg = CASES[name]
+    w = synth.workload(cfg["w"])
+    if "D" in cfg:
+        w = synth.workload(cfg["w"], head_dim=cfg["D"])
+    B, H, T = cfg["B"], cfg["H"], cfg["T"]
+    Hq = cfg.get("Hq", H * w.group)
+    k, v, q = gen(w, B, H, T, Hq)
+    bias = None
+    flags = 0
+    if cfg.get("center"):
+        bias = np.stack([synth.head_params(w, h)[0] for h in range(H)]).astype(np.float32)
+        flags = K.KVQ_CENTER_K
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=w.head_dim, capacity=T + 37, flags=flags,
+                     **cfg["lay"])
+    return w, pl, ol, k, v, q, bias, cfg
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_quantize_and_decode_parity(name):
+    w, pl, ol, k, v, q, bias, cfg = make_case(name)
+    say("quantize+decode", name, pl)
+    c, o = build_pair(pl, ol, k, v, w.dtype, cfg.get("chunks"), k_bias=bias)
+    assert_same_state(c, o)
+    got, err = check_decode(pl, c, o, q, w.dtype)
+    # deterministic: a second run gives the same bytes
+    again = K.kvq_decode_attention(pl, c, to_dev(q, w.dtype)).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), again.view(np.uint32))
+    # explicit softmax scale
+    check_decode(pl, c, o, q, w.dtype, sm_scale=0.05)
+
+
+def test_decode_query_dtypes_and_single_slot():
+    w, pl, ol, k, v, q, bias, cfg = make_case("affine4_g64_bf16")
+    say("decode q dtypes / T=1")
+    c, o = build_pair(pl, ol, k[:, :, :1], v[:, :, :1], w.dtype)
+    out = K.kvq_decode_attention(pl, c, to_dev(q, w.dtype)).cpu().numpy()
+    ref = o.decode(q, w.dtype)
+    assert attn_err(out, ref) <= 1e-6      # one slot: the value row itself
+    c, o = build_pair(pl, ol, k, v, w.dtype)
+    qf = synth.widen(q, "bf16")
+    for qdt in ("f32", "f16"):
+        qq = synth.cast(qf, qdt)
+        check_decode(pl, c, o, qq, qdt)
+
+
+def test_empty_cache_decodes_to_zeros():
+    pl, ol = layouts(batch=2, n_kv_heads=2, head_dim=64, capacity=10, in_dtype="f16",
+                     k_group=64, v_group=64)
+    c = K.Cache(pl)
+    q = torch.randn(2, 4, 64, device=DEV, dtype=torch.float16)
+    out = torch.full((2, 4, 64), 7.0, device=DEV)
+    K.kvq_decode_attention(pl, c, q, out=out)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_constant_channels_use_subnormal_eps_scale():
+    """[P1] bug class 1: constant slices quantize with scale fp16(1e-5), a subnormal."""
+    pl, ol = layouts(batch=1, n_kv_heads=2, head_dim=32, capacity=64, k_kind="kivi_ch", k_bits=8,
+                     k_group=32, v_kind="tok_affine", v_bits=4, v_group=32, in_dtype="f16")
+    k = np.full((1, 2, 40, 32), 0.1, np.float16)
+    v = np.full((1, 2, 40, 32), -3.5, np.float16)
+    k[0, 1, :, 5] = np.float16(6.1e-5)
+    say("constant channels")
+    c, o = build_pair(pl, ol, k, v, "f16")
+    assert_same_state(c, o)
+    table = c.k_meta.cpu().numpy().view(np.uint16)
+    assert 168 in table        # fp16 bit pattern of the eps scale
+
+
+def test_centering_disabled_is_a_byte_noop():
+    """[P3] regression safety: centering off, or an all-zero bias, leaves every byte unchanged."""
+    w = synth.workload("q4_0_centered")
+    k, v, q = gen(w, 2, 8, 300)
+    pl0, ol0 = layouts(batch=2, n_kv_heads=8, head_dim=128, capacity=300, k_kind="tok_sym4",
+                       k_bits=4, k_group=32, v_kind="tok_affine", v_bits=8, v_group=128, in_dtype="f16")
+    plz, _ = layouts(batch=2, n_kv_heads=8, head_dim=128, capacity=300, k_kind="tok_sym4",
+                     k_bits=4, k_group=32, v_kind="tok_affine", v_bits=8, v_group=128,
+                     in_dtype="f16", flags=K.KVQ_CENTER_K)
+    say("centering no-op")
+    c0, o0 = build_pair(pl0, ol0, k, v, "f16")
+    cz = K.Cache(plz, k_bias=torch.zeros(8, 128))
+    K.kvq_quantize_append(plz, cz, to_dev(k, "f16"), to_dev(v, "f16"))
+    torch.cuda.synchronize()
+    for name in ("k_codes", "k_meta", "v_codes", "v_meta", "pos"):
+        assert torch.equal(getattr(c0, name), getattr(cz, name)), name
+    assert_same_state(c0, o0)
+
+
+def test_shift_invariance_on_gpu():
+    """[P3] "Why this is safe": a full-precision fp32 K cache centered through the
+    test seam attends exactly like the uncentered one (to fp32 rounding)."""
+    rng = np.random.default_rng(77)
+    B, H, T, D = 2, 4, 900, 128
+    k = (rng.standard_normal((B, H, T, D)) + rng.standard_normal((1, H, 1, D)) * 1.5).astype(np.float32)
+    v = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    q = rng.standard_normal((B, 4 * H, D)).astype(np.float32)
+    kbar = (rng.standard_normal((H, D)) * 1.5).astype(np.float32)
+    base = dict(batch=B, n_kv_heads=H, head_dim=D, capacity=T, k_kind="plain", k_bits=4,
+                k_group=32, v_kind="plain", v_bits=4, v_group=32, in_dtype="f32")
+    pl, ol = layouts(**base)
+    plc, _ = layouts(flags=K.KVQ_CENTER_K | K.KVQ_TEST_CENTER_ANY, **base)
+    say("shift invariance")
+    c, o = build_pair(pl, ol, k, v, "f32")
+    cc = K.Cache(plc, k_bias=torch.from_numpy(kbar))
+    K.kvq_quantize_append(plc, cc, to_dev(k, "f32"), to_dev(v, "f32"))
+    a = K.kvq_decode_attention(pl, c, to_dev(q, "f32")).cpu().numpy().astype(np.float64)
+    b = K.kvq_decode_attention(plc, cc, to_dev(q, "f32")).cpu().numpy().astype(np.float64)
+    nmse = np.sum((a - b) ** 2) / np.sum(a ** 2)
+    assert nmse < 1e-9, nmse
+    assert attn_err(b, a) < 1e-4
+    assert attn_err(a, o.decode(q, "f32")) <= TOL
+
+
+def test_append_past_capacity_raises_and_keeps_state():
+    pl, ol = layouts(batch=1, n_kv_heads=2, head_dim=64, capacity=50, in_dtype="f16",
+                     k_group=64, v_group=64)
+    c = K.Cache(pl)
+    x = torch.randn(1, 2, 40, 64, device=DEV, dtype=torch.float16)
+    K.kvq_quantize_append(pl, c, x, x)
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_quantize_append(pl, c, x, x)
+    assert e.value.status == K.KVQ_ERR_CAPACITY
+    assert c.n_stored == 40
+
+
+# ---------------------------------------------------------------- eviction
+
+def stream_pair(pl, ol, k, v, dtype, sink, window, evict_every=1):
+    """Append token by token, evicting when the cap is exceeded; product caches ping-pong."""
+    cur, spare = K.Cache(pl), K.Cache(pl)
+    o = OracleCache(ol)
+    T = k.shape[2]
+    for t in range(T):
+        K.kvq_quantize_append(pl, cur, to_dev(np.ascontiguousarray(k[:, :, t:t + 1]), dtype),
+                              to_dev(np.ascontiguousarray(v[:, :, t:t + 1]), dtype))
+        o.append(k[:, :, t:t + 1], v[:, :, t:t + 1])
+        if (t + 1) % evict_every == 0:
+            st = K.kvq_evict_streaming(pl, cur, spare, sink, window)
+            e = o.evict(sink, window)
+            assert (st == K.KVQ_NOOP) == (e is None)
+            if st == K.KVQ_OK:
+                cur, spare = spare, cur
+                o = e
+    torch.cuda.synchronize()
+    return cur, o
+
+
+def test_streaming_kivi_int8_tinygpt_500_positions():
+    """[P1] smoke-test shape: sink 4 + window 256 over 500 positions; KIVI int8
+    keys, per-channel tables compacted; state and decode match the oracle."""
+    w = synth.workload("kivi_int8_tiny")
+    k, v, q = gen(w, 1, 8, 500)
+    pl, ol = layouts(batch=1, n_kv_heads=8, head_dim=32, capacity=261, k_kind="kivi_ch", k_bits=8,
+                     k_group=32, v_kind="tok_affine", v_bits=8, v_group=32, in_dtype="f32")
+    say("stream kivi int8 500")
+    c, o = stream_pair(pl, ol, k, v, "f32", 4, 256)
+    assert c.n_stored == 260 and c.next_pos == 500
+    assert_same_state(c, o)
+    assert np.array_equal(c.pos.cpu().numpy().view(np.int32)[:260], np.r_[0:4, 244:500])
+    check_decode(pl, c, o, q, "f32")
+
+
+@pytest.mark.parametrize("name", ["affine4_g64_bf16", "sym4_centered", "kivi4_llama3b", "plain_f32"])
+def test_batch_evict_parity(name):
+    w, pl, ol, k, v, q, bias, cfg = make_case(name)
+    say("batch evict", name)
+    c, o = build_pair(pl, ol, k, v, w.dtype, k_bias=bias)
+    dst = K.Cache(pl, k_bias=None if bias is None else torch.from_numpy(bias))
+    T = k.shape[2]
+    sink, window = 5, 256 + 7
+    assert K.kvq_evict_streaming(pl, c, dst, sink, window) == K.KVQ_OK
+    e = o.evict(sink, window)
+    torch.cuda.synchronize()
+    assert_same_state(dst, e)
+    check_decode(pl, dst, e, q, w.dtype)
+    # idempotent: nothing more to drop
+    assert K.kvq_evict_streaming(pl, dst, c, sink, window) == K.KVQ_NOOP
+    # append after eviction continues positions and groups
+    k2, v2, _ = gen(w, pl.batch, pl.n_kv_heads, 45)
+    K.kvq_quantize_append(pl, dst, to_dev(k2, w.dtype), to_dev(v2, w.dtype))
+    e.append(k2, v2)
+    torch.cuda.synchronize()
+    assert_same_state(dst, e)
+    check_decode(pl, dst, e, q, w.dtype)
+
+
+def test_periodic_eviction_and_batch_eviction_kivi4():
+    w = synth.workload("llama3b_kivi_int4")
+    k, v, q = gen(w, 1, 8, 200)
+    pl, ol = layouts(batch=1, n_kv_heads=8, head_dim=128, capacity=200, k_kind="kivi_ch", k_bits=4,
+                     k_group=32, v_kind="tok_affine", v_bits=4, v_group=32, in_dtype="f16")
+    say("stream vs batch kivi4")
+    cs, os_ = stream_pair(pl, ol, k, v, "f16", 3, 64, evict_every=7)
+    cb, ob = build_pair(pl, ol, k, v, "f16")
+    dst = K.Cache(pl)
+    assert K.kvq_evict_streaming(pl, cb, dst, 3, 64) == K.KVQ_OK
+    torch.cuda.synchronize()
+    # streaming state: slots [0,3) + last window after the final eviction point
+    assert_same_state(cs, os_)
+    assert_same_state(dst, ob.evict(3, 64))
