@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the compressed-KV decode path on one MI355X.
+
+A timed step is one decode-attention call over the whole batch of the
+headline workload (mlx-style 4-bit affine g64 K and V, bf16, batch 64,
+32 query / 8 kv heads x 128, T = 32768): every cached byte is read once.
+The other rows of the hot path are timed in the same run on their own
+workloads and reported under "rows":
+  A  quantize-on-write: prefill of the whole cache (n_new = T) and the
+     per-step append of one token per sequence
+  C  StreamingLLM compaction of the headline cache to sink 4 + window 16380
+  D  SnapKV prefill selection (8 kv-heads x 128, S = 8192, window 32,
+     sink 4, budget 512): scores/s
+Inputs are seeded synthetic data (synth) already resident in HBM when the
+timed region starts.  Times come from HIP events on the stream the kernels
+run on.  The CPU oracle is timed on a bounded sample as the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+FAST_SRC = os.path.join(ROOT, "evicted_kv_cache_amd", "csrc", "decode_fast.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_affine4_g64_traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def decode_algorithmic_bytes(B, Hkv, Hq, D, T, bits, group, q_bytes=2):
+    """Bytes a decode step must move: K and V codes and (scale, zero) fp16 per
+    group for T slots, the queries, and the fp32 outputs."""
+    per_token_head = 2 * (D * bits // 8 + (D // group) * 4)
+    return B * Hkv * T * per_token_head + B * Hq * D * q_bytes + B * Hq * D * 4
+
+
+def time_stream(fn, steps, warmup, torch):
+    """Average ms per call of fn over `steps` calls, with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for _ in range(steps):
+        fn()
+    end.record(s)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except OSError:
+        return None
+    if t.get("source_sha256_16") != source_hash(FAST_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, target_s=12.0):
+    """Time the CPU oracle's decode on a bounded sample of (batch, kv-head) slices."""
+    import numpy as np
+
+    import synth
+    from oracle.cache import Layout as OLayout
+    from oracle.cache import OracleCache
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+    e = w.extra
+
+    def slice_cache(b, h):
+        k, v, q = synth.slice_cast(w, b, h)
+        ol = OLayout(batch=1, n_kv_heads=1, head_dim=w.head_dim, capacity=w.seq_len,
+                     k_kind=e["k_kind"], k_bits=e["k_bits"], k_group=e["k_group"],
+                     v_kind="tok_affine", v_bits=e["v_bits"], v_group=e["v_group"], in_dtype=w.dtype)
+        o = OracleCache(ol)
+        o.append(k[None, None], v[None, None])
+        return o, q[None]
+
+    # probe one slice to size the sample
+    o, q = slice_cache(0, 0)
+    t0 = time.perf_counter()
+    o.decode(q, w.dtype, threads=1)
+    one = time.perf_counter() - t0          # single-thread seconds per kv-head slice (4 q-heads)
+    n = max(threads, int(target_s * threads / max(one, 1e-3)))
+    n = min(n, w.batch * w.n_kv_heads)
+    slices = [(i // w.n_kv_heads, i % w.n_kv_heads) for i in range(n)]
+    caches = [slice_cache(b, h) for b, h in slices]
+    from concurrent.futures import ThreadPoolExecutor
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(lambda oc: oc[0].decode(oc[1], w.dtype, threads=1), caches))
+    dt = time.perf_counter() - t0
+    nbytes = decode_algorithmic_bytes(1, 1, w.group, w.head_dim, w.seq_len, e["k_bits"], e["k_group"]) * n
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {w.batch * w.n_kv_heads} (batch, kv-head) slices of the headline "
+                      f"workload ({n * w.group} query heads over T={w.seq_len}), fp64 decode, "
+                      f"{dt:.1f} s wall on {threads} threads"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rows", default="ACD", help="extra rows to time (subset of ACD)")
+    ap.add_argument("--mode", default="full", choices=["full", "decode", "copy"],
+                    help="decode: only the timed decode steps (for counter runs); "
+                         "copy: a plain 2 GiB device copy (bandwidth probe / counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import evicted_kv_cache_amd as K
+    import synth
+
+    dev = "cuda"
+    if args.mode == "copy":
+        n = 1 << 31
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms = time_stream(lambda: dst.copy_(src), args.steps, args.warmup, torch)
+        print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n,
+                          "ms": round(ms, 4), "GB/s": round(2 * n / ms / 1e6, 1)}), flush=True)
+        return
+    if args.mode == "decode":
+        args.rows = ""
+        args.no_cpu_baseline = True
+    w = synth.workload("affine4_g64")
+    e = w.extra
+    B, Hkv, Hq, D, T = w.batch, w.n_kv_heads, w.n_q_heads, w.head_dim, w.seq_len
+    log("generating", w.name)
+    t0 = time.time()
+    Kh, Vh, Qh = synth.full(w, threads=max(1, min(16, os.cpu_count() or 1)))
+    log(f"generated in {time.time() - t0:.1f}s")
+
+    def bf16(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    L = K.Layout(batch=B, n_kv_heads=Hkv, head_dim=D, capacity=T, k_kind=e["k_kind"],
+                 k_bits=e["k_bits"], k_group=e["k_group"], v_kind="tok_affine",
+                 v_bits=e["v_bits"], v_group=e["v_group"], in_dtype="bf16")
+    cache = K.Cache(L)
+    kd, vd = bf16(Kh), bf16(Vh)
+    q = bf16(Qh)
+    del Kh, Vh
+    rows = {}
+
+    # ---- row A: prefill quantize-on-write (n_new = T), timed once after a warm-up cache
+    if "A" in args.rows:
+        scratch = K.Cache(L)
+        K.kvq_quantize_append(L, scratch, kd, vd)
+        torch.cuda.synchronize()
+        del scratch
+        s = torch.cuda.current_stream()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(s)
+        K.kvq_quantize_append(L, cache, kd, vd)
+        ev1.record(s)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1)
+        nbytes = 2 * kd.numel() * 2 + 2 * (cache.sizes.k_codes + cache.sizes.k_meta) + T * 4
+        rows["A_quantize_prefill"] = {"workload": f"{w.name} prefill n_new={T}", "ms": round(ms, 4),
+                                      "GB/s": round(nbytes / ms / 1e6, 1),
+                                      "frac_hbm": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
+    else:
+        K.kvq_quantize_append(L, cache, kd, vd)
+    torch.cuda.synchronize()
+    del kd, vd
+
+    # ---- row B (the step): decode attention over the full cache
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(K.kvq_decode_workspace_bytes(L, Hq), 16), dtype=torch.uint8, device=dev)
+
+    def step():
+        K.kvq_decode_attention(L, cache, q, out=out, ws=ws)
+
+    log("timing decode")
+    ms = time_stream(step, args.steps, args.warmup, torch)
+    nbytes = decode_algorithmic_bytes(B, Hkv, Hq, D, T, e["k_bits"], e["k_group"])
+    gbs = nbytes / ms / 1e6
+    log(f"decode {ms * 1e3:.1f} us/step  {gbs:.1f} GB/s  {gbs / PEAK_HBM_GBS:.3f} of HBM peak")
+    traffic = load_traffic()
+
+    # ---- row A (decode-time append of one token per sequence) on a cache with room
+    if "A" in args.rows:
+        L1 = K.Layout(**{**L.__dict__, "capacity": 4096})
+        c1 = K.Cache(L1)
+        one_k = torch.randn(B, Hkv, 1, D, device=dev).to(torch.bfloat16)
+        ms1 = time_stream(lambda: (K.kvq_cache_reset(c1) if c1.n_stored >= 4000 else None,
+                                   K.kvq_quantize_append(L1, c1, one_k, one_k)), 200, 10, torch)
+        rows["A_append_one_token"] = {"workload": f"{w.name} append n_new=1 (B={B}, Hkv={Hkv})",
+                                      "us": round(ms1 * 1e3, 2)}
+
+    # ---- row C: StreamingLLM compaction of the headline cache
+    if "C" in args.rows:
+        dst = K.Cache(L)
+        sink, window = 4, T // 2 - 4
+        def evict():
+            st = K.kvq_evict_streaming(L, cache, dst, sink, window)
+            assert st == K.KVQ_OK
+        msc = time_stream(evict, 10, 2, torch)
+        row_bytes = 2 * (D * e["k_bits"] // 8 + (D // e["k_group"]) * 4)
+        cbytes = 2 * B * Hkv * (sink + window) * row_bytes + 2 * (sink + window) * 4
+        rows["C_evict"] = {"workload": f"{w.name} T={T} -> sink {sink} + window {window}",
+                           "ms": round(msc, 4), "GB/s": round(cbytes / msc / 1e6, 1),
+                           "frac_hbm": round(cbytes / msc / 1e6 / PEAK_HBM_GBS, 4)}
+        del dst
+
+    # ---- row D: SnapKV prefill selection
+    if "D" in args.rows:
+        ws_ = synth.workload("snapkv_prefill")
+        ks, vs, _ = synth.full(ws_, threads=16)
+        ksd = torch.from_numpy(ks).to(dev)
+        vsd = torch.from_numpy(vs).to(dev)
+        ex = ws_.extra
+        Bs, Hs, Ss, Ds = ks.shape
+        n_keep = min(ex["budget"], Ss)
+        sc = torch.empty((Bs, Hs, Ss), dtype=torch.float32, device=dev)
+        kept = torch.empty((Bs, Hs, n_keep), dtype=torch.int32, device=dev)
+        ko = torch.empty((Bs, Hs, n_keep, Ds), dtype=torch.float16, device=dev)
+        vo = torch.empty_like(ko)
+        wsb = torch.empty(K.kvq_snapkv_workspace_bytes(Bs, Hs, Ss, Ds, ex["obs_window"]),
+                          dtype=torch.uint8, device=dev)
+        msd = time_stream(lambda: K.kvq_snapkv_select(ksd, vsd, ex["obs_window"], ex["n_sink"],
+                                                      ex["budget"], sc, kept, ko, vo, wsb),
+                          200, 10, torch)
+        sbytes = ks.nbytes + 2 * n_keep * Hs * Ds * 2 * 2 + sc.numel() * 4 + kept.numel() * 4
+        rows["D_snapkv"] = {"workload": f"{ws_.name} S={Ss} w={ex['obs_window']} sink={ex['n_sink']} "
+                                        f"budget={ex['budget']} Hkv={Hs} D={Ds}",
+                            "us": round(msd * 1e3, 2), "scores/s": round(Hs * Ss / (msd * 1e-3), 1),
+                            "GB/s": round(sbytes / msd / 1e6, 1)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing CPU oracle baseline")
+        cpu = cpu_baseline(w)
+
+    result = {
+        "metric": "quantized decode-attention GB/s and % HBM roofline at T=32K; SnapKV prefill scores/s",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 q / u4 codes, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1), synth.affine4_g64)",
+        "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
+                   "head_dim": D, "seq_len": T, "k_format": "tok_affine u4 g64 fp16 scale+zero",
+                   "v_format": "tok_affine u4 g64 fp16 scale+zero",
+                   "token_q_heads_per_s": round(B * Hq * T / (ms * 1e-3), 1),
+                   "token_kv_heads_per_s": round(B * Hkv * T / (ms * 1e-3), 1),
+                   "algorithmic_bytes_per_step": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_tok4_kernel<bf16, 64, 64> (one launch per step)"},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -190,6 +190,11 @@ class Cache:
         return self.c.next_pos
 
 
+def kvq_cache_reset(cache: Cache) -> None:
+    """Zero the cache's host counters (an empty cache; device buffers untouched)."""
+    _check(lib().kvq_cache_reset(ctypes.byref(cache.c)), "kvq_cache_reset")
+
+
 def kvq_quantize_append(layout: Layout, cache: Cache, k_new, v_new, stream=None) -> None:
     """k_new, v_new: [B][Hkv][n_new][D] contiguous device tensors of in_dtype."""
     assert k_new.is_contiguous() and v_new.is_contiguous()

@@ -250,7 +250,8 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* c, const v
     a.in_dtype = L->in_dtype; a.q_dtype = q_dtype;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
     a.scale_log2 = scale * 1.4426950408889634f;
-    decode_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
+    if (decode_fast_applies(a)) decode_fast_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
+    else decode_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
     a.ws_o = static_cast<float*>(ws);
     a.ws_ml = a.ws_o + (size_t)a.B * a.Hq * a.n_splits * D;
     return hip_status(launch_decode(a, s));

@@ -256,6 +256,13 @@ size_t decode_workspace_bytes(int B, int Hq, int D, int cap) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     hipError_t e;
+    if (decode_fast_applies(a)) {
+        e = launch_decode_fast(a, s);
+        if (e != hipSuccess || a.n_splits == 1) return e;
+        hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(128), 0, s,
+                           a.ws_o, a.ws_ml, a.out, a.D, a.n_splits);
+        return hipGetLastError();
+    }
     switch (a.k_kind) {
         case KVQ_PLAIN: e = launch_generic_v<KVQ_PLAIN>(a, s); break;
         case KVQ_KIVI_CH: e = launch_generic_v<KVQ_KIVI_CH>(a, s); break;

@@ -1,0 +1,448 @@
+// decode_fast.hip -- bandwidth-tuned decode attention for per-token 4-bit
+// affine K and V (mlx-lm-style group quantization, "Low-bit KV caches on MLX",
+// s.1) at head_dim 128 and 4 query heads per kv-head (gfx950).
+//
+// Decode streams the whole cache once per step ("Low-bit KV caches on MLX",
+// s.5: decode spends its time reading the cache).  At 4.5 bits per element
+// and 4 query heads per kv-head the VALU has ~2.8 lane-ops per cached element
+// at the HBM roofline, so the kernel is built around keeping per-element
+// VALU work minimal:
+//
+// * Workgroup = 4 waves on one (batch, kv-head[, token split]); each wave
+//   owns a contiguous run of 32-token tiles with its own online softmax; the
+//   waves merge through LDS (token splits merge in a combine kernel).
+// * Codes become fp16 operands with one AND: a nibble left in place is the
+//   fp16 subnormal u * 2^-24 (low nibble of a byte) or u * 2^-20 (high
+//   nibble); v_dot2_f32_f16 multiplies subnormals exactly, so each
+//   instruction does two exact MACs into fp32 and the power-of-two scales are
+//   folded into the query (x 1/16 for high nibbles) or applied at the end.
+// * QK^T: lane (token t, quarter of head_dim) reads 16 bytes of codes per
+//   token; the query is held as fp16 pairs scaled by a power of two shared by
+//   the head group (exact for bf16/fp16 queries).  The group's scale s and zero
+//   z are factored out of the dot product:  q . k = s (q . u) + z sum(q).
+//   The four quarter partial logits are combined with a DPP reduce-scatter
+//   that leaves lane quarter h with query head h.
+// * Softmax: lane (t, h) computes p for head h of tokens t and t+16 (one
+//   exp each) and writes the fp16 weight pair (p_t s_t, p_t+16 s_t+16) to
+//   LDS; the running max is rescaled only when a wave sees a larger logit,
+//   so weights stay <= 1 and never overflow fp16.
+// * PV: lane (phase, 8-channel chunk) reads the codes of tokens t and t+16,
+//   v_perm_b32 interleaves their bytes and one AND per channel gives the
+//   (u_t, u_t+16) subnormal pair; v_dot2_f32_f16 with the weight pair does
+//   two token MACs.  The zero points and the fp16 rounding of the weights
+//   are accounted exactly in fp32:
+//     o = sum_t w^_t u_t + sum_t p_t (z_t + 8 s_t) - 8 sum_t w^_t
+//   so rounding a weight only perturbs w (u - 8).
+// * Tails need no clamping: loads go through buffer resources whose size is
+//   the valid part of the tile, and out-of-range loads return zero.
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kGQ = 4;          // query heads per kv-head
+constexpr int kTileT = 32;      // tokens per wave tile
+constexpr int kWaves = 4;
+constexpr int kRowB = kD / 2;   // bytes of 4-bit codes per token
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                  false);
+}
+// Round-to-nearest-even pack of two fp32 into an fp16 pair.
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+    half2_t h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float dpp_add_xor1(float v) {   // v + v[lane ^ 1]
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// Query element as fp32.
+template <int QDT>
+__device__ __forceinline__ float q_elem(uint32_t bits16) {
+    if constexpr (QDT == KVQ_BF16) return bf16_bits_to_f32(bits16);
+    else return f16_bits_to_f32(bits16);
+}
+
+template <int NVG>
+struct VMeta { uint32_t m[2][NVG]; };   // (scale, zero) of tokens t, t+16 per V group
+
+// Per-tile loads of one lane.
+template <int NVG>
+struct TileLoads {
+    u32x4 k[2];          // codes of the lane's quarter for tokens t and t+16
+    uint32_t km[2];      // K (scale, zero) of the quarter's group, tokens t and t+16
+    VMeta<NVG> vm;
+    uint32_t v[4][2];    // V code words (8 channels) of tokens ph+4j and ph+4j+16
+};
+
+// GK, GV: channels per K / V group (32, 64 or 128).
+template <int QDT, int GK, int GV>
+__global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
+    constexpr int NKG = kD / GK;      // K groups per row
+    constexpr int NVG = kD / GV;      // V groups per row
+
+    // the wave index is uniform across the wave; say so, so that tile bases and
+    // buffer descriptors stay in scalar registers
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * a.Hkv + hk;
+    const int t_lo = split * a.split_len;
+    const int t_hi = min(a.T, t_lo + a.split_len);
+    const int n_tiles = (t_hi - t_lo + kTileT - 1) / kTileT;
+    const int tile0 = (n_tiles * wave) / kWaves, tile1 = (n_tiles * (wave + 1)) / kWaves;
+
+    __shared__ uint32_t wbuf[kWaves][16][NVG][kGQ];           // fp16 weight pairs of a tile
+    __shared__ float comb_o[kWaves][kGQ][kD];
+    __shared__ float comb_ml[kWaves][kGQ][2];
+
+    // QK role: token t16 (and t16 + 16), quarter q4 of head_dim; after the
+    // reduce-scatter the lane owns query head hq = q4.
+    const int t16 = lane >> 2, q4 = lane & 3;
+    const int kg = (32 * q4) / GK;                          // K group of the quarter
+    // PV role: phase ph (tokens ph + 4j, j < 4, and +16), chunk c (channels 8c..8c+7)
+    const int ph = lane >> 4, c = lane & 15;
+    const int vg_c = (8 * c) / GV;
+
+    // ---- query: fp16 pairs for this lane's quarter, scaled by 2^-e (shared by the group)
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + hk * kGQ) * kD;
+    float qmax = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 x = *reinterpret_cast<const uint4*>(q16 + h * kD + 32 * q4 + 8 * k);
+            const uint32_t e4[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                qmax = fmaxf(qmax, fmaxf(fabsf(q_elem<QDT>(e4[i] & 0xFFFFu)), fabsf(q_elem<QDT>(e4[i] >> 16))));
+        }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+    // scale so the largest |q| lands in [2^14, 2^15): exact fp16 for bf16/fp16 inputs
+    int qexp = 0;
+    if (qmax > 0.0f) { frexpf(qmax, &qexp); qexp -= 15; }
+    const float qscale = ldexpf(1.0f, -qexp);
+    uint32_t qv[kGQ][16];
+    float qsum[kGQ];
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) {
+        float s = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 xx = *reinterpret_cast<const uint4*>(q16 + h * kD + 32 * q4 + 8 * k);
+            const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = q_elem<QDT>(e4[i] & 0xFFFFu);
+                x[2 * i + 1] = q_elem<QDT>(e4[i] >> 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s += x[i];
+            qv[h][4 * k + 0] = pack_f16(x[0] * qscale, x[4] * qscale);
+            qv[h][4 * k + 1] = pack_f16(x[1] * qscale * 0.0625f, x[5] * qscale * 0.0625f);
+            qv[h][4 * k + 2] = pack_f16(x[2] * qscale, x[6] * qscale);
+            qv[h][4 * k + 3] = pack_f16(x[3] * qscale * 0.0625f, x[7] * qscale * 0.0625f);
+        }
+        qsum[h] = s;
+    }
+    // logit (base 2) = cexp (s 2^(qexp+24) (q' . u') + z qsum)
+    const float cexp = a.scale_log2;
+    const float kC = ldexpf(cexp, qexp + 24);
+    float qsc[kGQ];
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) qsc[h] = qsum[h] * cexp;
+
+    const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
+    const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kRowB;
+    const uint32_t* kmeta = static_cast<const uint32_t*>(a.k_meta) + bh * a.cap * NKG;
+    const uint32_t* vmeta = static_cast<const uint32_t*>(a.v_meta) + bh * a.cap * NVG;
+
+    float m_lane = -INFINITY;     // running max of head q4
+    float l_lane = 0.0f;          // running sum of head q4 (this lane's tokens)
+    float corr[NVG];              // head q4, per V group
+#pragma unroll
+    for (int g = 0; g < NVG; ++g) corr[g] = 0.0f;
+    float acc[kGQ][8];            // PV: head h, channel 8c + i (scaled by 2^-24 / 2^-20)
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = 0.0f;
+
+    auto load_tile = [&](int tile, TileLoads<NVG>& L) {
+        const int tb = t_lo + tile * kTileT;
+        const uint32_t nv = (uint32_t)min(kTileT, t_hi - tb);          // valid tokens in the tile
+        const __amdgpu_buffer_rsrc_t rk = rsrc(kcodes + (int64_t)tb * kRowB, nv * kRowB);
+        const __amdgpu_buffer_rsrc_t rkm = rsrc(kmeta + (int64_t)tb * NKG, nv * NKG * 4);
+        const __amdgpu_buffer_rsrc_t rvm = rsrc(vmeta + (int64_t)tb * NVG, nv * NVG * 4);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vcodes + (int64_t)tb * kRowB, nv * kRowB);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t tok = t16 + 16 * p;
+            L.k[p] = bload128(rk, tok * kRowB + 16 * q4);
+            L.km[p] = bload32(rkm, (tok * NKG + kg) * 4);
+            if constexpr (NVG == 1) {
+                L.vm.m[p][0] = bload32(rvm, tok * 4);
+            } else if constexpr (NVG == 2) {
+                const u32x2 x = bload64(rvm, tok * 8);
+                L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y;
+            } else {
+                const u32x4 x = bload128(rvm, tok * 16);
+                L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y; L.vm.m[p][2] = x.z; L.vm.m[p][3] = x.w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t tt = ph + 4 * j;
+            L.v[j][0] = bload32(rv, tt * kRowB + 4 * c);
+            L.v[j][1] = bload32(rv, (tt + 16) * kRowB + 4 * c);
+        }
+    };
+
+    auto process = [&](const TileLoads<NVG>& L, int tile) {
+        const int tb = t_lo + tile * kTileT;
+
+        // -------------------------------------------- QK^T, two passes (t16, t16 + 16)
+        float xs[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            float dsum[kGQ] = {0.0f, 0.0f, 0.0f, 0.0f};
+            const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t w = kw[k];
+                const uint32_t w8 = w >> 8;
+                const uint32_t u0 = w & 0x000F000Fu, u1 = w & 0x00F000F0u;     // (n0,n4), (n1,n5)
+                const uint32_t u2 = w8 & 0x000F000Fu, u3 = w8 & 0x00F000F0u;   // (n2,n6), (n3,n7)
+#pragma unroll
+                for (int h = 0; h < kGQ; ++h) {
+                    dsum[h] = dot2_f16(u0, qv[h][4 * k + 0], dsum[h]);
+                    dsum[h] = dot2_f16(u1, qv[h][4 * k + 1], dsum[h]);
+                    dsum[h] = dot2_f16(u2, qv[h][4 * k + 2], dsum[h]);
+                    dsum[h] = dot2_f16(u3, qv[h][4 * k + 3], dsum[h]);
+                }
+            }
+            const float s = f16_bits_to_f32(L.km[p] & 0xFFFFu) * kC;
+            const float z = f16_bits_to_f32(L.km[p] >> 16);
+            float part[kGQ];
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h) part[h] = fmaf(s, dsum[h], z * qsc[h]);
+            // reduce-scatter over the 4 quarter lanes: lane q4 keeps head q4
+            const bool o1 = q4 & 1, o2 = q4 & 2;
+            const float k0 = o1 ? part[1] : part[0], g0 = o1 ? part[0] : part[1];
+            const float k1 = o1 ? part[3] : part[2], g1 = o1 ? part[2] : part[3];
+            const float r0 = k0 + dpp_xor1(g0);   // heads (o1) and (o1 + 2) over lanes {q4, q4^1}
+            const float r1 = k1 + dpp_xor1(g1);
+            const float kk = o2 ? r1 : r0, gg = o2 ? r0 : r1;
+            const float x = kk + dpp_xor2(gg);
+            xs[p] = (tb + t16 + 16 * p < t_hi) ? x : -INFINITY;
+        }
+
+        // -------------------------------------------- online softmax (rescale on a new max)
+        const bool grow = (xs[0] > m_lane) || (xs[1] > m_lane);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            float mt = fmaxf(xs[0], xs[1]);
+#pragma unroll
+            for (int off = 4; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+            const float m_new = fmaxf(m_lane, mt);
+            const float alpha = exp2f(m_lane - m_new);
+            m_lane = m_new;
+            l_lane *= alpha;
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) corr[g] *= alpha;
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h) {
+                // lane h owns head h
+                const float ah = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), h));
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[h][i] *= ah;
+            }
+        }
+        const float p0 = exp2f(xs[0] - m_lane);
+        const float p1 = exp2f(xs[1] - m_lane);
+        l_lane += p0 + p1;
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) {
+            const float s0 = f16_bits_to_f32(L.vm.m[0][g] & 0xFFFFu);
+            const float z0 = f16_bits_to_f32(L.vm.m[0][g] >> 16);
+            const float s1 = f16_bits_to_f32(L.vm.m[1][g] & 0xFFFFu);
+            const float z1 = f16_bits_to_f32(L.vm.m[1][g] >> 16);
+            const uint32_t pair = pack_f16(p0 * s0, p1 * s1);
+            float cg = corr[g];
+            cg = fmaf(p0, fmaf(8.0f, s0, z0), cg);
+            cg = fmaf(p1, fmaf(8.0f, s1, z1), cg);
+            corr[g] = dot2_f16(pair, 0xC800C800u /* (-8, -8) */, cg);
+            wbuf[wave][t16][g][q4] = pair;
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        // -------------------------------------------- PV
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint4 wp = *reinterpret_cast<const uint4*>(&wbuf[wave][ph + 4 * j][vg_c][0]);
+            const uint32_t wpair[kGQ] = {wp.x, wp.y, wp.z, wp.w};
+            const uint32_t w0 = L.v[j][0], w1 = L.v[j][1];
+            // X = [w1.b1 w1.b0 w0.b1 w0.b0], Y = [w1.b3 w1.b2 w0.b3 w0.b2]
+            const uint32_t X = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
+            const uint32_t Y = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
+            const uint32_t X8 = X >> 8, Y8 = Y >> 8;
+            const uint32_t cp[8] = {X & 0x000F000Fu, X & 0x00F000F0u, X8 & 0x000F000Fu, X8 & 0x00F000F0u,
+                                    Y & 0x000F000Fu, Y & 0x00F000F0u, Y8 & 0x000F000Fu, Y8 & 0x00F000F0u};
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[h][i] = dot2_f16(wpair[h], cp[i], acc[h][i]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // two load buffers in ping-pong: the next tile's loads are in flight while
+    // the current tile is computed
+    TileLoads<NVG> A, B2;
+    if (tile0 < tile1) load_tile(tile0, A);
+    for (int tile = tile0; tile < tile1; tile += 2) {
+        if (tile + 1 < tile1) load_tile(tile + 1, B2);
+        process(A, tile);
+        if (tile + 1 >= tile1) break;
+        if (tile + 2 < tile1) load_tile(tile + 2, A);
+        process(B2, tile + 1);
+    }
+
+    // ---------------------------------------------------- wave-level reduction
+    // PV: sum the 4 phases (lanes c, c+16, c+32, c+48) and undo the code scales
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v = acc[h][i];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            acc[h][i] = v * ((i & 1) ? 1048576.0f : 16777216.0f);   // 2^20 (high nibble), 2^24
+        }
+    // head q4 sums over the lane's tokens: reduce over lanes with equal q4
+#pragma unroll
+    for (int off = 4; off < 64; off <<= 1) {
+        l_lane += __shfl_xor(l_lane, off);
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) corr[g] += __shfl_xor(corr[g], off);
+    }
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) {
+        // corrections of head h for this chunk's V group live in lane h
+        float cv = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) {
+            const float cg = __shfl(corr[g], h);
+            cv = (g == vg_c) ? cg : cv;
+        }
+        if (lane < 16) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) comb_o[wave][h][c * 8 + i] = acc[h][i] + cv;
+        }
+    }
+    if (lane < kGQ) {
+        comb_ml[wave][lane][0] = m_lane;
+        comb_ml[wave][lane][1] = l_lane;
+    }
+    __syncthreads();
+    // ---------------------------------------------------- merge the 4 waves
+    const int ns = a.n_splits;
+    for (int idx = threadIdx.x; idx < kGQ * kD; idx += 256) {
+        const int h = idx / kD, d = idx % kD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb_ml[w][h][0]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = comb_ml[w][h][0];
+            const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+            num = fmaf(f, comb_o[w][h][d], num);
+            den = fmaf(f, comb_ml[w][h][1], den);
+        }
+        const int64_t row = (int64_t)b * a.Hq + hk * kGQ + h;
+        if (ns == 1) {
+            a.out[row * kD + d] = num / den;
+        } else {
+            a.ws_o[(row * ns + split) * kD + d] = num;
+            if (d == 0) {
+                a.ws_ml[(row * ns + split) * 2 + 0] = M;
+                a.ws_ml[(row * ns + split) * 2 + 1] = den;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+// Fast path applies to: per-token 4-bit affine K and V, D = 128, 4 query
+// heads per kv-head, bf16 or fp16 queries.
+bool decode_fast_applies(const DecodeArgs& a) {
+    return a.k_kind == KVQ_TOK_AFFINE && a.v_kind == KVQ_TOK_AFFINE && a.k_bits == 4 &&
+           a.v_bits == 4 && a.D == kD && a.Hq == kGQ * a.Hkv &&
+           (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16);
+}
+
+// Split plan: one workgroup per (batch, kv-head) when that fills the chip
+// twice over, otherwise split the tokens so that about 512 workgroups run.
+void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len) {
+    const int units = B * Hkv;
+    int ns = (512 + units - 1) / units;
+    const int min_len = kWaves * kTileT * 4;       // at least 4 tiles per wave
+    const int max_ns = (T + min_len - 1) / min_len;
+    if (ns > max_ns) ns = max_ns;
+    if (ns < 1) ns = 1;
+    int len = (T + ns - 1) / ns;
+    len = ((len + kTileT - 1) / kTileT) * kTileT;
+    *split_len = len;
+    *n_splits = (T + len - 1) / len;
+}
+
+template <int QDT>
+static hipError_t launch_fast_q(const DecodeArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
+#define KVQ_FAST(GK, GV)                                                                      \
+    if (a.k_group == GK && a.v_group == GV) {                                                 \
+        hipLaunchKernelGGL((decode_tok4_kernel<QDT, GK, GV>), grid, dim3(256), 0, s, a);      \
+        return hipGetLastError();                                                             \
+    }
+    KVQ_FAST(64, 64) KVQ_FAST(32, 32) KVQ_FAST(128, 128) KVQ_FAST(64, 32) KVQ_FAST(32, 64)
+    KVQ_FAST(64, 128) KVQ_FAST(128, 64) KVQ_FAST(32, 128) KVQ_FAST(128, 32)
+#undef KVQ_FAST
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) {
+    if (a.q_dtype == KVQ_BF16) return launch_fast_q<KVQ_BF16>(a, s);
+    return launch_fast_q<KVQ_F16>(a, s);
+}
+
+}  // namespace kvq

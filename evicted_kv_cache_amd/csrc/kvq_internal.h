@@ -104,6 +104,9 @@ struct DecodeArgs {
     int n_splits, split_len;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+bool decode_fast_applies(const DecodeArgs& a);
+void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Hq, int D, int cap);
 void decode_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
 
