@@ -61,14 +61,14 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
     half2_t h = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, h);
 }
-__device__ __forceinline__ float dpp_add_xor1(float v) {   // v + v[lane ^ 1]
-    return v + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_xor1(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+// fp16 halves of a packed pair, widened (folds into v_fma_mix_f32 operands)
+__device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(half2_t, u).x; }
+__device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit_cast(half2_t, u).y; }
+// DPP quad rotations: value of lane (l - k) mod 4 within the lane's quad.
+template <int K>
+__device__ __forceinline__ float quad_from_minus(float v) {
+    constexpr int ctrl = K == 1 ? 0x93 : K == 2 ? 0x4E : 0x39;   // quad_perm [3,0,1,2] / [2,3,0,1] / [1,2,3,0]
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -94,7 +94,7 @@ __device__ __forceinline__ float q_elem(uint32_t bits16) {
 template <int NVG>
 struct VMeta { uint32_t m[2][NVG]; };   // (scale, zero) of tokens t, t+16 per V group
 
-// Per-tile loads of one lane.
+// Loads of one lane, issued a tile ahead of their use (ping-pong buffers).
 template <int NVG>
 struct TileLoads {
     u32x4 k[2];          // codes of the lane's quarter for tokens t and t+16
@@ -150,10 +150,13 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     int qexp = 0;
     if (qmax > 0.0f) { frexpf(qmax, &qexp); qexp -= 15; }
     const float qscale = ldexpf(1.0f, -qexp);
+    // register j of this lane holds query head (q4 + j) % 4, so that the four
+    // quarter partials of head h meet in lane quarter h by quad rotations only
     uint32_t qv[kGQ][16];
     float qsum[kGQ];
 #pragma unroll
-    for (int h = 0; h < kGQ; ++h) {
+    for (int j = 0; j < kGQ; ++j) {
+        const int h = (q4 + j) & 3;
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -167,19 +170,19 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) s += x[i];
-            qv[h][4 * k + 0] = pack_f16(x[0] * qscale, x[4] * qscale);
-            qv[h][4 * k + 1] = pack_f16(x[1] * qscale * 0.0625f, x[5] * qscale * 0.0625f);
-            qv[h][4 * k + 2] = pack_f16(x[2] * qscale, x[6] * qscale);
-            qv[h][4 * k + 3] = pack_f16(x[3] * qscale * 0.0625f, x[7] * qscale * 0.0625f);
+            qv[j][4 * k + 0] = pack_f16(x[0] * qscale, x[4] * qscale);
+            qv[j][4 * k + 1] = pack_f16(x[1] * qscale * 0.0625f, x[5] * qscale * 0.0625f);
+            qv[j][4 * k + 2] = pack_f16(x[2] * qscale, x[6] * qscale);
+            qv[j][4 * k + 3] = pack_f16(x[3] * qscale * 0.0625f, x[7] * qscale * 0.0625f);
         }
-        qsum[h] = s;
+        qsum[j] = s;
     }
     // logit (base 2) = cexp (s 2^(qexp+24) (q' . u') + z qsum)
-    const float cexp = a.scale_log2;
-    const float kC = ldexpf(cexp, qexp + 24);
-    float qsc[kGQ];
+    const float kC = ldexpf(a.scale_log2, qexp + 24);
+    // per head: z * qsum / 2^(qexp+24), so that logit = kC (s (q' . u') + z qsk)
+    float qsk[kGQ];
 #pragma unroll
-    for (int h = 0; h < kGQ; ++h) qsc[h] = qsum[h] * cexp;
+    for (int h = 0; h < kGQ; ++h) qsk[h] = ldexpf(qsum[h], -(qexp + 24));
 
     const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
     const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kRowB;
@@ -205,6 +208,12 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         const __amdgpu_buffer_rsrc_t rvm = rsrc(vmeta + (int64_t)tb * NVG, nv * NVG * 4);
         const __amdgpu_buffer_rsrc_t rv = rsrc(vcodes + (int64_t)tb * kRowB, nv * kRowB);
 #pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t tt = ph + 4 * j;
+            L.v[j][0] = bload32(rv, tt * kRowB + 4 * c);
+            L.v[j][1] = bload32(rv, (tt + 16) * kRowB + 4 * c);
+        }
+#pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = t16 + 16 * p;
             L.k[p] = bload128(rk, tok * kRowB + 16 * q4);
@@ -219,17 +228,10 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                 L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y; L.vm.m[p][2] = x.z; L.vm.m[p][3] = x.w;
             }
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t tt = ph + 4 * j;
-            L.v[j][0] = bload32(rv, tt * kRowB + 4 * c);
-            L.v[j][1] = bload32(rv, (tt + 16) * kRowB + 4 * c);
-        }
     };
 
     auto process = [&](const TileLoads<NVG>& L, int tile) {
         const int tb = t_lo + tile * kTileT;
-
         // -------------------------------------------- QK^T, two passes (t16, t16 + 16)
         float xs[2];
 #pragma unroll
@@ -250,19 +252,12 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                     dsum[h] = dot2_f16(u3, qv[h][4 * k + 3], dsum[h]);
                 }
             }
-            const float s = f16_bits_to_f32(L.km[p] & 0xFFFFu) * kC;
-            const float z = f16_bits_to_f32(L.km[p] >> 16);
             float part[kGQ];
 #pragma unroll
-            for (int h = 0; h < kGQ; ++h) part[h] = fmaf(s, dsum[h], z * qsc[h]);
-            // reduce-scatter over the 4 quarter lanes: lane q4 keeps head q4
-            const bool o1 = q4 & 1, o2 = q4 & 2;
-            const float k0 = o1 ? part[1] : part[0], g0 = o1 ? part[0] : part[1];
-            const float k1 = o1 ? part[3] : part[2], g1 = o1 ? part[2] : part[3];
-            const float r0 = k0 + dpp_xor1(g0);   // heads (o1) and (o1 + 2) over lanes {q4, q4^1}
-            const float r1 = k1 + dpp_xor1(g1);
-            const float kk = o2 ? r1 : r0, gg = o2 ? r0 : r1;
-            const float x = kk + dpp_xor2(gg);
+            for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16hi(L.km[p]) * qsk[h]);
+            // head q4 of this token: part[0] here plus part[k] of lane quarter q4 - k
+            const float x = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
+                             quad_from_minus<3>(part[3])) * kC;
             xs[p] = (tb + t16 + 16 * p < t_hi) ? x : -INFINITY;
         }
 
@@ -291,14 +286,11 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         l_lane += p0 + p1;
 #pragma unroll
         for (int g = 0; g < NVG; ++g) {
-            const float s0 = f16_bits_to_f32(L.vm.m[0][g] & 0xFFFFu);
-            const float z0 = f16_bits_to_f32(L.vm.m[0][g] >> 16);
-            const float s1 = f16_bits_to_f32(L.vm.m[1][g] & 0xFFFFu);
-            const float z1 = f16_bits_to_f32(L.vm.m[1][g] >> 16);
-            const uint32_t pair = pack_f16(p0 * s0, p1 * s1);
+            const uint32_t m0 = L.vm.m[0][g], m1 = L.vm.m[1][g];
+            const uint32_t pair = pack_f16(p0 * f16lo(m0), p1 * f16lo(m1));
             float cg = corr[g];
-            cg = fmaf(p0, fmaf(8.0f, s0, z0), cg);
-            cg = fmaf(p1, fmaf(8.0f, s1, z1), cg);
+            cg = fmaf(p0, fmaf(8.0f, f16lo(m0), f16hi(m0)), cg);
+            cg = fmaf(p1, fmaf(8.0f, f16lo(m1), f16hi(m1)), cg);
             corr[g] = dot2_f16(pair, 0xC800C800u /* (-8, -8) */, cg);
             wbuf[wave][t16][g][q4] = pair;
         }
