@@ -175,16 +175,23 @@ kvq_status kvq_quantize_append(const kvq_layout* L, kvq_cache* c, const void* k_
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int B = L->batch, H = L->n_kv_heads, D = L->head_dim;
 
-    // V (and per-token K) rows: quantized once, at write time.
-    RowQuantArgs v{};
-    v.src = v_new; v.codes = c->v_codes; v.meta = c->v_meta; v.bias = nullptr;
-    v.B = B; v.H = H; v.n = n_new; v.D = D; v.cap = L->capacity; v.slot0 = c->n_stored;
-    v.kind = L->v_kind; v.bits = L->v_bits; v.group = L->v_group; v.in_dtype = L->in_dtype;
-    hipError_t e = launch_row_quant(v, s);
+    // V rows, per-token K rows and positions: one launch; values are
+    // quantized once, at write time.
+    RowAppendArgs ra{};
+    ra.rows.B = B; ra.rows.H = H; ra.rows.n = n_new; ra.rows.D = D; ra.rows.cap = L->capacity;
+    ra.rows.slot0 = c->n_stored; ra.rows.in_dtype = L->in_dtype;
+    ra.k_src = k_new; ra.k_codes = c->k_codes; ra.k_meta = c->k_meta;
+    ra.k_bias = (L->flags & KVQ_CENTER_K) ? c->k_bias : nullptr;
+    ra.k_kind = L->k_kind; ra.k_bits = L->k_bits; ra.k_group = L->k_group;
+    ra.v_src = v_new; ra.v_codes = c->v_codes; ra.v_meta = c->v_meta;
+    ra.v_kind = L->v_kind; ra.v_bits = L->v_bits; ra.v_group = L->v_group;
+    ra.pos = c->pos; ra.first_pos = c->next_pos;
+    hipError_t e = launch_row_append(ra, s);
     if (e != hipSuccess) return KVQ_ERR_HIP;
 
     int new_quant = c->n_stored + n_new;
     if (L->k_kind == KVQ_KIVI_CH) {
+        // per-channel keys: the residual group fills and closes separately
         ChannelQuantArgs k{};
         k.k_new = k_new; k.resid = c->k_resid; k.codes = c->k_codes; k.table = c->k_meta;
         k.k_row = c->k_row;
@@ -195,18 +202,9 @@ kvq_status kvq_quantize_append(const kvq_layout* L, kvq_cache* c, const void* k_
         k.n_quant = c->n_quant;
         k.n_groups = (k.r0 + n_new) / L->k_group;
         e = launch_channel_quant(k, s);
+        if (e != hipSuccess) return KVQ_ERR_HIP;
         new_quant = c->n_quant + k.n_groups * L->k_group;
-    } else {
-        RowQuantArgs k{};
-        k.src = k_new; k.codes = c->k_codes; k.meta = c->k_meta;
-        k.bias = (L->flags & KVQ_CENTER_K) ? c->k_bias : nullptr;
-        k.B = B; k.H = H; k.n = n_new; k.D = D; k.cap = L->capacity; k.slot0 = c->n_stored;
-        k.kind = L->k_kind; k.bits = L->k_bits; k.group = L->k_group; k.in_dtype = L->in_dtype;
-        e = launch_row_quant(k, s);
     }
-    if (e != hipSuccess) return KVQ_ERR_HIP;
-    e = launch_fill_pos(c->pos, c->n_stored, c->next_pos, n_new, s);
-    if (e != hipSuccess) return KVQ_ERR_HIP;
 
     if (c->n_head == c->n_stored) c->n_head += n_new;   // never evicted: positions == slots
     c->n_stored += n_new;

@@ -19,20 +19,21 @@
 namespace kvq {
 namespace {
 
-template <typename U>
-__global__ __launch_bounds__(256) void gather_rows_kernel(const U* __restrict__ src, U* __restrict__ dst,
-                                                          int units_per_row, int BH, int cap, int n,
-                                                          int sink, int window) {
-    const int m = sink + window;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t total = (int64_t)BH * m * units_per_row;
-    if (idx >= total) return;
-    const int64_t r = idx / units_per_row;
-    const int u = (int)(idx - r * units_per_row);
-    const int64_t bh = r / m;
-    const int i = (int)(r - bh * m);
-    const int si = i < sink ? i : n - window + (i - sink);
-    dst[(bh * cap + i) * units_per_row + u] = src[(bh * cap + si) * units_per_row + u];
+// Copy `bytes` (a multiple of 2) from src to dst in the widest aligned unit.
+__device__ __forceinline__ void copy_row(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int bytes) {
+    if ((bytes & 15) == 0) {
+        for (int o = 0; o < bytes; o += 16)
+            *reinterpret_cast<uint4*>(dst + o) = *reinterpret_cast<const uint4*>(src + o);
+    } else if ((bytes & 7) == 0) {
+        for (int o = 0; o < bytes; o += 8)
+            *reinterpret_cast<uint2*>(dst + o) = *reinterpret_cast<const uint2*>(src + o);
+    } else if ((bytes & 3) == 0) {
+        for (int o = 0; o < bytes; o += 4)
+            *reinterpret_cast<uint32_t*>(dst + o) = *reinterpret_cast<const uint32_t*>(src + o);
+    } else {
+        for (int o = 0; o < bytes; o += 2)
+            *reinterpret_cast<uint16_t*>(dst + o) = *reinterpret_cast<const uint16_t*>(src + o);
+    }
 }
 
 struct RowRemap {
@@ -55,16 +56,39 @@ __device__ __forceinline__ RowRemap row_remap(const int32_t* k_row, int n, int s
     return r;
 }
 
-__global__ __launch_bounds__(256) void pos_rows_kernel(EvictArgs a) {
+// Thread (row, u) copies 16-byte unit u of every slot-indexed buffer whose row
+// has that many units (code rows are multiples of 16 bytes); unit 0 also
+// copies the shorter rows (per-token metadata) and, for (0, 0, i), moves
+// pos[i] and k_row[i].  Consecutive threads touch consecutive units.
+__global__ __launch_bounds__(256) void gather_kernel(EvictArgs a, int upr) {
     const int m = a.sink + a.window;
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= m) return;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t r = idx / upr;
+    const int u = (int)(idx - r * upr);
+    if (r >= (int64_t)a.BH * m) return;
+    const int64_t bh = r / m;
+    const int i = (int)(r - bh * m);
     const int si = i < a.sink ? i : a.n - a.window + (i - a.sink);
-    a.dst_pos[i] = a.src_pos[si];
-    if (a.src_row && i < a.n_quant_new) {
-        const RowRemap r = row_remap(a.src_row, a.n, a.sink, a.window);
-        const int old = a.src_row[si];
-        a.dst_row[i] = i < a.sink ? old : old - r.w_first + r.base;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (k >= a.n_buf) break;
+        const int rb = a.row_bytes[k];
+        const uint8_t* src = static_cast<const uint8_t*>(a.src[k]) + (bh * a.cap + si) * rb;
+        uint8_t* dst = static_cast<uint8_t*>(a.dst[k]) + (bh * a.cap + i) * rb;
+        if ((rb & 15) == 0) {
+            if (u * 16 < rb)
+                *reinterpret_cast<uint4*>(dst + u * 16) = *reinterpret_cast<const uint4*>(src + u * 16);
+        } else if (u == 0) {
+            copy_row(src, dst, rb);
+        }
+    }
+    if (bh == 0 && u == 0) {
+        a.dst_pos[i] = a.src_pos[si];
+        if (a.src_row && i < a.n_quant_new) {
+            const RowRemap rr = row_remap(a.src_row, a.n, a.sink, a.window);
+            const int old = a.src_row[si];
+            a.dst_row[i] = i < a.sink ? old : old - rr.w_first + rr.base;
+        }
     }
 }
 
@@ -95,35 +119,17 @@ __global__ __launch_bounds__(256) void copy16_kernel(const uint4* __restrict__ s
     if (i < n16) dst[i] = src[i];
 }
 
-template <typename U>
-hipError_t gather(const void* src, void* dst, int row_bytes, const EvictArgs& a, hipStream_t s) {
-    const int upr = row_bytes / (int)sizeof(U);
-    const int64_t total = (int64_t)a.BH * (a.sink + a.window) * upr;
-    const unsigned blocks = (unsigned)((total + 255) / 256);
-    hipLaunchKernelGGL((gather_rows_kernel<U>), dim3(blocks), dim3(256), 0, s,
-                       static_cast<const U*>(src), static_cast<U*>(dst), upr, a.BH, a.cap, a.n,
-                       a.sink, a.window);
-    return hipGetLastError();
-}
-
 }  // namespace
 
 hipError_t launch_evict(const EvictArgs& a, hipStream_t s) {
     hipError_t e;
-    for (int k = 0; k < a.n_buf; ++k) {
-        const int rb = a.row_bytes[k];
-        if (rb % 16 == 0) e = gather<uint4>(a.src[k], a.dst[k], rb, a, s);
-        else if (rb % 8 == 0) e = gather<uint2>(a.src[k], a.dst[k], rb, a, s);
-        else if (rb % 4 == 0) e = gather<uint32_t>(a.src[k], a.dst[k], rb, a, s);
-        else if (rb % 2 == 0) e = gather<uint16_t>(a.src[k], a.dst[k], rb, a, s);
-        else e = gather<uint8_t>(a.src[k], a.dst[k], rb, a, s);
-        if (e != hipSuccess) return e;
-    }
-    const int m = a.sink + a.window;
-    hipLaunchKernelGGL(pos_rows_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, a);
+    int upr = 1;                                   // 16-byte units of the widest row
+    for (int k = 0; k < a.n_buf; ++k) upr = a.row_bytes[k] / 16 > upr ? a.row_bytes[k] / 16 : upr;
+    const int64_t threads = (int64_t)a.BH * (a.sink + a.window) * upr;
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a, upr);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (a.src_row) {
-        const int n_quant_old = a.n_quant_new + (a.n - m);
+        const int n_quant_old = a.n_quant_new + (a.n - (a.sink + a.window));
         const int64_t total = (int64_t)a.BH * a.rows * (a.table_row_bytes / 16);
         hipLaunchKernelGGL(table_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a,
                            n_quant_old);

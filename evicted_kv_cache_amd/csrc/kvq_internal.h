@@ -68,7 +68,16 @@ struct RowQuantArgs {
     int B, H, n, D, cap, slot0;
     int kind, bits, group, in_dtype;
 };
-hipError_t launch_row_quant(const RowQuantArgs& a, hipStream_t s);
+// One fused launch: K rows (per-token kinds), V rows and positions.
+struct RowAppendArgs {
+    RowQuantArgs rows;      // shape: B, H, n, D, cap, slot0, in_dtype
+    const void* k_src; void* k_codes; void* k_meta; const float* k_bias;
+    int k_kind, k_bits, k_group;
+    const void* v_src; void* v_codes; void* v_meta;
+    int v_kind, v_bits, v_group;
+    int32_t* pos; int first_pos;
+};
+hipError_t launch_row_append(const RowAppendArgs& a, hipStream_t s);
 
 // KIVI per-channel: close `n_groups` groups made of the current residual
 // (r0 keys) followed by new keys, then store the remaining new keys in the
@@ -87,7 +96,6 @@ struct ChannelQuantArgs {
 };
 hipError_t launch_channel_quant(const ChannelQuantArgs& a, hipStream_t s);
 
-hipError_t launch_fill_pos(int32_t* pos, int slot0, int first_pos, int n, hipStream_t s);
 
 // Decode attention.
 struct DecodeArgs {

@@ -39,11 +39,12 @@ __device__ __forceinline__ half8 load_half8(const uint16_t* p) {
 // acc row index (within a 32-row tile) of accumulator element v for lane half kh.
 __device__ __forceinline__ int acc_row(int v, int kh) { return 8 * (v >> 2) + 4 * kh + (v & 3); }
 
+template <int D>
 __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kh = lane >> 5, l32 = lane & 31;
-    const int S = a.S, D = a.D;
+    const int S = a.S;
     const int wc = min(a.w, S);
     const int row0 = S - wc;
     const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
@@ -55,6 +56,7 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     for (int nt = 0; nt * 32 < wc; ++nt) {
         const int wr = nt * 32 + l32;
         floatx16 acc = {};
+#pragma unroll
         for (int ks = 0; ks < D; ks += 16) {
             const int d0 = ks + kh * 8;
             half8 A = {}, Bv = {};
@@ -88,25 +90,42 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     }
 }
 
+template <int D>
 __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kh = lane >> 5, l32 = lane & 31;
-    const int S = a.S, D = a.D;
+    const int S = a.S;
     const int wc = min(a.w, S);
     const int row0 = S - wc;
     const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
     const float c = 1.4426950408889634f / sqrtf((float)D);
     __shared__ float Mrow[kMaxWindow], invL[kMaxWindow];
-    if (tid < wc) {
-        const float* st = a.stats + (((int64_t)b * a.H + h) * a.n_chunks * wc + tid) * 2;
-        float M = -INFINITY;
-        for (int ch = 0; ch < a.n_chunks; ++ch) M = fmaxf(M, st[(int64_t)ch * wc * 2]);
-        float L = 0.0f;
-        for (int ch = 0; ch < a.n_chunks; ++ch)
-            L += st[(int64_t)ch * wc * 2 + 1] * exp2f(st[(int64_t)ch * wc * 2] - M);
-        Mrow[tid] = M;
-        invL[tid] = 1.0f / L;
+    {
+        // merge the per-chunk (max, sum) of every window row: tpr threads per
+        // row stride over the chunks, then combine with lane shuffles
+        const int tpr = wc <= 32 ? 8 : (wc <= 64 ? 4 : 2);
+        const int r = tid / tpr, j = tid % tpr;
+        float M = -INFINITY, L = 0.0f;
+        if (r < wc) {
+            const float* st = a.stats + (((int64_t)b * a.H + h) * a.n_chunks * wc + r) * 2;
+            for (int ch = j; ch < a.n_chunks; ch += tpr) {
+                const float m2 = st[(int64_t)ch * wc * 2], l2 = st[(int64_t)ch * wc * 2 + 1];
+                const float Mn = fmaxf(M, m2);
+                L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
+                M = Mn;
+            }
+        }
+        for (int off = 1; off < tpr; off <<= 1) {
+            const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(L, off);
+            const float Mn = fmaxf(M, m2);
+            L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
+            M = Mn;
+        }
+        if (r < wc && j == 0) {
+            Mrow[r] = M;
+            invL[r] = 1.0f / L;
+        }
     }
     __syncthreads();
     const int key = chunk * kChunk + wave * 32 + l32;
@@ -114,6 +133,7 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     for (int mt = 0; mt * 32 < wc; ++mt) {
         const int wr = mt * 32 + l32;
         floatx16 acc = {};
+#pragma unroll
         for (int ks = 0; ks < D; ks += 16) {
             const int d0 = ks + kh * 8;
             half8 A = {}, Bv = {};
@@ -142,7 +162,8 @@ __device__ __forceinline__ uint32_t order_key(float s) {
 }
 
 // Inclusive scan of one value per thread over a block of nthreads (<= 1024)
-// threads; returns the inclusive prefix, and *total the block sum.
+// threads; returns the inclusive prefix, and *total the block sum.  Wave
+// scans by shuffles; the (<= 16) wave totals are scanned by wave 0.
 __device__ uint32_t block_scan(uint32_t v, uint32_t* lds16, uint32_t* total) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = (blockDim.x + 63) >> 6;
@@ -154,10 +175,16 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t* lds16, uint32_t* total) {
     }
     if (lane == 63) lds16[wave] = x;
     __syncthreads();
-    if (tid == 0) {
-        uint32_t run = 0;
-        for (int w = 0; w < nw; ++w) { const uint32_t t = lds16[w]; lds16[w] = run; run += t; }
-        lds16[16] = run;
+    if (wave == 0) {
+        const uint32_t t = lane < nw ? lds16[lane] : 0u;
+        uint32_t incl = t;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const uint32_t y = __shfl_up(incl, off);
+            if (lane >= off) incl += y;
+        }
+        if (lane < nw) lds16[lane] = incl - t;      // exclusive prefix of the wave totals
+        if (lane == nw - 1) lds16[16] = incl;
     }
     __syncthreads();
     const uint32_t res = x + lds16[wave];
@@ -166,6 +193,11 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t* lds16, uint32_t* total) {
     return res;
 }
 
+// Keys of one head are staged in LDS when S <= kSelLds (64 KB), else read
+// from global memory on every pass.
+constexpr int kSelLds = 16384;
+
+template <bool LDS_KEYS>
 __global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, int S, int n_sink,
                                                            int budget, int32_t* kept_all) {
     const int64_t bh = blockIdx.x;
@@ -180,20 +212,34 @@ __global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, 
         for (int i = tid; i < n_keep; i += blockDim.x) kept[i] = i;
         return;
     }
-    __shared__ uint32_t hist[256];
+    extern __shared__ uint32_t keys_lds[];
+    if constexpr (LDS_KEYS) {
+        for (int j = tid; j < S; j += blockDim.x) keys_lds[j] = order_key(sc[j]);
+        __syncthreads();
+    }
+    auto key_of = [&](int j) -> uint32_t {
+        if constexpr (LDS_KEYS) return keys_lds[j];
+        else return order_key(sc[j]);
+    };
+    __shared__ uint32_t whist[16][256];     // one histogram per wave: no cross-wave contention
     __shared__ uint32_t lds16[17];
     __shared__ uint32_t s_prefix, s_krem;
     uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
+    const int wv = tid >> 6;
     for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) hist[tid] = 0;
+        for (int i = tid; i < 16 * 256; i += blockDim.x) (&whist[0][0])[i] = 0;
         __syncthreads();
         for (int j = n_s + tid; j < S; j += blockDim.x) {
-            const uint32_t key = order_key(sc[j]);
-            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            const uint32_t key = key_of(j);
+            if ((key & mask) == prefix) atomicAdd(&whist[wv][(key >> shift) & 255u], 1u);
         }
         __syncthreads();
-        // bins from the top: thread t holds bin 255 - t
-        const uint32_t cnt = tid < 256 ? hist[255 - tid] : 0u;
+        // bins from the top: thread t holds bin 255 - t, summed over the waves
+        uint32_t cnt = 0;
+        if (tid < 256) {
+#pragma unroll
+            for (int w = 0; w < 16; ++w) cnt += whist[w][255 - tid];
+        }
         uint32_t tot;
         const uint32_t incl = block_scan(cnt, lds16, &tot);
         if (tid < 256 && incl - cnt < krem && incl >= krem) {
@@ -210,7 +256,7 @@ __global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, 
     const int per = (S + (int)blockDim.x - 1) / (int)blockDim.x;
     const int j0 = min(S, tid * per), j1 = min(S, j0 + per);
     uint32_t nties = 0;
-    for (int j = max(j0, n_s); j < j1; ++j) nties += (order_key(sc[j]) == tau);
+    for (int j = max(j0, n_s); j < j1; ++j) nties += (key_of(j) == tau);
     uint32_t tot;
     uint32_t tie_rank = block_scan(nties, lds16, &tot) - nties;
     uint32_t nsel = 0;
@@ -218,7 +264,7 @@ __global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, 
         bool sel;
         if (j < n_s) sel = true;
         else {
-            const uint32_t key = order_key(sc[j]);
+            const uint32_t key = key_of(j);
             if (key > tau) sel = true;
             else if (key == tau) sel = (tie_rank++ < krem);
             else sel = false;
@@ -231,7 +277,7 @@ __global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, 
         bool sel;
         if (j < n_s) sel = true;
         else {
-            const uint32_t key = order_key(sc[j]);
+            const uint32_t key = key_of(j);
             if (key > tau) sel = true;
             else if (key == tau) sel = (tie_rank++ < krem);
             else sel = false;
@@ -268,19 +314,30 @@ size_t snapkv_ws_bytes(int B, int H, int S, int D, int w) {
     return stats + (size_t)B * H * S * sizeof(float);
 }
 
-hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s) {
+template <int D>
+static hipError_t launch_scores_d(const SnapArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_chunks, (unsigned)a.H, (unsigned)a.B);
-    hipLaunchKernelGGL(snap_stats_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((snap_stats_kernel<D>), grid, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(snap_scores_kernel, grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((snap_scores_kernel<D>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
+}
+
+hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s) {
+    if (a.D == 128) return launch_scores_d<128>(a, s);
+    if (a.D == 64) return launch_scores_d<64>(a, s);
+    return launch_scores_d<32>(a, s);
 }
 
 hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_sink, int budget,
                                 int32_t* kept, hipStream_t s) {
-    hipLaunchKernelGGL(snap_select_kernel, dim3((unsigned)(B * H)), dim3(1024), 0, s,
-                       scores, S, n_sink, budget, kept);
+    if (S <= kSelLds)
+        hipLaunchKernelGGL((snap_select_kernel<true>), dim3((unsigned)(B * H)), dim3(1024),
+                           (size_t)S * sizeof(uint32_t), s, scores, S, n_sink, budget, kept);
+    else
+        hipLaunchKernelGGL((snap_select_kernel<false>), dim3((unsigned)(B * H)), dim3(1024), 0, s,
+                           scores, S, n_sink, budget, kept);
     return hipGetLastError();
 }
 

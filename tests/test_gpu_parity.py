@@ -299,3 +299,27 @@ def test_periodic_eviction_and_batch_eviction_kivi4():
     # streaming state: slots [0,3) + last window after the final eviction point
     assert_same_state(cs, os_)
     assert_same_state(dst, ob.evict(3, 64))
+
+
+def test_quantize_codes_on_rounding_boundaries():
+    """Quotients exactly on, and one ulp either side of, half-integers (where a
+    reciprocal-based quotient could round differently): codes stay bit-exact."""
+    rng = np.random.default_rng(99)
+    B, H, T, D = 1, 2, 64, 64
+    # groups of 32 with min 0 and max 15/8 -> scale 1/8, zero 0 (4-bit); interior
+    # values (k + 0.5)/8 nudged by -1, 0, +1 ulp
+    k = rng.integers(0, 15, size=(B, H, T, D)).astype(np.float32)
+    x = (k + 0.5) / 8
+    nudge = rng.integers(-1, 2, size=x.shape)
+    x = np.where(nudge < 0, np.nextafter(x, -np.inf), np.where(nudge > 0, np.nextafter(x, np.inf), x))
+    x = x.astype(np.float32)
+    x[..., 0::32] = 0.0
+    x[..., 1::32] = 15 / 8
+    v = x.copy()
+    for k_kind, k_bits, k_group in (("tok_affine", 4, 32), ("tok_affine", 8, 32), ("tok_sym4", 4, 32),
+                                    ("kivi_ch", 4, 32)):
+        pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=D, capacity=T, k_kind=k_kind, k_bits=k_bits,
+                         k_group=k_group, v_kind="tok_affine", v_bits=4, v_group=32, in_dtype="f32")
+        say("rounding boundaries", k_kind, k_bits)
+        c, o = build_pair(pl, ol, x, v, "f32")
+        assert_same_state(c, o)
