@@ -218,8 +218,19 @@ def main():
         one_k = torch.randn(B, Hkv, 1, D, device=dev).to(torch.bfloat16)
         ms1 = time_stream(lambda: (K.kvq_cache_reset(c1) if c1.n_stored >= 4000 else None,
                                    K.kvq_quantize_append(L1, c1, one_k, one_k)), 200, 10, torch)
+        # device time per append: 64 appends captured in one HIP graph and
+        # replayed, so host marshalling is out of the timed region
+        K.kvq_cache_reset(c1)
+        n_cap = 64
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n_cap):
+                K.kvq_quantize_append(L1, c1, one_k, one_k)
+        msg = time_stream(g.replay, 20, 3, torch) / n_cap
         rows["A_append_one_token"] = {"workload": f"{w.name} append n_new=1 (B={B}, Hkv={Hkv})",
-                                      "us": round(ms1 * 1e3, 2)}
+                                      "us": round(msg * 1e3, 2),
+                                      "us_host_inclusive": round(ms1 * 1e3, 2)}
+        del g
 
     # ---- row C: StreamingLLM compaction of the headline cache
     if "C" in args.rows:
