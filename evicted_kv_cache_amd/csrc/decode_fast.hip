@@ -20,21 +20,27 @@
 //   token; the query is held as fp16 pairs scaled by a power of two shared by
 //   the head group (exact for bf16/fp16 queries).  The group's scale s and zero
 //   z are factored out of the dot product:  q . k = s (q . u) + z sum(q).
-//   The four quarter partial logits are combined with a DPP reduce-scatter
-//   that leaves lane quarter h with query head h.
+//   The four quarter partials are reduced over the lane quad with DPP adds
+//   that leave lane quarter h with query head h.  With K groups of at least
+//   64 channels the reduce runs in two steps: within each 64-channel half
+//   (one scale, applied once to the pair sum), then across the halves; the
+//   zero-point terms z sum(q) of both groups are added after the reduce.
 // * Softmax: lane (t, h) computes p for head h of tokens t and t+16 (one
 //   exp each) and writes the fp16 weight pair (p_t s_t, p_t+16 s_t+16) to
 //   LDS; the running max is rescaled only when a wave sees a larger logit,
 //   so weights stay <= 1 and never overflow fp16.
-// * PV: lane (phase, 8-channel chunk) reads the codes of tokens t and t+16,
-//   v_perm_b32 interleaves their bytes and one AND per channel gives the
-//   (u_t, u_t+16) subnormal pair; v_dot2_f32_f16 with the weight pair does
-//   two token MACs.  The zero points and the fp16 rounding of the weights
-//   are accounted exactly in fp32:
+// * PV: lane (phase, 8-channel chunk) reads the codes of tokens t and t+16;
+//   one v_perm_b32 per byte position gives the pair of whole bytes
+//   (b_t, b_t+16), b = u_2k + 16 u_2k+1, as fp16 subnormals, and one AND its
+//   low nibbles; v_dot2_f32_f16 with the weight pair does two token MACs on
+//   each, and the high-nibble channel is (byte sum - low sum) / 16 at the end.
+//   The zero points and the fp16 rounding of the weights are accounted
+//   exactly in fp32:
 //     o = sum_t w^_t u_t + sum_t p_t (z_t + 8 s_t) - 8 sum_t w^_t
 //   so rounding a weight only perturbs w (u - 8).
 // * Tails need no clamping: loads go through buffer resources whose size is
-//   the valid part of the tile, and out-of-range loads return zero.
+//   the valid part of the tile, and out-of-range loads return zero.  Only the
+//   last tile of a split can hold invalid tokens; it alone masks its logits.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -56,10 +62,24 @@ __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                   false);
 }
+// First product of a chain: v_dot2_f32_f16 with an inline zero accumulator
+// (the tied-accumulator form would need a separate move of zero).
+__device__ __forceinline__ float dot2_f16_first(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
 // Round-to-nearest-even pack of two fp32 into an fp16 pair.
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
     half2_t h = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, h);
+}
+// (low fp16 half of h) * y in one v_fma_mix_f32 with a +0 addend (a -0
+// product comes out as +0, which no caller distinguishes)
+__device__ __forceinline__ float mul_lo(uint32_t h, float y) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(y));
+    return r;
 }
 // fp16 halves of a packed pair, widened (folds into v_fma_mix_f32 operands)
 __device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(half2_t, u).x; }
@@ -70,6 +90,15 @@ __device__ __forceinline__ float quad_from_minus(float v) {
     constexpr int ctrl = K == 1 ? 0x93 : K == 2 ? 0x4E : 0x39;   // quad_perm [3,0,1,2] / [2,3,0,1] / [1,2,3,0]
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
 }
+
+// DPP quad exchange: value of lane l ^ X (X = 1 or 2) within the lane's quad.
+template <int X>
+__device__ __forceinline__ float quad_xor(float v) {
+    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+}
+template <bool B>
+struct Flag { static constexpr bool value = B; };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -99,6 +128,7 @@ template <int NVG>
 struct TileLoads {
     u32x4 k[2];          // codes of the lane's quarter for tokens t and t+16
     uint32_t km[2];      // K (scale, zero) of the quarter's group, tokens t and t+16
+    uint32_t kmo[2];     // K (scale, zero) of the other 64-channel half's group (K groups of 64)
     VMeta<NVG> vm;
     uint32_t v[4][2];    // V code words (8 channels) of tokens ph+4j and ph+4j+16
 };
@@ -108,6 +138,12 @@ template <int QDT, int GK, int GV>
 __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     constexpr int NKG = kD / GK;      // K groups per row
     constexpr int NVG = kD / GV;      // V groups per row
+    // When each 64-channel half of head_dim lies in one K group (GK >= 64),
+    // the four quarter partials of a head are reduced in two steps: first
+    // within the half (same scale, applied once to the pair sum), then across
+    // the halves.  With GK = 32 every quarter is scaled before one 3-step
+    // rotation reduce.
+    constexpr bool kHalfReduce = GK >= 64;
 
     // the wave index is uniform across the wave; say so, so that tile bases and
     // buffer descriptors stay in scalar registers
@@ -127,6 +163,14 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     // reduce-scatter the lane owns query head hq = q4.
     const int t16 = lane >> 2, q4 = lane & 3;
     const int kg = (32 * q4) / GK;                          // K group of the quarter
+    // query head held in dot register j.  Half reduce: register order
+    // [q4, q4^2, q4^1, q4^3], so that step 1 (partner q4^1) adds registers
+    // (0, 2) and (1, 3) of the two lanes and step 2 (partner q4^2) leaves
+    // head q4 in lane quarter q4.  Rotation reduce: head (q4 + j) % 4.
+    auto head_of = [&](int j) {
+        if constexpr (kHalfReduce) return q4 ^ (j == 1 ? 2 : j == 2 ? 1 : j);
+        else return (q4 + j) & 3;
+    };
     // PV role: phase ph (tokens ph + 4j, j < 4, and +16), chunk c (channels 8c..8c+7)
     const int ph = lane >> 4, c = lane & 15;
     const int vg_c = (8 * c) / GV;
@@ -156,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     float qsum[kGQ];
 #pragma unroll
     for (int j = 0; j < kGQ; ++j) {
-        const int h = (q4 + j) & 3;
+        const int h = head_of(j);
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -183,6 +227,25 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     float qsk[kGQ];
 #pragma unroll
     for (int h = 0; h < kGQ; ++h) qsk[h] = ldexpf(qsum[h], -(qexp + 24));
+    // half reduce: the zero-point term of head q4 is added after the reduce,
+    // as z_own qz_own + z_other qz_other with qz = scale_log2 * (sum of q over
+    // the K group) for the group of this lane's half and the other group
+    float qz_own = 0.0f, qz_oth = 0.0f;
+    if constexpr (kHalfReduce) {
+        const uint16_t* qh = q16 + q4 * kD;
+#pragma unroll
+        for (int k = 0; k < kD / 8; ++k) {
+            const uint4 xx = *reinterpret_cast<const uint4*>(qh + 8 * k);
+            const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
+            float t = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) t += q_elem<QDT>(e4[i] & 0xFFFFu) + q_elem<QDT>(e4[i] >> 16);
+            if ((8 * k) / GK == kg) qz_own += t;
+            else qz_oth += t;
+        }
+        qz_own *= a.scale_log2;
+        qz_oth *= a.scale_log2;
+    }
 
     const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
     const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kRowB;
@@ -194,7 +257,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     float corr[NVG];              // head q4, per V group
 #pragma unroll
     for (int g = 0; g < NVG; ++g) corr[g] = 0.0f;
-    float acc[kGQ][8];            // PV: head h, channel 8c + i (scaled by 2^-24 / 2^-20)
+    float acc[kGQ][8];            // PV: head h; i = 2k: channel 8c+2k, i = 2k+1: byte k (scaled 2^-24)
 #pragma unroll
     for (int h = 0; h < kGQ; ++h)
 #pragma unroll
@@ -202,7 +265,9 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 
     auto load_tile = [&](int tile, TileLoads<NVG>& L) {
         const int tb = t_lo + tile * kTileT;
-        const uint32_t nv = (uint32_t)min(kTileT, t_hi - tb);          // valid tokens in the tile
+        // valid tokens in the tile (0 past the end: those loads return zeros);
+        // kept in a scalar register so the buffer descriptors stay uniform
+        const uint32_t nv = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kTileT, t_hi - tb)));
         const __amdgpu_buffer_rsrc_t rk = rsrc(kcodes + (int64_t)tb * kRowB, nv * kRowB);
         const __amdgpu_buffer_rsrc_t rkm = rsrc(kmeta + (int64_t)tb * NKG, nv * NKG * 4);
         const __amdgpu_buffer_rsrc_t rvm = rsrc(vmeta + (int64_t)tb * NVG, nv * NVG * 4);
@@ -218,6 +283,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             const uint32_t tok = t16 + 16 * p;
             L.k[p] = bload128(rk, tok * kRowB + 16 * q4);
             L.km[p] = bload32(rkm, (tok * NKG + kg) * 4);
+            if constexpr (GK == 64) L.kmo[p] = bload32(rkm, (tok * NKG + (kg ^ 1)) * 4);
             if constexpr (NVG == 1) {
                 L.vm.m[p][0] = bload32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
@@ -230,13 +296,14 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         }
     };
 
-    auto process = [&](const TileLoads<NVG>& L, int tile) {
+    auto process = [&](const TileLoads<NVG>& L, int tile, auto tail) {
+        constexpr bool kTail = decltype(tail)::value;     // the tile may hold invalid tokens
         const int tb = t_lo + tile * kTileT;
         // -------------------------------------------- QK^T, two passes (t16, t16 + 16)
         float xs[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            float dsum[kGQ] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float dsum[kGQ];
             const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
@@ -246,19 +313,31 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                 const uint32_t u2 = w8 & 0x000F000Fu, u3 = w8 & 0x00F000F0u;   // (n2,n6), (n3,n7)
 #pragma unroll
                 for (int h = 0; h < kGQ; ++h) {
-                    dsum[h] = dot2_f16(u0, qv[h][4 * k + 0], dsum[h]);
+                    dsum[h] = k == 0 ? dot2_f16_first(u0, qv[h][0]) : dot2_f16(u0, qv[h][4 * k + 0], dsum[h]);
                     dsum[h] = dot2_f16(u1, qv[h][4 * k + 1], dsum[h]);
                     dsum[h] = dot2_f16(u2, qv[h][4 * k + 2], dsum[h]);
                     dsum[h] = dot2_f16(u3, qv[h][4 * k + 3], dsum[h]);
                 }
             }
-            float part[kGQ];
+            float x;
+            if constexpr (kHalfReduce) {
+                // step 1 within the half, scale of the half's group, step 2 across halves
+                const float h0 = mul_lo(L.km[p], dsum[0] + quad_xor<1>(dsum[2]));
+                const float h1 = mul_lo(L.km[p], dsum[1] + quad_xor<1>(dsum[3]));
+                const float sum = h0 + quad_xor<2>(h1);
+                float zt = f16hi(L.km[p]) * qz_own;
+                if constexpr (GK == 64) zt = fmaf(f16hi(L.kmo[p]), qz_oth, zt);
+                x = fmaf(sum, kC, zt);
+            } else {
+                float part[kGQ];
 #pragma unroll
-            for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16hi(L.km[p]) * qsk[h]);
-            // head q4 of this token: part[0] here plus part[k] of lane quarter q4 - k
-            const float x = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
-                             quad_from_minus<3>(part[3])) * kC;
-            xs[p] = (tb + t16 + 16 * p < t_hi) ? x : -INFINITY;
+                for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16hi(L.km[p]) * qsk[h]);
+                // head q4 of this token: part[0] here plus part[k] of lane quarter q4 - k
+                x = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
+                     quad_from_minus<3>(part[3])) * kC;
+            }
+            if constexpr (kTail) xs[p] = (tb + t16 + 16 * p < t_hi) ? x : -INFINITY;
+            else xs[p] = x;
         }
 
         // -------------------------------------------- online softmax (rescale on a new max)
@@ -268,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 #pragma unroll
             for (int off = 4; off < 64; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
             const float m_new = fmaxf(m_lane, mt);
-            const float alpha = exp2f(m_lane - m_new);
+            const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);
             m_lane = m_new;
             l_lane *= alpha;
 #pragma unroll
@@ -281,13 +360,14 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                 for (int i = 0; i < 8; ++i) acc[h][i] *= ah;
             }
         }
-        const float p0 = exp2f(xs[0] - m_lane);
-        const float p1 = exp2f(xs[1] - m_lane);
+        // v_exp_f32: weights below 2^-126 of the running max may flush to zero
+        const float p0 = __builtin_amdgcn_exp2f(xs[0] - m_lane);
+        const float p1 = __builtin_amdgcn_exp2f(xs[1] - m_lane);
         l_lane += p0 + p1;
 #pragma unroll
         for (int g = 0; g < NVG; ++g) {
             const uint32_t m0 = L.vm.m[0][g], m1 = L.vm.m[1][g];
-            const uint32_t pair = pack_f16(p0 * f16lo(m0), p1 * f16lo(m1));
+            const uint32_t pair = pack_f16(mul_lo(m0, p0), mul_lo(m1, p1));
             float cg = corr[g];
             cg = fmaf(p0, fmaf(8.0f, f16lo(m0), f16hi(m0)), cg);
             cg = fmaf(p1, fmaf(8.0f, f16lo(m1), f16hi(m1)), cg);
@@ -302,12 +382,16 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             const uint4 wp = *reinterpret_cast<const uint4*>(&wbuf[wave][ph + 4 * j][vg_c][0]);
             const uint32_t wpair[kGQ] = {wp.x, wp.y, wp.z, wp.w};
             const uint32_t w0 = L.v[j][0], w1 = L.v[j][1];
-            // X = [w1.b1 w1.b0 w0.b1 w0.b0], Y = [w1.b3 w1.b2 w0.b3 w0.b2]
-            const uint32_t X = __builtin_amdgcn_perm(w1, w0, 0x05040100u);
-            const uint32_t Y = __builtin_amdgcn_perm(w1, w0, 0x07060302u);
-            const uint32_t X8 = X >> 8, Y8 = Y >> 8;
-            const uint32_t cp[8] = {X & 0x000F000Fu, X & 0x00F000F0u, X8 & 0x000F000Fu, X8 & 0x00F000F0u,
-                                    Y & 0x000F000Fu, Y & 0x00F000F0u, Y8 & 0x000F000Fu, Y8 & 0x00F000F0u};
+            // byte k of both tokens as an fp16 subnormal pair (b_t, b_t+16),
+            // b = u_2k + 16 u_2k+1, and its low nibbles (u_2k of both tokens);
+            // the high-nibble channel is separated once at the end
+            uint32_t cp[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t P = __builtin_amdgcn_perm(w1, w0, 0x0C040C00u + 0x00010001u * k);
+                cp[2 * k] = P & 0x000F000Fu;
+                cp[2 * k + 1] = P;
+            }
 #pragma unroll
             for (int h = 0; h < kGQ; ++h)
 #pragma unroll
@@ -318,18 +402,30 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 
     // two load buffers in ping-pong: the next tile's loads are in flight while
     // the current tile is computed
+    // Full tiles run in a ping-pong loop with unconditional prefetches (a
+    // prefetch past the end reads zeros and is never used); only the split's
+    // last tile can be partial and is processed with token masking.
     TileLoads<NVG> A, B2;
-    if (tile0 < tile1) load_tile(tile0, A);
-    for (int tile = tile0; tile < tile1; tile += 2) {
-        if (tile + 1 < tile1) load_tile(tile + 1, B2);
-        process(A, tile);
-        if (tile + 1 >= tile1) break;
-        if (tile + 2 < tile1) load_tile(tile + 2, A);
-        process(B2, tile + 1);
+    const int full_end = min(tile1, (t_hi - t_lo) / kTileT);
+    int tile = tile0;
+    load_tile(tile, A);
+    for (; tile + 1 < full_end; tile += 2) {
+        load_tile(tile + 1, B2);
+        process(A, tile, Flag<false>{});
+        load_tile(tile + 2, A);
+        process(B2, tile + 1, Flag<false>{});
     }
+    if (tile < full_end) {                // one full tile left
+        process(A, tile, Flag<false>{});
+        ++tile;
+        if (tile < tile1) load_tile(tile, A);
+    }
+    if (tile < tile1) process(A, tile, Flag<true>{});
 
     // ---------------------------------------------------- wave-level reduction
-    // PV: sum the 4 phases (lanes c, c+16, c+32, c+48) and undo the code scales
+    // PV: sum the 4 phases (lanes c, c+16, c+32, c+48), undo the 2^-24 code
+    // scale and split each byte sum into its two channels:
+    // u_2k+1 = (b - u_2k) / 16
 #pragma unroll
     for (int h = 0; h < kGQ; ++h)
 #pragma unroll
@@ -337,7 +433,15 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             float v = acc[h][i];
             v += __shfl_xor(v, 16);
             v += __shfl_xor(v, 32);
-            acc[h][i] = v * ((i & 1) ? 1048576.0f : 16777216.0f);   // 2^20 (high nibble), 2^24
+            acc[h][i] = v;
+        }
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float lo = acc[h][2 * k], whole = acc[h][2 * k + 1];
+            acc[h][2 * k] = lo * 16777216.0f;                   // 2^24
+            acc[h][2 * k + 1] = (whole - lo) * 1048576.0f;      // 2^24 / 16
         }
     // head q4 sums over the lane's tokens: reduce over lanes with equal q4
 #pragma unroll

@@ -41,6 +41,7 @@ def sampled_parity(w, pl, c, out, samples, k_bias=None):
         ref = o.decode(q[None], w.dtype)[0]
         got = out[b, h * g:(h + 1) * g]
         err = attn_err(got, ref)
+        say(f"  attention error {err:.3e} (tolerance {TOL:.0e})")
         assert err <= TOL, (b, h, err)
 
 

@@ -59,6 +59,7 @@ def check_decode(pl, c, o, q, qdt, sm_scale=0.0, tol=TOL):
     got = out.cpu().numpy()
     ref = o.decode(q, qdt, sm_scale)
     err = attn_err(got, ref)
+    say(f"  attention error {err:.3e} (tolerance {tol:.0e})")
     assert np.all(np.isfinite(got))
     assert err <= tol, err
     return got, err
@@ -142,6 +143,23 @@ def test_decode_query_dtypes_and_single_slot():
     for qdt in ("f32", "f16"):
         qq = synth.cast(qf, qdt)
         check_decode(pl, c, o, qq, qdt)
+
+
+@pytest.mark.parametrize("kg,vg", [(kg, vg) for kg in (32, 64, 128) for vg in (32, 64, 128)])
+def test_fast_decode_group_combinations(kg, vg):
+    """4-bit affine K and V at head_dim 128 with 4 query heads per kv-head, for
+    every K / V group size pair: a ragged length split over T (batch 1 x 2
+    kv-heads), so splits hold odd and even tile counts and a partial tile."""
+    w = synth.workload("affine4_g64")
+    B, H, T = 1, 2, 2224
+    k, v, q = gen(w, B, H, T, Hq=8)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind="tok_affine", k_bits=4,
+                     k_group=kg, v_kind="tok_affine", v_bits=4, v_group=vg, in_dtype="bf16")
+    say("fast decode groups", kg, vg)
+    c, o = build_pair(pl, ol, k, v, "bf16", chunks=[(0, 1000), (1000, T)])
+    assert_same_state(c, o)
+    check_decode(pl, c, o, q, "bf16")
+    check_decode(pl, c, o, synth.cast(synth.widen(q, "bf16"), "f16"), "f16")
 
 
 def test_empty_cache_decodes_to_zeros():
