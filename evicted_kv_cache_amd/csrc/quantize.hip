@@ -2,8 +2,8 @@
 //
 // Per-token groups along head_dim (TOK_AFFINE, for V and for mlx-style K) and
 // symmetric 4-bit blocks with optional mean-centering (TOK_SYM4) run one row
-// per group of head_dim/4 lanes, 4 consecutive channels per lane; group
-// min/max (or max|x|) is a butterfly over the lanes of one group.
+// per head_dim/16 lanes, 16 consecutive channels per lane; group min/max (or
+// max|x|) is a butterfly over the lanes of one group.
 // KIVI per-channel keys close whole token groups: one lane per channel pair
 // walks the group's tokens.
 //
@@ -20,17 +20,6 @@
 
 namespace kvq {
 namespace {
-
-template <int DT>
-__device__ __forceinline__ void copy4_raw(const void* src, int64_t si, void* dst, int64_t di) {
-    if constexpr (DT == KVQ_F32) {
-        *reinterpret_cast<float4*>(static_cast<float*>(dst) + di) =
-            *reinterpret_cast<const float4*>(static_cast<const float*>(src) + si);
-    } else {
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(dst) + di) =
-            *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + si);
-    }
-}
 
 // rint(num / den) with the IEEE-rounded quotient, via a reciprocal.  With
 // r = fl(1/den), y = fl(num * r) is within |num/den| * 2^-23 of the exact
@@ -58,185 +47,236 @@ __device__ __forceinline__ uint32_t affine_code(float x, float s, float z, float
 // Row formats of the fused row kernel.
 enum RowFmt { kFmtNone = 0, kFmtPlain = 1, kFmtAff4 = 2, kFmtAff8 = 3, kFmtSym4 = 4 };
 
+constexpr int kEpl = 16;        // elements (channels) per lane in the row kernel
+constexpr int kRowIter = 4;     // row passes per block
+
+// 16 consecutive elements of a row as fp32 (exact widening).
 template <int DT>
-__device__ __forceinline__ void load8_as_f32(const void* p, int64_t i, float v[8]) {
+__device__ __forceinline__ void load16_as_f32(const void* p, int64_t i, float v[kEpl]) {
     if constexpr (DT == KVQ_F32) {
-        const float4 a = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-        const float4 b = *reinterpret_cast<const float4*>(static_cast<const float*>(p) + i + 4);
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-    } else {
-        const uint4 x = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+        const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            if constexpr (DT == KVQ_F16) {
-                v[2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu);
-                v[2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
-            } else {
-                v[2 * k] = bf16_bits_to_f32(w[k] & 0xFFFFu);
-                v[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+            const float4 a = q[k];
+            v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
+        }
+    } else {
+        const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 x = q[h];
+            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (DT == KVQ_F16) {
+                    v[8 * h + 2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu);
+                    v[8 * h + 2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
+                } else {
+                    v[8 * h + 2 * k] = bf16_bits_to_f32(w[k] & 0xFFFFu);
+                    v[8 * h + 2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+                }
             }
         }
     }
 }
 
-// One row part of the fused kernel: lanes of a row hold 8 consecutive channels each.
+// One row part of the fused kernel (K or V).
 struct RowPart {
     const void* src; void* codes; void* meta; const float* bias; int group;
 };
 
-template <int DT, int FMT>
-__device__ __forceinline__ void quant_vals8(const RowPart& r, float x[8], int64_t drow, int64_t bh,
-                                            int lane, int D, int H);
+// max / min over the `lanes` lanes (2, 4 or 8, aligned) holding one group
+__device__ __forceinline__ float group_max(float v, int lanes) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    if (lanes > 2) v = fmaxf(v, __shfl_xor(v, 2));
+    if (lanes > 4) v = fmaxf(v, __shfl_xor(v, 4));
+    return v;
+}
+__device__ __forceinline__ float group_min(float v, int lanes) {
+    v = fminf(v, __shfl_xor(v, 1));
+    if (lanes > 2) v = fminf(v, __shfl_xor(v, 2));
+    if (lanes > 4) v = fminf(v, __shfl_xor(v, 4));
+    return v;
+}
 
-// Plain rows are copied (or, for the centering test seam, centered in fp32);
-// the other formats quantize 8 preloaded values per lane.
+// Quantize the 16 values x of this lane (channels 16 lane .. 16 lane + 15 of
+// row drow) and store codes and metadata.  rint of each quotient comes from
+// the reciprocal product y = num * fl(1/den): with |num/den| <= 256 it is
+// within 2^-15 of the exact quotient and the IEEE quotient within 2^-16, so
+// rint(y) equals rint of the IEEE quotient unless y lies within 2^-14 of a
+// half-integer, i.e. |y - rint(y)| > 0.5 - 2^-14.  Waves with such an
+// element (about 1 in 8000 elements) recompute those with the IEEE divide.
 template <int DT, int FMT>
-__device__ __forceinline__ void quant_row8(const RowPart& r, int64_t row, int64_t drow, int64_t bh,
-                                           int lane, int D, int H) {
-    const int d0 = lane * 8;
-    if constexpr (FMT == kFmtPlain) {
-        if (DT == KVQ_F32 && r.bias) {
-            // test seam: centered keys kept at full precision (fp32 subtract)
-            const float* x = static_cast<const float*>(r.src) + row * D + d0;
-            const float* bb = r.bias + (int64_t)(bh % H) * D + d0;
-            float* y = static_cast<float*>(r.codes) + drow * D + d0;
+__device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t drow, int h, int lane,
+                                        int D) {
+    constexpr float kBand = 0.49993896484375f;    // 0.5 - 2^-14
+    float y[kEpl];
+    bool near = false;
+    uint32_t pk[kEpl / 2];                        // 4-bit: pk[0..1]; 8-bit: pk[0..3]
+    if constexpr (FMT == kFmtSym4) {
+        if (r.bias) {
+            const float* bb = r.bias + (int64_t)h * D + lane * kEpl;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) y[k] = x[k] - bb[k];
-        } else if constexpr (DT == KVQ_F32) {
-            const float4* x = reinterpret_cast<const float4*>(static_cast<const float*>(r.src) + row * D + d0);
-            float4* y = reinterpret_cast<float4*>(static_cast<float*>(r.codes) + drow * D + d0);
-            y[0] = x[0]; y[1] = x[1];
-        } else {
-            *reinterpret_cast<uint4*>(static_cast<uint16_t*>(r.codes) + drow * D + d0) =
-                *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(r.src) + row * D + d0);
+            for (int k = 0; k < kEpl; ++k) x[k] = x[k] - bb[k];
         }
-        return;
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < kEpl; ++k) amax = fmaxf(amax, fabsf(x[k]));
+        amax = fmaxf(amax, __shfl_xor(amax, 1));      // 2 lanes per block of 32
+        float dd = amax / 7.0f;
+        dd = fmaxf(dd, kEps);
+        const uint16_t d16 = f32_to_f16_bits(dd);
+        const float df = f16_bits_to_f32(d16);
+        const float rdf = 1.0f / df;
+#pragma unroll
+        for (int k = 0; k < kEpl; ++k) {
+            const float q = x[k] * rdf;
+            y[k] = rintf(q);
+            near |= fabsf(q - y[k]) > kBand;
+        }
+        if (__builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+            for (int k = 0; k < kEpl; ++k) {
+                const float q = x[k] * rdf;
+                if (fabsf(q - rintf(q)) > kBand) y[k] = rintf(x[k] / df);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kEpl; ++k) y[k] = fminf(fmaxf(y[k], -8.0f), 7.0f) + 8.0f;
+        if ((lane & 1) == 0) static_cast<uint16_t*>(r.meta)[drow * (D >> 5) + (lane >> 1)] = d16;
     } else {
-        float x[8];
-        load8_as_f32<DT>(r.src, row * D + d0, x);
-        quant_vals8<DT, FMT>(r, x, drow, bh, lane, D, H);
+        constexpr int BITS = FMT == kFmtAff4 ? 4 : 8;
+        constexpr float top = (float)((1 << BITS) - 1);
+        const int lpg = r.group / kEpl;               // lanes per group (2, 4 or 8)
+        float mn = x[0], mx = x[0];
+#pragma unroll
+        for (int k = 1; k < kEpl; ++k) { mn = fminf(mn, x[k]); mx = fmaxf(mx, x[k]); }
+        mn = group_min(mn, lpg);
+        mx = group_max(mx, lpg);
+        const float range = mx - mn;
+        float sc = range / top;
+        sc = fmaxf(sc, kEps);
+        const uint16_t s16 = f32_to_f16_bits(sc);
+        const uint16_t z16 = f32_to_f16_bits(mn);
+        const float sf = f16_bits_to_f32(s16);
+        const float zf = f16_bits_to_f32(z16);
+        const float rs = 1.0f / sf;
+#pragma unroll
+        for (int k = 0; k < kEpl; ++k) {
+            const float q = (x[k] - zf) * rs;
+            y[k] = rintf(q);
+            near |= fabsf(q - y[k]) > kBand;
+        }
+        if (__builtin_amdgcn_ballot_w64(near) != 0) {
+#pragma unroll
+            for (int k = 0; k < kEpl; ++k) {
+                const float diff = x[k] - zf;
+                const float q = diff * rs;
+                if (fabsf(q - rintf(q)) > kBand) y[k] = rintf(diff / sf);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kEpl; ++k) y[k] = fminf(fmaxf(y[k], 0.0f), top);   // NaN -> 0
+        if ((lane & (lpg - 1)) == 0)
+            static_cast<uint32_t*>(r.meta)[drow * (D / r.group) + lane / lpg] =
+                (uint32_t)s16 | ((uint32_t)z16 << 16);
+    }
+    if constexpr (FMT == kFmtAff8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            pk[k] = (uint32_t)y[4 * k] | ((uint32_t)y[4 * k + 1] << 8) | ((uint32_t)y[4 * k + 2] << 16) |
+                    ((uint32_t)y[4 * k + 3] << 24);
+        reinterpret_cast<uint4*>(r.codes)[drow * (D >> 4) + lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w |= (uint32_t)y[8 * k + i] << (4 * i);
+            pk[k] = w;
+        }
+        reinterpret_cast<uint2*>(r.codes)[drow * (D >> 4) + lane] = make_uint2(pk[0], pk[1]);
     }
 }
 
-template <int DT, int FMT>
-__device__ __forceinline__ void quant_vals8(const RowPart& r, float x[8], int64_t drow, int64_t bh,
-                                            int lane, int D, int H) {
-    const int d0 = lane * 8;
-    {
-        uint32_t u[8];
-        if constexpr (FMT == kFmtSym4) {
-            if (r.bias) {
-                const float* bb = r.bias + (int64_t)(bh % H) * D + d0;
+// Plain rows are copied (or, for the centering test seam, centered in fp32).
+template <int DT>
+__device__ __forceinline__ void copy_row16(const RowPart& r, int64_t row, int64_t drow, int h, int lane, int D) {
+    const int d0 = lane * kEpl;
+    if constexpr (DT == KVQ_F32) {
+        const float4* x = reinterpret_cast<const float4*>(static_cast<const float*>(r.src) + row * D + d0);
+        float4* y = reinterpret_cast<float4*>(static_cast<float*>(r.codes) + drow * D + d0);
+        if (r.bias) {
+            // test seam: centered keys kept at full precision (fp32 subtract)
+            const float4* bb = reinterpret_cast<const float4*>(r.bias + (int64_t)h * D + d0);
 #pragma unroll
-                for (int k = 0; k < 8; ++k) x[k] = x[k] - bb[k];
+            for (int k = 0; k < 4; ++k) {
+                const float4 a = x[k], c = bb[k];
+                y[k] = make_float4(a.x - c.x, a.y - c.y, a.z - c.z, a.w - c.w);
             }
-            float amax = 0.0f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(x[k]));
-            amax = fmaxf(amax, __shfl_xor(amax, 1));     // 4 lanes per block of 32
-            amax = fmaxf(amax, __shfl_xor(amax, 2));
-            float dd = amax / 7.0f;
-            dd = fmaxf(dd, kEps);
-            const uint16_t d16 = f32_to_f16_bits(dd);
-            const float df = f16_bits_to_f32(d16);
-            const float rdf = 1.0f / df;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                float y = rint_div(x[k], df, rdf);
-                y = fmaxf(y, -8.0f);
-                y = fminf(y, 7.0f);
-                u[k] = (uint32_t)(int)(y + 8.0f);
-            }
-            if ((lane & 3) == 0) static_cast<uint16_t*>(r.meta)[drow * (D >> 5) + (d0 >> 5)] = d16;
         } else {
-            constexpr int BITS = FMT == kFmtAff4 ? 4 : 8;
-            const int lpg = r.group >> 3;                 // lanes per group (4, 8 or 16)
-            float mn = x[0], mx = x[0];
 #pragma unroll
-            for (int k = 1; k < 8; ++k) { mn = fminf(mn, x[k]); mx = fmaxf(mx, x[k]); }
-            for (int off = 1; off < lpg; off <<= 1) {
-                mn = fminf(mn, __shfl_xor(mn, off));
-                mx = fmaxf(mx, __shfl_xor(mx, off));
-            }
-            constexpr float top = (float)((1 << BITS) - 1);
-            float range = mx - mn;
-            float sc = range / top;
-            sc = fmaxf(sc, kEps);
-            const uint16_t s16 = f32_to_f16_bits(sc);
-            const uint16_t z16 = f32_to_f16_bits(mn);
-            const float sf = f16_bits_to_f32(s16);
-            const float zf = f16_bits_to_f32(z16);
-            const float rs = 1.0f / sf;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) u[k] = affine_code(x[k], sf, zf, rs, top);
-            if ((lane & (lpg - 1)) == 0)
-                static_cast<uint32_t*>(r.meta)[drow * (D / r.group) + d0 / r.group] =
-                    (uint32_t)s16 | ((uint32_t)z16 << 16);
+            for (int k = 0; k < 4; ++k) y[k] = x[k];
         }
-        if constexpr (FMT == kFmtAff8) {
-            uint2 pk;
-            pk.x = u[0] | (u[1] << 8) | (u[2] << 16) | (u[3] << 24);
-            pk.y = u[4] | (u[5] << 8) | (u[6] << 16) | (u[7] << 24);
-            reinterpret_cast<uint2*>(r.codes)[drow * (D >> 3) + lane] = pk;
-        } else {
-            uint32_t pk = 0;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) pk |= u[k] << (4 * k);
-            static_cast<uint32_t*>(r.codes)[drow * (D >> 3) + lane] = pk;
-        }
+    } else {
+        const uint4* x = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(r.src) + row * D + d0);
+        uint4* y = reinterpret_cast<uint4*>(static_cast<uint16_t*>(r.codes) + drow * D + d0);
+        y[0] = x[0];
+        y[1] = x[1];
     }
 }
 
 // Fused append of K rows (unless KIVI per-channel, FK == kFmtNone), V rows
-// and positions.  Blocks [0, nbk) quantize K rows, the rest V rows; block 0
-// also writes the positions of the new slots.
+// and positions.  Block (x = bh * n_chunks + chunk, z) covers rows
+// [chunk * rows_per_chunk, +rows_per_chunk) of sequence slice bh, of K
+// (z = 0) or V (z = 1, or z = 0 when K takes the channel path); a row is
+// D / 16 lanes of 16 channels, and each thread takes kRowIter rows, loaded
+// before any is quantized.  Blocks of bh = 0 also write the positions of
+// their rows.
 template <int DT, int FK, int FV>
 __global__ __launch_bounds__(256) void row_append_kernel(RowQuantArgs a, RowPart kp, RowPart vp,
-                                                         int nbk, int nb_total, int32_t* pos, int first_pos) {
-    const int tpr = a.D >> 3;                         // lanes per row (4, 8 or 16)
-    const int rows_per_block = 256 / tpr;
-    if (blockIdx.x == 0 && pos) {
-        for (int i = threadIdx.x; i < a.n; i += 256) pos[a.slot0 + i] = first_pos + i;
+                                                         int n_chunks, int32_t* pos, int first_pos) {
+    const int lpr = a.D / kEpl;                       // lanes per row (2, 4 or 8)
+    const int rpp = 256 / lpr;                        // rows per pass
+    const int rpc = rpp * kRowIter;                   // rows per chunk
+    const int bh = blockIdx.x / n_chunks;             // uniform: scalar division
+    const int chunk = blockIdx.x - bh * n_chunks;
+    const bool is_v = FK == kFmtNone || blockIdx.z == 1;
+    const int lane = threadIdx.x % lpr;
+    const int i_base = chunk * rpc + threadIdx.x / lpr;
+    if (pos && bh == 0 && !(FK != kFmtNone && is_v)) {
+        const int i_end = min(a.n, (chunk + 1) * rpc);
+        for (int i = chunk * rpc + threadIdx.x; i < i_end; i += 256) pos[a.slot0 + i] = first_pos + i;
     }
-    const int64_t total = (int64_t)a.B * a.H * a.n;
-    const int lane = threadIdx.x % tpr;
-    // grid-stride over row blocks: [0, nbk) are K row blocks, the rest V.
-    // Two row blocks per iteration, both loads issued before either is
-    // quantized, so each lane keeps two 16-byte loads in flight.
-    auto row_of = [&](int blk_all, bool& is_k, int64_t& row) {
-        is_k = blk_all < nbk;
-        const int blk = is_k ? blk_all : blk_all - nbk;
-        row = (int64_t)blk * rows_per_block + threadIdx.x / tpr;
-        return blk_all < nb_total && row < total;
-    };
-    for (int b0 = blockIdx.x; b0 < nb_total; b0 += 2 * gridDim.x) {
-        bool ka, kb;
-        int64_t ra, rb;
-        const bool va = row_of(b0, ka, ra);
-        const bool vb = row_of(b0 + gridDim.x, kb, rb);
-        constexpr bool plain_k = FK == kFmtPlain || FK == kFmtNone, plain_v = FV == kFmtPlain;
-        float xa[8], xb[8];
-        if (va && !(ka ? plain_k : plain_v)) load8_as_f32<DT>(ka ? kp.src : vp.src, ra * a.D + lane * 8, xa);
-        if (vb && !(kb ? plain_k : plain_v)) load8_as_f32<DT>(kb ? kp.src : vp.src, rb * a.D + lane * 8, xb);
+    const int h = bh % a.H;
+    auto run = [&](const RowPart& part, auto fmt_tag) {
+        constexpr int FMT = decltype(fmt_tag)::value;
+        if constexpr (FMT == kFmtPlain) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const bool v = t == 0 ? va : vb;
-            if (!v) continue;                             // whole rows (hence groups) skip together
-            const bool is_k = t == 0 ? ka : kb;
-            const int64_t row = t == 0 ? ra : rb;
-            float* x = t == 0 ? xa : xb;
-            const int64_t bh = row / a.n;
-            const int i = (int)(row - bh * a.n);
-            const int64_t drow = bh * a.cap + a.slot0 + i;
-            if (is_k) {
-                if constexpr (FK == kFmtPlain) quant_row8<DT, FK>(kp, row, drow, bh, lane, a.D, a.H);
-                else if constexpr (FK != kFmtNone) quant_vals8<DT, FK>(kp, x, drow, bh, lane, a.D, a.H);
-            } else {
-                if constexpr (FV == kFmtPlain) quant_row8<DT, FV>(vp, row, drow, bh, lane, a.D, a.H);
-                else quant_vals8<DT, FV>(vp, x, drow, bh, lane, a.D, a.H);
+            for (int it = 0; it < kRowIter; ++it) {
+                const int i = i_base + it * rpp;
+                if (i < a.n)
+                    copy_row16<DT>(part, (int64_t)bh * a.n + i, (int64_t)bh * a.cap + a.slot0 + i, h, lane, a.D);
+            }
+        } else {
+            float x[kRowIter][kEpl];
+#pragma unroll
+            for (int it = 0; it < kRowIter; ++it) {
+                const int i = i_base + it * rpp;
+                if (i < a.n) load16_as_f32<DT>(part.src, ((int64_t)bh * a.n + i) * a.D + lane * kEpl, x[it]);
+            }
+#pragma unroll
+            for (int it = 0; it < kRowIter; ++it) {
+                const int i = i_base + it * rpp;
+                if (i < a.n)         // whole rows (hence groups) skip together
+                    quant16<DT, FMT>(part, x[it], (int64_t)bh * a.cap + a.slot0 + i, h, lane, a.D);
             }
         }
+    };
+    if (is_v) {
+        run(vp, std::integral_constant<int, FV>{});
+    } else if constexpr (FK != kFmtNone) {
+        run(kp, std::integral_constant<int, FK>{});
     }
 }
 
@@ -322,16 +362,14 @@ int row_fmt(int kind, int bits) {
 
 template <int DT, int FK, int FV>
 hipError_t launch_append_fv(const RowAppendArgs& a, hipStream_t s) {
-    const int tpr = a.rows.D / 8;
-    const int rpb = 256 / tpr;
-    const int64_t rows = (int64_t)a.rows.B * a.rows.H * a.rows.n;
-    const int nb = (int)((rows + rpb - 1) / rpb);
-    const int nbk = FK == kFmtNone ? 0 : nb;
-    const int nb_total = nbk + nb;
-    const int grid = nb_total < 4096 ? nb_total : 4096;   // 16 blocks per CU, grid-stride beyond
-    hipLaunchKernelGGL((row_append_kernel<DT, FK, FV>), dim3((unsigned)grid), dim3(256), 0, s,
-                       a.rows, RowPart{a.k_src, a.k_codes, a.k_meta, a.k_bias, a.k_group},
-                       RowPart{a.v_src, a.v_codes, a.v_meta, nullptr, a.v_group}, nbk, nb_total, a.pos,
+    const int rpc = (256 / (a.rows.D / kEpl)) * kRowIter;
+    const int n_chunks = (a.rows.n + rpc - 1) / rpc;
+    const int64_t nx = (int64_t)a.rows.B * a.rows.H * n_chunks;
+    if (nx > 0x7FFFFFFF) return hipErrorInvalidValue;
+    dim3 grid((unsigned)nx, 1, FK == kFmtNone ? 1 : 2);
+    hipLaunchKernelGGL((row_append_kernel<DT, FK, FV>), grid, dim3(256), 0, s, a.rows,
+                       RowPart{a.k_src, a.k_codes, a.k_meta, a.k_bias, a.k_group},
+                       RowPart{a.v_src, a.v_codes, a.v_meta, nullptr, a.v_group}, n_chunks, a.pos,
                        a.first_pos);
     return hipGetLastError();
 }
