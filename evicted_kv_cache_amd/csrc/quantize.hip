@@ -48,7 +48,7 @@ __device__ __forceinline__ uint32_t affine_code(float x, float s, float z, float
 enum RowFmt { kFmtNone = 0, kFmtPlain = 1, kFmtAff4 = 2, kFmtAff8 = 3, kFmtSym4 = 4 };
 
 constexpr int kEpl = 16;        // elements (channels) per lane in the row kernel
-constexpr int kRowIter = 4;     // row passes per block
+constexpr int kRowIter = 2;     // row passes per block
 
 // 16 consecutive elements of a row as fp32 (exact widening).
 template <int DT>
@@ -85,27 +85,39 @@ struct RowPart {
     const void* src; void* codes; void* meta; const float* bias; int group;
 };
 
-// max / min over the `lanes` lanes (2, 4 or 8, aligned) holding one group
+// DPP lane exchanges inside a row of 16 lanes: partner l^1, l^2 (quad
+// permutes) and the mirror within 8 lanes (l -> 7 - l), which after the two
+// quad steps pairs the two quads of an 8-lane group.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141;
+
+// max / min over the `lanes` lanes (2, 4 or 8, aligned) holding one group;
+// `lanes` is uniform, so the steps are scalar branches
 __device__ __forceinline__ float group_max(float v, int lanes) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    if (lanes > 2) v = fmaxf(v, __shfl_xor(v, 2));
-    if (lanes > 4) v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, dpp<kDppXor1>(v));
+    if (lanes > 2) v = fmaxf(v, dpp<kDppXor2>(v));
+    if (lanes > 4) v = fmaxf(v, dpp<kDppHalfMirror>(v));
     return v;
 }
 __device__ __forceinline__ float group_min(float v, int lanes) {
-    v = fminf(v, __shfl_xor(v, 1));
-    if (lanes > 2) v = fminf(v, __shfl_xor(v, 2));
-    if (lanes > 4) v = fminf(v, __shfl_xor(v, 4));
+    v = fminf(v, dpp<kDppXor1>(v));
+    if (lanes > 2) v = fminf(v, dpp<kDppXor2>(v));
+    if (lanes > 4) v = fminf(v, dpp<kDppHalfMirror>(v));
     return v;
 }
 
 // Quantize the 16 values x of this lane (channels 16 lane .. 16 lane + 15 of
 // row drow) and store codes and metadata.  rint of each quotient comes from
-// the reciprocal product y = num * fl(1/den): with |num/den| <= 256 it is
-// within 2^-15 of the exact quotient and the IEEE quotient within 2^-16, so
-// rint(y) equals rint of the IEEE quotient unless y lies within 2^-14 of a
-// half-integer, i.e. |y - rint(y)| > 0.5 - 2^-14.  Waves with such an
-// element (about 1 in 8000 elements) recompute those with the IEEE divide.
+// y = num * r with r = v_rcp_f32(den) (within 1 ulp of 1/den): y is within
+// 1.5 * 2^-23 |q| of the exact quotient q and the IEEE quotient within
+// 2^-24 |q|, so for |q| < 255 they differ by less than 2^-14 and rint(y)
+// equals rint of the IEEE quotient unless y lies within 2^-14 of a
+// half-integer, i.e. |y - rint(y)| > 0.5 - 2^-14 (quotients of 255 and more
+// clamp to the top code either way).  Waves with such an element (about 1
+// in 8000 elements) recompute those with the IEEE divide.
 template <int DT, int FMT>
 __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t drow, int h, int lane,
                                         int D) {
@@ -122,18 +134,20 @@ __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t
         float amax = 0.0f;
 #pragma unroll
         for (int k = 0; k < kEpl; ++k) amax = fmaxf(amax, fabsf(x[k]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));      // 2 lanes per block of 32
+        amax = fmaxf(amax, dpp<kDppXor1>(amax));     // 2 lanes per block of 32
         float dd = amax / 7.0f;
         dd = fmaxf(dd, kEps);
         const uint16_t d16 = f32_to_f16_bits(dd);
         const float df = f16_bits_to_f32(d16);
-        const float rdf = 1.0f / df;
+        const float rdf = __builtin_amdgcn_rcpf(df);
+        float dev = 0.0f;                             // max |q - rint(q)|
 #pragma unroll
         for (int k = 0; k < kEpl; ++k) {
             const float q = x[k] * rdf;
             y[k] = rintf(q);
-            near |= fabsf(q - y[k]) > kBand;
+            dev = fmaxf(dev, fabsf(q - y[k]));
         }
+        near = dev > kBand;
         if (__builtin_amdgcn_ballot_w64(near) != 0) {
 #pragma unroll
             for (int k = 0; k < kEpl; ++k) {
@@ -147,7 +161,9 @@ __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t
     } else {
         constexpr int BITS = FMT == kFmtAff4 ? 4 : 8;
         constexpr float top = (float)((1 << BITS) - 1);
+        const int gsh = __builtin_ctz(r.group);       // group sizes are powers of two
         const int lpg = r.group / kEpl;               // lanes per group (2, 4 or 8)
+        const int lsh = gsh - 4;                      // log2(lanes per group)
         float mn = x[0], mx = x[0];
 #pragma unroll
         for (int k = 1; k < kEpl; ++k) { mn = fminf(mn, x[k]); mx = fmaxf(mx, x[k]); }
@@ -160,13 +176,15 @@ __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t
         const uint16_t z16 = f32_to_f16_bits(mn);
         const float sf = f16_bits_to_f32(s16);
         const float zf = f16_bits_to_f32(z16);
-        const float rs = 1.0f / sf;
+        const float rs = __builtin_amdgcn_rcpf(sf);
+        float dev = 0.0f;                             // max |q - rint(q)|
 #pragma unroll
         for (int k = 0; k < kEpl; ++k) {
             const float q = (x[k] - zf) * rs;
             y[k] = rintf(q);
-            near |= fabsf(q - y[k]) > kBand;
+            dev = fmaxf(dev, fabsf(q - y[k]));
         }
+        near = dev > kBand;
         if (__builtin_amdgcn_ballot_w64(near) != 0) {
 #pragma unroll
             for (int k = 0; k < kEpl; ++k) {
@@ -178,22 +196,32 @@ __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t
 #pragma unroll
         for (int k = 0; k < kEpl; ++k) y[k] = fminf(fmaxf(y[k], 0.0f), top);   // NaN -> 0
         if ((lane & (lpg - 1)) == 0)
-            static_cast<uint32_t*>(r.meta)[drow * (D / r.group) + lane / lpg] =
+            static_cast<uint32_t*>(r.meta)[(drow << (__builtin_ctz(D) - gsh)) + (lane >> lsh)] =
                 (uint32_t)s16 | ((uint32_t)z16 << 16);
     }
+    // y holds integral codes in [0, top]; v_cvt_pk_u8_f32 converts one to a
+    // byte lane of a packed word
     if constexpr (FMT == kFmtAff8) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            pk[k] = (uint32_t)y[4 * k] | ((uint32_t)y[4 * k + 1] << 8) | ((uint32_t)y[4 * k + 2] << 16) |
-                    ((uint32_t)y[4 * k + 3] << 24);
-        reinterpret_cast<uint4*>(r.codes)[drow * (D >> 4) + lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    } else {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < 4; ++k) {
             uint32_t w = 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w |= (uint32_t)y[8 * k + i] << (4 * i);
+            for (int i = 0; i < 4; ++i) w = __builtin_amdgcn_cvt_pk_u8_f32(y[4 * k + i], i, w);
             pk[k] = w;
+        }
+        reinterpret_cast<uint4*>(r.codes)[drow * (D >> 4) + lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    } else {
+        // even elements to the byte lanes of e, odd ones to o: e | o << 4 is
+        // the nibble-packed word (element 2i low nibble of byte i)
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t e = 0, o = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                e = __builtin_amdgcn_cvt_pk_u8_f32(y[8 * k + 2 * i], i, e);
+                o = __builtin_amdgcn_cvt_pk_u8_f32(y[8 * k + 2 * i + 1], i, o);
+            }
+            pk[k] = e | (o << 4);
         }
         reinterpret_cast<uint2*>(r.codes)[drow * (D >> 4) + lane] = make_uint2(pk[0], pk[1]);
     }
