@@ -14,11 +14,13 @@
 // rows, so each key's sum over window rows stays inside a lane.  Recomputing
 // the block is cheaper than storing the w x S fp32 logits.
 //
-// Selection is a deterministic MSB-first radix select over order-preserving
-// 32-bit keys of the fp32 scores (4 passes of 8 bits, LDS histograms), then
-// ties at the threshold are resolved by ascending position with a block
-// prefix scan, and the kept set is emitted in ascending order by a second
-// scan.  No floating-point atomics are used, so results are reproducible.
+// Selection works on order-preserving 32-bit keys of the fp32 scores, one
+// workgroup per head: for S <= 16384 the keys stay in registers and the
+// threshold (k-th largest key) is found by nested 4096-bucket LDS histograms
+// over the candidate key range; longer sequences use an MSB-first radix
+// select (4 passes of 8 bits, LDS histograms).  Ties at the threshold go to the lower positions, and the
+// kept set is emitted in ascending order through block prefix scans.  No
+// floating-point atomics are used, so results are reproducible.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -53,17 +55,25 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     __shared__ float sm[4][kMaxWindow], sl[4][kMaxWindow];
 
     const int key = key_base + l32;
+    // this lane's key fragments, loaded once: all loads in flight together
+    constexpr int NK = D / 16;
+    half8 A[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+        A[q] = half8{};
+        if (key < S) A[q] = load_half8(K + (int64_t)key * D + q * 16 + kh * 8);
+    }
     for (int nt = 0; nt * 32 < wc; ++nt) {
         const int wr = nt * 32 + l32;
+        half8 Bv[NK];
+#pragma unroll
+        for (int q = 0; q < NK; ++q) {
+            Bv[q] = half8{};
+            if (wr < wc) Bv[q] = load_half8(K + (int64_t)(row0 + wr) * D + q * 16 + kh * 8);
+        }
         floatx16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < D; ks += 16) {
-            const int d0 = ks + kh * 8;
-            half8 A = {}, Bv = {};
-            if (key < S) A = load_half8(K + (int64_t)key * D + d0);
-            if (wr < wc) Bv = load_half8(K + (int64_t)(row0 + wr) * D + d0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bv, acc, 0, 0, 0);
-        }
+        for (int q = 0; q < NK; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[q], Bv[q], acc, 0, 0, 0);
         // acc[v] = logit(key_base + acc_row(v, kh), window row wr)
         float mx = -INFINITY;
 #pragma unroll
@@ -101,6 +111,16 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
     const float c = 1.4426950408889634f / sqrtf((float)D);
     __shared__ float Mrow[kMaxWindow], invL[kMaxWindow];
+    // this lane's key fragments, loaded before the stats merge so that both
+    // memory latencies overlap
+    const int key = chunk * kChunk + wave * 32 + l32;
+    constexpr int NK = D / 16;
+    half8 Bk[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+        Bk[q] = half8{};
+        if (key < S) Bk[q] = load_half8(K + (int64_t)key * D + q * 16 + kh * 8);
+    }
     {
         // merge the per-chunk (max, sum) of every window row: tpr threads per
         // row stride over the chunks, then combine with lane shuffles
@@ -109,11 +129,22 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
         float M = -INFINITY, L = 0.0f;
         if (r < wc) {
             const float* st = a.stats + (((int64_t)b * a.H + h) * a.n_chunks * wc + r) * 2;
-            for (int ch = j; ch < a.n_chunks; ch += tpr) {
-                const float m2 = st[(int64_t)ch * wc * 2], l2 = st[(int64_t)ch * wc * 2 + 1];
-                const float Mn = fmaxf(M, m2);
-                L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
-                M = Mn;
+            // chunks j, j + tpr, ...: eight loads in flight before they are merged
+            for (int ch0 = j; ch0 < a.n_chunks; ch0 += 8 * tpr) {
+                float2 ml[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int ch = ch0 + u * tpr;
+                    ml[u] = ch < a.n_chunks ? *reinterpret_cast<const float2*>(st + (int64_t)ch * wc * 2)
+                                            : make_float2(-INFINITY, 0.0f);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float m2 = ml[u].x, l2 = ml[u].y;
+                    const float Mn = fmaxf(M, m2);
+                    L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
+                    M = Mn;
+                }
             }
         }
         for (int off = 1; off < tpr; off <<= 1) {
@@ -128,19 +159,18 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
         }
     }
     __syncthreads();
-    const int key = chunk * kChunk + wave * 32 + l32;
     float score = 0.0f;
     for (int mt = 0; mt * 32 < wc; ++mt) {
         const int wr = mt * 32 + l32;
+        half8 A[NK];
+#pragma unroll
+        for (int q = 0; q < NK; ++q) {
+            A[q] = half8{};
+            if (wr < wc) A[q] = load_half8(K + (int64_t)(row0 + wr) * D + q * 16 + kh * 8);
+        }
         floatx16 acc = {};
 #pragma unroll
-        for (int ks = 0; ks < D; ks += 16) {
-            const int d0 = ks + kh * 8;
-            half8 A = {}, Bv = {};
-            if (wr < wc) A = load_half8(K + (int64_t)(row0 + wr) * D + d0);
-            if (key < S) Bv = load_half8(K + (int64_t)key * D + d0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, Bv, acc, 0, 0, 0);
-        }
+        for (int q = 0; q < NK; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[q], Bk[q], acc, 0, 0, 0);
         // acc[v] = logit(window row mt*32 + acc_row(v, kh), key)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
@@ -193,13 +223,10 @@ __device__ uint32_t block_scan(uint32_t v, uint32_t* lds16, uint32_t* total) {
     return res;
 }
 
-// Keys of one head are staged in LDS when S <= kSelLds (64 KB), else read
-// from global memory on every pass.
-constexpr int kSelLds = 16384;
-
-template <bool LDS_KEYS>
-__global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, int S, int n_sink,
-                                                           int budget, int32_t* kept_all) {
+// Radix select for long sequences (S > 16384): 4 passes of 8 bits over the
+// keys, read from global memory on every pass, with per-wave LDS histograms.
+__global__ __launch_bounds__(1024) void snap_select_radix_kernel(const float* scores, int S, int n_sink,
+                                                                 int budget, int32_t* kept_all) {
     const int64_t bh = blockIdx.x;
     const int tid = threadIdx.x;
     const int n_keep = min(budget, S);
@@ -212,15 +239,7 @@ __global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, 
         for (int i = tid; i < n_keep; i += blockDim.x) kept[i] = i;
         return;
     }
-    extern __shared__ uint32_t keys_lds[];
-    if constexpr (LDS_KEYS) {
-        for (int j = tid; j < S; j += blockDim.x) keys_lds[j] = order_key(sc[j]);
-        __syncthreads();
-    }
-    auto key_of = [&](int j) -> uint32_t {
-        if constexpr (LDS_KEYS) return keys_lds[j];
-        else return order_key(sc[j]);
-    };
+    auto key_of = [&](int j) -> uint32_t { return order_key(sc[j]); };
     __shared__ uint32_t whist[16][256];     // one histogram per wave: no cross-wave contention
     __shared__ uint32_t lds16[17];
     __shared__ uint32_t s_prefix, s_krem;
@@ -286,6 +305,184 @@ __global__ __launch_bounds__(1024) void snap_select_kernel(const float* scores, 
     }
 }
 
+// Register-resident select for S <= 1024 * KPT: thread t holds the keys of
+// positions t*KPT .. t*KPT+KPT-1 (sinks and positions past S as key 0, below
+// every real key).  The threshold tau -- the k-th largest candidate key -- is
+// found by bucketing: the candidate range [min, max] is split into 4096
+// equal buckets (an LDS histogram; keys are order-preserving float bits, so
+// buckets are close to logarithmic in the score and atomics rarely collide),
+// a scan from the top finds the bucket holding the k-th largest key, and the
+// search repeats inside that bucket with 12 more bits until a bucket is a
+// single key value (at most three levels).  One block scan of the packed
+// per-thread counts (sinks or above tau, equal to tau) then gives every kept
+// position its output slot: positions above tau keep their order, and the
+// first krem positions equal to tau are taken.
+constexpr int kSelThreads = 1024;    // select block: 16 waves
+constexpr int kSelBits = 12;
+constexpr int kSelBuckets = 1 << kSelBits;              // 16 KB LDS histogram
+constexpr int kSelPer = kSelBuckets / kSelThreads;      // buckets per thread (4)
+
+// Inclusive wave scan with DPP: row shifts 1, 2, 4, 8 scan each row of 16
+// lanes, then row broadcasts of lanes 15 and 31 carry the row totals.
+__device__ __forceinline__ uint32_t wave_scan_dpp(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);   // row_bcast:15 -> rows 1, 3
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);   // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
+// Exclusive scan of v over the 1024 threads with one barrier: a wave scan,
+// then every wave reads the 16 wave totals.  `tot16` must not be reused
+// before the next barrier.
+__device__ __forceinline__ uint32_t scan1024(uint32_t v, uint32_t* tot16, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint32_t x = wave_scan_dpp(v);
+    if (lane == 63) tot16[wave] = x;
+    __syncthreads();
+    const uint4* p = reinterpret_cast<const uint4*>(tot16);
+    const uint4 q0 = p[0], q1 = p[1], q2 = p[2], q3 = p[3];
+    const uint32_t t[16] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w,
+                            q2.x, q2.y, q2.z, q2.w, q3.x, q3.y, q3.z, q3.w};
+    uint32_t before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        before += w < wave ? t[w] : 0u;
+        all += t[w];
+    }
+    *total = all;
+    return before + x - v;
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const float* scores, int S, int n_sink,
+                                                                      int budget, int32_t* kept_all) {
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n_keep = min(budget, S);
+    const int n_s = min(n_sink, n_keep);
+    const int k = n_keep - n_s;
+    const int C = S - n_s;
+    const float* sc = scores + bh * S;
+    int32_t* kept = kept_all + bh * n_keep;
+    if (k == C || k == 0) {                       // all candidates, or sinks only
+        for (int i = tid; i < n_keep; i += blockDim.x) kept[i] = i;
+        return;
+    }
+    __shared__ __align__(16) uint32_t hist[kSelBuckets];
+    __shared__ __align__(16) uint32_t tot16[4][16];
+    __shared__ uint32_t pick[2];
+    uint32_t key[KPT];
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+    {
+        // bounds-checked buffer loads: positions past S read as 0
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), (short)0, S * 4, 0x00020000);
+        uint32_t raw[KPT];
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (tid * KPT + i) * 4, 0, 0);
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const int j = tid * KPT + i;
+            key[i] = (j >= n_s && j < S) ? order_key(__uint_as_float(raw[i])) : 0u;
+            if (key[i] != 0u) { kmin = min(kmin, key[i]); kmax = max(kmax, key[i]); }
+        }
+    }
+    // zero the histogram while the keys load
+    uint4* h4 = reinterpret_cast<uint4*>(hist);
+#pragma unroll
+    for (int q = 0; q < kSelPer / 4; ++q) h4[tid * (kSelPer / 4) + q] = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    }
+    if (lane == 0) { tot16[0][wave] = kmin; tot16[1][wave] = kmax; }
+    __syncthreads();
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) { lo = min(lo, tot16[0][w]); hi = max(hi, tot16[1][w]); }
+    // bucket search over the keys in [base, base + lim): bucket (key - base) >> shift
+    uint32_t base = lo, krem = (uint32_t)k;       // krem: rank of tau from the top of the range
+    const uint32_t range = hi - lo;               // <= 0xFFFFFFFE: real keys are >= 0x007FFFFF
+    uint32_t lim = range + 1u;
+    int shift = range == 0u ? 0 : max(0, 32 - __clz((int)range) - kSelBits);   // range < 2^(shift + kSelBits)
+    for (int level = 0;; ++level) {
+        if (level > 0) {
+            // zero for this level (the previous level's reads ended at a barrier)
+#pragma unroll
+            for (int q = 0; q < kSelPer / 4; ++q) h4[tid * (kSelPer / 4) + q] = make_uint4(0u, 0u, 0u, 0u);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) {
+            const uint32_t off = key[i] - base;       // keys below base wrap to large values
+            if (key[i] != 0u && off < lim) atomicAdd(&hist[off >> shift], 1u);
+        }
+        __syncthreads();
+        // thread t owns the buckets kSelBuckets-1-kSelPer*t downwards (scan from the top)
+        const int top = kSelBuckets - kSelPer * (tid + 1);     // lowest bucket of this thread
+        uint32_t cnt[kSelPer];
+#pragma unroll
+        for (int q = 0; q < kSelPer / 4; ++q) {
+            const uint4 x = h4[top / 4 + q];
+            cnt[4 * q] = x.x; cnt[4 * q + 1] = x.y; cnt[4 * q + 2] = x.z; cnt[4 * q + 3] = x.w;
+        }
+        uint32_t v = 0;
+#pragma unroll
+        for (int q = 0; q < kSelPer; ++q) v += cnt[q];
+        uint32_t tot;
+        const uint32_t excl = scan1024(v, tot16[2 + (level & 1)], &tot);
+        if (excl < krem && excl + v >= krem) {
+            uint32_t run = excl;
+#pragma unroll
+            for (int q = kSelPer - 1; q >= 0; --q) {      // descending buckets
+                if (run < krem && run + cnt[q] >= krem) { pick[0] = (uint32_t)(top + q); pick[1] = run; }
+                run += cnt[q];
+            }
+        }
+        __syncthreads();
+        const uint32_t bucket = pick[0], above = pick[1];
+        base += bucket << shift;
+        krem -= above;
+        if (shift == 0) break;                    // the bucket is one key value
+        lim = 1u << shift;
+        shift = max(0, shift - kSelBits);
+        __syncthreads();                          // everyone has read pick / hist
+    }
+    const uint32_t tau = base;                    // k-th largest key; krem keys equal to it are kept
+    uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int j = tid * KPT + i;
+        n_gt += (j < n_s || key[i] > tau);
+        n_eq += (key[i] == tau);
+    }
+    uint32_t tot;
+    const uint32_t packed = n_gt | (n_eq << 16);
+    __syncthreads();                              // tot16 rows are reused below
+    const uint32_t excl = scan1024(packed, tot16[0], &tot);
+    uint32_t a_run = excl & 0xFFFFu, e_run = excl >> 16;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+        const int j = tid * KPT + i;
+        if (j >= S) break;
+        if (j < n_s || key[i] > tau) {
+            const uint32_t out = a_run + min(e_run, krem);
+            if (out < (uint32_t)n_keep) kept[out] = j;
+            ++a_run;
+        } else if (key[i] == tau) {
+            if (e_run < krem) {
+                const uint32_t out = a_run + e_run;
+                if (out < (uint32_t)n_keep) kept[out] = j;
+            }
+            ++e_run;
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void snap_gather_kernel(SnapArgs a, int n_keep) {
     const int upr = a.D / 8;                      // 16-byte units per fp16 row
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -332,12 +529,15 @@ hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s) {
 
 hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_sink, int budget,
                                 int32_t* kept, hipStream_t s) {
-    if (S <= kSelLds)
-        hipLaunchKernelGGL((snap_select_kernel<true>), dim3((unsigned)(B * H)), dim3(1024),
-                           (size_t)S * sizeof(uint32_t), s, scores, S, n_sink, budget, kept);
+    if (S <= kSelThreads * 8)
+        hipLaunchKernelGGL((snap_select_reg_kernel<8>), dim3((unsigned)(B * H)), dim3(kSelThreads), 0, s, scores, S,
+                           n_sink, budget, kept);
+    else if (S <= kSelThreads * 16)
+        hipLaunchKernelGGL((snap_select_reg_kernel<16>), dim3((unsigned)(B * H)), dim3(kSelThreads), 0, s, scores, S,
+                           n_sink, budget, kept);
     else
-        hipLaunchKernelGGL((snap_select_kernel<false>), dim3((unsigned)(B * H)), dim3(1024), 0, s,
-                           scores, S, n_sink, budget, kept);
+        hipLaunchKernelGGL(snap_select_radix_kernel, dim3((unsigned)(B * H)), dim3(1024), 0, s, scores, S,
+                           n_sink, budget, kept);
     return hipGetLastError();
 }
 

@@ -104,6 +104,11 @@ def test_snapkv_identical_keys_keep_the_first_positions():
     (3000, 0, 1, 3),
     (5000, 17, 4999, 5),
     (777, 4, 100, 1),         # all candidates tie
+    (8193, 4, 512, 0),        # 16 keys per thread
+    (12000, 4, 700, 5),
+    (16384, 4, 512, 0),
+    (20000, 4, 512, 0),       # radix select over global keys
+    (20000, 0, 1000, 9),
 ])
 def test_select_from_scores_bit_exact(S, sink, budget, levels):
     rng = np.random.default_rng(S + budget + levels)
