@@ -121,6 +121,13 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
         Bk[q] = half8{};
         if (key < S) Bk[q] = load_half8(K + (int64_t)key * D + q * 16 + kh * 8);
     }
+    // first window tile's fragments, also before the merge
+    half8 A[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+        A[q] = half8{};
+        if (l32 < wc) A[q] = load_half8(K + (int64_t)(row0 + l32) * D + q * 16 + kh * 8);
+    }
     {
         // merge the per-chunk (max, sum) of every window row: tpr threads per
         // row stride over the chunks, then combine with lane shuffles
@@ -162,11 +169,12 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     float score = 0.0f;
     for (int mt = 0; mt * 32 < wc; ++mt) {
         const int wr = mt * 32 + l32;
-        half8 A[NK];
+        if (mt > 0) {
 #pragma unroll
-        for (int q = 0; q < NK; ++q) {
-            A[q] = half8{};
-            if (wr < wc) A[q] = load_half8(K + (int64_t)(row0 + wr) * D + q * 16 + kh * 8);
+            for (int q = 0; q < NK; ++q) {
+                A[q] = half8{};
+                if (wr < wc) A[q] = load_half8(K + (int64_t)(row0 + wr) * D + q * 16 + kh * 8);
+            }
         }
         floatx16 acc = {};
 #pragma unroll
