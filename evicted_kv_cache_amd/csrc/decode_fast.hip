@@ -1,6 +1,8 @@
-// decode_fast.hip -- bandwidth-tuned decode attention for per-token 4-bit
-// affine K and V (mlx-lm-style group quantization, "Low-bit KV caches on MLX",
-// s.1) at head_dim 128 and 4 query heads per kv-head (gfx950).
+// decode_fast.hip -- bandwidth-tuned decode attention for per-token 4-bit K
+// (affine groups, mlx-lm style, "Low-bit KV caches on MLX", s.1; or symmetric
+// blocks of 32, "kv-cache: optional per-channel K-cache mean-centering for
+// Q4_0") and per-token affine 4- or 8-bit V, at head_dim 128 and 4 query heads
+// per kv-head (gfx950).
 //
 // Decode streams the whole cache once per step ("Low-bit KV caches on MLX",
 // s.5: decode spends its time reading the cache).  At 4.5 bits per element
@@ -52,7 +54,10 @@ constexpr int kD = 128;
 constexpr int kGQ = 4;          // query heads per kv-head
 constexpr int kTileT = 32;      // tokens per wave tile
 constexpr int kWaves = 4;
-constexpr int kRowB = kD / 2;   // bytes of 4-bit codes per token
+constexpr int kRowB = kD / 2;   // bytes of 4-bit K codes per token
+// K code formats of the fast path
+constexpr int kKAff4 = 0;       // per-token affine groups: (scale, zero) fp16 pairs
+constexpr int kKSym4 = 1;       // symmetric blocks of 32: one fp16 scale d, value (u - 8) d
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -106,6 +111,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
+__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
 __device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
 }
@@ -124,20 +132,28 @@ template <int NVG>
 struct VMeta { uint32_t m[2][NVG]; };   // (scale, zero) of tokens t, t+16 per V group
 
 // Loads of one lane, issued a tile ahead of their use (ping-pong buffers).
-template <int NVG>
+// VW: 32-bit words of V codes per token and lane (8 channels: 1 at 4 bits, 2 at 8).
+template <int NVG, int VW>
 struct TileLoads {
     u32x4 k[2];          // codes of the lane's quarter for tokens t and t+16
-    uint32_t km[2];      // K (scale, zero) of the quarter's group, tokens t and t+16
+    uint32_t km[2];      // K (scale, zero) of the quarter's group (sym4: the scale d), tokens t, t+16
     uint32_t kmo[2];     // K (scale, zero) of the other 64-channel half's group (K groups of 64)
     VMeta<NVG> vm;
-    uint32_t v[4][2];    // V code words (8 channels) of tokens ph+4j and ph+4j+16
+    uint32_t v[4][2][VW];  // V code words (8 channels) of tokens ph+4j and ph+4j+16
 };
 
-// GK, GV: channels per K / V group (32, 64 or 128).
-template <int QDT, int GK, int GV>
+// KF: K format (kKAff4 or kKSym4, whose blocks are GK = 32 channels);
+// GK, GV: channels per K / V group (32, 64 or 128); VB: bits per V code (4 or 8).
+template <int QDT, int KF, int GK, int VB, int GV>
 __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
+    static_assert(KF == kKAff4 || GK == 32, "symmetric K blocks are 32 channels");
     constexpr int NKG = kD / GK;      // K groups per row
     constexpr int NVG = kD / GV;      // V groups per row
+    constexpr int VW = VB / 4;        // V code words per token and lane
+    constexpr int kVRowB = kD * VB / 8;   // bytes of V codes per token
+    constexpr float kVCenter = VB == 4 ? 8.0f : 128.0f;          // codes are centered on this
+    constexpr uint32_t kVCenterNeg = VB == 4 ? 0xC800C800u : 0xD800D800u;   // fp16 (-c, -c)
+    constexpr int kKMetaB = KF == kKSym4 ? 2 : 4;                 // bytes per K group and token
     // When each 64-channel half of head_dim lies in one K group (GK >= 64),
     // the four quarter partials of a head are reduced in two steps: first
     // within the half (same scale, applied once to the pair sum), then across
@@ -227,6 +243,9 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     float qsk[kGQ];
 #pragma unroll
     for (int h = 0; h < kGQ; ++h) qsk[h] = ldexpf(qsum[h], -(qexp + 24));
+    float qsk8[kGQ];              // symmetric K: the zero point -8 d, as -8 qsk
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) qsk8[h] = -8.0f * qsk[h];
     // half reduce: the zero-point term of head q4 is added after the reduce,
     // as z_own qz_own + z_other qz_other with qz = scale_log2 * (sum of q over
     // the K group) for the group of this lane's half and the other group
@@ -248,8 +267,8 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     }
 
     const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
-    const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kRowB;
-    const uint32_t* kmeta = static_cast<const uint32_t*>(a.k_meta) + bh * a.cap * NKG;
+    const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kVRowB;
+    const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + bh * a.cap * NKG * kKMetaB;
     const uint32_t* vmeta = static_cast<const uint32_t*>(a.v_meta) + bh * a.cap * NVG;
 
     float m_lane = -INFINITY;     // running max of head q4
@@ -263,27 +282,39 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[h][i] = 0.0f;
 
-    auto load_tile = [&](int tile, TileLoads<NVG>& L) {
+    auto load_tile = [&](int tile, TileLoads<NVG, VW>& L) {
         const int tb = t_lo + tile * kTileT;
         // valid tokens in the tile (0 past the end: those loads return zeros);
         // kept in a scalar register so the buffer descriptors stay uniform
         const uint32_t nv = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kTileT, t_hi - tb)));
         const __amdgpu_buffer_rsrc_t rk = rsrc(kcodes + (int64_t)tb * kRowB, nv * kRowB);
-        const __amdgpu_buffer_rsrc_t rkm = rsrc(kmeta + (int64_t)tb * NKG, nv * NKG * 4);
+        const __amdgpu_buffer_rsrc_t rkm = rsrc(kmeta + (int64_t)tb * NKG * kKMetaB, nv * NKG * kKMetaB);
         const __amdgpu_buffer_rsrc_t rvm = rsrc(vmeta + (int64_t)tb * NVG, nv * NVG * 4);
-        const __amdgpu_buffer_rsrc_t rv = rsrc(vcodes + (int64_t)tb * kRowB, nv * kRowB);
+        const __amdgpu_buffer_rsrc_t rv = rsrc(vcodes + (int64_t)tb * kVRowB, nv * kVRowB);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t tt = ph + 4 * j;
-            L.v[j][0] = bload32(rv, tt * kRowB + 4 * c);
-            L.v[j][1] = bload32(rv, (tt + 16) * kRowB + 4 * c);
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const uint32_t off = (tt + 16 * e) * kVRowB + 4 * VW * c;
+                if constexpr (VW == 1) {
+                    L.v[j][e][0] = bload32(rv, off);
+                } else {
+                    const u32x2 x = bload64(rv, off);
+                    L.v[j][e][0] = x.x; L.v[j][e][1] = x.y;
+                }
+            }
         }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = t16 + 16 * p;
             L.k[p] = bload128(rk, tok * kRowB + 16 * q4);
-            L.km[p] = bload32(rkm, (tok * NKG + kg) * 4);
-            if constexpr (GK == 64) L.kmo[p] = bload32(rkm, (tok * NKG + (kg ^ 1)) * 4);
+            if constexpr (KF == kKSym4) {
+                L.km[p] = bload16(rkm, (tok * NKG + kg) * 2);
+            } else {
+                L.km[p] = bload32(rkm, (tok * NKG + kg) * 4);
+                if constexpr (GK == 64) L.kmo[p] = bload32(rkm, (tok * NKG + (kg ^ 1)) * 4);
+            }
             if constexpr (NVG == 1) {
                 L.vm.m[p][0] = bload32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
@@ -296,7 +327,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         }
     };
 
-    auto process = [&](const TileLoads<NVG>& L, int tile, auto tail) {
+    auto process = [&](const TileLoads<NVG, VW>& L, int tile, auto tail) {
         constexpr bool kTail = decltype(tail)::value;     // the tile may hold invalid tokens
         const int tb = t_lo + tile * kTileT;
         // -------------------------------------------- QK^T, two passes (t16, t16 + 16)
@@ -330,8 +361,14 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                 x = fmaf(sum, kC, zt);
             } else {
                 float part[kGQ];
+                if constexpr (KF == kKSym4) {
+                    // zero point -8 d:  d (q'.u') - 8 d qsk
 #pragma unroll
-                for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16hi(L.km[p]) * qsk[h]);
+                    for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16lo(L.km[p]) * qsk8[h]);
+                } else {
+#pragma unroll
+                    for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16hi(L.km[p]) * qsk[h]);
+                }
                 // head q4 of this token: part[0] here plus part[k] of lane quarter q4 - k
                 x = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
                      quad_from_minus<3>(part[3])) * kC;
@@ -369,9 +406,9 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             const uint32_t m0 = L.vm.m[0][g], m1 = L.vm.m[1][g];
             const uint32_t pair = pack_f16(mul_lo(m0, p0), mul_lo(m1, p1));
             float cg = corr[g];
-            cg = fmaf(p0, fmaf(8.0f, f16lo(m0), f16hi(m0)), cg);
-            cg = fmaf(p1, fmaf(8.0f, f16lo(m1), f16hi(m1)), cg);
-            corr[g] = dot2_f16(pair, 0xC800C800u /* (-8, -8) */, cg);
+            cg = fmaf(p0, fmaf(kVCenter, f16lo(m0), f16hi(m0)), cg);
+            cg = fmaf(p1, fmaf(kVCenter, f16lo(m1), f16hi(m1)), cg);
+            corr[g] = dot2_f16(pair, kVCenterNeg /* (-c, -c) */, cg);
             wbuf[wave][t16][g][q4] = pair;
         }
         __builtin_amdgcn_wave_barrier();
@@ -381,16 +418,23 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         for (int j = 0; j < 4; ++j) {
             const uint4 wp = *reinterpret_cast<const uint4*>(&wbuf[wave][ph + 4 * j][vg_c][0]);
             const uint32_t wpair[kGQ] = {wp.x, wp.y, wp.z, wp.w};
-            const uint32_t w0 = L.v[j][0], w1 = L.v[j][1];
-            // byte k of both tokens as an fp16 subnormal pair (b_t, b_t+16),
-            // b = u_2k + 16 u_2k+1, and its low nibbles (u_2k of both tokens);
-            // the high-nibble channel is separated once at the end
             uint32_t cp[8];
+            if constexpr (VB == 4) {
+                const uint32_t w0 = L.v[j][0][0], w1 = L.v[j][1][0];
+                // byte k of both tokens as an fp16 subnormal pair (b_t, b_t+16),
+                // b = u_2k + 16 u_2k+1, and its low nibbles (u_2k of both tokens);
+                // the high-nibble channel is separated once at the end
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t P = __builtin_amdgcn_perm(w1, w0, 0x0C040C00u + 0x00010001u * k);
-                cp[2 * k] = P & 0x000F000Fu;
-                cp[2 * k + 1] = P;
+                for (int k = 0; k < 4; ++k) {
+                    const uint32_t P = __builtin_amdgcn_perm(w1, w0, 0x0C040C00u + 0x00010001u * k);
+                    cp[2 * k] = P & 0x000F000Fu;
+                    cp[2 * k + 1] = P;
+                }
+            } else {
+                // 8-bit codes: byte i of both tokens is channel 8c + i
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    cp[i] = __builtin_amdgcn_perm(L.v[j][1][i >> 2], L.v[j][0][i >> 2], 0x0C040C00u + 0x00010001u * (i & 3));
             }
 #pragma unroll
             for (int h = 0; h < kGQ; ++h)
@@ -405,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     // Full tiles run in a ping-pong loop with unconditional prefetches (a
     // prefetch past the end reads zeros and is never used); only the split's
     // last tile can be partial and is processed with token masking.
-    TileLoads<NVG> A, B2;
+    TileLoads<NVG, VW> A, B2;
     const int full_end = min(tile1, (t_hi - t_lo) / kTileT);
     int tile = tile0;
     load_tile(tile, A);
@@ -440,8 +484,13 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float lo = acc[h][2 * k], whole = acc[h][2 * k + 1];
-            acc[h][2 * k] = lo * 16777216.0f;                   // 2^24
-            acc[h][2 * k + 1] = (whole - lo) * 1048576.0f;      // 2^24 / 16
+            if constexpr (VB == 4) {
+                acc[h][2 * k] = lo * 16777216.0f;                   // 2^24
+                acc[h][2 * k + 1] = (whole - lo) * 1048576.0f;      // 2^24 / 16
+            } else {
+                acc[h][2 * k] = lo * 16777216.0f;
+                acc[h][2 * k + 1] = whole * 16777216.0f;
+            }
         }
     // head q4 sums over the lane's tokens: reduce over lanes with equal q4
 #pragma unroll
@@ -502,9 +551,9 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 // Fast path applies to: per-token 4-bit affine K and V, D = 128, 4 query
 // heads per kv-head, bf16 or fp16 queries.
 bool decode_fast_applies(const DecodeArgs& a) {
-    return a.k_kind == KVQ_TOK_AFFINE && a.v_kind == KVQ_TOK_AFFINE && a.k_bits == 4 &&
-           a.v_bits == 4 && a.D == kD && a.Hq == kGQ * a.Hkv &&
-           (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16);
+    const bool k_ok = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4;
+    const bool v_ok = a.v_kind == KVQ_TOK_AFFINE && (a.v_bits == 4 || a.v_bits == 8);
+    return k_ok && v_ok && a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16);
 }
 
 // Split plan: one workgroup per (batch, kv-head) when that fills the chip
@@ -522,18 +571,32 @@ void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len) {
     *n_splits = (T + len - 1) / len;
 }
 
+template <int QDT, int KF, int GK, int VB>
+static hipError_t launch_fast_v(const DecodeArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
+    switch (a.v_group) {
+        case 32: hipLaunchKernelGGL((decode_tok4_kernel<QDT, KF, GK, VB, 32>), grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_tok4_kernel<QDT, KF, GK, VB, 64>), grid, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_tok4_kernel<QDT, KF, GK, VB, 128>), grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int QDT, int KF, int GK>
+static hipError_t launch_fast_k(const DecodeArgs& a, hipStream_t s) {
+    return a.v_bits == 8 ? launch_fast_v<QDT, KF, GK, 8>(a, s) : launch_fast_v<QDT, KF, GK, 4>(a, s);
+}
+
 template <int QDT>
 static hipError_t launch_fast_q(const DecodeArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
-#define KVQ_FAST(GK, GV)                                                                      \
-    if (a.k_group == GK && a.v_group == GV) {                                                 \
-        hipLaunchKernelGGL((decode_tok4_kernel<QDT, GK, GV>), grid, dim3(256), 0, s, a);      \
-        return hipGetLastError();                                                             \
+    if (a.k_kind == KVQ_TOK_SYM4) return launch_fast_k<QDT, kKSym4, 32>(a, s);
+    switch (a.k_group) {
+        case 32: return launch_fast_k<QDT, kKAff4, 32>(a, s);
+        case 64: return launch_fast_k<QDT, kKAff4, 64>(a, s);
+        case 128: return launch_fast_k<QDT, kKAff4, 128>(a, s);
+        default: return hipErrorInvalidValue;
     }
-    KVQ_FAST(64, 64) KVQ_FAST(32, 32) KVQ_FAST(128, 128) KVQ_FAST(64, 32) KVQ_FAST(32, 64)
-    KVQ_FAST(64, 128) KVQ_FAST(128, 64) KVQ_FAST(32, 128) KVQ_FAST(128, 32)
-#undef KVQ_FAST
-    return hipErrorInvalidValue;
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) {

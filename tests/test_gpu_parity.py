@@ -162,6 +162,28 @@ def test_fast_decode_group_combinations(kg, vg):
     check_decode(pl, c, o, synth.cast(synth.widen(q, "bf16"), "f16"), "f16")
 
 
+@pytest.mark.parametrize("k_kind,kg,vb,vg", [
+    ("tok_sym4", 32, 4, 64), ("tok_sym4", 32, 8, 32), ("tok_sym4", 32, 8, 128),
+    ("tok_affine", 64, 8, 64), ("tok_affine", 128, 8, 128), ("tok_affine", 32, 8, 64),
+])
+def test_fast_decode_k_formats_and_8bit_v(k_kind, kg, vb, vg):
+    """Symmetric (Q4_0-style) or affine 4-bit K with 4- or 8-bit per-token V at
+    head_dim 128, 4 query heads per kv-head: ragged length split over T."""
+    w = synth.workload("q4_0_centered")
+    B, H, T = 1, 2, 2000
+    k, v, q = gen(w, B, H, T, Hq=8)
+    bias = np.stack([synth.head_params(w, h)[0] for h in range(H)]).astype(np.float32)
+    flags = K.KVQ_CENTER_K if k_kind == "tok_sym4" else 0
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind=k_kind, k_bits=4, k_group=kg,
+                     v_kind="tok_affine", v_bits=vb, v_group=vg, in_dtype="f16", flags=flags)
+    say("fast decode formats", k_kind, kg, vb, vg)
+    c, o = build_pair(pl, ol, k, v, "f16", chunks=[(0, 1333), (1333, T)],
+                      k_bias=bias if flags else None)
+    assert_same_state(c, o)
+    check_decode(pl, c, o, q, "f16")
+    check_decode(pl, c, o, synth.cast(synth.widen(q, "f16"), "bf16"), "bf16")
+
+
 def test_empty_cache_decodes_to_zeros():
     pl, ol = layouts(batch=2, n_kv_heads=2, head_dim=64, capacity=10, in_dtype="f16",
                      k_group=64, v_group=64)
