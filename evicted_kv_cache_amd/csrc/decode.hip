@@ -19,51 +19,98 @@
 namespace kvq {
 namespace {
 
-constexpr int kTile = 256;
-constexpr int kMaxGroup = 8;   // query heads per kv-head
+constexpr int kTile = 64;       // tokens per tile
+constexpr int kMaxGroup = 8;    // query heads per kv-head
+constexpr int kMaxD = 128;
 
-__device__ __forceinline__ uint32_t code_at(const uint8_t* row, int d, int bits) {
-    if (bits == 4) return (row[d >> 1] >> ((d & 1) * 4)) & 0xFu;
-    return row[d];
-}
-
-template <int KK, int DT>
-__device__ __forceinline__ float k_value(const DecodeArgs& a, int64_t bh, int t, int d) {
-    const int D = a.D;
-    if constexpr (KK == KVQ_PLAIN) {
-        return load_as_f32<DT>(a.k_codes, (bh * a.cap + t) * D + d);
-    } else if constexpr (KK == KVQ_TOK_AFFINE) {
-        const int64_t slot = bh * a.cap + t;
-        const uint8_t* row = static_cast<const uint8_t*>(a.k_codes) + slot * (D * a.k_bits / 8);
-        const uint32_t m = static_cast<const uint32_t*>(a.k_meta)[slot * (D / a.k_group) + d / a.k_group];
-        return (float)code_at(row, d, a.k_bits) * f16_bits_to_f32(m & 0xFFFFu) + f16_bits_to_f32(m >> 16);
-    } else if constexpr (KK == KVQ_TOK_SYM4) {
-        const int64_t slot = bh * a.cap + t;
-        const uint8_t* row = static_cast<const uint8_t*>(a.k_codes) + slot * (D / 2);
-        const uint16_t sc = static_cast<const uint16_t*>(a.k_meta)[slot * (D / 32) + d / 32];
-        return ((float)code_at(row, d, 4) - 8.0f) * f16_bits_to_f32(sc);
-    } else {  // KIVI_CH
-        if (t >= a.n_quant)
-            return load_as_f32<DT>(a.k_resid, (bh * a.Gt + (t - a.n_quant)) * D + d);
-        const int64_t slot = bh * a.cap + t;
-        const uint8_t* row = static_cast<const uint8_t*>(a.k_codes) + slot * (D * a.k_bits / 8);
-        const int rows = a.cap / a.Gt + 3;
-        const int r = a.k_row[t];
-        const uint32_t m = static_cast<const uint32_t*>(a.k_meta)[(bh * rows + r) * D + d];
-        return (float)code_at(row, d, a.k_bits) * f16_bits_to_f32(m & 0xFFFFu) + f16_bits_to_f32(m >> 16);
+// 8 consecutive elements of a row of dtype `dt` as fp32 (exact widening).
+__device__ __forceinline__ void load8(const void* base, int64_t elem, int dt, float x[8]) {
+    if (dt == KVQ_F32) {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+        const float4 u = p[0], v = p[1];
+        x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w; x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
+    } else {
+        const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (dt == KVQ_F16) {
+                x[2 * i] = f16_bits_to_f32(ww[i] & 0xFFFFu);
+                x[2 * i + 1] = f16_bits_to_f32(ww[i] >> 16);
+            } else {
+                x[2 * i] = bf16_bits_to_f32(ww[i] & 0xFFFFu);
+                x[2 * i + 1] = bf16_bits_to_f32(ww[i] >> 16);
+            }
+        }
     }
 }
 
-template <int VK, int DT>
-__device__ __forceinline__ float v_value(const DecodeArgs& a, int64_t bh, int t, int d) {
+// The 8 codes of channels 8c .. 8c+7 of a code row (4 or 8 bits per code).
+__device__ __forceinline__ void codes8(const uint8_t* row, int c, int bits, float u[8]) {
+    if (bits == 4) {
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 4 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = (float)((w >> (4 * i)) & 0xFu);
+    } else {
+        const uint2 w = *reinterpret_cast<const uint2*>(row + 8 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            u[i] = (float)((w.x >> (8 * i)) & 0xFFu);
+            u[4 + i] = (float)((w.y >> (8 * i)) & 0xFFu);
+        }
+    }
+}
+
+// Dequantized keys of token t, channels 8c .. 8c+7 (k = u s + z, or as stored).
+template <int KK>
+__device__ __forceinline__ void k_values8(const DecodeArgs& a, int64_t bh, int t, int c, float x[8]) {
+    const int D = a.D;
+    const int64_t slot = bh * a.cap + t;
+    if constexpr (KK == KVQ_PLAIN) {
+        load8(a.k_codes, slot * D + 8 * c, a.in_dtype, x);
+    } else if constexpr (KK == KVQ_KIVI_CH) {
+        if (t >= a.n_quant) {                  // open group: full-precision residual
+            load8(a.k_resid, (bh * a.Gt + (t - a.n_quant)) * D + 8 * c, a.in_dtype, x);
+            return;
+        }
+        float u[8];
+        codes8(static_cast<const uint8_t*>(a.k_codes) + slot * (D * a.k_bits / 8), c, a.k_bits, u);
+        const int rows = a.cap / a.Gt + 3;
+        const uint4* m = reinterpret_cast<const uint4*>(static_cast<const uint32_t*>(a.k_meta) +
+                                                        ((bh * rows + a.k_row[t]) * D + 8 * c));
+        const uint4 m0 = m[0], m1 = m[1];
+        const uint32_t mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fmaf(u[i], f16_bits_to_f32(mm[i] & 0xFFFFu), f16_bits_to_f32(mm[i] >> 16));
+    } else if constexpr (KK == KVQ_TOK_SYM4) {
+        float u[8];
+        codes8(static_cast<const uint8_t*>(a.k_codes) + slot * (D / 2), c, 4, u);
+        const float d = f16_bits_to_f32(static_cast<const uint16_t*>(a.k_meta)[slot * (D / 32) + (8 * c) / 32]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (u[i] - 8.0f) * d;
+    } else {  // TOK_AFFINE
+        float u[8];
+        codes8(static_cast<const uint8_t*>(a.k_codes) + slot * (D * a.k_bits / 8), c, a.k_bits, u);
+        const uint32_t m = static_cast<const uint32_t*>(a.k_meta)[slot * (D / a.k_group) + (8 * c) / a.k_group];
+        const float sc = f16_bits_to_f32(m & 0xFFFFu), z = f16_bits_to_f32(m >> 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fmaf(u[i], sc, z);
+    }
+}
+
+template <int VK>
+__device__ __forceinline__ void v_values8(const DecodeArgs& a, int64_t bh, int t, int c, float x[8]) {
     const int D = a.D;
     const int64_t slot = bh * a.cap + t;
     if constexpr (VK == KVQ_PLAIN) {
-        return load_as_f32<DT>(a.v_codes, slot * D + d);
+        load8(a.v_codes, slot * D + 8 * c, a.in_dtype, x);
     } else {
-        const uint8_t* row = static_cast<const uint8_t*>(a.v_codes) + slot * (D * a.v_bits / 8);
-        const uint32_t m = static_cast<const uint32_t*>(a.v_meta)[slot * (D / a.v_group) + d / a.v_group];
-        return (float)code_at(row, d, a.v_bits) * f16_bits_to_f32(m & 0xFFFFu) + f16_bits_to_f32(m >> 16);
+        float u[8];
+        codes8(static_cast<const uint8_t*>(a.v_codes) + slot * (D * a.v_bits / 8), c, a.v_bits, u);
+        const uint32_t m = static_cast<const uint32_t*>(a.v_meta)[slot * (D / a.v_group) + (8 * c) / a.v_group];
+        const float sc = f16_bits_to_f32(m & 0xFFFFu), z = f16_bits_to_f32(m >> 16);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fmaf(u[i], sc, z);
     }
 }
 
@@ -78,97 +125,154 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-template <int KK, int VK, int DT, int QDT>
+// Generic split-T decode for every layout (D <= 128, up to 8 query heads
+// per kv-head).  Per 64-token tile the block dequantizes K and V into LDS as
+// fp32 (8 consecutive channels per work item: one code load and one
+// metadata load; keys stored transposed), computes the logits (thread =
+// token x head slot, consecutive lanes read consecutive keys), updates the
+// online softmax per head, and accumulates P V (thread = channel x token
+// range, so each value is read once for all heads).
+template <int KK, int VK, int D>
 __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
-    const int split = blockIdx.x;
-    const int hk = blockIdx.y;
-    const int b = blockIdx.z;
+    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
-    const int D = a.D;
+    constexpr int c8 = D / 8;
+    constexpr int kItems = kTile * c8 / 256;     // 8-channel items per thread and tile (1, 2 or 4)
     const int gq = a.Hq / a.Hkv;
     const int64_t bh = (int64_t)b * a.Hkv + hk;
 
-    __shared__ float q_s[kMaxGroup][128];
-    __shared__ float p_s[kMaxGroup][kTile];
+    __shared__ __align__(16) float q_s[kMaxGroup][kMaxD];
+    __shared__ float k_s[kMaxD * kTile];      // transposed: [channel][token]
+    __shared__ __align__(16) float v_s[kTile * kMaxD];
+    __shared__ __align__(16) float p_s[kMaxGroup][kTile];
     __shared__ float m_s[kMaxGroup], l_s[kMaxGroup], alpha_s[kMaxGroup];
 
     for (int idx = tid; idx < gq * D; idx += 256) {
-        const int h = idx / D, d = idx % D;
-        q_s[h][d] = load_as_f32<QDT>(a.q, ((int64_t)b * a.Hq + hk * gq + h) * D + d) * a.scale_log2;
+        const int h = idx / D, d = idx - h * D;
+        const int64_t qi = ((int64_t)b * a.Hq + hk * gq + h) * D + d;
+        float qv;
+        if (a.q_dtype == KVQ_F32) qv = static_cast<const float*>(a.q)[qi];
+        else if (a.q_dtype == KVQ_F16) qv = f16_bits_to_f32(static_cast<const uint16_t*>(a.q)[qi]);
+        else qv = bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[qi]);
+        q_s[h][d] = qv * a.scale_log2;
     }
-    if (tid < kMaxGroup) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; }
-    __syncthreads();
+    if (tid < kMaxGroup) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; alpha_s[tid] = 1.0f; }
 
     const int t_begin = split * a.split_len;
     const int t_end = min(a.T, t_begin + a.split_len);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};   // outputs o_idx = tid + 256 k  (gq * D <= 1024)
+    // PV role: channel d, token range `part` of the tile
+    constexpr int TH = 256 / D;             // token ranges per tile (2, 4 or 8)
+    const int pd = tid % D, part = tid / D;
+    constexpr int tpp = kTile / TH;         // tokens per range
+    float acc[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) acc[h] = 0.0f;
+    // QK role: token t, head slot (heads slot and slot + 4)
+    const int qt = tid & 63, slot = tid >> 6;
 
     for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
-        const int t = t0 + tid;
-        float lg[kMaxGroup];
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) lg[h] = 0.0f;
-        if (t < t_end) {
-            for (int d = 0; d < D; ++d) {
-                const float kv = k_value<KK, DT>(a, bh, t, d);
-#pragma unroll
-                for (int h = 0; h < kMaxGroup; ++h)
-                    if (h < gq) lg[h] = fmaf(q_s[h][d], kv, lg[h]);
-            }
-        } else {
-#pragma unroll
-            for (int h = 0; h < kMaxGroup; ++h) lg[h] = -INFINITY;
-        }
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h)
-            if (h < gq) p_s[h][tid] = lg[h];
-        __syncthreads();
-        const int wave = tid >> 6, lane = tid & 63;
-        for (int h = wave; h < gq; h += 4) {
-            float mx = -INFINITY;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, p_s[h][lane + 64 * i]);
-            mx = wave_max(mx);
-            const float m_old = m_s[h];
-            const float m_new = fmaxf(m_old, mx);
-            float sum = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float e = exp2f(p_s[h][lane + 64 * i] - m_new);
-                p_s[h][lane + 64 * i] = e;
-                sum += e;
-            }
-            sum = wave_sum(sum);
-            if (lane == 0) {
-                const float alpha = exp2f(m_old - m_new);
-                l_s[h] = l_s[h] * alpha + sum;
-                m_s[h] = m_new;
-                alpha_s[h] = alpha;
-            }
-        }
-        __syncthreads();
         const int nt = min(kTile, t_end - t0);
+        __syncthreads();                    // previous tile's reads of k_s / v_s / p_s are done
+        // keys: thread = token (tid % 64) x channel chunks tid / 64 + 4 r, so
+        // consecutive lanes write consecutive tokens of the transposed tile;
+        // values: consecutive lanes take consecutive channel chunks of a token.
+        // All loads of the tile are issued before any value is stored.
+        {
+            float xk[kItems][8], xv[kItems][8];
+            const int kt = tid & 63;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int o_idx = tid + 256 * k;
-            if (o_idx < gq * D) {
-                const int h = o_idx / D, d = o_idx % D;
-                float s = acc[k] * alpha_s[h];
-                for (int tt = 0; tt < nt; ++tt)
-                    s = fmaf(p_s[h][tt], v_value<VK, DT>(a, bh, t0 + tt, d), s);
-                acc[k] = s;
+            for (int r = 0; r < kItems; ++r) {
+                if (kt < nt) k_values8<KK>(a, bh, t0 + kt, (tid >> 6) + 4 * r, xk[r]);
+                const int it = tid + 256 * r, vt = it / c8, vc = it - vt * c8;
+                if (vt < nt) v_values8<VK>(a, bh, t0 + vt, vc, xv[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < kItems; ++r) {
+                if (kt < nt) {
+                    const int c = (tid >> 6) + 4 * r;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) k_s[(8 * c + i) * kTile + kt] = xk[r][i];
+                }
+                const int it = tid + 256 * r, vt = it / c8, vc = it - vt * c8;
+                if (vt < nt) {
+                    *reinterpret_cast<float4*>(&v_s[vt * D + 8 * vc]) = make_float4(xv[r][0], xv[r][1], xv[r][2], xv[r][3]);
+                    *reinterpret_cast<float4*>(&v_s[vt * D + 8 * vc + 4]) = make_float4(xv[r][4], xv[r][5], xv[r][6], xv[r][7]);
+                }
             }
         }
         __syncthreads();
-    }
-    const int ns = a.n_splits;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int o_idx = tid + 256 * k;
-        if (o_idx < gq * D) {
-            const int h = o_idx / D, d = o_idx % D;
-            a.ws_o[(((int64_t)b * a.Hq + hk * gq + h) * ns + split) * D + d] = acc[k];
+        {
+            float lg0 = 0.0f, lg1 = 0.0f;
+            const int h0 = slot, h1 = slot + 4;
+            if (qt < nt) {
+#pragma unroll 4
+                for (int d = 0; d < D; d += 4) {
+                    const float4 qa = *reinterpret_cast<const float4*>(&q_s[h0][d]);
+                    const float4 qb = *reinterpret_cast<const float4*>(&q_s[h1][d]);
+                    const float k0 = k_s[d * kTile + qt], k1 = k_s[(d + 1) * kTile + qt];
+                    const float k2 = k_s[(d + 2) * kTile + qt], k3 = k_s[(d + 3) * kTile + qt];
+                    lg0 = fmaf(qa.x, k0, lg0); lg0 = fmaf(qa.y, k1, lg0); lg0 = fmaf(qa.z, k2, lg0); lg0 = fmaf(qa.w, k3, lg0);
+                    lg1 = fmaf(qb.x, k0, lg1); lg1 = fmaf(qb.y, k1, lg1); lg1 = fmaf(qb.z, k2, lg1); lg1 = fmaf(qb.w, k3, lg1);
+                }
+            } else {
+                lg0 = lg1 = -INFINITY;
+            }
+            if (h0 < gq) p_s[h0][qt] = lg0;
+            if (h1 < gq) p_s[h1][qt] = lg1;
         }
+        __syncthreads();
+        {
+            const int wave = tid >> 6, lane = tid & 63;
+            for (int h = wave; h < gq; h += 4) {
+                const float lg = p_s[h][lane];
+                const float m_old = m_s[h];
+                const float m_new = fmaxf(m_old, wave_max(lg));
+                const float e = exp2f(lg - m_new);
+                p_s[h][lane] = e;
+                const float sum = wave_sum(e);
+                if (lane == 0) {
+                    const float alpha = exp2f(m_old - m_new);
+                    l_s[h] = l_s[h] * alpha + sum;
+                    m_s[h] = m_new;
+                    alpha_s[h] = alpha;
+                }
+            }
+        }
+        __syncthreads();
+        {
+#pragma unroll
+            for (int h = 0; h < kMaxGroup; ++h) acc[h] *= alpha_s[h];
+            // four tokens at a time: weights of a head as one 16-byte LDS read
+            // (weights past nt are zero: exp2 of -inf; values past tb read as 0)
+            const int ta = part * tpp, tb = min(nt, ta + tpp);
+            for (int t = ta; t < tb; t += 4) {
+                float vv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) vv[u] = t + u < tb ? v_s[(t + u) * D + pd] : 0.0f;   // rows past nt are stale
+#pragma unroll
+                for (int h = 0; h < kMaxGroup; ++h) {
+                    if (h < gq) {
+                        const float4 pw = *reinterpret_cast<const float4*>(&p_s[h][t]);
+                        acc[h] = fmaf(pw.x, vv[0], acc[h]);
+                        acc[h] = fmaf(pw.y, vv[1], acc[h]);
+                        acc[h] = fmaf(pw.z, vv[2], acc[h]);
+                        acc[h] = fmaf(pw.w, vv[3], acc[h]);
+                    }
+                }
+            }
+        }
+    }
+    // sum the token ranges (reusing k_s) and write the split's partials
+    __syncthreads();
+    float* red = k_s;                       // [TH][gq][D]
+    for (int h = 0; h < gq; ++h) red[(part * gq + h) * D + pd] = acc[h];
+    __syncthreads();
+    const int ns = a.n_splits;
+    for (int idx = tid; idx < gq * D; idx += 256) {
+        const int h = idx / D, d = idx - h * D;
+        float o = 0.0f;
+        for (int pp = 0; pp < TH; ++pp) o += red[(pp * gq + h) * D + d];
+        a.ws_o[(((int64_t)b * a.Hq + hk * gq + h) * ns + split) * D + d] = o;
     }
     if (tid < gq) {
         float* ml = a.ws_ml + (((int64_t)b * a.Hq + hk * gq + tid) * ns + split) * 2;
@@ -177,21 +281,50 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     }
 }
 
-// out[row][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s.
+// out[row][d] = sum_s 2^(m_s - M) o_s[d] / sum_s 2^(m_s - M) l_s.  The
+// per-split (m, l) pairs are staged in LDS by the block; the partial outputs
+// are read eight splits at a time.
+constexpr int kCombineMaxSplits = 1024;
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, const float* ws_ml,
                                                              float* out, int D, int ns) {
     const int64_t row = blockIdx.x;
     const int d = threadIdx.x;
-    if (d >= D) return;
+    __shared__ float w_s[kCombineMaxSplits];
+    __shared__ float red[2][4];
     const float* ml = ws_ml + row * ns * 2;
+    float mloc = -INFINITY;
+    for (int s = d; s < ns; s += blockDim.x) mloc = fmaxf(mloc, ml[2 * s]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 1)); mloc = fmaxf(mloc, __shfl_xor(mloc, 2));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 4)); mloc = fmaxf(mloc, __shfl_xor(mloc, 8));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16)); mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    if ((d & 63) == 0) red[0][d >> 6] = mloc;
+    __syncthreads();
     float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, ml[2 * s]);
-    float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < ns; ++s) {
+    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) M = fmaxf(M, red[0][w]);
+    float dloc = 0.0f;
+    for (int s = d; s < ns; s += blockDim.x) {
         const float w = exp2f(ml[2 * s] - M);
-        den = fmaf(w, ml[2 * s + 1], den);
-        num = fmaf(w, ws_o[(row * ns + s) * D + d], num);
+        w_s[s] = w;
+        dloc = fmaf(w, ml[2 * s + 1], dloc);
     }
+    dloc += __shfl_xor(dloc, 1); dloc += __shfl_xor(dloc, 2); dloc += __shfl_xor(dloc, 4);
+    dloc += __shfl_xor(dloc, 8); dloc += __shfl_xor(dloc, 16); dloc += __shfl_xor(dloc, 32);
+    if ((d & 63) == 0) red[1][d >> 6] = dloc;
+    __syncthreads();
+    float den = 0.0f;
+    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) den += red[1][w];
+    if (d >= D) return;
+    const float* o = ws_o + row * ns * D + d;
+    float num = 0.0f;
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = o[(int64_t)(s + u) * D];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) num = fmaf(w_s[s + u], v[u], num);
+    }
+    for (; s < ns; ++s) num = fmaf(w_s[s], o[(int64_t)s * D], num);
     out[row * D + d] = num / den;
 }
 
@@ -200,30 +333,21 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
-template <int KK, int VK, int DT>
-hipError_t launch_generic_q(const DecodeArgs& a, hipStream_t s) {
+template <int KK, int VK>
+hipError_t launch_generic_kv(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
-    switch (a.q_dtype) {
-        case KVQ_F32: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, DT, KVQ_F32>), grid, dim3(256), 0, s, a); break;
-        case KVQ_F16: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, DT, KVQ_F16>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, DT, KVQ_BF16>), grid, dim3(256), 0, s, a); break;
+    switch (a.D) {
+        case 32: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 32>), grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 64>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 128>), grid, dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
 }
 
-template <int KK, int VK>
-hipError_t launch_generic_dt(const DecodeArgs& a, hipStream_t s) {
-    switch (a.in_dtype) {
-        case KVQ_F32: return launch_generic_q<KK, VK, KVQ_F32>(a, s);
-        case KVQ_F16: return launch_generic_q<KK, VK, KVQ_F16>(a, s);
-        default: return launch_generic_q<KK, VK, KVQ_BF16>(a, s);
-    }
-}
-
 template <int KK>
 hipError_t launch_generic_v(const DecodeArgs& a, hipStream_t s) {
-    if (a.v_kind == KVQ_PLAIN) return launch_generic_dt<KK, KVQ_PLAIN>(a, s);
-    return launch_generic_dt<KK, KVQ_TOK_AFFINE>(a, s);
+    if (a.v_kind == KVQ_PLAIN) return launch_generic_kv<KK, KVQ_PLAIN>(a, s);
+    return launch_generic_kv<KK, KVQ_TOK_AFFINE>(a, s);
 }
 
 }  // namespace
@@ -256,6 +380,7 @@ size_t decode_workspace_bytes(int B, int Hq, int D, int cap) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     hipError_t e;
+    if (a.n_splits > kCombineMaxSplits) return hipErrorInvalidValue;   // both plans stay <= 512
     if (decode_fast_applies(a)) {
         e = launch_decode_fast(a, s);
         if (e != hipSuccess || a.n_splits == 1) return e;
