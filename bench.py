@@ -11,6 +11,8 @@ workloads and reported under "rows":
   C  StreamingLLM compaction of the headline cache to sink 4 + window 16380
   D  SnapKV prefill selection (8 kv-heads x 128, S = 8192, window 32,
      sink 4, budget 512): scores/s
+  B  decode on the other cache formats: Q4_0-style centered K + int8 V
+     (batch 16, T = 16384) and a KIVI int4 Llama-3.2-3B layer (T = 8192)
 Inputs are seeded synthetic data (synth) already resident in HBM when the
 timed region starts.  Times come from HIP events on the stream the kernels
 run on.  The CPU oracle is timed on a bounded sample as the CPU baseline.
@@ -127,7 +129,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", default="ACD", help="extra rows to time (subset of ACD)")
+    ap.add_argument("--rows", default="ACDB", help="extra rows to time (subset of ACDB)")
     ap.add_argument("--mode", default="full", choices=["full", "decode", "copy"],
                     help="decode: only the timed decode steps (for counter runs); "
                          "copy: a plain 2 GiB device copy (bandwidth probe / counter calibration)")
@@ -270,6 +272,51 @@ def main():
                                         f"budget={ex['budget']} Hkv={Hs} D={Ds}",
                             "us": round(msd * 1e3, 2), "scores/s": round(Hs * Ss / (msd * 1e-3), 1),
                             "GB/s": round(sbytes / msd / 1e6, 1)}
+
+    # ---- row B, other decode workloads: Q4_0-style centered K + int8 V (B=16,
+    # T=16384; HBM-bound) and a Llama-3.2-3B-shaped KIVI int4 layer (B=1,
+    # T=8192; latency-bound).  Device time per step from a replayed graph of
+    # 10 steps, so host marshalling is not in the timed region.
+    if "B" in args.rows:
+        for wname in ("q4_0_centered", "llama3b_kivi_int4"):
+            wb = synth.workload(wname)
+            eb = wb.extra
+            Bb, Hb, Hqb, Db, Tb = wb.batch, wb.n_kv_heads, wb.n_q_heads, wb.head_dim, wb.seq_len
+            kh, vh, qh = synth.full(wb, threads=max(1, min(16, os.cpu_count() or 1)))
+            kdb, vdb, qb = (torch.from_numpy(x).to(dev) for x in (kh, vh, qh))
+            del kh, vh
+            bias, flags = None, 0
+            if eb["k_kind"] == "tok_sym4":
+                bias = torch.from_numpy(np.stack([synth.head_params(wb, h)[0] for h in range(Hb)]))
+                flags = K.KVQ_CENTER_K
+            Lb = K.Layout(batch=Bb, n_kv_heads=Hb, head_dim=Db, capacity=Tb, k_kind=eb["k_kind"],
+                          k_bits=eb["k_bits"], k_group=eb["k_group"], v_kind="tok_affine",
+                          v_bits=eb["v_bits"], v_group=eb["v_group"], in_dtype=wb.dtype, flags=flags)
+            cb = K.Cache(Lb, k_bias=bias)
+            K.kvq_quantize_append(Lb, cb, kdb, vdb)
+            del kdb, vdb
+            outb = torch.empty((Bb, Hqb, Db), dtype=torch.float32, device=dev)
+            wsb = torch.empty(max(K.kvq_decode_workspace_bytes(Lb, Hqb), 16), dtype=torch.uint8, device=dev)
+            stepb = lambda: K.kvq_decode_attention(Lb, cb, qb, out=outb, ws=wsb)
+            stepb()
+            torch.cuda.synchronize()
+            gb = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gb):
+                for _ in range(10):
+                    stepb()
+            usb = time_stream(gb.replay, 10, 2, torch) / 10 * 1e3
+            qo = Bb * Hqb * Db * (2 + 4)
+            if eb["k_kind"] == "tok_sym4":     # codes + fp16 block scales; int8 V + (scale, zero)
+                nb = Bb * Hb * Tb * (Db // 2 + (Db // 32) * 2 + Db * eb["v_bits"] // 8 + (Db // eb["v_group"]) * 4) + qo
+            else:                              # KIVI: codes + one table row per 32 tokens; int4 V
+                nb = Bb * Hb * (Tb * Db * eb["k_bits"] // 8 + (Tb // eb["k_group"]) * Db * 4 +
+                                Tb * Db * eb["v_bits"] // 8 + Tb * (Db // eb["v_group"]) * 4) + qo
+            rows[f"B_decode_{wname}"] = {
+                "workload": f"{wname} B={Bb} Hq/Hkv={Hqb}/{Hb} D={Db} T={Tb} K {eb['k_kind']} "
+                            f"{eb['k_bits']}-bit, V affine {eb['v_bits']}-bit",
+                "us": round(usb, 2), "algorithmic_bytes": nb, "GB/s": round(nb / usb / 1e3, 1),
+                "frac_hbm": round(nb / usb / 1e3 / PEAK_HBM_GBS, 4)}
+            del gb, cb, outb, wsb
 
     cpu = None
     if not args.no_cpu_baseline:
