@@ -45,6 +45,8 @@ def lib():
         L.kvo_dequant.argtypes = [P, i32, i32]
         L.kvo_decode_head.argtypes = [P, P, i32, P, f64, P]
         L.kvo_snapkv_scores.argtypes = [P, i32, i32, i32, P]
+        L.kvo_snapkv_scores_rows.argtypes = [P, i32, P, i32, i32, P]
+        L.kvo_maxpool1d.argtypes = [P, i32, i32, P]
         L.kvo_snapkv_select.restype = i32
         L.kvo_snapkv_select.argtypes = [P, i32, i32, i32, P]
         _lib = L
@@ -191,6 +193,24 @@ def snapkv_scores(K: np.ndarray, w: int) -> np.ndarray:
     S, D = K.shape
     out = np.empty(S, dtype=np.float64)
     lib().kvo_snapkv_scores(_p(K), S, D, w, _p(out))
+    return out
+
+
+def snapkv_scores_rows(Q: np.ndarray, K: np.ndarray) -> np.ndarray:
+    """fp64 scores [S] of one kv-head from observation rows Q [n][D] and K [S][D] (fp32)."""
+    Q = np.ascontiguousarray(Q, dtype=np.float32)
+    K = np.ascontiguousarray(K, dtype=np.float32)
+    S, D = K.shape
+    out = np.empty(S, dtype=np.float64)
+    lib().kvo_snapkv_scores_rows(_p(Q), Q.shape[0], _p(K), S, D, _p(out))
+    return out
+
+
+def maxpool1d(x: np.ndarray, kernel: int) -> np.ndarray:
+    """Max over a centered window of odd width `kernel`, clipped at the ends (fp32)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty_like(x)
+    lib().kvo_maxpool1d(_p(x), x.shape[0], kernel, _p(out))
     return out
 
 

@@ -295,6 +295,47 @@ void kvo_snapkv_scores(const float* K, int S, int D, int w, double* score)
     free(row);
 }
 
+void kvo_snapkv_scores_rows(const float* Q, int n_rows, const float* K, int S, int D, double* score)
+{
+    for (int j = 0; j < S; ++j) score[j] = 0.0;
+    if (S <= 0 || n_rows <= 0) return;
+    double inv_sqrt_d = 1.0 / sqrt((double)D);
+    double* row = (double*)malloc(sizeof(double) * (size_t)S);
+    for (int r = 0; r < n_rows; ++r) {
+        double m = -INFINITY;
+        for (int j = 0; j < S; ++j) {
+            double acc = 0.0;
+            for (int d = 0; d < D; ++d)
+                acc += (double)Q[(int64_t)r * D + d] * (double)K[(int64_t)j * D + d];
+            row[j] = acc * inv_sqrt_d;
+            if (row[j] > m) m = row[j];
+        }
+        double denom = 0.0;
+        for (int j = 0; j < S; ++j) {
+            row[j] = exp(row[j] - m);
+            denom += row[j];
+        }
+        for (int j = 0; j < S; ++j)
+            score[j] += row[j] / denom;
+    }
+    for (int j = 0; j < S; ++j)
+        score[j] /= (double)n_rows;
+    free(row);
+}
+
+void kvo_maxpool1d(const float* in, int S, int kernel, float* out)
+{
+    int r = (kernel - 1) / 2;
+    for (int j = 0; j < S; ++j) {
+        int lo = j - r < 0 ? 0 : j - r;
+        int hi = j + r > S - 1 ? S - 1 : j + r;
+        float m = in[lo];
+        for (int t = lo + 1; t <= hi; ++t)
+            if (in[t] > m) m = in[t];
+        out[j] = m;
+    }
+}
+
 typedef struct { float s; int32_t i; } kvo_cand;
 
 /* Higher score first; equal scores: lower position first. */

@@ -91,6 +91,19 @@ void kvo_decode_head(const kvo_view* K, const kvo_view* V, int T,
  * the window; w clamped to S.  K: [S][D] fp32.  score: [S].                   */
 void kvo_snapkv_scores(const float* K, int S, int D, int w, double* score);
 
+/* ---- SnapKV with given observation rows (fp64) ---------------------------- *
+ * [P2] "Proxy limitation": the SnapKV paper scores with the prompt's final
+ * query vectors rather than the trailing key rows.  score[j] = mean over the
+ * n_rows rows r of softmax_j(Q[r] . K[j] / sqrt(D)), no mask.
+ * Q: [n_rows][D] fp32, K: [S][D] fp32, score: [S].                          */
+void kvo_snapkv_scores_rows(const float* Q, int n_rows, const float* K, int S, int D, double* score);
+
+/* ---- max-pool smoothing of scores ------------------------------------------ *
+ * [P2] "Proxy limitation": the paper smooths the scores with a max-pool of
+ * width kernel > 1 before ranking.  out[j] = max of in[j'] over
+ * j - (kernel-1)/2 <= j' <= j + (kernel-1)/2, 0 <= j' < S.  kernel odd.     */
+void kvo_maxpool1d(const float* in, int S, int kernel, float* out);
+
 /* ---- D2: sink guarantee + top-k + sorted union -------------------------- *
  * [P2] "How it works" steps 2-3.  Ties are broken by the lower index.
  * kept: [min(budget, S)] ascending positions.  Returns the count.           */

@@ -41,6 +41,10 @@ MUTANTS = {
     "window_front": ("for (int i = S - wc; i < S; ++i) {", "for (int i = 0; i < wc; ++i) {"),
     # tie-break prefers the higher position
     "tie_high": ("return (x->i > y->i) - (x->i < y->i);", "return (x->i < y->i) - (x->i > y->i);"),
+    # query-row scores divided by S instead of the row count
+    "rows_mean_over_S": ("score[j] /= (double)n_rows;", "score[j] /= (double)S;"),
+    # max-pool window one short on each side
+    "pool_narrow": ("int r = (kernel - 1) / 2;", "int r = (kernel - 1) / 2 - 1;"),
 }
 
 

@@ -429,6 +429,53 @@ def test_snapkv_end_to_end_shapes_and_coverage():
         assert s[kept[0, h]].sum() >= s[rand].sum()
 
 
+def test_snapkv_query_rows_pins():
+    """[P2] "Proxy limitation" variant: observation rows given explicitly.
+    Pinned to the key-proxy scorer (same rows), to the uniform closed form for
+    zero queries, and to a closed form for a one-hot query over one-hot keys."""
+    rng = np.random.default_rng(11)
+    K = rng.standard_normal((90, 32)).astype(np.float32)
+    # the trailing key rows as explicit rows reproduce the proxy scores exactly
+    assert np.array_equal(oracle.snapkv_scores_rows(K[-12:], K), oracle.snapkv_scores(K, 12))
+    # zero queries: every logit 0, so every score is 1/S
+    z = oracle.snapkv_scores_rows(np.zeros((5, 32), np.float32), K)
+    assert np.allclose(z, 1.0 / 90, rtol=0, atol=1e-15)
+    # one-hot keys e_(j mod D), query c e_0: logit c/sqrt(D) for j = 0 and 32, else 0
+    D, S, c = 32, 40, 6.0
+    Kh = np.zeros((S, D), np.float32)
+    Kh[np.arange(S), np.arange(S) % D] = 1.0
+    q = np.zeros((1, D), np.float32)
+    q[0, 0] = c
+    sc = oracle.snapkv_scores_rows(q, Kh)
+    e = math.exp(c / math.sqrt(D))
+    hot = e / (2 * e + (S - 2))
+    cold = 1.0 / (2 * e + (S - 2))
+    assert abs(sc[0] - hot) < 1e-15 and abs(sc[32] - hot) < 1e-15
+    assert np.allclose(np.delete(sc, [0, 32]), cold, rtol=1e-14, atol=0)
+    # rows are averaged: permuting them changes nothing, duplicating all of them neither
+    Q = rng.standard_normal((7, 32)).astype(np.float32)
+    a = oracle.snapkv_scores_rows(Q, K)
+    assert np.allclose(oracle.snapkv_scores_rows(Q[::-1], K), a, rtol=1e-13, atol=0)
+    assert np.allclose(oracle.snapkv_scores_rows(np.concatenate([Q, Q]), K), a, rtol=1e-13, atol=0)
+    assert abs(a.sum() - 1.0) < 1e-12
+
+
+def test_maxpool_pins():
+    """[P2] "Proxy limitation": max-pool smoothing of width k before ranking.
+    Pinned to scipy's maximum filter (edge clamping adds no new values), the
+    identity at k = 1 and the global max at k >= 2S - 1."""
+    from scipy.ndimage import maximum_filter1d
+    rng = np.random.default_rng(12)
+    for S in (1, 2, 7, 100):
+        x = rng.random(S).astype(np.float32)
+        x[S // 2] = x[0]                      # ties
+        for k in (1, 3, 5, 7, 31):
+            got = oracle.maxpool1d(x, k)
+            assert np.array_equal(got, maximum_filter1d(x, size=k, mode="nearest")), (S, k)
+        assert np.array_equal(oracle.maxpool1d(x, 1), x)
+        assert np.all(oracle.maxpool1d(x, 2 * S + 1) == x.max())
+
+
 def test_bits_per_element_accounting():
     """[P4] s.2 / s.4: 4-bit g64 with fp16 scale+bias is 4.5 bits/elt, g32 is 5.0."""
     for case in golden("p4_bits_per_element.json")["cases"]:
