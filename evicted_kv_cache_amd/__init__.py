@@ -7,9 +7,10 @@ raises, and so does a call when no GPU is present.
 
 The functions carry the C ABI names (see include/kvq.h):
 ``kvq_cache_sizes``, ``kvq_quantize_append``, ``kvq_decode_attention``,
-``kvq_evict_streaming``, ``kvq_snapkv_select``,
-``kvq_snapkv_select_from_scores``, ``kvq_decode_workspace_bytes``,
-``kvq_snapkv_workspace_bytes``.
+``kvq_evict_streaming``, ``kvq_snapkv_select``, ``kvq_snapkv_select_ex``,
+``kvq_snapkv_select_from_scores``, ``kvq_snapkv_pool_scores``,
+``kvq_decode_workspace_bytes``, ``kvq_snapkv_workspace_bytes``,
+``kvq_snapkv_workspace_bytes_ex``.
 """
 from __future__ import annotations
 
@@ -35,7 +36,8 @@ DTYPES = {"f32": KVQ_F32, "f16": KVQ_F16, "bf16": KVQ_BF16}
 EXPORTS = ("kvq_cache_sizes", "kvq_cache_reset", "kvq_quantize_append",
            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_evict_streaming",
            "kvq_snapkv_workspace_bytes", "kvq_snapkv_select",
-           "kvq_snapkv_select_from_scores", "kvq_status_string", "kvq_version")
+           "kvq_snapkv_select_from_scores", "kvq_snapkv_workspace_bytes_ex",
+           "kvq_snapkv_select_ex", "kvq_snapkv_pool_scores", "kvq_status_string", "kvq_version")
 
 
 class KvqError(RuntimeError):
@@ -57,6 +59,11 @@ class c_cache(ctypes.Structure):
                 ("k_row", ctypes.c_void_p), ("k_bias", ctypes.c_void_p),
                 ("n_stored", ctypes.c_int32), ("n_quant", ctypes.c_int32),
                 ("next_pos", ctypes.c_int32), ("n_head", ctypes.c_int32)]
+
+
+class c_snapkv_opts(ctypes.Structure):
+    _fields_ = [("q_window", ctypes.c_void_p), ("n_q_heads", ctypes.c_int32),
+                ("pool_kernel", ctypes.c_int32)]
 
 
 class c_sizes(ctypes.Structure):
@@ -88,6 +95,10 @@ def lib():
         L.kvq_snapkv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
         L.kvq_snapkv_select.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         L.kvq_snapkv_select_from_scores.argtypes = [P, i32, i32, i32, i32, i32, P, P]
+        L.kvq_snapkv_workspace_bytes_ex.restype = sz
+        L.kvq_snapkv_workspace_bytes_ex.argtypes = [P, i32, i32, i32, i32, i32]
+        L.kvq_snapkv_select_ex.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
+        L.kvq_snapkv_pool_scores.argtypes = [P, P, i32, i32, i32, i32, P]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_version.restype = i32
@@ -272,6 +283,67 @@ def kvq_snapkv_select(k, v, obs_window: int, n_sink: int, budget: int, scores=No
                                    v_out.data_ptr(), ws.data_ptr(), ws.numel(), _stream(stream)),
            "kvq_snapkv_select")
     return scores, kept, k_out, v_out
+
+
+def _snap_opts(q_window, pool_kernel: int):
+    torch = _torch()
+    if q_window is None:
+        return c_snapkv_opts(None, 0, pool_kernel)
+    assert q_window.dtype == torch.float16 and q_window.is_contiguous() and q_window.dim() == 4
+    return c_snapkv_opts(q_window.data_ptr(), q_window.shape[1], pool_kernel)
+
+
+def kvq_snapkv_workspace_bytes_ex(batch, n_kv_heads, seq_len, head_dim, obs_window,
+                                  q_window=None, pool_kernel: int = 1) -> int:
+    o = _snap_opts(q_window, pool_kernel)
+    return int(lib().kvq_snapkv_workspace_bytes_ex(ctypes.byref(o), batch, n_kv_heads, seq_len,
+                                                   head_dim, obs_window))
+
+
+def kvq_snapkv_select_ex(k, v, obs_window: int, n_sink: int, budget: int, q_window=None,
+                         pool_kernel: int = 1, scores=None, kept=None, k_out=None, v_out=None,
+                         ws=None, stream=None):
+    """kvq_snapkv_select with query windows q_window [B][Hq][obs_window][D] fp16
+    (None: the key proxy) and max-pool width pool_kernel (1: none).
+    Returns (scores, kept, k_out, v_out); scores are the unpooled ones."""
+    torch = _torch()
+    assert k.dtype == torch.float16 and v.dtype == torch.float16
+    assert k.is_contiguous() and v.is_contiguous()
+    B, H, S, D = k.shape
+    if q_window is not None:
+        assert q_window.shape[0] == B and q_window.shape[2] == obs_window and q_window.shape[3] == D
+    n_keep = min(budget, S)
+    dev = k.device
+    if scores is None:
+        scores = torch.empty((B, H, S), dtype=torch.float32, device=dev)
+    if kept is None:
+        kept = torch.empty((B, H, n_keep), dtype=torch.int32, device=dev)
+    if k_out is None:
+        k_out = torch.empty((B, H, n_keep, D), dtype=torch.float16, device=dev)
+    if v_out is None:
+        v_out = torch.empty((B, H, n_keep, D), dtype=torch.float16, device=dev)
+    o = _snap_opts(q_window, pool_kernel)
+    if ws is None:
+        nb = lib().kvq_snapkv_workspace_bytes_ex(ctypes.byref(o), B, H, S, D, obs_window)
+        ws = torch.empty(max(int(nb), 16), dtype=torch.uint8, device=dev)
+    _check(lib().kvq_snapkv_select_ex(ctypes.byref(o), k.data_ptr(), v.data_ptr(), B, H, S, D,
+                                      obs_window, n_sink, budget, scores.data_ptr(),
+                                      kept.data_ptr(), k_out.data_ptr(), v_out.data_ptr(),
+                                      ws.data_ptr(), ws.numel(), _stream(stream)),
+           "kvq_snapkv_select_ex")
+    return scores, kept, k_out, v_out
+
+
+def kvq_snapkv_pool_scores(scores, pool_kernel: int, pooled=None, stream=None):
+    """Max-pool smoothing of [B][Hkv][S] fp32 scores over odd width pool_kernel."""
+    torch = _torch()
+    assert scores.dtype == torch.float32 and scores.is_contiguous()
+    B, H, S = scores.shape
+    if pooled is None:
+        pooled = torch.empty_like(scores)
+    _check(lib().kvq_snapkv_pool_scores(scores.data_ptr(), pooled.data_ptr(), B, H, S, pool_kernel,
+                                        _stream(stream)), "kvq_snapkv_pool_scores")
+    return pooled
 
 
 def kvq_snapkv_select_from_scores(scores, n_sink: int, budget: int, kept=None, stream=None):

@@ -319,23 +319,51 @@ kvq_status kvq_evict_streaming(const kvq_layout* L, const kvq_cache* src, kvq_ca
     return KVQ_OK;
 }
 
-size_t kvq_snapkv_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t w) {
-    if (B < 1 || H < 1 || S < 1 || w < 1 || (D != 32 && D != 64 && D != 128)) return 0;
-    return snapkv_ws_bytes(B, H, S, D, w);
+// Observation rows per kv-head for a SnapKV call: the last min(w, S) key
+// rows, or G * w query rows with query windows; -1 when the options are
+// invalid, -2 when they are valid but unsupported.
+static int snap_rows(const kvq_snapkv_opts* o, int32_t H, int32_t S, int32_t w) {
+    int64_t rows = w < S ? w : S;
+    if (o && o->q_window) {
+        if (o->n_q_heads < H || o->n_q_heads % H != 0 || w > S) return -1;
+        rows = (int64_t)(o->n_q_heads / H) * w;
+    }
+    return rows > 128 ? -2 : (int)rows;
 }
 
-kvq_status kvq_snapkv_select(const void* k, const void* v, int32_t B, int32_t H, int32_t S,
-                             int32_t D, int32_t w, int32_t n_sink, int32_t budget, float* scores,
-                             int32_t* kept, void* k_out, void* v_out, void* ws, size_t ws_bytes,
-                             void* stream) {
+static int snap_pool(const kvq_snapkv_opts* o) { return o ? o->pool_kernel : 1; }
+
+size_t kvq_snapkv_workspace_bytes_ex(const kvq_snapkv_opts* opts, int32_t B, int32_t H, int32_t S, int32_t D,
+                                     int32_t w) {
+    if (B < 1 || H < 1 || S < 1 || w < 1 || (D != 32 && D != 64 && D != 128)) return 0;
+    const int rows = snap_rows(opts, H, S, w);
+    const int pool = snap_pool(opts);
+    if (rows < 1 || pool < 1 || pool % 2 == 0) return 0;
+    return snapkv_ws_bytes(B, H, S, D, rows, pool > 1);
+}
+
+size_t kvq_snapkv_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, int32_t w) {
+    return kvq_snapkv_workspace_bytes_ex(nullptr, B, H, S, D, w);
+}
+
+kvq_status kvq_snapkv_select_ex(const kvq_snapkv_opts* opts, const void* k, const void* v, int32_t B, int32_t H,
+                                int32_t S, int32_t D, int32_t w, int32_t n_sink, int32_t budget, float* scores,
+                                int32_t* kept, void* k_out, void* v_out, void* ws, size_t ws_bytes,
+                                void* stream) {
     if (!k || !v || !kept || !k_out || !v_out) return KVQ_ERR_INVALID_ARG;
     if (B < 1 || H < 1 || S < 1 || w < 1 || budget < 1 || n_sink < 0) return KVQ_ERR_INVALID_ARG;
     if (D != 32 && D != 64 && D != 128) return D > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
-    if ((w < S ? w : S) > 128) return KVQ_ERR_UNSUPPORTED;
+    const int pool = snap_pool(opts);
+    if (pool < 1 || pool % 2 == 0) return KVQ_ERR_INVALID_ARG;
+    if (pool > 31) return KVQ_ERR_UNSUPPORTED;
+    const int rows = snap_rows(opts, H, S, w);
+    if (rows == -1) return KVQ_ERR_INVALID_ARG;
+    if (rows == -2) return KVQ_ERR_UNSUPPORTED;
     if ((int64_t)B * H * S > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
-    const void* ptrs[7] = {k, v, scores, kept, k_out, v_out, ws};
+    const void* qw = opts ? opts->q_window : nullptr;
+    const void* ptrs[8] = {k, v, scores, kept, k_out, v_out, ws, qw};
     for (const void* p : ptrs) if (p && !aligned16(p)) return KVQ_ERR_ALIGNMENT;
-    const size_t need = snapkv_ws_bytes(B, H, S, D, w);
+    const size_t need = snapkv_ws_bytes(B, H, S, D, rows, pool > 1);
     if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     SnapArgs a{};
@@ -343,15 +371,52 @@ kvq_status kvq_snapkv_select(const void* k, const void* v, int32_t B, int32_t H,
     a.kept = kept; a.k_out = static_cast<uint16_t*>(k_out); a.v_out = static_cast<uint16_t*>(v_out);
     a.B = B; a.H = H; a.S = S; a.D = D; a.w = w; a.n_sink = n_sink; a.budget = budget;
     a.n_chunks = (S + 127) / 128;
-    const int wc = w < S ? w : S;
-    size_t stats = (size_t)B * H * a.n_chunks * wc * 2 * sizeof(float);
+    a.n_rows = rows;
+    if (qw) {
+        a.obs = static_cast<const uint16_t*>(qw);
+        a.obs_stride = (int64_t)rows * D;
+    } else {
+        a.obs = a.k + (int64_t)(S - rows) * D;
+        a.obs_stride = (int64_t)S * D;
+    }
+    size_t stats = (size_t)B * H * a.n_chunks * rows * 2 * sizeof(float);
     stats = (stats + 255) & ~(size_t)255;
-    a.stats = static_cast<float*>(ws);
-    a.scores = scores ? scores : reinterpret_cast<float*>(static_cast<char*>(ws) + stats);
+    size_t sc = ((size_t)B * H * S * sizeof(float) + 255) & ~(size_t)255;
+    char* wsb = static_cast<char*>(ws);
+    a.stats = reinterpret_cast<float*>(wsb);
+    a.scores = scores ? scores : reinterpret_cast<float*>(wsb + stats);
     if (launch_snapkv_scores(a, s) != hipSuccess) return KVQ_ERR_HIP;
-    if (launch_snapkv_select(a.scores, B, H, S, n_sink, budget, kept, s) != hipSuccess) return KVQ_ERR_HIP;
+    const float* rank = a.scores;
+    if (pool > 1) {
+        float* pooled = reinterpret_cast<float*>(wsb + stats + sc);
+        if (launch_snapkv_pool(a.scores, pooled, (int64_t)B * H, S, pool, s) != hipSuccess) return KVQ_ERR_HIP;
+        rank = pooled;
+    }
+    if (launch_snapkv_select(rank, B, H, S, n_sink, budget, kept, s) != hipSuccess) return KVQ_ERR_HIP;
     if (launch_snapkv_gather(a, s) != hipSuccess) return KVQ_ERR_HIP;
     return KVQ_OK;
+}
+
+kvq_status kvq_snapkv_select(const void* k, const void* v, int32_t B, int32_t H, int32_t S,
+                             int32_t D, int32_t w, int32_t n_sink, int32_t budget, float* scores,
+                             int32_t* kept, void* k_out, void* v_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+    return kvq_snapkv_select_ex(nullptr, k, v, B, H, S, D, w, n_sink, budget, scores, kept, k_out, v_out, ws,
+                                ws_bytes, stream);
+}
+
+kvq_status kvq_snapkv_pool_scores(const float* scores, float* pooled, int32_t B, int32_t H, int32_t S,
+                                  int32_t pool_kernel, void* stream) {
+    if (!scores || !pooled) return KVQ_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || S < 1 || pool_kernel < 1 || pool_kernel % 2 == 0) return KVQ_ERR_INVALID_ARG;
+    if (pool_kernel > 31) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * S > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    const char* a0 = reinterpret_cast<const char*>(scores);
+    const char* b0 = reinterpret_cast<const char*>(pooled);
+    const size_t n = (size_t)B * H * S * sizeof(float);
+    if (a0 < b0 + n && b0 < a0 + n) return KVQ_ERR_INVALID_ARG;
+    return hip_status(launch_snapkv_pool(scores, pooled, (int64_t)B * H, S, pool_kernel,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_snapkv_select_from_scores(const float* scores, int32_t B, int32_t H, int32_t S,

@@ -133,11 +133,14 @@ hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
 // SnapKV.
 struct SnapArgs {
     const uint16_t* k; const uint16_t* v;
+    // observation rows of (b, h): obs + (b * H + h) * obs_stride + r * D, r < n_rows
+    const uint16_t* obs; int64_t obs_stride; int n_rows;
     float* scores; int32_t* kept; uint16_t* k_out; uint16_t* v_out;
-    float* stats;          // [B][H][n_chunks][w][2]
+    float* stats;          // [B][H][n_chunks][n_rows][2]
     int B, H, S, D, w, n_sink, budget, n_chunks;
 };
-size_t snapkv_ws_bytes(int B, int H, int S, int D, int w);
+size_t snapkv_ws_bytes(int B, int H, int S, int D, int n_rows, bool pooled);
+hipError_t launch_snapkv_pool(const float* in, float* out, int64_t rows, int S, int kernel, hipStream_t s);
 hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s);
 hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_sink, int budget,
                                 int32_t* kept, hipStream_t s);

@@ -47,9 +47,9 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kh = lane >> 5, l32 = lane & 31;
     const int S = a.S;
-    const int wc = min(a.w, S);
-    const int row0 = S - wc;
+    const int wc = a.n_rows;
     const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
+    const uint16_t* O = a.obs + ((int64_t)b * a.H + h) * a.obs_stride;   // observation rows
     const float c = 1.4426950408889634f / sqrtf((float)D);
     const int key_base = chunk * kChunk + wave * 32;
     __shared__ float sm[4][kMaxWindow], sl[4][kMaxWindow];
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
 #pragma unroll
         for (int q = 0; q < NK; ++q) {
             Bv[q] = half8{};
-            if (wr < wc) Bv[q] = load_half8(K + (int64_t)(row0 + wr) * D + q * 16 + kh * 8);
+            if (wr < wc) Bv[q] = load_half8(O + (int64_t)wr * D + q * 16 + kh * 8);
         }
         floatx16 acc = {};
 #pragma unroll
@@ -106,9 +106,9 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kh = lane >> 5, l32 = lane & 31;
     const int S = a.S;
-    const int wc = min(a.w, S);
-    const int row0 = S - wc;
+    const int wc = a.n_rows;
     const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
+    const uint16_t* O = a.obs + ((int64_t)b * a.H + h) * a.obs_stride;   // observation rows
     const float c = 1.4426950408889634f / sqrtf((float)D);
     __shared__ float Mrow[kMaxWindow], invL[kMaxWindow];
     // this lane's key fragments, loaded before the stats merge so that both
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
 #pragma unroll
     for (int q = 0; q < NK; ++q) {
         A[q] = half8{};
-        if (l32 < wc) A[q] = load_half8(K + (int64_t)(row0 + l32) * D + q * 16 + kh * 8);
+        if (l32 < wc) A[q] = load_half8(O + (int64_t)l32 * D + q * 16 + kh * 8);
     }
     {
         // merge the per-chunk (max, sum) of every window row: tpr threads per
@@ -173,7 +173,7 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
 #pragma unroll
             for (int q = 0; q < NK; ++q) {
                 A[q] = half8{};
-                if (wr < wc) A[q] = load_half8(K + (int64_t)(row0 + wr) * D + q * 16 + kh * 8);
+                if (wr < wc) A[q] = load_half8(O + (int64_t)wr * D + q * 16 + kh * 8);
             }
         }
         floatx16 acc = {};
@@ -508,15 +508,41 @@ __global__ __launch_bounds__(256) void snap_gather_kernel(SnapArgs a, int n_keep
     reinterpret_cast<uint4*>(a.v_out)[r * upr + u] = vs[src * upr + u];
 }
 
+// Max-pool smoothing of a score row: out[r][j] = max of in[r][j'] over
+// |j' - j| <= half, clipped to [0, S).
+__global__ __launch_bounds__(256) void snap_pool_kernel(const float* __restrict__ in, float* __restrict__ out,
+                                                        int64_t rows, int S, int half) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * S) return;
+    const int64_t r = idx / S;
+    const int j = (int)(idx - r * S);
+    const float* x = in + r * S;
+    const int lo = max(0, j - half), hi = min(S - 1, j + half);
+    float m = x[lo];
+    for (int t = lo + 1; t <= hi; ++t) m = fmaxf(m, x[t]);
+    out[idx] = m;
+}
+
 }  // namespace
 
-size_t snapkv_ws_bytes(int B, int H, int S, int D, int w) {
+// Workspace: chunk statistics, then scores (used when the caller passes no
+// scores buffer), then pooled scores (when pooling).
+size_t snapkv_ws_bytes(int B, int H, int S, int D, int n_rows, bool pooled) {
     (void)D;
-    const int wc = w < S ? w : S;
     const int n_chunks = (S + kChunk - 1) / kChunk;
-    size_t stats = (size_t)B * H * n_chunks * wc * 2 * sizeof(float);
+    size_t stats = (size_t)B * H * n_chunks * n_rows * 2 * sizeof(float);
     stats = (stats + 255) & ~(size_t)255;
-    return stats + (size_t)B * H * S * sizeof(float);
+    size_t sc = (size_t)B * H * S * sizeof(float);
+    sc = (sc + 255) & ~(size_t)255;
+    return stats + sc + (pooled ? sc : 0);
+}
+
+hipError_t launch_snapkv_pool(const float* in, float* out, int64_t rows, int S, int kernel, hipStream_t s) {
+    const int64_t n = rows * S;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(snap_pool_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in, out, rows, S,
+                       (kernel - 1) / 2);
+    return hipGetLastError();
 }
 
 template <int D>

@@ -214,7 +214,7 @@ kvq_status kvq_evict_streaming(const kvq_layout* layout, const kvq_cache* src,
                                kvq_cache* dst, int32_t sink, int32_t window,
                                void* stream);
 
-/* Workspace bytes for kvq_snapkv_select / kvq_snapkv_select_from_scores. */
+/* Workspace bytes for kvq_snapkv_select (0 for invalid or unsupported sizes). */
 size_t kvq_snapkv_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t seq_len,
                                   int32_t head_dim, int32_t obs_window);
 
@@ -243,6 +243,50 @@ kvq_status kvq_snapkv_select_from_scores(const float* scores, int32_t batch,
                                          int32_t n_kv_heads, int32_t seq_len,
                                          int32_t n_sink, int32_t budget,
                                          int32_t* kept, void* stream);
+
+/* SnapKV variants of the paper that the page leaves out ([P2] "Proxy
+ * limitation"): the prompt's final query vectors as the observation window,
+ * and max-pool smoothing of the scores before ranking.
+ *   q_window     device [B][n_q_heads][obs_window][D] fp16 queries, or NULL:
+ *                the last obs_window key rows stand in for them (the page's
+ *                proxy).  With queries, a kv-head's score is the mean over
+ *                all n_q_heads/Hkv * obs_window rows of its query-head group
+ *                (query head hq belongs to kv-head hq / (n_q_heads / Hkv)).
+ *   n_q_heads    query heads when q_window is set: a multiple of Hkv, with
+ *                (n_q_heads / Hkv) * obs_window <= 128 and obs_window <= S
+ *                (the window is the prompt's own last queries).
+ *   pool_kernel  odd width 1..31: positions are ranked by the maximum score
+ *                over [j - (w-1)/2, j + (w-1)/2] (clipped at the ends); 1 = none.
+ *                The scores output stays unpooled.                           */
+typedef struct kvq_snapkv_opts {
+    const void* q_window;
+    int32_t n_q_heads;
+    int32_t pool_kernel;
+} kvq_snapkv_opts;
+
+/* Workspace bytes for kvq_snapkv_select_ex (opts NULL: as kvq_snapkv_select;
+ * 0 for invalid or unsupported options or sizes).                           */
+size_t kvq_snapkv_workspace_bytes_ex(const kvq_snapkv_opts* opts, int32_t batch, int32_t n_kv_heads,
+                                     int32_t seq_len, int32_t head_dim, int32_t obs_window);
+
+/* kvq_snapkv_select with the options above (opts NULL gives the same result
+ * as kvq_snapkv_select).  Errors as kvq_snapkv_select, plus
+ * KVQ_ERR_INVALID_ARG for an even or non-positive pool_kernel, n_q_heads
+ * not a positive multiple of Hkv or obs_window > S with q_window set;
+ * KVQ_ERR_ALIGNMENT for a q_window not 16-byte aligned; KVQ_ERR_UNSUPPORTED for pool_kernel > 31
+ * or more than 128 observation rows per kv-head.                            */
+kvq_status kvq_snapkv_select_ex(const kvq_snapkv_opts* opts, const void* k, const void* v,
+                                int32_t batch, int32_t n_kv_heads, int32_t seq_len, int32_t head_dim,
+                                int32_t obs_window, int32_t n_sink, int32_t budget, float* scores,
+                                int32_t* kept, void* k_out, void* v_out, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/* Max-pool smoothing alone: pooled[b][h][j] = max of scores[b][h][j'] over
+ * |j' - j| <= (pool_kernel - 1) / 2, 0 <= j' < S.  Device [B][Hkv][S] fp32;
+ * pooled must not overlap scores.  pool_kernel odd, 1..31.                  */
+kvq_status kvq_snapkv_pool_scores(const float* scores, float* pooled, int32_t batch,
+                                  int32_t n_kv_heads, int32_t seq_len, int32_t pool_kernel,
+                                  void* stream);
 
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);

@@ -11,6 +11,9 @@ Draw order inside a slice stream: K [T][D], then V [T][D], then the queries of
 that kv-head's query-head group [G][D].  Per-kv-head parameters (the K channel
 bias and the choice of outlier channels) come from a second stream
 ``default_rng([seed, config_id, HEAD_STREAM, h])``, drawn in that order.
+The prompt's last queries (SnapKV observation windows) of slice (b, h) come
+from a third stream ``default_rng([seed, config_id, QWIN_STREAM, b, h])``:
+[G][n][D] for the G query heads of kv-head h.
 All draws are float32 standard normals; N(0, sigma) means standard deviation
 sigma.  Values are cast to the workload's dtype with round-to-nearest-even.
 
@@ -35,6 +38,7 @@ import numpy as np
 
 SEED = 0
 HEAD_STREAM = 1 << 20
+QWIN_STREAM = 1 << 21
 
 
 @dataclass(frozen=True)
@@ -171,6 +175,13 @@ def slice_cast(w: Workload, b: int, h: int, T: int | None = None):
     """Slice (b, h) in the workload's storage dtype: (K, V, Q)."""
     k, v, q = slice_f32(w, b, h, T)
     return cast(k, w.dtype), cast(v, w.dtype), cast(q, w.dtype)
+
+
+def query_window(w: Workload, b: int, h: int, n: int, group: int | None = None):
+    """Observation-window queries [G][n][D] of kv-head h in storage dtype."""
+    G = w.group if group is None else group
+    rng = np.random.default_rng([SEED, w.config_id, QWIN_STREAM, b, h])
+    return cast(rng.standard_normal((G, n, w.head_dim), dtype=np.float32), w.dtype)
 
 
 def full(w: Workload, T: int | None = None, batch: int | None = None,

@@ -213,6 +213,45 @@ def test_snapkv_validation_without_gpu():
     assert lib.kvq_snapkv_select_from_scores(FAKE, 1, 8, 0, 4, 10, FAKE, None) == K.KVQ_ERR_INVALID_ARG
 
 
+def test_snapkv_options_validation_without_gpu():
+    lib = K.lib()
+
+    def opts(q=None, hq=0, pool=1):
+        return ctypes.byref(K.c_snapkv_opts(q, hq, pool))
+
+    def wsb(o, B=1, H=8, S=8192, D=128, w=32):
+        return lib.kvq_snapkv_workspace_bytes_ex(o, B, H, S, D, w)
+
+    base = K.kvq_snapkv_workspace_bytes(1, 8, 8192, 128, 32)
+    assert wsb(None) == base == wsb(opts())
+    # pooling adds one score buffer; query windows of G*w rows grow the statistics
+    assert wsb(opts(pool=7)) == base + 8 * 8192 * 4
+    assert wsb(opts(q=FAKE, hq=32)) > base
+    assert wsb(opts(pool=4)) == 0 and wsb(opts(q=FAKE, hq=12)) == 0
+    assert wsb(opts(q=FAKE, hq=64)) == 0                            # 8 * 32 rows > 128
+    big = wsb(opts(q=FAKE, hq=32, pool=5))
+
+    def call(o, S=8192, w=32, ws_bytes=big, k=FAKE):
+        return lib.kvq_snapkv_select_ex(o, k, FAKE, 1, 8, S, 128, w, 4, 512, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, ws_bytes, None)
+    assert call(opts(pool=0)) == K.KVQ_ERR_INVALID_ARG
+    assert call(opts(pool=6)) == K.KVQ_ERR_INVALID_ARG
+    assert call(opts(pool=33)) == K.KVQ_ERR_UNSUPPORTED
+    assert call(opts(q=FAKE, hq=12)) == K.KVQ_ERR_INVALID_ARG      # not a multiple of Hkv
+    assert call(opts(q=FAKE, hq=4)) == K.KVQ_ERR_INVALID_ARG       # fewer query than kv heads
+    assert call(opts(q=FAKE, hq=64)) == K.KVQ_ERR_UNSUPPORTED      # 256 rows per kv-head
+    assert call(opts(q=FAKE, hq=32), S=16) == K.KVQ_ERR_INVALID_ARG  # window longer than prompt
+    assert call(opts(q=MIS, hq=32)) == K.KVQ_ERR_ALIGNMENT
+    assert call(opts(q=FAKE, hq=32, pool=5), ws_bytes=big - 1) == K.KVQ_ERR_WORKSPACE
+    assert call(opts(pool=5), ws_bytes=base) == K.KVQ_ERR_WORKSPACE   # pooled buffer missing
+    assert call(opts(q=FAKE, hq=32, pool=5), k=MIS) == K.KVQ_ERR_ALIGNMENT
+    pool = lib.kvq_snapkv_pool_scores
+    assert pool(FAKE, FAKE + 16 * 4, 1, 1, 100, 3, None) == K.KVQ_ERR_INVALID_ARG   # overlap
+    assert pool(FAKE, 0x100000, 1, 1, 100, 2, None) == K.KVQ_ERR_INVALID_ARG
+    assert pool(FAKE, 0x100000, 1, 1, 100, 35, None) == K.KVQ_ERR_UNSUPPORTED
+    assert pool(None, 0x100000, 1, 1, 100, 3, None) == K.KVQ_ERR_INVALID_ARG
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(K, "_lib", None)
