@@ -50,31 +50,34 @@ enum RowFmt { kFmtNone = 0, kFmtPlain = 1, kFmtAff4 = 2, kFmtAff8 = 3, kFmtSym4 
 constexpr int kEpl = 16;        // elements (channels) per lane in the row kernel
 constexpr int kRowIter = 2;     // row passes per block
 
-// 16 consecutive elements of a row as fp32 (exact widening).
+// The 16 consecutive input elements of one lane in one row, as loaded
+// (widened only when used, so that every row's loads are in flight first).
 template <int DT>
-__device__ __forceinline__ void load16_as_f32(const void* p, int64_t i, float v[kEpl]) {
-    if constexpr (DT == KVQ_F32) {
-        const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+struct Raw16 { uint4 w[DT == KVQ_F32 ? 4 : 2]; };
+
+template <int DT>
+__device__ __forceinline__ void load_raw16(const char* p, Raw16<DT>& r) {
+    const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int k = 0; k < (DT == KVQ_F32 ? 4 : 2); ++k) r.w[k] = q[k];
+}
+
+// Exact widening to fp32.
+template <int DT>
+__device__ __forceinline__ void widen16(const Raw16<DT>& r, float v[kEpl]) {
+#pragma unroll
+    for (int h = 0; h < (DT == KVQ_F32 ? 4 : 2); ++h) {
+        const uint32_t w[4] = {r.w[h].x, r.w[h].y, r.w[h].z, r.w[h].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float4 a = q[k];
-            v[4 * k] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
-        }
-    } else {
-        const uint4* q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint4 x = q[h];
-            const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                if constexpr (DT == KVQ_F16) {
-                    v[8 * h + 2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu);
-                    v[8 * h + 2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
-                } else {
-                    v[8 * h + 2 * k] = bf16_bits_to_f32(w[k] & 0xFFFFu);
-                    v[8 * h + 2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
-                }
+            if constexpr (DT == KVQ_F32) {
+                v[4 * h + k] = __uint_as_float(w[k]);
+            } else if constexpr (DT == KVQ_F16) {
+                v[8 * h + 2 * k] = f16_bits_to_f32(w[k] & 0xFFFFu);
+                v[8 * h + 2 * k + 1] = f16_bits_to_f32(w[k] >> 16);
+            } else {
+                v[8 * h + 2 * k] = bf16_bits_to_f32(w[k] & 0xFFFFu);
+                v[8 * h + 2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
             }
         }
     }
@@ -178,23 +181,32 @@ __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t
         const float zf = f16_bits_to_f32(z16);
         const float rs = __builtin_amdgcn_rcpf(sf);
         float dev = 0.0f;                             // max |q - rint(q)|
+        // 4-bit codes: q = fma(x, rs, -zf rs) saves the subtract.  The exact
+        // product inside the fma leaves the reciprocal's error (2^-23 |q|,
+        // |q| <= 16) and the rounding of -zf rs (2^-24 |zf / sf|), together
+        // below 2^-14.5 while |zf| <= 512 sf, so the near-tie band still
+        // covers the difference to the IEEE quotient.  A lane whose zero
+        // point lies further out sends all its elements to the exact path.
+        const float c = -zf * rs;
+        const bool far = BITS == 4 && !(fabsf(zf) <= 512.0f * sf);
 #pragma unroll
         for (int k = 0; k < kEpl; ++k) {
-            const float q = (x[k] - zf) * rs;
+            const float q = BITS == 4 ? fmaf(x[k], rs, c) : (x[k] - zf) * rs;
             y[k] = rintf(q);
             dev = fmaxf(dev, fabsf(q - y[k]));
         }
+        if (far) dev = 1.0f;
         near = dev > kBand;
         if (__builtin_amdgcn_ballot_w64(near) != 0) {
 #pragma unroll
             for (int k = 0; k < kEpl; ++k) {
                 const float diff = x[k] - zf;
-                const float q = diff * rs;
-                if (fabsf(q - rintf(q)) > kBand) y[k] = rintf(diff / sf);
+                const float q = BITS == 4 ? fmaf(x[k], rs, c) : diff * rs;
+                if (far || fabsf(q - rintf(q)) > kBand) y[k] = rintf(diff / sf);
             }
         }
 #pragma unroll
-        for (int k = 0; k < kEpl; ++k) y[k] = fminf(fmaxf(y[k], 0.0f), top);   // NaN -> 0
+        for (int k = 0; k < kEpl; ++k) y[k] = __builtin_amdgcn_fmed3f(y[k], 0.0f, top);
         if ((lane & (lpg - 1)) == 0)
             static_cast<uint32_t*>(r.meta)[(drow << (__builtin_ctz(D) - gsh)) + (lane >> lsh)] =
                 (uint32_t)s16 | ((uint32_t)z16 << 16);
@@ -255,49 +267,56 @@ __device__ __forceinline__ void copy_row16(const RowPart& r, int64_t row, int64_
 }
 
 // Fused append of K rows (unless KIVI per-channel, FK == kFmtNone), V rows
-// and positions.  Block (x = bh * n_chunks + chunk, z) covers rows
+// and positions.  Block (x = chunk, y = slice bh - bh0, z) covers rows
 // [chunk * rows_per_chunk, +rows_per_chunk) of sequence slice bh, of K
 // (z = 0) or V (z = 1, or z = 0 when K takes the channel path); a row is
-// D / 16 lanes of 16 channels, and each thread takes kRowIter rows, loaded
-// before any is quantized.  Blocks of bh = 0 also write the positions of
-// their rows.
+// D / 16 = 2^lpr_sh lanes of 16 channels, and each thread takes kRowIter
+// rows, all loaded before any is widened or quantized.  Blocks of bh = 0
+// also write the positions of their rows.
 template <int DT, int FK, int FV>
-__global__ __launch_bounds__(256) void row_append_kernel(RowQuantArgs a, RowPart kp, RowPart vp,
-                                                         int n_chunks, int32_t* pos, int first_pos) {
-    const int lpr = a.D / kEpl;                       // lanes per row (2, 4 or 8)
-    const int rpp = 256 / lpr;                        // rows per pass
-    const int rpc = rpp * kRowIter;                   // rows per chunk
-    const int bh = blockIdx.x / n_chunks;             // uniform: scalar division
-    const int chunk = blockIdx.x - bh * n_chunks;
+__global__ __launch_bounds__(256) void row_append_kernel(RowQuantArgs a, RowPart kp, RowPart vp, int bh0,
+                                                         int lpr_sh, int32_t* pos, int first_pos) {
+    constexpr int ES = DT == KVQ_F32 ? 4 : 2;          // input bytes per element
+    const int rpp_sh = 8 - lpr_sh;                    // log2 rows per pass
+    const int rpc = kRowIter << rpp_sh;               // rows per chunk
+    const int chunk = blockIdx.x;
+    const int bh = bh0 + blockIdx.y;
     const bool is_v = FK == kFmtNone || blockIdx.z == 1;
-    const int lane = threadIdx.x % lpr;
-    const int i_base = chunk * rpc + threadIdx.x / lpr;
+    const int lane = threadIdx.x & ((1 << lpr_sh) - 1);
+    const int i_base = chunk * rpc + (threadIdx.x >> lpr_sh);
     if (pos && bh == 0 && !(FK != kFmtNone && is_v)) {
         const int i_end = min(a.n, (chunk + 1) * rpc);
         for (int i = chunk * rpc + threadIdx.x; i < i_end; i += 256) pos[a.slot0 + i] = first_pos + i;
     }
-    const int h = bh % a.H;
+    const int64_t drow0 = (int64_t)bh * a.cap + a.slot0;
     auto run = [&](const RowPart& part, auto fmt_tag) {
         constexpr int FMT = decltype(fmt_tag)::value;
         if constexpr (FMT == kFmtPlain) {
+            const int h = bh % a.H;
 #pragma unroll
             for (int it = 0; it < kRowIter; ++it) {
-                const int i = i_base + it * rpp;
-                if (i < a.n)
-                    copy_row16<DT>(part, (int64_t)bh * a.n + i, (int64_t)bh * a.cap + a.slot0 + i, h, lane, a.D);
+                const int i = i_base + (it << rpp_sh);
+                if (i < a.n) copy_row16<DT>(part, (int64_t)bh * a.n + i, drow0 + i, h, lane, a.D);
             }
         } else {
-            float x[kRowIter][kEpl];
+            const char* src = static_cast<const char*>(part.src) + ((int64_t)bh * a.n * a.D + lane * kEpl) * ES;
+            const uint32_t row_bytes = (uint32_t)a.D * ES;
+            Raw16<DT> raw[kRowIter];
 #pragma unroll
             for (int it = 0; it < kRowIter; ++it) {
-                const int i = i_base + it * rpp;
-                if (i < a.n) load16_as_f32<DT>(part.src, ((int64_t)bh * a.n + i) * a.D + lane * kEpl, x[it]);
+                // rows past the end load the last row (always valid) and are not stored
+                const int i = min(i_base + (it << rpp_sh), a.n - 1);
+                load_raw16<DT>(src + (uint64_t)(uint32_t)i * row_bytes, raw[it]);
             }
+            const int h = FMT == kFmtSym4 && part.bias ? bh % a.H : 0;
 #pragma unroll
             for (int it = 0; it < kRowIter; ++it) {
-                const int i = i_base + it * rpp;
-                if (i < a.n)         // whole rows (hence groups) skip together
-                    quant16<DT, FMT>(part, x[it], (int64_t)bh * a.cap + a.slot0 + i, h, lane, a.D);
+                const int i = i_base + (it << rpp_sh);
+                if (i < a.n) {       // whole rows (hence groups) skip together
+                    float x[kEpl];
+                    widen16<DT>(raw[it], x);
+                    quant16<DT, FMT>(part, x, drow0 + i, h, lane, a.D);
+                }
             }
         }
     };
@@ -390,16 +409,22 @@ int row_fmt(int kind, int bits) {
 
 template <int DT, int FK, int FV>
 hipError_t launch_append_fv(const RowAppendArgs& a, hipStream_t s) {
-    const int rpc = (256 / (a.rows.D / kEpl)) * kRowIter;
+    const int lpr_sh = __builtin_ctz(a.rows.D / kEpl);     // D in {32, 64, 128}
+    const int rpc = (256 >> lpr_sh) * kRowIter;
     const int n_chunks = (a.rows.n + rpc - 1) / rpc;
-    const int64_t nx = (int64_t)a.rows.B * a.rows.H * n_chunks;
-    if (nx > 0x7FFFFFFF) return hipErrorInvalidValue;
-    dim3 grid((unsigned)nx, 1, FK == kFmtNone ? 1 : 2);
-    hipLaunchKernelGGL((row_append_kernel<DT, FK, FV>), grid, dim3(256), 0, s, a.rows,
-                       RowPart{a.k_src, a.k_codes, a.k_meta, a.k_bias, a.k_group},
-                       RowPart{a.v_src, a.v_codes, a.v_meta, nullptr, a.v_group}, n_chunks, a.pos,
-                       a.first_pos);
-    return hipGetLastError();
+    const int bh_total = a.rows.B * a.rows.H;
+    // slices go on grid y (at most 65535 per launch)
+    for (int bh0 = 0; bh0 < bh_total; bh0 += 65535) {
+        const int nbh = bh_total - bh0 < 65535 ? bh_total - bh0 : 65535;
+        dim3 grid((unsigned)n_chunks, (unsigned)nbh, FK == kFmtNone ? 1 : 2);
+        hipLaunchKernelGGL((row_append_kernel<DT, FK, FV>), grid, dim3(256), 0, s, a.rows,
+                           RowPart{a.k_src, a.k_codes, a.k_meta, a.k_bias, a.k_group},
+                           RowPart{a.v_src, a.v_codes, a.v_meta, nullptr, a.v_group}, bh0, lpr_sh, a.pos,
+                           a.first_pos);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 template <int DT, int FK>
