@@ -363,3 +363,45 @@ def test_quantize_codes_on_rounding_boundaries():
         say("rounding boundaries", k_kind, k_bits)
         c, o = build_pair(pl, ol, x, v, "f32")
         assert_same_state(c, o)
+
+
+@pytest.mark.parametrize("offset", [48.0, 1024.0])
+def test_quantize_codes_with_offset_zero_points(offset):
+    """4-bit codes of groups whose zero point sits `offset` away from 0: 48
+    (|z| / s = 384, the fused-quotient path) and 1024 (|z| / s = 8192, where
+    every element goes to the exact quotient).  Quotients on, and one ulp
+    either side of, half-integers stay bit-exact."""
+    rng = np.random.default_rng(int(offset))
+    B, H, T, D = 1, 2, 64, 128
+    k = rng.integers(0, 15, size=(B, H, T, D)).astype(np.float32)
+    x = (np.float32(offset) + (k + 0.5) / 8).astype(np.float32)
+    nudge = rng.integers(-1, 2, size=x.shape)
+    x = np.where(nudge < 0, np.nextafter(x, -np.inf), np.where(nudge > 0, np.nextafter(x, np.inf), x))
+    x = x.astype(np.float32)
+    x[..., 0::64] = offset                  # group min: zero = offset exactly
+    x[..., 1::64] = offset + 15 / 8         # group max: scale = 1/8
+    # odd tokens: the offset only on some groups, so fused and exact lanes share waves
+    x[:, :, 1::2, 64:] -= np.float32(offset)
+    v = x.copy()
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=D, capacity=T, k_kind="tok_affine", k_bits=4,
+                     k_group=64, v_kind="tok_affine", v_bits=4, v_group=32, in_dtype="f32")
+    say("offset zero points", offset)
+    c, o = build_pair(pl, ol, x, v, "f32")
+    assert_same_state(c, o)
+
+
+def test_quantize_codes_random_offsets_bf16():
+    """Random per-group offsets up to +-2000 and spreads from 1e-3 to 1 (bf16
+    inputs): lanes of one wave take both quotient forms; codes bit-exact."""
+    rng = np.random.default_rng(7)
+    B, H, T, D = 2, 2, 96, 128
+    off = rng.uniform(-2000, 2000, size=(B, H, T, D // 64, 1))
+    spread = 10.0 ** rng.uniform(-3, 0, size=(B, H, T, D // 64, 1))
+    x = (off + spread * rng.standard_normal((B, H, T, D // 64, 64))).reshape(B, H, T, D).astype(np.float32)
+    x[:, :, ::3] = rng.standard_normal((B, H, (T + 2) // 3, D)).astype(np.float32)
+    xb = synth.cast(x, "bf16")
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=D, capacity=T, k_kind="tok_affine", k_bits=4,
+                     k_group=64, v_kind="tok_affine", v_bits=4, v_group=64, in_dtype="bf16")
+    say("random offsets bf16")
+    c, o = build_pair(pl, ol, xb, xb, "bf16")
+    assert_same_state(c, o)
