@@ -19,6 +19,13 @@ semantics the HIP library must reproduce:
   packed keys, softmax, weighted sum of the packed values) in fp64.
 * SnapKV ([P2] "How it works"): observation-window scores, sink guarantee,
   top-k by score with lower position first on ties, ascending union, gather.
+  Chunked prefill ([P2] "How it works" and "RoPE position semantics": every
+  prefill call selects again, so the budget stays capped across chunks; kept
+  rows keep their absolute positions) re-runs the selection over the kept
+  rows followed by the new chunk.  Decode appends never pass through it.
+* Kept rows stacked into a quantized cache ([P2]: the kept tokens can carry
+  any quantizer) are appended at their own positions, which differ between
+  kv-heads, so such a cache keeps one position row per (batch, kv-head).
 """
 from __future__ import annotations
 
@@ -28,9 +35,9 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import (CHANNEL, PLAIN, SYM4, TOK_AFFINE, decode_head, make_view,
+from . import (CHANNEL, PLAIN, SYM4, TOK_AFFINE, decode_head, make_view, maxpool1d,
                quant_channel_group, quant_sym4, quant_tok_affine, snapkv_scores,
-               snapkv_select, widen)
+               snapkv_scores_rows, snapkv_select, widen)
 
 _NP_STORE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}
 
@@ -52,6 +59,7 @@ class Layout:
     v_bits: int = 4
     v_group: int = 64
     in_dtype: str = "f16"
+    pos_per_head: bool = False    # positions [B][H][capacity] instead of [capacity]
 
     @property
     def table_rows(self) -> int:
@@ -66,7 +74,7 @@ class OracleCache:
         B, H, D, C = L.batch, L.n_kv_heads, L.head_dim, L.capacity
         st = _NP_STORE[L.in_dtype]
         self.k_bias = None if k_bias is None else np.asarray(k_bias, dtype=np.float32)
-        self.pos = np.zeros(C, dtype=np.int32)
+        self.pos = np.zeros((B, H, C) if L.pos_per_head else C, dtype=np.int32)
         self.k_row = np.zeros(C, dtype=np.int32)
         self.k_plain = self.k_u = self.k_meta = self.k_table = self.k_resid = None
         if L.k_kind == "plain":
@@ -91,15 +99,24 @@ class OracleCache:
         self.next_pos = 0
 
     # ------------------------------------------------------------------ append
-    def append(self, k_new: np.ndarray, v_new: np.ndarray) -> None:
-        """k_new, v_new: [B][H][n][D] in the layout's input dtype."""
+    def append(self, k_new: np.ndarray, v_new: np.ndarray, positions: np.ndarray | None = None,
+               next_pos: int | None = None) -> None:
+        """k_new, v_new: [B][H][n][D] in the layout's input dtype.
+
+        The new slots take positions next_pos, next_pos + 1, ...; or, when
+        ``positions`` is given ([B][H][n] for a per-head layout, else [n]),
+        those positions, after which the generation counter becomes
+        ``next_pos``."""
         L = self.L
         n = k_new.shape[2]
         if self.n_stored + n > L.capacity:
             raise OracleError("capacity")
         s0 = self.n_stored
         sl = slice(s0, s0 + n)
-        self.pos[sl] = self.next_pos + np.arange(n, dtype=np.int32)
+        if positions is None:
+            self.pos[..., sl] = self.next_pos + np.arange(n, dtype=np.int32)
+        else:
+            self.pos[..., sl] = np.asarray(positions, dtype=np.int32)
         # V: per token, at write time ([P1]: "Computed once per new token").
         if L.v_kind == "plain":
             self.v_plain[:, :, sl] = v_new
@@ -129,7 +146,7 @@ class OracleCache:
                 if r + 1 == Gt:
                     self._close_group()
         self.n_stored += n
-        self.next_pos += n
+        self.next_pos = self.next_pos + n if positions is None else int(next_pos)
         if L.k_kind != "kivi_ch":
             self.n_quant = self.n_stored
 
@@ -162,7 +179,7 @@ class OracleCache:
         keep = np.concatenate([np.arange(0, sink), np.arange(n - window, n)]).astype(np.int64)
         new = OracleCache(L, self.k_bias)
         m = keep.size
-        new.pos[:m] = self.pos[keep]
+        new.pos[..., :m] = self.pos[..., keep]
         for name in ("k_plain", "k_u", "k_meta", "v_plain", "v_u", "v_meta"):
             a = getattr(self, name)
             if a is not None and not (name == "k_meta" and L.k_kind == "kivi_ch"):
@@ -252,3 +269,69 @@ def snapkv(K: np.ndarray, V: np.ndarray, obs_window: int, n_sink: int, budget: i
     bi = np.arange(B)[:, None, None]
     hi = np.arange(H)[None, :, None]
     return scores, kept, K[bi, hi, kept], V[bi, hi, kept]
+
+
+@dataclass
+class SnapState:
+    """Rows kept by SnapKV so far: k, v [B][H][n][D] fp16 in ascending
+    position order, their absolute positions pos [B][H][n], and the position
+    of the next prefill token."""
+    k: np.ndarray
+    v: np.ndarray
+    pos: np.ndarray
+    next_pos: int
+
+    @staticmethod
+    def empty(B: int, H: int, D: int) -> "SnapState":
+        z = np.zeros((B, H, 0, D), dtype=np.float16)
+        return SnapState(z, z.copy(), np.zeros((B, H, 0), dtype=np.int32), 0)
+
+
+def snapkv_chunk(state: SnapState, k_chunk: np.ndarray, v_chunk: np.ndarray, obs_window: int,
+                 n_sink: int, budget: int, q_window: np.ndarray | None = None, pool_kernel: int = 1,
+                 threads: int = 8):
+    """One prefill call of SnapKV over the kept rows followed by a new chunk.
+
+    The candidates are state.k (positions state.pos) then k_chunk (positions
+    state.next_pos, +1, ...).  Observation rows: the last min(w, n) candidate
+    key rows, or with q_window [B][Hq][w][D] the w query rows of every query
+    head of the kv-head's group.  Scores per [P2] "How it works" step 1 (fp64),
+    rounded to fp32, max-pooled when pool_kernel > 1, then the sinks plus the
+    top (budget - sinks) as in steps 2-3; the kept rows and positions are
+    gathered in candidate order (ascending position).
+
+    Returns (new SnapState, scores fp64 [B][H][n], kept candidate indices
+    int32 [B][H][min(budget, n)]).
+    """
+    B, H, _, D = state.k.shape
+    S_c = k_chunk.shape[2]
+    K = np.concatenate([state.k, np.asarray(k_chunk, dtype=np.float16)], axis=2)
+    V = np.concatenate([state.v, np.asarray(v_chunk, dtype=np.float16)], axis=2)
+    new_pos = np.broadcast_to(state.next_pos + np.arange(S_c, dtype=np.int32), (B, H, S_c))
+    P = np.concatenate([state.pos, new_pos], axis=2)
+    n = K.shape[2]
+    n_keep = min(budget, n)
+    scores = np.zeros((B, H, n), dtype=np.float64)
+    kept = np.zeros((B, H, n_keep), dtype=np.int32)
+    Kf = K.astype(np.float32)
+
+    def one(bh):
+        b, h = divmod(bh, H)
+        if q_window is None:
+            rows = Kf[b, h, n - min(obs_window, n):]
+        else:
+            G = q_window.shape[1] // H
+            rows = q_window[b, h * G:(h + 1) * G].reshape(G * q_window.shape[2], D).astype(np.float32)
+        scores[b, h] = snapkv_scores_rows(rows, Kf[b, h])
+        rank = scores[b, h].astype(np.float32)
+        if pool_kernel > 1:
+            rank = maxpool1d(rank, pool_kernel)
+        kept[b, h] = snapkv_select(rank, n_sink, budget)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(one, range(B * H)))
+    bi = np.arange(B)[:, None, None]
+    hi = np.arange(H)[None, :, None]
+    new = SnapState(K[bi, hi, kept], V[bi, hi, kept], P[bi, hi, kept].astype(np.int32),
+                    state.next_pos + S_c)
+    return new, scores, kept

@@ -482,3 +482,103 @@ def test_bits_per_element_accounting():
         G, bits = case["group"], case["bits"]
         per_group_bits = G * bits + 2 * 16
         assert per_group_bits / G == case["bits_per_element"]
+
+
+def test_snapkv_chunked_single_chunk_is_one_shot():
+    """[P2] "How it works": one prefill call over an empty state is the
+    one-shot selection; kept rows keep their absolute positions."""
+    from oracle.cache import SnapState, snapkv, snapkv_chunk
+    rng = np.random.default_rng(21)
+    K = rng.standard_normal((1, 2, 300, 32)).astype(np.float16)
+    V = rng.standard_normal((1, 2, 300, 32)).astype(np.float16)
+    st, sc, kept = snapkv_chunk(SnapState.empty(1, 2, 32), K, V, 16, 4, 40)
+    ref_sc, ref_kept, ref_k, ref_v = snapkv(K, V, 16, 4, 40)
+    assert np.array_equal(sc, ref_sc) and np.array_equal(kept, ref_kept)
+    assert np.array_equal(st.k, ref_k) and np.array_equal(st.v, ref_v)
+    assert np.array_equal(st.pos, ref_kept) and st.next_pos == 300
+
+
+def test_snapkv_chunked_closed_form():
+    """Two prefill chunks whose scores are known in closed form.  Keys are
+    c e_0 ("hot") at positions divisible by 4 and at the chunk's last two
+    positions, e_1 otherwise; the last two rows (hot) are the observation
+    rows.  Hot keys score higher; equal scores go to the lower position.
+    The second chunk's hot keys are 2 c e_0, so they outscore the first
+    chunk's survivors and displace them (budget re-enforced, sinks kept)."""
+    from oracle.cache import SnapState, snapkv_chunk
+    D, c, w, sink, budget = 8, 3.0, 2, 2, 6
+
+    def chunk(p0, mag):
+        k = np.zeros((1, 1, 16, D), np.float16)
+        for i in range(16):
+            hot = (p0 + i) % 4 == 0 or i >= 14
+            k[0, 0, i, 0 if hot else 1] = mag if hot else 1.0
+        return k
+
+    k1 = chunk(0, c)
+    st, sc1, _ = snapkv_chunk(SnapState.empty(1, 1, D), k1, k1, w, sink, budget)
+    assert st.pos[0, 0].tolist() == [0, 1, 4, 8, 12, 14]
+    # scores: both observation rows see hot logit c^2/sqrt(D) at 6 keys, 0 at 10
+    e = math.exp(c * c / math.sqrt(D))
+    hot = e / (6 * e + 10)
+    assert abs(sc1[0, 0, 4] - hot) < 1e-15 and abs(sc1[0, 0, 3] - 1 / (6 * e + 10)) < 1e-15
+    k2 = chunk(16, 2 * c)
+    st2, sc2, _ = snapkv_chunk(st, k2, k2, w, sink, budget)
+    assert st2.pos[0, 0].tolist() == [0, 1, 16, 20, 24, 28] and st2.next_pos == 32
+    assert np.array_equal(st2.k[0, 0, 2:], k2[0, 0, [0, 4, 8, 12]])
+    # candidates: 6 survivors (hot at 0, 4, 8, 12, 14 with c; cold 1), 16 new (hot: 6 with 2c)
+    e1, e2 = math.exp(2 * c * c / math.sqrt(D)), math.exp(4 * c * c / math.sqrt(D))
+    Z = 5 * e1 + 6 * e2 + 11
+    assert abs(sc2[0, 0, 6] - e2 / Z) < 1e-14 and abs(sc2[0, 0, 2] - e1 / Z) < 1e-14
+
+
+def test_snapkv_chunked_invariants():
+    """Across uneven chunks: the budget stays capped (n_kept = min(budget,
+    tokens so far)), positions are ascending, absolute and include the sinks,
+    every kept row is the source row of its position, and while the prompt
+    fits the budget nothing is dropped."""
+    from oracle.cache import SnapState, snapkv_chunk
+    rng = np.random.default_rng(22)
+    B, H, D, w, sink, budget = 2, 2, 32, 8, 4, 64
+    sizes = [50, 1, 7, 130, 64, 3]
+    total = sum(sizes)
+    K = rng.standard_normal((B, H, total, D)).astype(np.float16)
+    V = rng.standard_normal((B, H, total, D)).astype(np.float16)
+    st = SnapState.empty(B, H, D)
+    t = 0
+    for S_c in sizes:
+        st, _, _ = snapkv_chunk(st, K[:, :, t:t + S_c], V[:, :, t:t + S_c], w, sink, budget)
+        t += S_c
+        assert st.next_pos == t and st.k.shape[2] == min(budget, t)
+        for b in range(B):
+            for h in range(H):
+                p = st.pos[b, h]
+                assert np.all(np.diff(p) > 0) and p[0] >= 0 and p[-1] < t
+                assert np.array_equal(p[:sink], np.arange(sink))
+                assert np.array_equal(st.k[b, h], K[b, h, p]) and np.array_equal(st.v[b, h], V[b, h, p])
+        if t <= budget:
+            assert np.array_equal(st.pos, np.broadcast_to(np.arange(t), (B, H, t)))
+
+
+def test_cache_positions_per_head_and_decode_appends():
+    """Kept rows appended at their own per-head positions; later decode
+    appends continue from the prompt length and are never evicted by
+    SnapKV (they bypass it); positions do not change attention."""
+    from oracle.cache import Layout, OracleCache
+    rng = np.random.default_rng(23)
+    B, H, D = 1, 2, 32
+    L = Layout(B, H, D, 16, k_kind="tok_affine", k_group=32, v_group=32, in_dtype="f16", pos_per_head=True)
+    Lp = Layout(B, H, D, 16, k_kind="tok_affine", k_group=32, v_group=32, in_dtype="f16")
+    k = rng.standard_normal((B, H, 5, D)).astype(np.float16)
+    v = rng.standard_normal((B, H, 5, D)).astype(np.float16)
+    pos = np.array([[[0, 1, 7, 9, 30], [0, 1, 2, 20, 31]]], np.int32)
+    c = OracleCache(L)
+    c.append(k, v, positions=pos, next_pos=40)
+    c.append(k[:, :, :1], v[:, :, :1])
+    assert c.next_pos == 41 and c.n_stored == 6
+    assert c.pos[0, 0].tolist()[:6] == [0, 1, 7, 9, 30, 40] and c.pos[0, 1].tolist()[:6] == [0, 1, 2, 20, 31, 40]
+    p = OracleCache(Lp)
+    p.append(k, v)
+    p.append(k[:, :, :1], v[:, :, :1])
+    q = rng.standard_normal((B, 2 * H, D)).astype(np.float16)
+    assert np.array_equal(c.decode(q, "f16"), p.decode(q, "f16"))
