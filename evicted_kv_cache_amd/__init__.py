@@ -10,7 +10,8 @@ The functions carry the C ABI names (see include/kvq.h):
 ``kvq_evict_streaming``, ``kvq_snapkv_select``, ``kvq_snapkv_select_ex``,
 ``kvq_snapkv_select_from_scores``, ``kvq_snapkv_pool_scores``,
 ``kvq_decode_workspace_bytes``, ``kvq_snapkv_workspace_bytes``,
-``kvq_snapkv_workspace_bytes_ex``.
+``kvq_snapkv_workspace_bytes_ex``, ``kvq_quantize_append_at``,
+``kvq_snapkv_chunk_workspace_bytes``, ``kvq_snapkv_prefill_chunk``.
 """
 from __future__ import annotations
 
@@ -27,7 +28,7 @@ KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY = -1, -2, -3
 KVQ_ERR_ALIGNMENT, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = -4, -5, -6
 KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2
 KVQ_PLAIN, KVQ_KIVI_CH, KVQ_TOK_AFFINE, KVQ_TOK_SYM4 = 0, 1, 2, 3
-KVQ_CENTER_K, KVQ_TEST_CENTER_ANY = 0x1, 0x2
+KVQ_CENTER_K, KVQ_TEST_CENTER_ANY, KVQ_POS_PER_HEAD = 0x1, 0x2, 0x4
 
 KINDS = {"plain": KVQ_PLAIN, "kivi_ch": KVQ_KIVI_CH, "tok_affine": KVQ_TOK_AFFINE,
          "tok_sym4": KVQ_TOK_SYM4}
@@ -37,7 +38,9 @@ EXPORTS = ("kvq_cache_sizes", "kvq_cache_reset", "kvq_quantize_append",
            "kvq_decode_workspace_bytes", "kvq_decode_attention", "kvq_evict_streaming",
            "kvq_snapkv_workspace_bytes", "kvq_snapkv_select",
            "kvq_snapkv_select_from_scores", "kvq_snapkv_workspace_bytes_ex",
-           "kvq_snapkv_select_ex", "kvq_snapkv_pool_scores", "kvq_status_string", "kvq_version")
+           "kvq_snapkv_select_ex", "kvq_snapkv_pool_scores", "kvq_quantize_append_at",
+           "kvq_snapkv_chunk_workspace_bytes", "kvq_snapkv_prefill_chunk", "kvq_status_string",
+           "kvq_version")
 
 
 class KvqError(RuntimeError):
@@ -64,6 +67,11 @@ class c_cache(ctypes.Structure):
 class c_snapkv_opts(ctypes.Structure):
     _fields_ = [("q_window", ctypes.c_void_p), ("n_q_heads", ctypes.c_int32),
                 ("pool_kernel", ctypes.c_int32)]
+
+
+class c_snapkv_state(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("pos", ctypes.c_void_p),
+                ("capacity", ctypes.c_int32), ("n_kept", ctypes.c_int32), ("next_pos", ctypes.c_int32)]
 
 
 class c_sizes(ctypes.Structure):
@@ -99,6 +107,10 @@ def lib():
         L.kvq_snapkv_workspace_bytes_ex.argtypes = [P, i32, i32, i32, i32, i32]
         L.kvq_snapkv_select_ex.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         L.kvq_snapkv_pool_scores.argtypes = [P, P, i32, i32, i32, i32, P]
+        L.kvq_quantize_append_at.argtypes = [P, P, P, P, i32, i32, P, i32, i32, P]
+        L.kvq_snapkv_chunk_workspace_bytes.restype = sz
+        L.kvq_snapkv_chunk_workspace_bytes.argtypes = [P, i32, i32, i32, i32, i32]
+        L.kvq_snapkv_prefill_chunk.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, sz, P]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_version.restype = i32
@@ -213,6 +225,21 @@ def kvq_quantize_append(layout: Layout, cache: Cache, k_new, v_new, stream=None)
     _check(lib().kvq_quantize_append(ctypes.byref(cl), ctypes.byref(cache.c), k_new.data_ptr(),
                                      v_new.data_ptr(), int(k_new.shape[2]), _stream(stream)),
            "kvq_quantize_append")
+
+
+def kvq_quantize_append_at(layout: Layout, cache: Cache, k_new, v_new, positions, next_pos: int,
+                           n_new: int | None = None, stream=None) -> None:
+    """Append rows [0, n_new) of each slice of k_new, v_new [B][Hkv][rows][D]
+    (contiguous; rows >= n_new) at the given positions ([B][Hkv][rows'] int32
+    with KVQ_POS_PER_HEAD, else [n_new]); the cache's counter becomes next_pos."""
+    assert k_new.is_contiguous() and v_new.is_contiguous() and positions.is_contiguous()
+    n = int(k_new.shape[2]) if n_new is None else int(n_new)
+    pos_rows = int(positions.shape[-1]) if positions.dim() == 3 else 0
+    cl = layout.c()
+    _check(lib().kvq_quantize_append_at(ctypes.byref(cl), ctypes.byref(cache.c), k_new.data_ptr(),
+                                        v_new.data_ptr(), n, int(k_new.shape[2]), positions.data_ptr(),
+                                        pos_rows, int(next_pos), _stream(stream)),
+           "kvq_quantize_append_at")
 
 
 def kvq_decode_workspace_bytes(layout: Layout, n_q_heads: int) -> int:
@@ -357,3 +384,51 @@ def kvq_snapkv_select_from_scores(scores, n_sink: int, budget: int, kept=None, s
                                                kept.data_ptr(), _stream(stream)),
            "kvq_snapkv_select_from_scores")
     return kept
+
+
+class SnapState:
+    """Rows kept by chunked SnapKV prefill: device k, v [B][Hkv][capacity][D]
+    fp16 and pos [B][Hkv][capacity] int32, plus the C struct's host counters."""
+
+    def __init__(self, batch: int, n_kv_heads: int, head_dim: int, capacity: int, device="cuda"):
+        torch = _torch()
+        self.k = torch.zeros((batch, n_kv_heads, capacity, head_dim), dtype=torch.float16, device=device)
+        self.v = torch.zeros_like(self.k)
+        self.pos = torch.zeros((batch, n_kv_heads, capacity), dtype=torch.int32, device=device)
+        self.c = c_snapkv_state(self.k.data_ptr(), self.v.data_ptr(), self.pos.data_ptr(), capacity, 0, 0)
+
+    @property
+    def n_kept(self) -> int:
+        return self.c.n_kept
+
+    @property
+    def next_pos(self) -> int:
+        return self.c.next_pos
+
+
+def kvq_snapkv_chunk_workspace_bytes(batch, n_kv_heads, head_dim, capacity, obs_window,
+                                     q_window=None, pool_kernel: int = 1) -> int:
+    o = _snap_opts(q_window, pool_kernel)
+    return int(lib().kvq_snapkv_chunk_workspace_bytes(ctypes.byref(o), batch, n_kv_heads, head_dim,
+                                                      capacity, obs_window))
+
+
+def kvq_snapkv_prefill_chunk(state_in: SnapState, state_out: SnapState, k_chunk, v_chunk,
+                             obs_window: int, n_sink: int, budget: int, q_window=None,
+                             pool_kernel: int = 1, scores=None, ws=None, stream=None):
+    """One chunk of SnapKV prefill: k_chunk, v_chunk [B][Hkv][n][D] fp16 are
+    appended to state_in's kept rows, the selection runs over all of them and
+    the kept rows land in state_out.  Returns state_out."""
+    torch = _torch()
+    assert k_chunk.dtype == torch.float16 and k_chunk.is_contiguous() and v_chunk.is_contiguous()
+    B, H, n, D = k_chunk.shape
+    o = _snap_opts(q_window, pool_kernel)
+    if ws is None:
+        nb = lib().kvq_snapkv_chunk_workspace_bytes(ctypes.byref(o), B, H, D, state_in.c.capacity, obs_window)
+        ws = torch.empty(max(int(nb), 16), dtype=torch.uint8, device=k_chunk.device)
+    _check(lib().kvq_snapkv_prefill_chunk(ctypes.byref(o), ctypes.byref(state_in.c), ctypes.byref(state_out.c),
+                                          k_chunk.data_ptr(), v_chunk.data_ptr(), n, B, H, D, obs_window,
+                                          n_sink, budget, _ptr(scores), ws.data_ptr(), ws.numel(),
+                                          _stream(stream)),
+           "kvq_snapkv_prefill_chunk")
+    return state_out

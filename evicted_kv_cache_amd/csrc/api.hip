@@ -23,7 +23,7 @@ kvq_status check_layout(const kvq_layout* L) {
     if (!L) return KVQ_ERR_INVALID_ARG;
     if (L->batch < 1 || L->n_kv_heads < 1 || L->capacity < 1) return KVQ_ERR_INVALID_ARG;
     if (!valid_dtype(L->in_dtype)) return KVQ_ERR_INVALID_ARG;
-    if (L->flags & ~(KVQ_CENTER_K | KVQ_TEST_CENTER_ANY)) return KVQ_ERR_INVALID_ARG;
+    if (L->flags & ~(KVQ_CENTER_K | KVQ_TEST_CENTER_ANY | KVQ_POS_PER_HEAD)) return KVQ_ERR_INVALID_ARG;
     const int D = L->head_dim;
     if (D != 32 && D != 64 && D != 128) return D > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
     switch (L->k_kind) {
@@ -97,7 +97,7 @@ void sizes_of(const kvq_layout* L, kvq_sizes* s) {
         s->v_codes = BH * C * D * L->v_bits / 8;
         s->v_meta = BH * C * (D / L->v_group) * 2 * 2;
     }
-    s->pos = C * 4;
+    s->pos = ((L->flags & KVQ_POS_PER_HEAD) ? BH : 1) * C * 4;
 }
 
 // Device buffers a layout needs must be present and aligned.
@@ -163,29 +163,26 @@ kvq_status kvq_cache_reset(kvq_cache* c) {
     return KVQ_OK;
 }
 
-kvq_status kvq_quantize_append(const kvq_layout* L, kvq_cache* c, const void* k_new,
-                               const void* v_new, int32_t n_new, void* stream) {
-    kvq_status st = check_layout(L);
-    if (st != KVQ_OK) return st;
-    if ((st = check_cache(L, c)) != KVQ_OK) return st;
-    if (n_new < 1 || !k_new || !v_new) return KVQ_ERR_INVALID_ARG;
-    if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
-    if ((int64_t)c->n_stored + n_new > L->capacity) return KVQ_ERR_CAPACITY;
-    if ((int64_t)c->next_pos + n_new > INT32_MAX) return KVQ_ERR_CAPACITY;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// Append n_new rows of each (b, h) slice (slices src_rows rows apart) at
+// positions pos_src (null: c->next_pos + i), then set the generation
+// counter to next_after.
+static kvq_status append_impl(const kvq_layout* L, kvq_cache* c, const void* k_new, const void* v_new,
+                              int32_t n_new, int32_t src_rows, const int32_t* pos_src, int32_t pos_rows,
+                              int64_t next_after, hipStream_t s) {
     const int B = L->batch, H = L->n_kv_heads, D = L->head_dim;
 
     // V rows, per-token K rows and positions: one launch; values are
     // quantized once, at write time.
     RowAppendArgs ra{};
     ra.rows.B = B; ra.rows.H = H; ra.rows.n = n_new; ra.rows.D = D; ra.rows.cap = L->capacity;
-    ra.rows.slot0 = c->n_stored; ra.rows.in_dtype = L->in_dtype;
+    ra.rows.slot0 = c->n_stored; ra.rows.in_dtype = L->in_dtype; ra.rows.src_rows = src_rows;
     ra.k_src = k_new; ra.k_codes = c->k_codes; ra.k_meta = c->k_meta;
     ra.k_bias = (L->flags & KVQ_CENTER_K) ? c->k_bias : nullptr;
     ra.k_kind = L->k_kind; ra.k_bits = L->k_bits; ra.k_group = L->k_group;
     ra.v_src = v_new; ra.v_codes = c->v_codes; ra.v_meta = c->v_meta;
     ra.v_kind = L->v_kind; ra.v_bits = L->v_bits; ra.v_group = L->v_group;
     ra.pos = c->pos; ra.first_pos = c->next_pos;
+    ra.pos_src = pos_src; ra.pos_src_rows = pos_rows; ra.pos_per_head = (L->flags & KVQ_POS_PER_HEAD) ? 1 : 0;
     hipError_t e = launch_row_append(ra, s);
     if (e != hipSuccess) return KVQ_ERR_HIP;
 
@@ -199,6 +196,7 @@ kvq_status kvq_quantize_append(const kvq_layout* L, kvq_cache* c, const void* k_
         k.Gt = L->k_group; k.bits = L->k_bits; k.in_dtype = L->in_dtype;
         k.r0 = c->n_stored - c->n_quant;
         k.n_new = n_new;
+        k.src_rows = src_rows;
         k.n_quant = c->n_quant;
         k.n_groups = (k.r0 + n_new) / L->k_group;
         e = launch_channel_quant(k, s);
@@ -206,11 +204,44 @@ kvq_status kvq_quantize_append(const kvq_layout* L, kvq_cache* c, const void* k_
         new_quant = c->n_quant + k.n_groups * L->k_group;
     }
 
-    if (c->n_head == c->n_stored) c->n_head += n_new;   // never evicted: positions == slots
+    if (c->n_head == c->n_stored) c->n_head += n_new;   // never evicted: slots in append order
     c->n_stored += n_new;
-    c->next_pos += n_new;
+    c->next_pos = (int32_t)next_after;
     c->n_quant = new_quant;
     return KVQ_OK;
+}
+
+kvq_status kvq_quantize_append(const kvq_layout* L, kvq_cache* c, const void* k_new,
+                               const void* v_new, int32_t n_new, void* stream) {
+    kvq_status st = check_layout(L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, c)) != KVQ_OK) return st;
+    if (n_new < 1 || !k_new || !v_new) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_ALIGNMENT;
+    if ((int64_t)c->n_stored + n_new > L->capacity) return KVQ_ERR_CAPACITY;
+    if ((int64_t)c->next_pos + n_new > INT32_MAX) return KVQ_ERR_CAPACITY;
+    return append_impl(L, c, k_new, v_new, n_new, n_new, nullptr, 0, (int64_t)c->next_pos + n_new,
+                       static_cast<hipStream_t>(stream));
+}
+
+kvq_status kvq_quantize_append_at(const kvq_layout* L, kvq_cache* c, const void* k_new, const void* v_new,
+                                  int32_t n_new, int32_t src_rows, const int32_t* positions,
+                                  int32_t pos_rows, int32_t next_pos, void* stream) {
+    kvq_status st = check_layout(L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, c)) != KVQ_OK) return st;
+    if (n_new < 1 || !k_new || !v_new || !positions) return KVQ_ERR_INVALID_ARG;
+    if (src_rows == 0) src_rows = n_new;
+    if (pos_rows == 0) pos_rows = n_new;
+    if (src_rows < n_new || pos_rows < n_new) return KVQ_ERR_INVALID_ARG;
+    if (next_pos < c->next_pos || next_pos < c->n_stored + n_new) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(positions)) return KVQ_ERR_ALIGNMENT;
+    // row starts of every slice must stay 16-byte aligned
+    if (((int64_t)src_rows * L->head_dim * esize(L->in_dtype)) % 16 != 0) return KVQ_ERR_ALIGNMENT;
+    if ((int64_t)c->n_stored + n_new > L->capacity) return KVQ_ERR_CAPACITY;
+    return append_impl(L, c, k_new, v_new, n_new, src_rows, positions,
+                       (L->flags & KVQ_POS_PER_HEAD) ? pos_rows : 0, next_pos,
+                       static_cast<hipStream_t>(stream));
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_q_heads) {
@@ -304,6 +335,7 @@ kvq_status kvq_evict_streaming(const kvq_layout* L, const kvq_cache* src, kvq_ca
     a.n_buf = nbuf;
     a.src_pos = src->pos; a.dst_pos = dst->pos;
     a.BH = L->batch * L->n_kv_heads; a.cap = L->capacity; a.n = n; a.sink = sink; a.window = window;
+    a.pos_per_head = (L->flags & KVQ_POS_PER_HEAD) ? 1 : 0;
     a.n_quant_new = sink + window - (L->k_kind == KVQ_KIVI_CH ? r : 0);
     if (L->k_kind == KVQ_KIVI_CH) {
         a.src_row = src->k_row; a.dst_row = dst->k_row;
@@ -346,54 +378,152 @@ size_t kvq_snapkv_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, in
     return kvq_snapkv_workspace_bytes_ex(nullptr, B, H, S, D, w);
 }
 
+// One SnapKV pass over S candidate rows per (b, h) (slices kv_stride elements
+// apart): scores, optional pooling, selection into kept, gather into
+// k_out / v_out (slices out_stride apart) with optional positions.  The
+// caller has validated everything; ws holds at least snapkv_ws_bytes.
+struct SnapRun {
+    const kvq_snapkv_opts* opts;
+    const void* k; const void* v; int64_t kv_stride;
+    int B, H, S, D, w, n_sink, budget, rows, pool;
+    float* scores; int32_t* kept;
+    void* k_out; void* v_out; int64_t out_stride;
+    const int32_t* pos_in; int pos_in_rows; int32_t* pos_out; int pos_out_rows;
+    char* ws;
+};
+
+static kvq_status snap_run(const SnapRun& r, hipStream_t s) {
+    SnapArgs a{};
+    a.k = static_cast<const uint16_t*>(r.k); a.v = static_cast<const uint16_t*>(r.v);
+    a.kept = r.kept; a.k_out = static_cast<uint16_t*>(r.k_out); a.v_out = static_cast<uint16_t*>(r.v_out);
+    a.B = r.B; a.H = r.H; a.S = r.S; a.D = r.D; a.w = r.w; a.n_sink = r.n_sink; a.budget = r.budget;
+    a.n_chunks = (r.S + 127) / 128;
+    a.n_rows = r.rows;
+    a.kv_stride = r.kv_stride; a.out_stride = r.out_stride;
+    a.pos_in = r.pos_in; a.pos_in_rows = r.pos_in_rows; a.pos_out = r.pos_out; a.pos_out_rows = r.pos_out_rows;
+    const void* qw = r.opts ? r.opts->q_window : nullptr;
+    if (qw) {
+        a.obs = static_cast<const uint16_t*>(qw);
+        a.obs_stride = (int64_t)r.rows * r.D;
+    } else {
+        a.obs = a.k + (int64_t)(r.S - r.rows) * r.D;
+        a.obs_stride = r.kv_stride;
+    }
+    size_t stats = (size_t)r.B * r.H * a.n_chunks * r.rows * 2 * sizeof(float);
+    stats = (stats + 255) & ~(size_t)255;
+    const size_t sc = ((size_t)r.B * r.H * r.S * sizeof(float) + 255) & ~(size_t)255;
+    a.stats = reinterpret_cast<float*>(r.ws);
+    a.scores = r.scores ? r.scores : reinterpret_cast<float*>(r.ws + stats);
+    if (launch_snapkv_scores(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    const float* rank = a.scores;
+    if (r.pool > 1) {
+        float* pooled = reinterpret_cast<float*>(r.ws + stats + sc);
+        if (launch_snapkv_pool(a.scores, pooled, (int64_t)r.B * r.H, r.S, r.pool, s) != hipSuccess)
+            return KVQ_ERR_HIP;
+        rank = pooled;
+    }
+    if (launch_snapkv_select(rank, r.B, r.H, r.S, r.n_sink, r.budget, r.kept, s) != hipSuccess)
+        return KVQ_ERR_HIP;
+    if (launch_snapkv_gather(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    return KVQ_OK;
+}
+
+// Validation common to the SnapKV calls: returns KVQ_OK and the observation
+// rows and pool width, or an error.
+static kvq_status snap_check(const kvq_snapkv_opts* opts, int32_t B, int32_t H, int32_t S, int32_t D,
+                             int32_t w, int32_t n_sink, int32_t budget, int* rows, int* pool) {
+    if (B < 1 || H < 1 || S < 1 || w < 1 || budget < 1 || n_sink < 0) return KVQ_ERR_INVALID_ARG;
+    if (D != 32 && D != 64 && D != 128) return D > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
+    *pool = snap_pool(opts);
+    if (*pool < 1 || *pool % 2 == 0) return KVQ_ERR_INVALID_ARG;
+    if (*pool > 31) return KVQ_ERR_UNSUPPORTED;
+    *rows = snap_rows(opts, H, S, w);
+    if (*rows == -1) return KVQ_ERR_INVALID_ARG;
+    if (*rows == -2) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)B * H * S > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
+    if (opts && opts->q_window && !aligned16(opts->q_window)) return KVQ_ERR_ALIGNMENT;
+    return KVQ_OK;
+}
+
 kvq_status kvq_snapkv_select_ex(const kvq_snapkv_opts* opts, const void* k, const void* v, int32_t B, int32_t H,
                                 int32_t S, int32_t D, int32_t w, int32_t n_sink, int32_t budget, float* scores,
                                 int32_t* kept, void* k_out, void* v_out, void* ws, size_t ws_bytes,
                                 void* stream) {
     if (!k || !v || !kept || !k_out || !v_out) return KVQ_ERR_INVALID_ARG;
-    if (B < 1 || H < 1 || S < 1 || w < 1 || budget < 1 || n_sink < 0) return KVQ_ERR_INVALID_ARG;
-    if (D != 32 && D != 64 && D != 128) return D > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
-    const int pool = snap_pool(opts);
-    if (pool < 1 || pool % 2 == 0) return KVQ_ERR_INVALID_ARG;
-    if (pool > 31) return KVQ_ERR_UNSUPPORTED;
-    const int rows = snap_rows(opts, H, S, w);
-    if (rows == -1) return KVQ_ERR_INVALID_ARG;
-    if (rows == -2) return KVQ_ERR_UNSUPPORTED;
-    if ((int64_t)B * H * S > INT32_MAX) return KVQ_ERR_UNSUPPORTED;
-    const void* qw = opts ? opts->q_window : nullptr;
-    const void* ptrs[8] = {k, v, scores, kept, k_out, v_out, ws, qw};
+    int rows = 0, pool = 1;
+    kvq_status st = snap_check(opts, B, H, S, D, w, n_sink, budget, &rows, &pool);
+    if (st != KVQ_OK) return st;
+    const void* ptrs[7] = {k, v, scores, kept, k_out, v_out, ws};
     for (const void* p : ptrs) if (p && !aligned16(p)) return KVQ_ERR_ALIGNMENT;
     const size_t need = snapkv_ws_bytes(B, H, S, D, rows, pool > 1);
     if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    const int n_keep = budget < S ? budget : S;
+    SnapRun r{opts, k, v, (int64_t)S * D, B, H, S, D, w, n_sink, budget, rows, pool, scores, kept,
+              k_out, v_out, (int64_t)n_keep * D, nullptr, 0, nullptr, 0, static_cast<char*>(ws)};
+    return snap_run(r, static_cast<hipStream_t>(stream));
+}
+
+// Workspace of a prefill chunk: a SnapKV pass over up to `capacity` rows plus
+// the kept indices.
+static size_t chunk_ws_bytes(int B, int H, int cap, int D, int rows, bool pooled) {
+    const size_t kept = ((size_t)B * H * cap * sizeof(int32_t) + 255) & ~(size_t)255;
+    return snapkv_ws_bytes(B, H, cap, D, rows, pooled) + kept;
+}
+
+size_t kvq_snapkv_chunk_workspace_bytes(const kvq_snapkv_opts* opts, int32_t B, int32_t H, int32_t D,
+                                        int32_t capacity, int32_t w) {
+    if (B < 1 || H < 1 || capacity < 1 || w < 1 || (D != 32 && D != 64 && D != 128)) return 0;
+    // observation rows: at most min(w, capacity) key rows, or G * w query rows
+    const int rows = snap_rows(opts, H, capacity, w < capacity ? w : capacity);
+    const int pool = snap_pool(opts);
+    if (rows < 1 || pool < 1 || pool % 2 == 0) return 0;
+    return chunk_ws_bytes(B, H, capacity, D, rows, pool > 1);
+}
+
+kvq_status kvq_snapkv_prefill_chunk(const kvq_snapkv_opts* opts, kvq_snapkv_state* in, kvq_snapkv_state* out,
+                                    const void* k_chunk, const void* v_chunk, int32_t chunk_len, int32_t B,
+                                    int32_t H, int32_t D, int32_t w, int32_t n_sink, int32_t budget,
+                                    float* scores, void* ws, size_t ws_bytes, void* stream) {
+    if (!in || !out || !k_chunk || !v_chunk || chunk_len < 1) return KVQ_ERR_INVALID_ARG;
+    if (!in->k || !in->v || !in->pos || !out->k || !out->v || !out->pos) return KVQ_ERR_INVALID_ARG;
+    if (in->capacity < 1 || out->capacity < 1 || in->n_kept < 0 || in->next_pos < in->n_kept)
+        return KVQ_ERR_INVALID_ARG;
+    const int64_t n64 = (int64_t)in->n_kept + chunk_len;
+    if (n64 > in->capacity || (int64_t)in->next_pos + chunk_len > INT32_MAX) return KVQ_ERR_CAPACITY;
+    const int S = (int)n64;
+    int rows = 0, pool = 1;
+    kvq_status st = snap_check(opts, B, H, S, D, w, n_sink, budget, &rows, &pool);
+    if (st != KVQ_OK) return st;
+    const int n_keep = budget < S ? budget : S;
+    if (n_keep > out->capacity) return KVQ_ERR_CAPACITY;
+    const void* ptrs[9] = {k_chunk, v_chunk, in->k, in->v, in->pos, out->k, out->v, out->pos, ws};
+    for (const void* p : ptrs) if (!aligned16(p)) return KVQ_ERR_ALIGNMENT;
+    if (scores && !aligned16(scores)) return KVQ_ERR_ALIGNMENT;
+    // the two states must not share memory
+    const size_t rb_in = (size_t)B * H * in->capacity * D * 2, rb_out = (size_t)B * H * out->capacity * D * 2;
+    const size_t pb_in = (size_t)B * H * in->capacity * 4, pb_out = (size_t)B * H * out->capacity * 4;
+    const void* ip[3] = {in->k, in->v, in->pos};
+    const void* op[3] = {out->k, out->v, out->pos};
+    const size_t inb[3] = {rb_in, rb_in, pb_in}, outb[3] = {rb_out, rb_out, pb_out};
+    for (int i = 0; i < 3; ++i)
+        for (int j = 0; j < 3; ++j)
+            if (overlaps(ip[i], inb[i], op[j], outb[j])) return KVQ_ERR_INVALID_ARG;
+    const size_t need = chunk_ws_bytes(B, H, in->capacity, D, rows, pool > 1);
+    if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    SnapArgs a{};
-    a.k = static_cast<const uint16_t*>(k); a.v = static_cast<const uint16_t*>(v);
-    a.kept = kept; a.k_out = static_cast<uint16_t*>(k_out); a.v_out = static_cast<uint16_t*>(v_out);
-    a.B = B; a.H = H; a.S = S; a.D = D; a.w = w; a.n_sink = n_sink; a.budget = budget;
-    a.n_chunks = (S + 127) / 128;
-    a.n_rows = rows;
-    if (qw) {
-        a.obs = static_cast<const uint16_t*>(qw);
-        a.obs_stride = (int64_t)rows * D;
-    } else {
-        a.obs = a.k + (int64_t)(S - rows) * D;
-        a.obs_stride = (int64_t)S * D;
-    }
-    size_t stats = (size_t)B * H * a.n_chunks * rows * 2 * sizeof(float);
-    stats = (stats + 255) & ~(size_t)255;
-    size_t sc = ((size_t)B * H * S * sizeof(float) + 255) & ~(size_t)255;
+    if (launch_snapkv_chunk_copy(k_chunk, v_chunk, in->k, in->v, in->pos, B, H, D, chunk_len, in->capacity,
+                                 in->n_kept, in->next_pos, s) != hipSuccess)
+        return KVQ_ERR_HIP;
     char* wsb = static_cast<char*>(ws);
-    a.stats = reinterpret_cast<float*>(wsb);
-    a.scores = scores ? scores : reinterpret_cast<float*>(wsb + stats);
-    if (launch_snapkv_scores(a, s) != hipSuccess) return KVQ_ERR_HIP;
-    const float* rank = a.scores;
-    if (pool > 1) {
-        float* pooled = reinterpret_cast<float*>(wsb + stats + sc);
-        if (launch_snapkv_pool(a.scores, pooled, (int64_t)B * H, S, pool, s) != hipSuccess) return KVQ_ERR_HIP;
-        rank = pooled;
-    }
-    if (launch_snapkv_select(rank, B, H, S, n_sink, budget, kept, s) != hipSuccess) return KVQ_ERR_HIP;
-    if (launch_snapkv_gather(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    int32_t* kept = reinterpret_cast<int32_t*>(wsb + snapkv_ws_bytes(B, H, in->capacity, D, rows, pool > 1));
+    SnapRun r{opts, in->k, in->v, (int64_t)in->capacity * D, B, H, S, D, w, n_sink, budget, rows, pool,
+              scores, kept, out->k, out->v, (int64_t)out->capacity * D, in->pos, in->capacity, out->pos,
+              out->capacity, wsb};
+    if ((st = snap_run(r, s)) != KVQ_OK) return st;
+    in->n_kept = S;
+    in->next_pos += chunk_len;
+    out->n_kept = n_keep;
+    out->next_pos = in->next_pos;
     return KVQ_OK;
 }
 

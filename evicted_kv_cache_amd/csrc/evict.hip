@@ -58,8 +58,9 @@ __device__ __forceinline__ RowRemap row_remap(const int32_t* k_row, int n, int s
 
 // Thread (row, u) copies 16-byte unit u of every slot-indexed buffer whose row
 // has that many units (code rows are multiples of 16 bytes); unit 0 also
-// copies the shorter rows (per-token metadata) and, for (0, 0, i), moves
-// pos[i] and k_row[i].  Consecutive threads touch consecutive units.
+// copies the shorter rows (per-token metadata) and the slot's position (per
+// (b, h) position rows; for shared positions (0, 0, i) moves pos[i]), and
+// (0, 0, i) moves k_row[i].  Consecutive threads touch consecutive units.
 __global__ __launch_bounds__(256) void gather_kernel(EvictArgs a, int upr) {
     const int m = a.sink + a.window;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -82,8 +83,9 @@ __global__ __launch_bounds__(256) void gather_kernel(EvictArgs a, int upr) {
             copy_row(src, dst, rb);
         }
     }
+    if (u == 0 && a.pos_per_head) a.dst_pos[bh * a.cap + i] = a.src_pos[bh * a.cap + si];
     if (bh == 0 && u == 0) {
-        a.dst_pos[i] = a.src_pos[si];
+        if (!a.pos_per_head) a.dst_pos[i] = a.src_pos[si];
         if (a.src_row && i < a.n_quant_new) {
             const RowRemap rr = row_remap(a.src_row, a.n, a.sink, a.window);
             const int old = a.src_row[si];

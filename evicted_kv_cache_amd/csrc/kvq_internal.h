@@ -67,6 +67,7 @@ struct RowQuantArgs {
     const float* bias;     // TOK_SYM4 centering [H][D] or nullptr
     int B, H, n, D, cap, slot0;
     int kind, bits, group, in_dtype;
+    int src_rows;          // rows between consecutive (b, h) slices of src (>= n)
 };
 // One fused launch: K rows (per-token kinds), V rows and positions.
 struct RowAppendArgs {
@@ -76,6 +77,9 @@ struct RowAppendArgs {
     const void* v_src; void* v_codes; void* v_meta;
     int v_kind, v_bits, v_group;
     int32_t* pos; int first_pos;
+    // positions of the new rows: pos_src (per-head rows of pos_src_rows when
+    // pos_per_head, else [n]) or, when null, first_pos + i
+    const int32_t* pos_src; int pos_src_rows; int pos_per_head;
 };
 hipError_t launch_row_append(const RowAppendArgs& a, hipStream_t s);
 
@@ -83,7 +87,7 @@ hipError_t launch_row_append(const RowAppendArgs& a, hipStream_t s);
 // (r0 keys) followed by new keys, then store the remaining new keys in the
 // residual.
 struct ChannelQuantArgs {
-    const void* k_new;     // [B][H][n_new][D]
+    const void* k_new;     // [B][H][src_rows][D], rows [0, n_new) appended
     void* resid;           // [B][H][Gt][D]
     void* codes;           // [B][H][cap][D*bits/8]
     void* table;           // [B][H][rows][D][2] fp16
@@ -93,6 +97,7 @@ struct ChannelQuantArgs {
     int n_new;
     int n_quant;           // coded slots before the append
     int n_groups;          // groups closed by this append
+    int src_rows;
 };
 hipError_t launch_channel_quant(const ChannelQuantArgs& a, hipStream_t s);
 
@@ -127,6 +132,7 @@ struct EvictArgs {
     const void* src_table; void* dst_table; int table_row_bytes; int rows;
     const void* src_resid; void* dst_resid; size_t resid_bytes;
     int BH, cap, n, sink, window, n_quant_new;
+    int pos_per_head;      // pos is [BH][cap] (else [cap], shared)
 };
 hipError_t launch_evict(const EvictArgs& a, hipStream_t s);
 
@@ -138,10 +144,19 @@ struct SnapArgs {
     float* scores; int32_t* kept; uint16_t* k_out; uint16_t* v_out;
     float* stats;          // [B][H][n_chunks][n_rows][2]
     int B, H, S, D, w, n_sink, budget, n_chunks;
+    int64_t kv_stride;     // elements between (b, h) slices of k and v
+    int64_t out_stride;    // elements between (b, h) slices of k_out and v_out
+    // optional: positions gathered with the rows (pos_in null: the row index)
+    const int32_t* pos_in; int32_t* pos_out; int pos_in_rows, pos_out_rows;
 };
 size_t snapkv_ws_bytes(int B, int H, int S, int D, int n_rows, bool pooled);
 hipError_t launch_snapkv_pool(const float* in, float* out, int64_t rows, int S, int kernel, hipStream_t s);
 hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s);
+// Copy chunk rows [B][H][n][D] fp16 into rows [row0, row0 + n) of a state
+// [B][H][cap][D] and set their positions first_pos + i ([B][H][cap] int32).
+hipError_t launch_snapkv_chunk_copy(const void* k_chunk, const void* v_chunk, void* k_state, void* v_state,
+                                    int32_t* pos_state, int B, int H, int D, int n, int cap, int row0,
+                                    int first_pos, hipStream_t s);
 hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_sink, int budget,
                                 int32_t* kept, hipStream_t s);
 hipError_t launch_snapkv_gather(const SnapArgs& a, hipStream_t s);

@@ -273,9 +273,14 @@ __device__ __forceinline__ void copy_row16(const RowPart& r, int64_t row, int64_
 // D / 16 = 2^lpr_sh lanes of 16 channels, and each thread takes kRowIter
 // rows, all loaded before any is widened or quantized.  Blocks of bh = 0
 // also write the positions of their rows.
+// Positions of the appended slots.
+struct PosWrite {
+    int32_t* pos; const int32_t* src; int src_rows; int first; int per_head;
+};
+
 template <int DT, int FK, int FV>
 __global__ __launch_bounds__(256) void row_append_kernel(RowQuantArgs a, RowPart kp, RowPart vp, int bh0,
-                                                         int lpr_sh, int32_t* pos, int first_pos) {
+                                                         int lpr_sh, PosWrite pw) {
     constexpr int ES = DT == KVQ_F32 ? 4 : 2;          // input bytes per element
     const int rpp_sh = 8 - lpr_sh;                    // log2 rows per pass
     const int rpc = kRowIter << rpp_sh;               // rows per chunk
@@ -284,9 +289,11 @@ __global__ __launch_bounds__(256) void row_append_kernel(RowQuantArgs a, RowPart
     const bool is_v = FK == kFmtNone || blockIdx.z == 1;
     const int lane = threadIdx.x & ((1 << lpr_sh) - 1);
     const int i_base = chunk * rpc + (threadIdx.x >> lpr_sh);
-    if (pos && bh == 0 && !(FK != kFmtNone && is_v)) {
+    if (pw.pos && (pw.per_head || bh == 0) && !(FK != kFmtNone && is_v)) {
         const int i_end = min(a.n, (chunk + 1) * rpc);
-        for (int i = chunk * rpc + threadIdx.x; i < i_end; i += 256) pos[a.slot0 + i] = first_pos + i;
+        int32_t* P = pw.pos + (pw.per_head ? (int64_t)bh * a.cap : 0) + a.slot0;
+        const int32_t* Ps = pw.src ? pw.src + (pw.per_head ? (int64_t)bh * pw.src_rows : 0) : nullptr;
+        for (int i = chunk * rpc + threadIdx.x; i < i_end; i += 256) P[i] = Ps ? Ps[i] : pw.first + i;
     }
     const int64_t drow0 = (int64_t)bh * a.cap + a.slot0;
     auto run = [&](const RowPart& part, auto fmt_tag) {
@@ -296,10 +303,10 @@ __global__ __launch_bounds__(256) void row_append_kernel(RowQuantArgs a, RowPart
 #pragma unroll
             for (int it = 0; it < kRowIter; ++it) {
                 const int i = i_base + (it << rpp_sh);
-                if (i < a.n) copy_row16<DT>(part, (int64_t)bh * a.n + i, drow0 + i, h, lane, a.D);
+                if (i < a.n) copy_row16<DT>(part, (int64_t)bh * a.src_rows + i, drow0 + i, h, lane, a.D);
             }
         } else {
-            const char* src = static_cast<const char*>(part.src) + ((int64_t)bh * a.n * a.D + lane * kEpl) * ES;
+            const char* src = static_cast<const char*>(part.src) + ((int64_t)bh * a.src_rows * a.D + lane * kEpl) * ES;
             const uint32_t row_bytes = (uint32_t)a.D * ES;
             Raw16<DT> raw[kRowIter];
 #pragma unroll
@@ -344,7 +351,7 @@ __global__ __launch_bounds__(64) void channel_close_kernel(ChannelQuantArgs a) {
     if (row < 0 || row >= a.rows) return;   // cannot happen while at most two position runs are kept
     auto val = [&](int tau, int c) -> float {
         if (tau < a.r0) return load_as_f32<DT>(a.resid, (bh * Gt + tau) * D + c);
-        return load_as_f32<DT>(a.k_new, (bh * a.n_new + (tau - a.r0)) * D + c);
+        return load_as_f32<DT>(a.k_new, (bh * a.src_rows + (tau - a.r0)) * D + c);
     };
     const int tau0 = j * Gt;
     float mn0 = val(tau0, c0), mx0 = mn0, mn1 = val(tau0, c0 + 1), mx1 = mn1;
@@ -397,7 +404,7 @@ __global__ __launch_bounds__(256) void resid_store_kernel(ChannelQuantArgs a, in
     const int rr = a.r0 + i - a.n_groups * a.Gt;
     using T = typename std::conditional<ES == 4, uint32_t, uint16_t>::type;
     static_cast<T*>(a.resid)[(bh * a.Gt + rr) * a.D + d] =
-        static_cast<const T*>(a.k_new)[(bh * a.n_new + i) * a.D + d];
+        static_cast<const T*>(a.k_new)[(bh * a.src_rows + i) * a.D + d];
 }
 
 int row_fmt(int kind, int bits) {
@@ -419,8 +426,8 @@ hipError_t launch_append_fv(const RowAppendArgs& a, hipStream_t s) {
         dim3 grid((unsigned)n_chunks, (unsigned)nbh, FK == kFmtNone ? 1 : 2);
         hipLaunchKernelGGL((row_append_kernel<DT, FK, FV>), grid, dim3(256), 0, s, a.rows,
                            RowPart{a.k_src, a.k_codes, a.k_meta, a.k_bias, a.k_group},
-                           RowPart{a.v_src, a.v_codes, a.v_meta, nullptr, a.v_group}, bh0, lpr_sh, a.pos,
-                           a.first_pos);
+                           RowPart{a.v_src, a.v_codes, a.v_meta, nullptr, a.v_group}, bh0, lpr_sh,
+                           PosWrite{a.pos, a.pos_src, a.pos_src_rows, a.first_pos, a.pos_per_head});
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     const int kh = lane >> 5, l32 = lane & 31;
     const int S = a.S;
     const int wc = a.n_rows;
-    const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
+    const uint16_t* K = a.k + ((int64_t)b * a.H + h) * a.kv_stride;
     const uint16_t* O = a.obs + ((int64_t)b * a.H + h) * a.obs_stride;   // observation rows
     const float c = 1.4426950408889634f / sqrtf((float)D);
     const int key_base = chunk * kChunk + wave * 32;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     const int kh = lane >> 5, l32 = lane & 31;
     const int S = a.S;
     const int wc = a.n_rows;
-    const uint16_t* K = a.k + ((int64_t)b * a.H + h) * S * D;
+    const uint16_t* K = a.k + ((int64_t)b * a.H + h) * a.kv_stride;
     const uint16_t* O = a.obs + ((int64_t)b * a.H + h) * a.obs_stride;   // observation rows
     const float c = 1.4426950408889634f / sqrtf((float)D);
     __shared__ float Mrow[kMaxWindow], invL[kMaxWindow];
@@ -499,13 +499,33 @@ __global__ __launch_bounds__(256) void snap_gather_kernel(SnapArgs a, int n_keep
     const int64_t r = idx / upr;
     const int u = (int)(idx - r * upr);
     const int64_t bh = r / n_keep;
+    const int rl = (int)(r - bh * n_keep);
     const int j = a.kept[r];
     if (j < 0 || j >= a.S) return;
-    const int64_t src = bh * a.S + j;
-    const uint4* ks = reinterpret_cast<const uint4*>(a.k);
-    const uint4* vs = reinterpret_cast<const uint4*>(a.v);
-    reinterpret_cast<uint4*>(a.k_out)[r * upr + u] = ks[src * upr + u];
-    reinterpret_cast<uint4*>(a.v_out)[r * upr + u] = vs[src * upr + u];
+    const int64_t src = (bh * a.kv_stride + (int64_t)j * a.D) / 8 + u;
+    const int64_t dst = (bh * a.out_stride + (int64_t)rl * a.D) / 8 + u;
+    reinterpret_cast<uint4*>(a.k_out)[dst] = reinterpret_cast<const uint4*>(a.k)[src];
+    reinterpret_cast<uint4*>(a.v_out)[dst] = reinterpret_cast<const uint4*>(a.v)[src];
+    if (u == 0 && a.pos_out)
+        a.pos_out[bh * a.pos_out_rows + rl] = a.pos_in ? a.pos_in[bh * a.pos_in_rows + j] : j;
+}
+
+// Chunk rows into a kept-row state: thread (row, unit) copies one 16-byte
+// unit of K and V; unit 0 also writes the row's position.
+__global__ __launch_bounds__(256) void snap_chunk_copy_kernel(const uint4* __restrict__ kc, const uint4* __restrict__ vc,
+                                                              uint4* __restrict__ ks, uint4* __restrict__ vs,
+                                                              int32_t* __restrict__ ps, int64_t rows, int n, int upr,
+                                                              int cap, int row0, int first_pos) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= rows * upr) return;
+    const int64_t r = idx / upr;
+    const int u = (int)(idx - r * upr);
+    const int64_t bh = r / n;
+    const int i = (int)(r - bh * n);
+    const int64_t dst = (bh * cap + row0 + i) * upr + u;
+    ks[dst] = kc[idx];
+    vs[dst] = vc[idx];
+    if (u == 0) ps[bh * cap + row0 + i] = first_pos + i;
 }
 
 // Max-pool smoothing of a score row: out[r][j] = max of in[r][j'] over
@@ -572,6 +592,20 @@ hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_
     else
         hipLaunchKernelGGL(snap_select_radix_kernel, dim3((unsigned)(B * H)), dim3(1024), 0, s, scores, S,
                            n_sink, budget, kept);
+    return hipGetLastError();
+}
+
+hipError_t launch_snapkv_chunk_copy(const void* k_chunk, const void* v_chunk, void* k_state, void* v_state,
+                                    int32_t* pos_state, int B, int H, int D, int n, int cap, int row0,
+                                    int first_pos, hipStream_t s) {
+    const int upr = D / 8;
+    const int64_t rows = (int64_t)B * H * n;
+    const int64_t total = rows * upr;
+    if (total == 0) return hipSuccess;
+    hipLaunchKernelGGL(snap_chunk_copy_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s,
+                       static_cast<const uint4*>(k_chunk), static_cast<const uint4*>(v_chunk),
+                       static_cast<uint4*>(k_state), static_cast<uint4*>(v_state), pos_state, rows, n, upr, cap,
+                       row0, first_pos);
     return hipGetLastError();
 }
 

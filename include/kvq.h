@@ -79,6 +79,8 @@ typedef enum { KVQ_PLAIN = 0, KVQ_KIVI_CH = 1, KVQ_TOK_AFFINE = 2, KVQ_TOK_SYM4 
 /* layout.flags */
 #define KVQ_CENTER_K         0x1  /* subtract cache.k_bias before quantizing K (TOK_SYM4 only) */
 #define KVQ_TEST_CENTER_ANY  0x2  /* test seam: also allow KVQ_CENTER_K with PLAIN keys */
+#define KVQ_POS_PER_HEAD     0x4  /* one position row per (batch, kv-head): caches that hold
+                                     SnapKV-kept rows, whose positions differ between heads */
 
 /* Quantization arithmetic (bit-exact specification, fp32, IEEE round to
  * nearest even, no fused multiply-add):
@@ -105,7 +107,7 @@ typedef struct kvq_layout {
     int32_t v_bits;       /* 4 or 8 (TOK_AFFINE) */
     int32_t v_group;      /* channels per group (32, 64 or 128, dividing D) */
     int32_t in_dtype;     /* kvq_dtype of appended K/V, PLAIN storage and the KIVI residual */
-    int32_t flags;        /* KVQ_CENTER_K | KVQ_TEST_CENTER_ANY */
+    int32_t flags;        /* KVQ_CENTER_K | KVQ_TEST_CENTER_ANY | KVQ_POS_PER_HEAD */
 } kvq_layout;
 
 /* One layer's cache.  Device buffers (sizes from kvq_cache_sizes):
@@ -120,7 +122,8 @@ typedef struct kvq_layout {
  *            the key of slot n_quant + i
  *   v_codes, v_meta  as for K with v_kind / v_bits / v_group
  *   pos      [capacity] int32 absolute position of each slot (shared over
- *            batch and heads; [P2]: positions stay the true positions)
+ *            batch and heads; [P2]: positions stay the true positions), or
+ *            [B][Hkv][capacity] with KVQ_POS_PER_HEAD
  *   k_row    KIVI_CH only: [capacity] int32 table row of each coded slot
  *   k_bias   [Hkv][D] fp32 mean subtracted from K before TOK_SYM4
  *            quantization when layout.flags has KVQ_CENTER_K ([P3]); else NULL
@@ -175,6 +178,30 @@ kvq_status kvq_cache_reset(kvq_cache* cache);
 kvq_status kvq_quantize_append(const kvq_layout* layout, kvq_cache* cache,
                                const void* k_new, const void* v_new,
                                int32_t n_new, void* stream);
+
+/* kvq_quantize_append for rows that carry their own positions: SnapKV-kept
+ * rows stacked into a quantized cache ([P2] "SnapKV-adapted": any quantizer
+ * can be stacked on the kept tokens; "RoPE position semantics": kept rows
+ * keep their true absolute positions).  Rows [0, n_new) of each (batch,
+ * kv-head) slice are appended exactly as kvq_quantize_append would.
+ *   k_new, v_new  device [B][Hkv][src_rows][D] in_dtype; src_rows >= n_new,
+ *                 0 means n_new (e.g. a kvq_snapkv_state: src_rows = its
+ *                 capacity).
+ *   positions     device int32: [B][Hkv][pos_rows] with KVQ_POS_PER_HEAD
+ *                 (pos_rows >= n_new, 0 means n_new), else [n_new].  Copied
+ *                 into the new slots' positions as given.
+ *   next_pos      the cache's generation counter afterwards (the prompt
+ *                 length for kept prefill rows); later kvq_quantize_append
+ *                 calls continue from it.  Must be >= the current counter
+ *                 and >= n_stored + n_new; positions themselves are not
+ *                 inspected on the host.
+ * Errors as kvq_quantize_append, plus KVQ_ERR_INVALID_ARG for a missing
+ * positions array, src_rows or pos_rows below n_new, or next_pos below the
+ * current counter or the stored count.                                    */
+kvq_status kvq_quantize_append_at(const kvq_layout* layout, kvq_cache* cache,
+                                  const void* k_new, const void* v_new, int32_t n_new,
+                                  int32_t src_rows, const int32_t* positions,
+                                  int32_t pos_rows, int32_t next_pos, void* stream);
 
 /* Workspace bytes kvq_decode_attention needs for this layout (any fill). */
 size_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t n_q_heads);
@@ -287,6 +314,54 @@ kvq_status kvq_snapkv_select_ex(const kvq_snapkv_opts* opts, const void* k, cons
 kvq_status kvq_snapkv_pool_scores(const float* scores, float* pooled, int32_t batch,
                                   int32_t n_kv_heads, int32_t seq_len, int32_t pool_kernel,
                                   void* stream);
+
+/* Chunked SnapKV prefill ([P2] "How it works": every prefill call scores
+ * and selects again, so the budget holds across chunks; "RoPE position
+ * semantics": kept rows keep their absolute positions, and decode appends
+ * never pass through the selection).  A state holds the rows kept so far:
+ *   k, v      device [B][Hkv][capacity][D] fp16, rows [0, n_kept) in
+ *             ascending position order
+ *   pos       device [B][Hkv][capacity] int32 absolute positions of the rows
+ *   n_kept    host counter; next_pos  host: position of the next prompt token
+ * Zero the counters for an empty state.                                     */
+typedef struct kvq_snapkv_state {
+    void* k;
+    void* v;
+    int32_t* pos;
+    int32_t capacity;
+    int32_t n_kept;
+    int32_t next_pos;
+} kvq_snapkv_state;
+
+/* Workspace bytes for kvq_snapkv_prefill_chunk with an `in` state of the
+ * given capacity (0 for invalid or unsupported sizes or options). */
+size_t kvq_snapkv_chunk_workspace_bytes(const kvq_snapkv_opts* opts, int32_t batch,
+                                        int32_t n_kv_heads, int32_t head_dim,
+                                        int32_t capacity, int32_t obs_window);
+
+/* One prefill chunk.  The chunk's rows (device [B][Hkv][chunk_len][D] fp16,
+ * positions in->next_pos + i) are first written after the kept rows of `in`
+ * (in->n_kept grows by chunk_len, in->next_pos by chunk_len).  Then SnapKV
+ * (kvq_snapkv_select_ex, with opts) runs over those n = n_kept + chunk_len
+ * candidate rows: the observation window is the last min(obs_window, n)
+ * candidate key rows, or opts->q_window (the queries of the chunk's last
+ * obs_window tokens, obs_window <= n).  The sinks are the first n_sink
+ * candidates, which are the prompt's first positions once they were kept.
+ * The min(budget, n) selected rows and their positions go to rows [0,
+ * n_keep) of `out` in ascending order; out->n_kept = n_keep and
+ * out->next_pos = in->next_pos.  Pass `out` as `in` for the next chunk.
+ *   scores  optional device [B][Hkv][n] fp32 (unpooled scores of the
+ *           candidates), or NULL.
+ * Errors: KVQ_ERR_CAPACITY when n > in->capacity or n_keep > out->capacity;
+ * KVQ_ERR_INVALID_ARG for overlapping states, missing buffers and the
+ * argument errors of kvq_snapkv_select_ex; KVQ_ERR_WORKSPACE, ALIGNMENT and
+ * UNSUPPORTED as there.                                                     */
+kvq_status kvq_snapkv_prefill_chunk(const kvq_snapkv_opts* opts, kvq_snapkv_state* in,
+                                    kvq_snapkv_state* out, const void* k_chunk,
+                                    const void* v_chunk, int32_t chunk_len, int32_t batch,
+                                    int32_t n_kv_heads, int32_t head_dim, int32_t obs_window,
+                                    int32_t n_sink, int32_t budget, float* scores, void* ws,
+                                    size_t ws_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* kvq_status_string(kvq_status status);

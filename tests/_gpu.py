@@ -37,7 +37,7 @@ def to_dev(x: np.ndarray, dtype: str) -> torch.Tensor:
 def layouts(**kw):
     """(product Layout, oracle Layout) with the same fields."""
     flags = kw.pop("flags", 0)
-    ol = OLayout(**kw)
+    ol = OLayout(pos_per_head=bool(flags & K.KVQ_POS_PER_HEAD), **kw)
     pl = K.Layout(flags=flags, **kw)
     return pl, ol
 
@@ -79,7 +79,11 @@ def gpu_state(c: K.Cache, bh=None):
     n, nq = c.n_stored, c.n_quant
     es = {"f32": 4, "f16": 2, "bf16": 2}[L.in_dtype]
     npdt = NP_OF[L.in_dtype]
-    st = {"pos": i32(c.pos, n)}
+    if L.flags & K.KVQ_POS_PER_HEAD:
+        st = {"pos": _sel(c.pos, B, H, C * 4, bh).view(np.int32).reshape(
+            B if bh is None else 1, H if bh is None else 1, C)[:, :, :n]}
+    else:
+        st = {"pos": i32(c.pos, n)}
     if L.k_kind == "plain":
         st["k_plain"] = _sel(c.k_codes, B, H, D * es, bh).view(npdt)[:, :, :n]
     else:
@@ -108,7 +112,7 @@ def gpu_state(c: K.Cache, bh=None):
 def oracle_state(o: OracleCache):
     L = o.L
     n, nq = o.n_stored, o.n_quant
-    st = {"pos": o.pos[:n]}
+    st = {"pos": o.pos[..., :n]}
     if L.k_kind == "plain":
         st["k_plain"] = o.k_plain[:, :, :n]
     else:

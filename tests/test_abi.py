@@ -252,6 +252,57 @@ def test_snapkv_options_validation_without_gpu():
     assert pool(None, 0x100000, 1, 1, 100, 3, None) == K.KVQ_ERR_INVALID_ARG
 
 
+def test_append_at_validation_without_gpu():
+    L = c5_layout(batch=2, capacity=100, in_dtype="f16", flags=K.KVQ_POS_PER_HEAD)
+    assert K.kvq_cache_sizes(L).pos == 2 * 8 * 100 * 4           # one position row per (b, h)
+    assert K.kvq_cache_sizes(c5_layout(batch=2, capacity=100)).pos == 100 * 4
+    lib = K.lib()
+
+    def call(c, n_new=10, src_rows=0, positions=FAKE, pos_rows=0, next_pos=50):
+        cl = L.c()
+        return lib.kvq_quantize_append_at(ctypes.byref(cl), ctypes.byref(c), FAKE, FAKE, n_new, src_rows,
+                                          positions, pos_rows, next_pos, None)
+    c = fake_cache(L, n_stored=0)
+    assert call(c, positions=None) == K.KVQ_ERR_INVALID_ARG
+    assert call(c, src_rows=5) == K.KVQ_ERR_INVALID_ARG          # fewer source rows than n_new
+    assert call(c, pos_rows=9) == K.KVQ_ERR_INVALID_ARG
+    assert call(c, next_pos=9) == K.KVQ_ERR_INVALID_ARG          # counter below the stored count
+    assert call(c, positions=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert call(c, n_new=101, next_pos=200) == K.KVQ_ERR_CAPACITY
+    c2 = fake_cache(L, n_stored=20)                              # its counter is 20
+    assert call(c2, next_pos=19) == K.KVQ_ERR_INVALID_ARG
+    assert c2.n_stored == 20 and c.n_stored == 0
+
+
+def test_snapkv_prefill_chunk_validation_without_gpu():
+    lib = K.lib()
+    B, H, D, cap = 1, 8, 128, 600
+    ws = K.kvq_snapkv_chunk_workspace_bytes(B, H, D, cap, 32)
+    assert ws > B * H * cap * 8                                  # scores + kept indices at least
+    assert K.kvq_snapkv_chunk_workspace_bytes(B, H, 96, cap, 32) == 0
+
+    def state(base, capacity=cap, n_kept=0, next_pos=0):
+        return K.c_snapkv_state(base, base + (1 << 30), base + (2 << 30), capacity, n_kept, next_pos)
+
+    def call(si, so, n=100, budget=512, ws_bytes=ws, kc=FAKE, opts=None):
+        return lib.kvq_snapkv_prefill_chunk(opts, ctypes.byref(si), ctypes.byref(so), kc, FAKE, n, B, H, D,
+                                            32, 4, budget, None, FAKE, ws_bytes, None)
+    A, Bs = 1 << 36, 1 << 37
+    assert call(state(A, n_kept=550, next_pos=550), state(Bs), n=51) == K.KVQ_ERR_CAPACITY   # past in capacity
+    assert call(state(A), state(Bs, capacity=50), n=100) == K.KVQ_ERR_CAPACITY             # out too small
+    assert call(state(A), state(A + 16)) == K.KVQ_ERR_INVALID_ARG                          # overlapping states
+    assert call(state(A), state(Bs), n=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(state(A, n_kept=10, next_pos=5), state(Bs)) == K.KVQ_ERR_INVALID_ARG       # counters
+    assert call(state(A), state(Bs), ws_bytes=ws - 1) == K.KVQ_ERR_WORKSPACE
+    assert call(state(A), state(Bs), kc=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert call(state(A), state(Bs), budget=0) == K.KVQ_ERR_INVALID_ARG
+    o = K.c_snapkv_opts(FAKE, 32, 4)
+    assert call(state(A), state(Bs), opts=ctypes.byref(o)) == K.KVQ_ERR_INVALID_ARG        # even pool width
+    si = state(A, n_kept=7, next_pos=9)
+    assert call(si, state(Bs), n=cap) == K.KVQ_ERR_CAPACITY
+    assert (si.n_kept, si.next_pos) == (7, 9)                                              # untouched on error
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(K, "_lib", None)
