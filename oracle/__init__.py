@@ -44,6 +44,8 @@ def lib():
         L.kvo_dequant.restype = f64
         L.kvo_dequant.argtypes = [P, i32, i32]
         L.kvo_decode_head.argtypes = [P, P, i32, P, f64, P]
+        L.kvo_rope_rotate.argtypes = [P, i32, f64, i32]
+        L.kvo_decode_head_rope.argtypes = [P, P, i32, P, f64, f64, i32, P]
         L.kvo_snapkv_scores.argtypes = [P, i32, i32, i32, P]
         L.kvo_snapkv_scores_rows.argtypes = [P, i32, P, i32, i32, P]
         L.kvo_maxpool1d.argtypes = [P, i32, i32, P]
@@ -170,6 +172,26 @@ def dequant(view, T: int, D: int) -> np.ndarray:
     for t in range(T):
         for d in range(D):
             out[t, d] = L.kvo_dequant(ctypes.byref(v), t, d)
+    return out
+
+
+def rope_rotate(x: np.ndarray, base: float, pos: int) -> np.ndarray:
+    """x [D] rotated at position pos (half-split pairs), fp64."""
+    x = np.array(x, dtype=np.float64)
+    lib().kvo_rope_rotate(_p(x), x.shape[0], float(base), int(pos))
+    return x
+
+
+def decode_head_rope(kview, vview, T: int, q: np.ndarray, scale: float, base: float,
+                     q_pos: int) -> np.ndarray:
+    """fp64 attention output [D] with keys rotated at their slot index and the
+    query at q_pos (q fp32 [D], stored before the rotation)."""
+    kv, _k = kview
+    vv, _v = vview
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    out = np.empty(q.shape[-1], dtype=np.float64)
+    lib().kvo_decode_head_rope(ctypes.byref(kv), ctypes.byref(vv), T, _p(q), float(scale), float(base),
+                               int(q_pos), _p(out))
     return out
 
 

@@ -35,7 +35,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-from . import (CHANNEL, PLAIN, SYM4, TOK_AFFINE, decode_head, make_view, maxpool1d,
+from . import (CHANNEL, PLAIN, SYM4, TOK_AFFINE, decode_head, decode_head_rope, make_view, maxpool1d,
                quant_channel_group, quant_sym4, quant_tok_affine, snapkv_scores,
                snapkv_scores_rows, snapkv_select, widen)
 
@@ -222,11 +222,16 @@ class OracleCache:
         return kv, vv
 
     def decode(self, q: np.ndarray, q_dtype: str, sm_scale: float = 0.0,
-               heads=None, threads: int = 8) -> np.ndarray:
+               heads=None, threads: int = 8, rope_base: float | None = None,
+               q_pos: int = 0) -> np.ndarray:
         """fp64 outputs [B][Hq][D] for queries q [B][Hq][D] (stored dtype).
 
         ``heads`` optionally restricts the work to a list of (b, hq) pairs;
-        other rows are left as NaN.
+        other rows are left as NaN.  With ``rope_base`` keys and queries are
+        taken as stored before the rotary embedding: the key of slot t is
+        rotated at position t (its index in the compressed cache, [P1] "RoPE
+        caveat": re-positioning at the compressed slot index) and the query
+        at q_pos.
         """
         L = self.L
         B, Hq, D = q.shape
@@ -239,7 +244,10 @@ class OracleCache:
         def one(bh):
             b, hq = bh
             kv, vv = self.views(b, hq // gq)
-            out[b, hq] = decode_head(kv, vv, self.n_stored, qf[b, hq], scale)
+            if rope_base is None:
+                out[b, hq] = decode_head(kv, vv, self.n_stored, qf[b, hq], scale)
+            else:
+                out[b, hq] = decode_head_rope(kv, vv, self.n_stored, qf[b, hq], scale, rope_base, q_pos)
 
         with ThreadPoolExecutor(max(1, threads)) as ex:
             list(ex.map(one, todo))

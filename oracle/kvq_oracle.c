@@ -262,6 +262,60 @@ void kvo_decode_head(const kvo_view* K, const kvo_view* V, int T,
 }
 
 /* ------------------------------------------------------------------------- */
+/* RoPE on read ("StreamingLLM + KIVI", "RoPE caveat": keys stored before the  */
+/* rotation, rotated at their slot index in the compressed cache)             */
+/* ------------------------------------------------------------------------- */
+
+void kvo_rope_rotate(double* x, int D, double base, int pos)
+{
+    int half = D / 2;
+    for (int j = 0; j < half; ++j) {
+        double theta = pow(base, -2.0 * (double)j / (double)D);
+        double angle = (double)pos * theta;
+        double c = cos(angle), s = sin(angle);
+        double a = x[j], b = x[j + half];
+        x[j] = a * c - b * s;
+        x[j + half] = a * s + b * c;
+    }
+}
+
+void kvo_decode_head_rope(const kvo_view* K, const kvo_view* V, int T,
+                          const float* q, double scale, double base, int q_pos,
+                          double* out)
+{
+    int D = K->D;
+    for (int d = 0; d < D; ++d) out[d] = 0.0;
+    if (T <= 0) return;
+    double* qr = (double*)malloc(sizeof(double) * (size_t)D);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)D);
+    double* logit = (double*)malloc(sizeof(double) * (size_t)T);
+    for (int d = 0; d < D; ++d) qr[d] = (double)q[d];
+    kvo_rope_rotate(qr, D, base, q_pos);
+    double m = -INFINITY;
+    for (int t = 0; t < T; ++t) {
+        for (int d = 0; d < D; ++d) kr[d] = kvo_dequant(K, t, d);
+        kvo_rope_rotate(kr, D, base, t);
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += qr[d] * kr[d];
+        logit[t] = scale * acc;
+        if (logit[t] > m) m = logit[t];
+    }
+    double denom = 0.0;
+    for (int t = 0; t < T; ++t) {
+        logit[t] = exp(logit[t] - m);
+        denom += logit[t];
+    }
+    for (int t = 0; t < T; ++t) {
+        double p = logit[t] / denom;
+        for (int d = 0; d < D; ++d)
+            out[d] += p * kvo_dequant(V, t, d);
+    }
+    free(qr);
+    free(kr);
+    free(logit);
+}
+
+/* ------------------------------------------------------------------------- */
 /* SnapKV ([P2] "How it works")                                              */
 /* ------------------------------------------------------------------------- */
 

@@ -86,6 +86,19 @@ double kvo_dequant(const kvo_view* v, int t, int d);
 void kvo_decode_head(const kvo_view* K, const kvo_view* V, int T,
                      const float* q, double scale, double* out);
 
+/* ---- RoPE applied on read ("StreamingLLM + KIVI", "RoPE caveat") -------- *
+ * Keys stored before the rotary embedding are rotated when read, at their
+ * slot index in the compressed cache.  Rotation in the half-split form: for
+ * j < D/2 the pair (x_j, x_{j+D/2}) turns by the angle pos * base^(-2j/D).
+ * x: [D] fp64, rotated in place.                                             */
+void kvo_rope_rotate(double* x, int D, double base, int pos);
+
+/* kvo_decode_head with RoPE on read: the query is rotated at q_pos, the key
+ * of slot t at position t, then attention as kvo_decode_head (fp64).         */
+void kvo_decode_head_rope(const kvo_view* K, const kvo_view* V, int T,
+                          const float* q, double scale, double base, int q_pos,
+                          double* out);
+
 /* ---- D1: SnapKV observation-window scores (fp64) ------------------------ *
  * [P2] "How it works" step 1: softmax(K[-w:] K^T / sqrt(D)) mean-pooled over
  * the window; w clamped to S.  K: [S][D] fp32.  score: [S].                   */

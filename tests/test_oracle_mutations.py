@@ -45,6 +45,13 @@ MUTANTS = {
     "rows_mean_over_S": ("score[j] /= (double)n_rows;", "score[j] /= (double)S;"),
     # max-pool window one short on each side
     "pool_narrow": ("int r = (kernel - 1) / 2;", "int r = (kernel - 1) / 2 - 1;"),
+    # RoPE frequencies without the factor 2 in the exponent
+    "rope_theta": ("double theta = pow(base, -2.0 * (double)j / (double)D);",
+                   "double theta = pow(base, -(double)j / (double)D);"),
+    # RoPE: the first component rotated the wrong way
+    "rope_sign": ("x[j] = a * c - b * s;", "x[j] = a * c + b * s;"),
+    # keys rotated one position past their slot
+    "rope_key_pos": ("kvo_rope_rotate(kr, D, base, t);", "kvo_rope_rotate(kr, D, base, t + 1);"),
 }
 
 

@@ -582,3 +582,68 @@ def test_cache_positions_per_head_and_decode_appends():
     p.append(k[:, :, :1], v[:, :, :1])
     q = rng.standard_normal((B, 2 * H, D)).astype(np.float16)
     assert np.array_equal(c.decode(q, "f16"), p.decode(q, "f16"))
+
+
+def test_rope_rotation_pins():
+    """RoPE on read ([P1] "RoPE caveat"): half-split pairs (x_j, x_{j+D/2})
+    turned by pos * base^(-2j/D).  Pinned to closed forms for unit vectors,
+    to the same rotation written as complex multiplication, to the identity
+    at position 0, to norm preservation and to the relative-position
+    identity <rot(q, m), rot(k, n)> = <rot(q, m + c), rot(k, n + c)>."""
+    base = 10000.0
+    e0, e1 = np.eye(4)[0], np.eye(4)[1]
+    for p in (0, 1, 3, 17, 1000):
+        assert np.allclose(oracle.rope_rotate(e0, base, p), [math.cos(p), 0, math.sin(p), 0], rtol=0, atol=1e-15)
+        t1 = p * base ** -0.5
+        assert np.allclose(oracle.rope_rotate(e1, base, p), [0, math.cos(t1), 0, math.sin(t1)], rtol=0, atol=1e-15)
+    rng = np.random.default_rng(31)
+    D = 64
+    x = rng.standard_normal(D)
+    assert np.array_equal(oracle.rope_rotate(x, base, 0), x)
+    for p in (5, 123, 4095):
+        z = (x[:D // 2] + 1j * x[D // 2:]) * np.exp(1j * p * base ** (-2.0 * np.arange(D // 2) / D))
+        r = oracle.rope_rotate(x, base, p)
+        assert np.allclose(r, np.concatenate([z.real, z.imag]), rtol=0, atol=1e-12)
+        assert abs(np.linalg.norm(r) - np.linalg.norm(x)) < 1e-12
+    q, k = rng.standard_normal(D), rng.standard_normal(D)
+    ref = oracle.rope_rotate(q, base, 40) @ oracle.rope_rotate(k, base, 7)
+    for c in (1, 13, 500):
+        assert abs(oracle.rope_rotate(q, base, 40 + c) @ oracle.rope_rotate(k, base, 7 + c) - ref) < 1e-11
+
+
+def test_decode_rope_pins():
+    """Decode with keys rotated at their slot index and the query at q_pos.
+    Closed form: keys e_0 at every slot and query e_0 give logits
+    scale * cos(q_pos - t); one-hot values return the softmax weights.  Also
+    equal to the plain decode over keys and query rotated beforehand."""
+    from oracle.cache import Layout, OracleCache
+    D, T, base = 4, 4, 10000.0
+    L = Layout(1, 1, D, T, k_kind="plain", v_kind="plain", in_dtype="f32")
+    c = OracleCache(L)
+    k = np.zeros((1, 1, T, D), np.float32)
+    k[..., 0] = 1.0
+    v = np.eye(D, dtype=np.float32)[None, None]
+    c.append(k, v)
+    q = np.zeros((1, 1, D), np.float32)
+    q[..., 0] = 1.0
+    for q_pos in (3, 10):
+        out = c.decode(q, "f32", rope_base=base, q_pos=q_pos)[0, 0]
+        lg = np.array([math.cos(q_pos - t) for t in range(T)]) / math.sqrt(D)
+        w = np.exp(lg - lg.max())
+        assert np.allclose(out, w / w.sum(), rtol=0, atol=1e-15)
+    # against the plain decode of pre-rotated keys and query (fp32 storage of the rotation)
+    rng = np.random.default_rng(32)
+    D, T = 32, 50
+    L2 = Layout(1, 1, D, T, k_kind="plain", v_kind="plain", in_dtype="f32")
+    k = rng.standard_normal((1, 1, T, D)).astype(np.float32)
+    v = rng.standard_normal((1, 1, T, D)).astype(np.float32)
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    a = OracleCache(L2)
+    a.append(k, v)
+    kr = np.stack([oracle.rope_rotate(k[0, 0, t], base, t) for t in range(T)]).astype(np.float32)
+    b = OracleCache(L2)
+    b.append(kr[None, None], v)
+    qr = oracle.rope_rotate(q[0, 0], base, 60).astype(np.float32)[None, None]
+    ra = a.decode(q, "f32", rope_base=base, q_pos=60)
+    rb = b.decode(qr, "f32")
+    assert np.allclose(ra, rb, rtol=0, atol=1e-5)
