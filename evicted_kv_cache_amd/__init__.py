@@ -11,7 +11,8 @@ The functions carry the C ABI names (see include/kvq.h):
 ``kvq_snapkv_select_from_scores``, ``kvq_snapkv_pool_scores``,
 ``kvq_decode_workspace_bytes``, ``kvq_snapkv_workspace_bytes``,
 ``kvq_snapkv_workspace_bytes_ex``, ``kvq_quantize_append_at``,
-``kvq_snapkv_chunk_workspace_bytes``, ``kvq_snapkv_prefill_chunk``.
+``kvq_snapkv_chunk_workspace_bytes``, ``kvq_snapkv_prefill_chunk``,
+``kvq_rope_table``, ``kvq_decode_attention_rope``.
 """
 from __future__ import annotations
 
@@ -39,8 +40,8 @@ EXPORTS = ("kvq_cache_sizes", "kvq_cache_reset", "kvq_quantize_append",
            "kvq_snapkv_workspace_bytes", "kvq_snapkv_select",
            "kvq_snapkv_select_from_scores", "kvq_snapkv_workspace_bytes_ex",
            "kvq_snapkv_select_ex", "kvq_snapkv_pool_scores", "kvq_quantize_append_at",
-           "kvq_snapkv_chunk_workspace_bytes", "kvq_snapkv_prefill_chunk", "kvq_status_string",
-           "kvq_version")
+           "kvq_snapkv_chunk_workspace_bytes", "kvq_snapkv_prefill_chunk", "kvq_rope_table",
+           "kvq_decode_attention_rope", "kvq_status_string", "kvq_version")
 
 
 class KvqError(RuntimeError):
@@ -108,6 +109,8 @@ def lib():
         L.kvq_snapkv_select_ex.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         L.kvq_snapkv_pool_scores.argtypes = [P, P, i32, i32, i32, i32, P]
         L.kvq_quantize_append_at.argtypes = [P, P, P, P, i32, i32, P, i32, i32, P]
+        L.kvq_rope_table.argtypes = [P, i32, i32, f32, P]
+        L.kvq_decode_attention_rope.argtypes = [P, P, P, i32, i32, f32, P, i32, i32, P, P, sz, P]
         L.kvq_snapkv_chunk_workspace_bytes.restype = sz
         L.kvq_snapkv_chunk_workspace_bytes.argtypes = [P, i32, i32, i32, i32, i32]
         L.kvq_snapkv_prefill_chunk.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, sz, P]
@@ -269,6 +272,34 @@ def kvq_decode_attention(layout: Layout, cache: Cache, q, sm_scale: float = 0.0,
                                       ws.data_ptr(), ws.numel() * ws.element_size(),
                                       _stream(stream)),
            "kvq_decode_attention")
+    return out
+
+
+def kvq_rope_table(n_pos: int, head_dim: int, base: float = 10000.0, device="cuda", stream=None):
+    """(cos, sin) table [n_pos][head_dim/2][2] fp32 for RoPE on read."""
+    torch = _torch()
+    t = torch.empty((n_pos, head_dim // 2, 2), dtype=torch.float32, device=device)
+    _check(lib().kvq_rope_table(t.data_ptr(), n_pos, head_dim, float(base), _stream(stream)), "kvq_rope_table")
+    return t
+
+
+def kvq_decode_attention_rope(layout: Layout, cache: Cache, q, rope_table, q_pos: int,
+                              sm_scale: float = 0.0, out=None, ws=None, stream=None):
+    """kvq_decode_attention with keys rotated at their slot index and the
+    query (q [B][Hq][D], before the rotation) at q_pos."""
+    torch = _torch()
+    assert q.is_contiguous() and rope_table.is_contiguous() and rope_table.dtype == torch.float32
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(kvq_decode_workspace_bytes(layout, Hq), 16), dtype=torch.uint8, device=q.device)
+    cl = layout.c()
+    _check(lib().kvq_decode_attention_rope(ctypes.byref(cl), ctypes.byref(cache.c), q.data_ptr(), _qdtype(q),
+                                           Hq, float(sm_scale), rope_table.data_ptr(), int(rope_table.shape[0]),
+                                           int(q_pos), out.data_ptr(), ws.data_ptr(),
+                                           ws.numel() * ws.element_size(), _stream(stream)),
+           "kvq_decode_attention_rope")
     return out
 
 

@@ -249,17 +249,9 @@ size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_q_heads) {
     return decode_workspace_bytes(L->batch, n_q_heads, L->head_dim, L->capacity);
 }
 
-kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* c, const void* q,
-                                int32_t q_dtype, int32_t n_q_heads, float sm_scale, float* out,
-                                void* ws, size_t ws_bytes, void* stream) {
-    kvq_status st = check_layout(L);
-    if (st != KVQ_OK) return st;
-    if ((st = check_cache(L, c)) != KVQ_OK) return st;
-    if (!q || !out || !valid_dtype(q_dtype)) return KVQ_ERR_INVALID_ARG;
-    if (n_q_heads < 1 || n_q_heads % L->n_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
-    if (n_q_heads / L->n_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
-    if (!(sm_scale == sm_scale) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARG;
-    if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGNMENT;
+static kvq_status decode_impl(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
+                              int32_t n_q_heads, float sm_scale, const float* rope, int32_t q_pos, float* out,
+                              void* ws, size_t ws_bytes, void* stream) {
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int D = L->head_dim;
     if (c->n_stored == 0)
@@ -277,6 +269,7 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* c, const v
     a.k_kind = L->k_kind; a.k_bits = L->k_bits; a.k_group = L->k_group;
     a.v_kind = L->v_kind; a.v_bits = L->v_bits; a.v_group = L->v_group;
     a.in_dtype = L->in_dtype; a.q_dtype = q_dtype;
+    a.rope = rope; a.q_pos = q_pos;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
     a.scale_log2 = scale * 1.4426950408889634f;
     if (decode_fast_applies(a)) decode_fast_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
@@ -284,6 +277,48 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* c, const v
     a.ws_o = static_cast<float*>(ws);
     a.ws_ml = a.ws_o + (size_t)a.B * a.Hq * a.n_splits * D;
     return hip_status(launch_decode(a, s));
+}
+
+static kvq_status decode_check(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
+                               int32_t n_q_heads, float sm_scale, float* out) {
+    kvq_status st = check_layout(L);
+    if (st != KVQ_OK) return st;
+    if ((st = check_cache(L, c)) != KVQ_OK) return st;
+    if (!q || !out || !valid_dtype(q_dtype)) return KVQ_ERR_INVALID_ARG;
+    if (n_q_heads < 1 || n_q_heads % L->n_kv_heads != 0) return KVQ_ERR_INVALID_ARG;
+    if (n_q_heads / L->n_kv_heads > 8) return KVQ_ERR_UNSUPPORTED;
+    if (!(sm_scale == sm_scale) || isinf(sm_scale)) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(q) || !aligned16(out)) return KVQ_ERR_ALIGNMENT;
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* c, const void* q,
+                                int32_t q_dtype, int32_t n_q_heads, float sm_scale, float* out,
+                                void* ws, size_t ws_bytes, void* stream) {
+    kvq_status st = decode_check(L, c, q, q_dtype, n_q_heads, sm_scale, out);
+    if (st != KVQ_OK) return st;
+    return decode_impl(L, c, q, q_dtype, n_q_heads, sm_scale, nullptr, 0, out, ws, ws_bytes, stream);
+}
+
+kvq_status kvq_decode_attention_rope(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
+                                     int32_t n_q_heads, float sm_scale, const float* rope_table,
+                                     int32_t table_rows, int32_t q_pos, float* out, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    kvq_status st = decode_check(L, c, q, q_dtype, n_q_heads, sm_scale, out);
+    if (st != KVQ_OK) return st;
+    if (!rope_table || table_rows < 1 || q_pos < 0 || q_pos >= table_rows) return KVQ_ERR_INVALID_ARG;
+    if (c->n_stored > table_rows) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(rope_table)) return KVQ_ERR_ALIGNMENT;
+    return decode_impl(L, c, q, q_dtype, n_q_heads, sm_scale, rope_table, q_pos, out, ws, ws_bytes, stream);
+}
+
+kvq_status kvq_rope_table(float* table, int32_t n_pos, int32_t head_dim, float base, void* stream) {
+    if (!table || n_pos < 1) return KVQ_ERR_INVALID_ARG;
+    if (head_dim != 32 && head_dim != 64 && head_dim != 128)
+        return head_dim > 0 ? KVQ_ERR_UNSUPPORTED : KVQ_ERR_INVALID_ARG;
+    if (!(base > 1.0f) || isinf(base)) return KVQ_ERR_INVALID_ARG;
+    if (!aligned16(table)) return KVQ_ERR_ALIGNMENT;
+    return hip_status(launch_rope_table(table, n_pos, head_dim, (double)base, static_cast<hipStream_t>(stream)));
 }
 
 kvq_status kvq_evict_streaming(const kvq_layout* L, const kvq_cache* src, kvq_cache* dst,

@@ -157,6 +157,20 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
         q_s[h][d] = qv * a.scale_log2;
     }
     if (tid < kMaxGroup) { m_s[tid] = -INFINITY; l_s[tid] = 0.0f; alpha_s[tid] = 1.0f; }
+    constexpr int hd = D / 2;                 // RoPE pairs (x_j, x_{j + D/2})
+    const float2* rope = reinterpret_cast<const float2*>(a.rope);
+    if (rope) {
+        // the query turns at its own position
+        __syncthreads();
+        const float2* cs = rope + (int64_t)a.q_pos * hd;
+        for (int idx = tid; idx < gq * hd; idx += 256) {
+            const int h = idx / hd, j = idx - h * hd;
+            const float2 r = cs[j];
+            const float x0 = q_s[h][j], x1 = q_s[h][j + hd];
+            q_s[h][j] = x0 * r.x - x1 * r.y;
+            q_s[h][j + hd] = x0 * r.y + x1 * r.x;
+        }
+    }
 
     const int t_begin = split * a.split_len;
     const int t_end = min(a.T, t_begin + a.split_len);
@@ -201,6 +215,20 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
             }
         }
         __syncthreads();
+        if (rope) {
+            // keys turn at their slot index (the position in the compressed cache)
+            static_assert(kTile == 64, "token = idx & 63");
+            for (int idx = tid; idx < kTile * hd; idx += 256) {
+                const int t = idx & 63, j = idx >> 6;
+                if (t < nt) {
+                    const float2 r = rope[(int64_t)(t0 + t) * hd + j];
+                    const float x0 = k_s[j * kTile + t], x1 = k_s[(j + hd) * kTile + t];
+                    k_s[j * kTile + t] = x0 * r.x - x1 * r.y;
+                    k_s[(j + hd) * kTile + t] = x0 * r.y + x1 * r.x;
+                }
+            }
+            __syncthreads();
+        }
         {
             float lg0 = 0.0f, lg1 = 0.0f;
             const int h0 = slot, h1 = slot + 4;
@@ -328,6 +356,17 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, 
     out[row * D + d] = num / den;
 }
 
+// (cos, sin) of pos * base^(-2j/D) for pos < n_pos, j < D/2, computed in fp64.
+__global__ __launch_bounds__(256) void rope_table_kernel(float2* table, int n_pos, int hd, double base) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)n_pos * hd) return;
+    const int p = (int)(idx / hd), j = (int)(idx - (int64_t)p * hd);
+    const double theta = pow(base, -(double)j / (double)hd);
+    double sn, cs;
+    sincos((double)p * theta, &sn, &cs);
+    table[idx] = make_float2((float)cs, (float)sn);
+}
+
 __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
     const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) p[i] = 0.0f;
@@ -397,6 +436,13 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((unsigned)(a.B * a.Hq)), dim3(128), 0, s,
                        a.ws_o, a.ws_ml, a.out, a.D, a.n_splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* table, int n_pos, int D, double base, hipStream_t s) {
+    const int64_t n = (int64_t)n_pos * (D / 2);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       reinterpret_cast<float2*>(table), n_pos, D / 2, base);
     return hipGetLastError();
 }
 

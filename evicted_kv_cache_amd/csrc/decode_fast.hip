@@ -548,12 +548,14 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 
 }  // namespace
 
-// Fast path applies to: per-token 4-bit affine K and V, D = 128, 4 query
-// heads per kv-head, bf16 or fp16 queries.
+// Fast path applies to: per-token 4-bit affine or symmetric K and affine 4/8-bit
+// V, D = 128, 4 query heads per kv-head, bf16 or fp16 queries, no RoPE on read
+// (a per-key rotation would undo the factored scale).
 bool decode_fast_applies(const DecodeArgs& a) {
     const bool k_ok = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4;
     const bool v_ok = a.v_kind == KVQ_TOK_AFFINE && (a.v_bits == 4 || a.v_bits == 8);
-    return k_ok && v_ok && a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16);
+    return k_ok && v_ok && a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) &&
+           !a.rope;
 }
 
 // Split plan: one workgroup per (batch, kv-head) when that fills the chip

@@ -115,8 +115,12 @@ struct DecodeArgs {
     int in_dtype, q_dtype;
     float scale_log2;      // sm_scale * log2(e)
     int n_splits, split_len;
+    // RoPE on read (null: none): table [positions][D/2] of (cos, sin); the key
+    // of slot t is rotated at position t, the query at q_pos
+    const float* rope; int q_pos;
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_rope_table(float* table, int n_pos, int D, double base, hipStream_t s);
 bool decode_fast_applies(const DecodeArgs& a);
 void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);

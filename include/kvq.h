@@ -225,6 +225,31 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache
                                 float sm_scale, float* out,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* RoPE on read for StreamingLLM re-positioning ([P1] "RoPE caveat": keys
+ * are stored before the rotary embedding and rotated when read, at their
+ * slot index in the compressed cache, so sink and window keys sit at
+ * consecutive positions).  The rotation is the half-split form: for j < D/2
+ * the pair (x_j, x_{j+D/2}) turns by pos * base^(-2j/D).
+ *
+ * kvq_rope_table fills table (device [n_pos][D/2][2] fp32: cos, sin of each
+ * angle, computed in fp64).  base > 1 (10000 is the usual value).          */
+kvq_status kvq_rope_table(float* table, int32_t n_pos, int32_t head_dim, float base,
+                          void* stream);
+
+/* kvq_decode_attention with RoPE applied on read: the key of slot t is
+ * rotated at position t (its index in the compressed cache), the query
+ * (also given before the rotation) at q_pos -- for the newest token usually
+ * its own slot, n_stored - 1.  rope_table from kvq_rope_table with
+ * table_rows >= max(n_stored, q_pos + 1) rows.  Runs the LDS-tiled kernel
+ * for every layout.  Errors as kvq_decode_attention, plus
+ * KVQ_ERR_INVALID_ARG for a missing table, q_pos outside [0, table_rows) or
+ * n_stored > table_rows.                                                   */
+kvq_status kvq_decode_attention_rope(const kvq_layout* layout, const kvq_cache* cache,
+                                     const void* q, int32_t q_dtype, int32_t n_q_heads,
+                                     float sm_scale, const float* rope_table,
+                                     int32_t table_rows, int32_t q_pos, float* out, void* ws,
+                                     size_t ws_bytes, void* stream);
+
 /* StreamingLLM compaction ([P1] "Implementation", "StreamingLLM"): when
  * n_stored > sink + window, copy slots [0, sink) and the last `window` slots,
  * in order, from src into dst (out-of-place; dst has the same layout and its

@@ -303,6 +303,28 @@ def test_snapkv_prefill_chunk_validation_without_gpu():
     assert (si.n_kept, si.next_pos) == (7, 9)                                              # untouched on error
 
 
+def test_rope_validation_without_gpu():
+    lib = K.lib()
+    assert lib.kvq_rope_table(None, 10, 128, 10000.0, None) == K.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_rope_table(FAKE, 0, 128, 10000.0, None) == K.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_rope_table(FAKE, 10, 96, 10000.0, None) == K.KVQ_ERR_UNSUPPORTED
+    assert lib.kvq_rope_table(FAKE, 10, 128, 1.0, None) == K.KVQ_ERR_INVALID_ARG
+    assert lib.kvq_rope_table(MIS, 10, 128, 10000.0, None) == K.KVQ_ERR_ALIGNMENT
+    L = c5_layout(batch=1, capacity=100)
+    c = fake_cache(L, n_stored=50)
+
+    def call(table=FAKE, rows=64, q_pos=49, q=FAKE):
+        cl = L.c()
+        return lib.kvq_decode_attention_rope(ctypes.byref(cl), ctypes.byref(c), q, K.KVQ_BF16, 32, 0.0, table,
+                                             rows, q_pos, FAKE, FAKE, 1 << 30, None)
+    assert call(table=None) == K.KVQ_ERR_INVALID_ARG
+    assert call(q_pos=64) == K.KVQ_ERR_INVALID_ARG           # query position outside the table
+    assert call(q_pos=-1) == K.KVQ_ERR_INVALID_ARG
+    assert call(rows=49, q_pos=10) == K.KVQ_ERR_INVALID_ARG  # fewer table rows than stored slots
+    assert call(table=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert call(q=MIS) == K.KVQ_ERR_ALIGNMENT
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(K, "_lib", None)

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import evicted_kv_cache_amd as K
+import oracle
 import synth
 from oracle.cache import OracleCache
 
@@ -405,3 +406,55 @@ def test_quantize_codes_random_offsets_bf16():
     say("random offsets bf16")
     c, o = build_pair(pl, ol, xb, xb, "bf16")
     assert_same_state(c, o)
+
+
+# ------------------------------------------------ RoPE on read (re-positioning)
+
+def check_decode_rope(pl, c, o, q, qdt, table, q_pos, tol=TOL):
+    out = K.kvq_decode_attention_rope(pl, c, to_dev(q, qdt), table, q_pos)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = o.decode(q, qdt, rope_base=10000.0, q_pos=q_pos)
+    err = attn_err(got, ref)
+    say(f"  rope attention error {err:.3e} (q_pos {q_pos})")
+    assert np.all(np.isfinite(got)) and err <= tol, err
+
+
+def test_rope_table_matches_oracle_rotation():
+    """(cos, sin) of pos * base^(-2j/D) in fp32: each entry is the oracle's
+    rotation of the unit vector e_j at that position, to fp32 rounding."""
+    D, n = 128, 5000
+    say("rope table", D, n)
+    t = K.kvq_rope_table(n, D).cpu().numpy()
+    for p in (0, 1, 2, 77, 1023, 4999):
+        for j in (0, 1, 5, 31, 63):
+            e = np.zeros(D)
+            e[j] = 1.0
+            r = oracle.rope_rotate(e, 10000.0, p)
+            assert abs(t[p, j, 0] - r[j]) <= 1.2e-7 and abs(t[p, j, 1] - r[j + D // 2]) <= 1.2e-7, (p, j)
+
+
+@pytest.mark.parametrize("name", ["affine4_g64_bf16", "kivi4_llama3b", "sym4_centered", "affine8_d64", "plain_f32"])
+def test_decode_rope_on_read(name):
+    """Keys stored before the rotation, rotated at their slot index on read,
+    the query at the newest slot ([P1] "RoPE caveat", re-positioning)."""
+    w, pl, ol, k, v, q, bias, cfg = make_case(name)
+    say("rope decode", name)
+    c, o = build_pair(pl, ol, k, v, w.dtype, chunks=cfg.get("chunks"), k_bias=bias)
+    table = K.kvq_rope_table(pl.capacity + 8, pl.head_dim)
+    for q_pos in (c.n_stored - 1, c.n_stored + 3, 0):
+        check_decode_rope(pl, c, o, q, w.dtype, table, q_pos)
+
+
+def test_streaming_rope_repositioning_kivi_int8_tiny():
+    """StreamingLLM over 500 positions (sink 4 + window 256, KIVI int8): with
+    RoPE on read the sink and window keys sit at slots 0..259, the query at
+    the newest slot, so attention never sees a distance beyond the cache."""
+    w = synth.workload("kivi_int8_tiny")
+    k, v, q = gen(w, 1, 8, 500)
+    pl, ol = layouts(batch=1, n_kv_heads=8, head_dim=32, capacity=261, k_kind="kivi_ch", k_bits=8,
+                     k_group=32, v_kind="tok_affine", v_bits=8, v_group=32, in_dtype="f32")
+    say("stream rope kivi int8 500")
+    c, o = stream_pair(pl, ol, k, v, "f32", 4, 256)
+    table = K.kvq_rope_table(261, 32)
+    check_decode_rope(pl, c, o, q, "f32", table, c.n_stored - 1)
