@@ -29,11 +29,11 @@ kvq_status check_layout(const kvq_layout* L) {
     switch (L->k_kind) {
         case KVQ_PLAIN: break;
         case KVQ_KIVI_CH:
-            if (L->k_bits != 4 && L->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
+            if (L->k_bits != 2 && L->k_bits != 4 && L->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
             if (!is_pow2(L->k_group) || L->k_group < 8 || L->k_group > 128) return KVQ_ERR_UNSUPPORTED;
             break;
         case KVQ_TOK_AFFINE:
-            if (L->k_bits != 4 && L->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
+            if (L->k_bits != 2 && L->k_bits != 4 && L->k_bits != 8) return KVQ_ERR_UNSUPPORTED;
             if ((L->k_group != 32 && L->k_group != 64 && L->k_group != 128) || L->k_group > D)
                 return KVQ_ERR_UNSUPPORTED;
             break;
@@ -45,7 +45,7 @@ kvq_status check_layout(const kvq_layout* L) {
     switch (L->v_kind) {
         case KVQ_PLAIN: break;
         case KVQ_TOK_AFFINE:
-            if (L->v_bits != 4 && L->v_bits != 8) return KVQ_ERR_UNSUPPORTED;
+            if (L->v_bits != 2 && L->v_bits != 4 && L->v_bits != 8) return KVQ_ERR_UNSUPPORTED;
             if ((L->v_group != 32 && L->v_group != 64 && L->v_group != 128) || L->v_group > D)
                 return KVQ_ERR_UNSUPPORTED;
             break;

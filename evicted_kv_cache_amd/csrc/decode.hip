@@ -45,9 +45,13 @@ __device__ __forceinline__ void load8(const void* base, int64_t elem, int dt, fl
     }
 }
 
-// The 8 codes of channels 8c .. 8c+7 of a code row (4 or 8 bits per code).
+// The 8 codes of channels 8c .. 8c+7 of a code row (2, 4 or 8 bits per code).
 __device__ __forceinline__ void codes8(const uint8_t* row, int c, int bits, float u[8]) {
-    if (bits == 4) {
+    if (bits == 2) {
+        const uint32_t w = *reinterpret_cast<const uint16_t*>(row + 2 * c);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) u[i] = (float)((w >> (2 * i)) & 0x3u);
+    } else if (bits == 4) {
         const uint32_t w = *reinterpret_cast<const uint32_t*>(row + 4 * c);
 #pragma unroll
         for (int i = 0; i < 8; ++i) u[i] = (float)((w >> (4 * i)) & 0xFu);

@@ -45,7 +45,7 @@ __device__ __forceinline__ uint32_t affine_code(float x, float s, float z, float
 }
 
 // Row formats of the fused row kernel.
-enum RowFmt { kFmtNone = 0, kFmtPlain = 1, kFmtAff4 = 2, kFmtAff8 = 3, kFmtSym4 = 4 };
+enum RowFmt { kFmtNone = 0, kFmtPlain = 1, kFmtAff4 = 2, kFmtAff8 = 3, kFmtSym4 = 4, kFmtAff2 = 5 };
 
 constexpr int kEpl = 16;        // elements (channels) per lane in the row kernel
 constexpr int kRowIter = 2;     // row passes per block
@@ -162,7 +162,7 @@ __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t
         for (int k = 0; k < kEpl; ++k) y[k] = fminf(fmaxf(y[k], -8.0f), 7.0f) + 8.0f;
         if ((lane & 1) == 0) static_cast<uint16_t*>(r.meta)[drow * (D >> 5) + (lane >> 1)] = d16;
     } else {
-        constexpr int BITS = FMT == kFmtAff4 ? 4 : 8;
+        constexpr int BITS = FMT == kFmtAff4 ? 4 : FMT == kFmtAff2 ? 2 : 8;
         constexpr float top = (float)((1 << BITS) - 1);
         const int gsh = __builtin_ctz(r.group);       // group sizes are powers of two
         const int lpg = r.group / kEpl;               // lanes per group (2, 4 or 8)
@@ -213,7 +213,13 @@ __device__ __forceinline__ void quant16(const RowPart& r, float x[kEpl], int64_t
     }
     // y holds integral codes in [0, top]; v_cvt_pk_u8_f32 converts one to a
     // byte lane of a packed word
-    if constexpr (FMT == kFmtAff8) {
+    if constexpr (FMT == kFmtAff2) {
+        // 2-bit codes: element i of the lane at bits 2i of one word
+        uint32_t w = 0;
+#pragma unroll
+        for (int k = 0; k < kEpl; ++k) w |= (uint32_t)y[k] << (2 * k);
+        reinterpret_cast<uint32_t*>(r.codes)[drow * (D >> 4) + lane] = w;
+    } else if constexpr (FMT == kFmtAff8) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             uint32_t w = 0;
@@ -378,7 +384,12 @@ __global__ __launch_bounds__(64) void channel_close_kernel(ChannelQuantArgs a) {
         const uint32_t u0 = affine_code(val(tau0 + t, c0), s0f, z0f, r0f, top);
         const uint32_t u1 = affine_code(val(tau0 + t, c0 + 1), s1f, z1f, r1f, top);
         const int64_t slot = bh * a.cap + slot0 + t;
-        if constexpr (BITS == 4) {
+        if constexpr (BITS == 2) {
+            // four 2-bit codes per byte: the even lane of a channel-pair pair writes it
+            const uint32_t n = u0 | (u1 << 2);
+            const uint32_t m = (uint32_t)__shfl_xor((int)n, 1);
+            if ((dp & 1) == 0) static_cast<uint8_t*>(a.codes)[slot * (D >> 2) + (dp >> 1)] = (uint8_t)(n | (m << 4));
+        } else if constexpr (BITS == 4) {
             static_cast<uint8_t*>(a.codes)[slot * (D >> 1) + dp] = (uint8_t)(u0 | (u1 << 4));
         } else {
             static_cast<uint16_t*>(a.codes)[slot * (D >> 1) + dp] = (uint16_t)(u0 | (u1 << 8));
@@ -410,7 +421,7 @@ __global__ __launch_bounds__(256) void resid_store_kernel(ChannelQuantArgs a, in
 int row_fmt(int kind, int bits) {
     if (kind == KVQ_PLAIN) return kFmtPlain;
     if (kind == KVQ_TOK_SYM4) return kFmtSym4;
-    if (kind == KVQ_TOK_AFFINE) return bits == 4 ? kFmtAff4 : kFmtAff8;
+    if (kind == KVQ_TOK_AFFINE) return bits == 4 ? kFmtAff4 : bits == 2 ? kFmtAff2 : kFmtAff8;
     return kFmtNone;   // KIVI per-channel keys take the channel path
 }
 
@@ -439,6 +450,7 @@ hipError_t launch_append_fk(const RowAppendArgs& a, int fv, hipStream_t s) {
     switch (fv) {
         case kFmtPlain: return launch_append_fv<DT, FK, kFmtPlain>(a, s);
         case kFmtAff4: return launch_append_fv<DT, FK, kFmtAff4>(a, s);
+        case kFmtAff2: return launch_append_fv<DT, FK, kFmtAff2>(a, s);
         default: return launch_append_fv<DT, FK, kFmtAff8>(a, s);
     }
 }
@@ -451,6 +463,7 @@ hipError_t launch_append_dt(const RowAppendArgs& a, hipStream_t s) {
         case kFmtPlain: return launch_append_fk<DT, kFmtPlain>(a, fv, s);
         case kFmtAff4: return launch_append_fk<DT, kFmtAff4>(a, fv, s);
         case kFmtAff8: return launch_append_fk<DT, kFmtAff8>(a, fv, s);
+        case kFmtAff2: return launch_append_fk<DT, kFmtAff2>(a, fv, s);
         default: return launch_append_fk<DT, kFmtSym4>(a, fv, s);
     }
 }
@@ -459,7 +472,9 @@ template <int DT>
 hipError_t launch_channel_dt(const ChannelQuantArgs& a, hipStream_t s) {
     if (a.n_groups > 0) {
         dim3 grid((unsigned)a.n_groups, (unsigned)(a.B * a.H));
-        if (a.bits == 4)
+        if (a.bits == 2)
+            hipLaunchKernelGGL((channel_close_kernel<DT, 2>), grid, dim3(64), 0, s, a);
+        else if (a.bits == 4)
             hipLaunchKernelGGL((channel_close_kernel<DT, 4>), grid, dim3(64), 0, s, a);
         else
             hipLaunchKernelGGL((channel_close_kernel<DT, 8>), grid, dim3(64), 0, s, a);

@@ -91,7 +91,9 @@ typedef enum { KVQ_PLAIN = 0, KVQ_KIVI_CH = 1, KVQ_TOK_AFFINE = 2, KVQ_TOK_SYM4 
  *   symmetric block of 32: x' = x - bias; d = fp16(max(1e-5, max|x'| / 7));
  *       code u = clamp(rint(x' / d), -8, 7) + 8;  value (u - 8) * d.
  * Codes are stored packed: 8-bit codes one per byte; 4-bit codes two per
- * byte with element 2i in the low nibble of byte i.
+ * byte with element 2i in the low nibble of byte i; 2-bit codes (KIVI-2bit,
+ * [P2] "SnapKV-adapted" table; [P4] s.1 mx.quantize widths) four per byte,
+ * element 4i + r in bits [2r, 2r + 2) of byte i.
  */
 typedef struct kvq_layout {
     int32_t batch;        /* B >= 1 */
@@ -99,12 +101,12 @@ typedef struct kvq_layout {
     int32_t head_dim;     /* D in {32, 64, 128} */
     int32_t capacity;     /* slots per (batch, kv-head), >= 1 */
     int32_t k_kind;       /* kvq_kind */
-    int32_t k_bits;       /* 4 or 8 (KIVI_CH, TOK_AFFINE); 4 (TOK_SYM4); ignored for PLAIN */
+    int32_t k_bits;       /* 2, 4 or 8 (KIVI_CH, TOK_AFFINE); 4 (TOK_SYM4); ignored for PLAIN */
     int32_t k_group;      /* KIVI_CH: tokens per group (8..128, power of two);
                              TOK_AFFINE: channels per group (32, 64 or 128, dividing D);
                              TOK_SYM4: must be 32; PLAIN: ignored */
     int32_t v_kind;       /* KVQ_PLAIN or KVQ_TOK_AFFINE */
-    int32_t v_bits;       /* 4 or 8 (TOK_AFFINE) */
+    int32_t v_bits;       /* 2, 4 or 8 (TOK_AFFINE) */
     int32_t v_group;      /* channels per group (32, 64 or 128, dividing D) */
     int32_t in_dtype;     /* kvq_dtype of appended K/V, PLAIN storage and the KIVI residual */
     int32_t flags;        /* KVQ_CENTER_K | KVQ_TEST_CENTER_ANY | KVQ_POS_PER_HEAD */

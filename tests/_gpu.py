@@ -58,6 +58,10 @@ def unpack_codes(buf: torch.Tensor, B, H, cap, D, bits, bh=None) -> np.ndarray:
     if bits == 8:
         return raw.copy()
     out = np.empty((B, H, cap, D), dtype=np.uint8)
+    if bits == 2:
+        for r in range(4):
+            out[..., r::4] = (raw >> (2 * r)) & 0x3
+        return out
     out[..., 0::2] = raw & 0xF
     out[..., 1::2] = raw >> 4
     return out

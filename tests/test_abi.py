@@ -83,6 +83,8 @@ def test_cache_sizes_match_tinygpt_int8_value_bytes():
     (dict(head_dim=0), K.KVQ_ERR_INVALID_ARG),
     (dict(batch=0), K.KVQ_ERR_INVALID_ARG),
     (dict(k_bits=3), K.KVQ_ERR_UNSUPPORTED),
+    (dict(v_bits=6), K.KVQ_ERR_UNSUPPORTED),
+    (dict(k_kind="tok_sym4", k_bits=2, k_group=32), K.KVQ_ERR_UNSUPPORTED),
     (dict(k_group=48), K.KVQ_ERR_UNSUPPORTED),
     (dict(v_kind="tok_sym4"), K.KVQ_ERR_UNSUPPORTED),
     (dict(k_kind="kivi_ch", k_group=12), K.KVQ_ERR_UNSUPPORTED),
@@ -97,6 +99,15 @@ def test_layout_validation(kw, code):
     with pytest.raises(K.KvqError) as e:
         K.kvq_cache_sizes(c5_layout(**kw))
     assert e.value.status == code
+
+
+def test_two_bit_layouts_sizes():
+    """KIVI-2bit: four codes per byte for per-channel and per-token kinds."""
+    s = K.kvq_cache_sizes(c5_layout(k_kind="kivi_ch", k_bits=2, k_group=32, v_bits=2, v_group=32))
+    assert s.k_codes == s.v_codes == 64 * 8 * 32768 * 128 // 4
+    assert s.v_meta == 64 * 8 * 32768 * (128 // 32) * 4
+    s2 = K.kvq_cache_sizes(c5_layout(k_bits=2, v_bits=2, head_dim=32, k_group=32, v_group=32))
+    assert s2.k_codes == 64 * 8 * 32768 * 8
 
 
 def test_centering_gate_accepts_sym4_and_test_seam():

@@ -93,6 +93,16 @@ CASES = {
     "affine8_d64": dict(w="affine4_g64", B=3, H=2, T=600, Hq=4, D=64,
                         lay=dict(k_kind="tok_affine", k_bits=8, k_group=32, v_kind="tok_affine",
                                  v_bits=4, v_group=32, in_dtype="bf16")),
+    # KIVI-2bit: per-channel 2-bit K over 32-token groups, 2-bit V groups of 32
+    "kivi2_llama3b": dict(w="llama3b_kivi_int4", B=1, H=8, T=1000,
+                          lay=dict(k_kind="kivi_ch", k_bits=2, k_group=32, v_kind="tok_affine",
+                                   v_bits=2, v_group=32, in_dtype="f16"),
+                          chunks=[(0, 1), (1, 300), (300, 1000)]),
+    # 2-bit per-token K and V at head_dim 32 (rows of 8 bytes), fp32 inputs
+    "affine2_d32": dict(w="kivi_int8_tiny", B=2, H=8, T=333,
+                        lay=dict(k_kind="tok_affine", k_bits=2, k_group=32, v_kind="tok_affine",
+                                 v_bits=2, v_group=32, in_dtype="f32"),
+                        chunks=[(0, 100), (100, 333)]),
     # full-precision cache
     "plain_f32": dict(w="kivi_int8_tiny", B=1, H=8, T=300,
                       lay=dict(k_kind="plain", k_bits=4, k_group=32, v_kind="plain", v_bits=4,
@@ -302,7 +312,8 @@ def test_streaming_kivi_int8_tinygpt_500_positions():
     check_decode(pl, c, o, q, "f32")
 
 
-@pytest.mark.parametrize("name", ["affine4_g64_bf16", "sym4_centered", "kivi4_llama3b", "plain_f32"])
+@pytest.mark.parametrize("name", ["affine4_g64_bf16", "sym4_centered", "kivi4_llama3b", "plain_f32",
+                                  "kivi2_llama3b", "affine2_d32"])
 def test_batch_evict_parity(name):
     w, pl, ol, k, v, q, bias, cfg = make_case(name)
     say("batch evict", name)

@@ -647,3 +647,32 @@ def test_decode_rope_pins():
     ra = a.decode(q, "f32", rope_base=base, q_pos=60)
     rb = b.decode(qr, "f32")
     assert np.allclose(ra, rb, rtol=0, atol=1e-5)
+
+
+def test_two_bit_grids_and_error_bound():
+    """KIVI-2bit ([P2] "SnapKV-adapted" table; 2 bits per element): four
+    levels.  Lossless grids per token (groups of 32) and per channel (groups
+    of 32 tokens) give codes j with scale = range / 3 and zero = min; random
+    data stays within the O5 bound s/2 + |z - min| + 4 ulp."""
+    rng = np.random.default_rng(41)
+    j = rng.integers(0, 4, size=(40, 64))
+    j[:, 0], j[:, 1], j[:, 32], j[:, 33] = 0, 3, 0, 3
+    m0 = np.float32(-0.75)
+    x = (m0 + j.astype(np.float32) * np.float32(0.25)).astype(np.float32)
+    u, meta = oracle.quant_tok_affine(x, G=32, bits=2)
+    assert np.array_equal(u, j.astype(np.uint8))
+    assert np.all(oracle.f16_bits_to_f32(meta[..., 0]) == 0.25)
+    assert np.all(oracle.f16_bits_to_f32(meta[..., 1]) == m0)
+    xc = x[:32].copy()
+    xc[5, :], xc[9, :] = m0, m0 + np.float32(0.75)
+    uc, mc = oracle.quant_channel_group(xc, bits=2)
+    jc = np.round((xc - m0) / np.float32(0.25)).astype(np.uint8)
+    assert np.array_equal(uc, jc) and np.all(oracle.f16_bits_to_f32(mc[:, 0]) == 0.25)
+    y = rng.standard_normal((64, 32)).astype(np.float32)
+    u2, m2 = oracle.quant_tok_affine(y, G=32, bits=2)
+    assert u2.max() <= 3
+    s = oracle.f16_bits_to_f32(m2[..., 0]).astype(np.float64)[:, 0]
+    z = oracle.f16_bits_to_f32(m2[..., 1]).astype(np.float64)[:, 0]
+    xh = u2 * s[:, None] + z[:, None]
+    bound = s / 2 + np.abs(z - y.min(1)) + 4 * np.spacing(np.abs(y).max(1))
+    assert np.all(np.abs(xh - y).max(1) <= bound)
