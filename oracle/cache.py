@@ -254,6 +254,33 @@ class OracleCache:
         return out
 
 
+def prefill_attention(cache: "OracleCache", q: np.ndarray, q_dtype: str, sm_scale: float = 0.0,
+                      causal: bool = False, threads: int = 8) -> np.ndarray:
+    """Attention of n_q queries per head over the cache (a prefill chunk, [P4]
+    s.5's multi-query microbenchmark shape): fp64 outputs [B][Hq][n_q][D] for
+    q [B][Hq][n_q][D].  Each row is the decode of that query over the first T
+    slots, or with ``causal`` -- the chunk being the cache's last n_q slots --
+    over the first T - n_q + i + 1 slots for query i."""
+    L = cache.L
+    B, Hq, n_q, D = q.shape
+    T = cache.n_stored
+    gq = Hq // L.n_kv_heads
+    scale = sm_scale if sm_scale > 0 else 1.0 / math.sqrt(D)
+    qf = widen(q, q_dtype)
+    out = np.zeros((B, Hq, n_q, D), dtype=np.float64)
+
+    def one(bh):
+        b, hq = divmod(bh, Hq)
+        kv, vv = cache.views(b, hq // gq)
+        for i in range(n_q):
+            Ti = T - n_q + i + 1 if causal else T
+            out[b, hq, i] = decode_head(kv, vv, Ti, qf[b, hq, i], scale)
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(one, range(B * Hq)))
+    return out
+
+
 def snapkv(K: np.ndarray, V: np.ndarray, obs_window: int, n_sink: int, budget: int,
            threads: int = 8):
     """SnapKV over K, V [B][H][S][D] fp16.

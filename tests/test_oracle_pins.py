@@ -676,3 +676,32 @@ def test_two_bit_grids_and_error_bound():
     xh = u2 * s[:, None] + z[:, None]
     bound = s / 2 + np.abs(z - y.min(1)) + 4 * np.spacing(np.abs(y).max(1))
     assert np.all(np.abs(xh - y).max(1) <= bound)
+
+
+def test_prefill_attention_pins():
+    """Multi-query attention over the cache ([P4] s.5 prefill shape): brute
+    force with scipy's softmax and an explicit causal mask on the dequantized
+    values; one query reduces to the decode; the first causal row attends to
+    the prefix alone."""
+    from oracle.cache import Layout, OracleCache, prefill_attention
+    rng = np.random.default_rng(51)
+    B, H, G, T, D, n_q = 1, 2, 2, 40, 32, 6
+    L = Layout(B, H, D, T, k_kind="tok_affine", k_bits=4, k_group=32, v_kind="tok_affine", v_bits=8,
+               v_group=32, in_dtype="f32")
+    c = OracleCache(L)
+    k = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    c.append(k, v)
+    q = rng.standard_normal((B, H * G, n_q, D)).astype(np.float32)
+    for causal in (False, True):
+        out = prefill_attention(c, q, "f32", causal=causal)
+        for hq in range(H * G):
+            kv, vv = c.views(0, hq // G)
+            Kd, Vd = oracle.dequant(kv, T, D), oracle.dequant(vv, T, D)
+            lg = (q[0, hq].astype(np.float64) @ Kd.T) / math.sqrt(D)
+            if causal:
+                lg = np.where(np.arange(T)[None, :] <= (T - n_q + np.arange(n_q))[:, None], lg, -np.inf)
+            ref = scipy.special.softmax(lg, axis=-1) @ Vd
+            assert np.allclose(out[0, hq], ref, rtol=1e-12, atol=1e-12)
+    one = prefill_attention(c, q[:, :, :1], "f32")
+    assert np.array_equal(one[:, :, 0], c.decode(q[:, :, 0], "f32"))
