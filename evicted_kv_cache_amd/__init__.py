@@ -12,7 +12,8 @@ The functions carry the C ABI names (see include/kvq.h):
 ``kvq_decode_workspace_bytes``, ``kvq_snapkv_workspace_bytes``,
 ``kvq_snapkv_workspace_bytes_ex``, ``kvq_quantize_append_at``,
 ``kvq_snapkv_chunk_workspace_bytes``, ``kvq_snapkv_prefill_chunk``,
-``kvq_rope_table``, ``kvq_decode_attention_rope``.
+``kvq_rope_table``, ``kvq_decode_attention_rope``, ``kvq_prefill_workspace_bytes``,
+``kvq_prefill_attention``.
 """
 from __future__ import annotations
 
@@ -41,7 +42,8 @@ EXPORTS = ("kvq_cache_sizes", "kvq_cache_reset", "kvq_quantize_append",
            "kvq_snapkv_select_from_scores", "kvq_snapkv_workspace_bytes_ex",
            "kvq_snapkv_select_ex", "kvq_snapkv_pool_scores", "kvq_quantize_append_at",
            "kvq_snapkv_chunk_workspace_bytes", "kvq_snapkv_prefill_chunk", "kvq_rope_table",
-           "kvq_decode_attention_rope", "kvq_status_string", "kvq_version")
+           "kvq_decode_attention_rope", "kvq_prefill_workspace_bytes", "kvq_prefill_attention",
+           "kvq_status_string", "kvq_version")
 
 
 class KvqError(RuntimeError):
@@ -110,6 +112,9 @@ def lib():
         L.kvq_snapkv_pool_scores.argtypes = [P, P, i32, i32, i32, i32, P]
         L.kvq_quantize_append_at.argtypes = [P, P, P, P, i32, i32, P, i32, i32, P]
         L.kvq_rope_table.argtypes = [P, i32, i32, f32, P]
+        L.kvq_prefill_workspace_bytes.restype = sz
+        L.kvq_prefill_workspace_bytes.argtypes = [P, i32, i32]
+        L.kvq_prefill_attention.argtypes = [P, P, P, i32, i32, i32, f32, i32, P, P, sz, P]
         L.kvq_decode_attention_rope.argtypes = [P, P, P, i32, i32, f32, P, i32, i32, P, P, sz, P]
         L.kvq_snapkv_chunk_workspace_bytes.restype = sz
         L.kvq_snapkv_chunk_workspace_bytes.argtypes = [P, i32, i32, i32, i32, i32]
@@ -272,6 +277,30 @@ def kvq_decode_attention(layout: Layout, cache: Cache, q, sm_scale: float = 0.0,
                                       ws.data_ptr(), ws.numel() * ws.element_size(),
                                       _stream(stream)),
            "kvq_decode_attention")
+    return out
+
+
+def kvq_prefill_workspace_bytes(layout: Layout, n_q_heads: int, n_q: int) -> int:
+    cl = layout.c()
+    return int(lib().kvq_prefill_workspace_bytes(ctypes.byref(cl), n_q_heads, n_q))
+
+
+def kvq_prefill_attention(layout: Layout, cache: Cache, q, causal: bool = False, sm_scale: float = 0.0,
+                          out=None, ws=None, stream=None):
+    """q: [B][Hq][n_q][D] device tensor.  Returns out [B][Hq][n_q][D] fp32."""
+    torch = _torch()
+    assert q.is_contiguous() and q.dim() == 4
+    B, Hq, n_q, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, n_q, D), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(max(kvq_prefill_workspace_bytes(layout, Hq, n_q), 16), dtype=torch.uint8,
+                         device=q.device)
+    cl = layout.c()
+    _check(lib().kvq_prefill_attention(ctypes.byref(cl), ctypes.byref(cache.c), q.data_ptr(), _qdtype(q), Hq,
+                                       n_q, float(sm_scale), int(bool(causal)), out.data_ptr(), ws.data_ptr(),
+                                       ws.numel() * ws.element_size(), _stream(stream)),
+           "kvq_prefill_attention")
     return out
 
 

@@ -24,7 +24,8 @@ LIB = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_fast.hip", "evict.hip", "snapkv.hip"]
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_fast.hip", "prefill_attn.hip", "evict.hip",
+           "snapkv.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

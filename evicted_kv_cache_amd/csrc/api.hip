@@ -312,6 +312,54 @@ kvq_status kvq_decode_attention_rope(const kvq_layout* L, const kvq_cache* c, co
     return decode_impl(L, c, q, q_dtype, n_q_heads, sm_scale, rope_table, q_pos, out, ws, ws_bytes, stream);
 }
 
+// Workspace of kvq_prefill_attention: partials of the largest split plan a
+// cache of this capacity can need (the plan's split count grows with T).
+static size_t prefill_ws_bytes(const kvq_layout* L, int Hq, int n_q) {
+    const int ns = prefill_max_splits(L->batch, L->n_kv_heads, Hq, n_q, L->capacity);
+    return (size_t)L->batch * Hq * n_q * ns * (L->head_dim + 2) * sizeof(float);
+}
+
+size_t kvq_prefill_workspace_bytes(const kvq_layout* L, int32_t n_q_heads, int32_t n_q) {
+    if (check_layout(L) != KVQ_OK || n_q_heads < 1 || n_q < 1 || n_q_heads % L->n_kv_heads != 0) return 0;
+    return prefill_ws_bytes(L, n_q_heads, n_q);
+}
+
+kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
+                                 int32_t n_q_heads, int32_t n_q, float sm_scale, int32_t causal, float* out,
+                                 void* ws, size_t ws_bytes, void* stream) {
+    kvq_status st = decode_check(L, c, q, q_dtype, n_q_heads, sm_scale, out);
+    if (st != KVQ_OK) return st;
+    if (n_q < 1 || (causal != 0 && causal != 1)) return KVQ_ERR_INVALID_ARG;
+    if (causal && c->n_stored < n_q) return KVQ_ERR_INVALID_ARG;     // the chunk must be in the cache
+    const int64_t rows = (int64_t)L->batch * n_q_heads * n_q;
+    if (rows > INT32_MAX || L->batch > 65535) return KVQ_ERR_UNSUPPORTED;
+    const int64_t R = (int64_t)(n_q_heads / L->n_kv_heads) * n_q;
+    if ((int64_t)L->n_kv_heads * ((R + 255) / 256) > 65535) return KVQ_ERR_UNSUPPORTED;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = L->head_dim;
+    if (c->n_stored == 0) return hip_status(launch_zero_f32(out, (size_t)rows * D, s));
+    if (!ws || ws_bytes < prefill_ws_bytes(L, n_q_heads, n_q)) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(ws)) return KVQ_ERR_ALIGNMENT;
+
+    DecodeArgs a{};
+    a.k_codes = c->k_codes; a.k_meta = c->k_meta; a.k_resid = c->k_resid;
+    a.v_codes = c->v_codes; a.v_meta = c->v_meta; a.k_row = c->k_row;
+    a.q = q; a.out = out;
+    a.B = L->batch; a.Hkv = L->n_kv_heads; a.Hq = n_q_heads; a.D = D; a.cap = L->capacity;
+    a.T = c->n_stored; a.n_quant = c->n_quant; a.Gt = L->k_group;
+    a.k_kind = L->k_kind; a.k_bits = L->k_bits; a.k_group = L->k_group;
+    a.v_kind = L->v_kind; a.v_bits = L->v_bits; a.v_group = L->v_group;
+    a.in_dtype = L->in_dtype; a.q_dtype = q_dtype;
+    const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    int n_rb = 1;
+    prefill_plan(a.B, a.Hkv, a.Hq, n_q, a.T, &n_rb, &a.n_splits, &a.split_len);
+    if (a.n_splits > prefill_max_splits(a.B, a.Hkv, a.Hq, n_q, L->capacity)) return KVQ_ERR_WORKSPACE;
+    a.ws_o = static_cast<float*>(ws);
+    a.ws_ml = a.ws_o + (size_t)rows * a.n_splits * D;
+    return hip_status(launch_prefill_attention(a, n_q, n_rb, causal, s));
+}
+
 kvq_status kvq_rope_table(float* table, int32_t n_pos, int32_t head_dim, float base, void* stream) {
     if (!table || n_pos < 1) return KVQ_ERR_INVALID_ARG;
     if (head_dim != 32 && head_dim != 64 && head_dim != 128)

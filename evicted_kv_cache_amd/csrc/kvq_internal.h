@@ -121,6 +121,14 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_rope_table(float* table, int n_pos, int D, double base, hipStream_t s);
+// log-sum-exp merge of per-split partials ws_o [rows][ns][D], ws_ml [rows][ns][2]
+hipError_t launch_decode_combine(const float* ws_o, const float* ws_ml, float* out, int64_t rows, int D, int ns,
+                                 hipStream_t s);
+// Multi-query attention over the cache (DecodeArgs with T, splits and q as
+// [B][Hq][n_q][D]; out [B][Hq][n_q][D]).
+void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, int* n_rb, int* n_splits, int* split_len);
+int prefill_max_splits(int B, int Hkv, int Hq, int n_q, int T);
+hipError_t launch_prefill_attention(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s);
 bool decode_fast_applies(const DecodeArgs& a);
 void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);

@@ -1,0 +1,268 @@
+// prefill_attn.hip -- multi-query attention over the packed cache (gfx950).
+//
+// A prefill chunk of n_q queries per head attends to the compressed cache
+// ("Low-bit KV caches on MLX", s.5: the multi-query microbenchmark shape of
+// 128 queries with GQA 4:1 over 2K-64K cached tokens, where attention is a
+// dense contraction).  Per (batch, kv-head) the G * n_q query rows of the
+// head group share every key and value, so the work is two products per
+// 64-token tile on the matrix cores:
+//
+//   S^T = K Q^T      (64 tokens x 32 query rows per wave, K-dim = head_dim)
+//   O^T += V^T P^T   (head_dim x 32 query rows per wave, K-dim = 64 tokens)
+//
+// with v_mfma_f32_32x32x16_f16.  The workgroup dequantizes each tile once into
+// LDS as fp16 (keys token-major, values transposed) for all its waves.  Keys
+// and queries are each held as an fp16 pair (x_hi + x_lo, x_lo the rounding
+// residual), and the scores take K_hi Q_hi + K_lo Q_hi + K_hi Q_lo, so the
+// logits are fp32-accurate even where large keys (outlier channels) would
+// make a single fp16 rounding move the softmax; values and probabilities
+// enter the second product as single fp16 (their rounding stays relative to
+// the output).  The
+// online softmax runs in fp32 on the score accumulators, where each lane holds
+// one query column.  Tokens are handed to the second product in the order the
+// score accumulators hold them, and the value tile is stored in that order,
+// so probabilities go from registers to the matrix cores without a shuffle.
+// Splits over the tokens write unnormalized partials (m, l, o) that the
+// decode's log-sum-exp combine merges.
+#include <math.h>
+
+#include "dequant8.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPT = 64;          // tokens per tile
+constexpr int kWaves = 8;        // waves per workgroup, 32 query rows each
+constexpr int kRows = 32 * kWaves;
+constexpr int kPad = 8;          // halfs of padding per LDS row (bank spread)
+
+// Row of the 32x32 block held by accumulator element v of lane half kh.
+__device__ __forceinline__ int acc_row(int v, int kh) { return 8 * (v >> 2) + 4 * kh + (v & 3); }
+
+// Column of token t (0..63) in the transposed value tile.  For K-step s of
+// the second product, lane half kh supplies the probabilities of tokens
+// 16s + 8(j >> 2) + 4kh + (j & 3), j < 8 (the score accumulator layout);
+// storing that token at column 16s + 8kh + j lines the value rows up with them.
+__device__ __forceinline__ int v_col(int t) {
+    const int s = t >> 4, r = t & 15;
+    return 16 * s + 8 * ((r & 7) >> 2) + 4 * (r >> 3) + (r & 3);
+}
+
+__device__ __forceinline__ half8 to_half8(const float x[8]) {
+    half8 h;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) h[j] = (_Float16)x[j];
+    return h;
+}
+// fp16 pair with x = hi + lo to about 2^-22 relative
+__device__ __forceinline__ void split_half8(const float x[8], half8& hi, half8& lo) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        hi[j] = (_Float16)x[j];
+        lo[j] = (_Float16)(x[j] - (float)hi[j]);
+    }
+}
+
+// Block (split, hk * n_rb + rb, b): query rows [rb * kRows, +kRows) of kv-head
+// hk's group (row r = h * n_q + i: query head hk * G + h, query i), tokens of
+// the split.  Causal rows see slots t <= T - n_q + i.
+template <int KK, int VK, int D>
+__global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
+    constexpr int NK = D / 16;               // K-steps of the score product
+    constexpr int ND = D / 32;               // 32-row blocks of the output
+    constexpr int C8 = D / 8;                // 8-channel chunks per row
+    const int split = blockIdx.x;
+    const int hk = blockIdx.y / n_rb, rb = blockIdx.y - hk * n_rb;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int kh = lane >> 5, l32 = lane & 31;
+    const int G = a.Hq / a.Hkv;
+    const int R = G * n_q;
+    const int64_t bh = (int64_t)b * a.Hkv + hk;
+    const int T = a.T;
+
+    __shared__ __align__(16) _Float16 k_lds[kPT][D + kPad];      // keys, fp16 high part
+    __shared__ __align__(16) _Float16 kl_lds[kPT][D + kPad];     // keys, rounding residual
+    __shared__ __align__(16) _Float16 v_lds[D][kPT + kPad];
+
+    // this lane's query row: fragments for every K-step, scaled to base-2 logits
+    const int r = rb * kRows + wave * 32 + l32;
+    const bool row_ok = r < R;
+    const int h = row_ok ? r / n_q : 0, i = row_ok ? r - (r / n_q) * n_q : 0;
+    const int64_t grow = ((int64_t)b * a.Hq + hk * G + h) * n_q + i;     // global query row
+    half8 qf[NK], qfl[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+        float x[8] = {};
+        if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] *= a.scale_log2;
+        split_half8(x, qf[q], qfl[q]);
+    }
+    const int lim = causal ? T - n_q + i : T - 1;   // last visible slot
+
+    const int t_lo = split * a.split_len;
+    const int t_hi = min(T, t_lo + a.split_len);
+    float m = -INFINITY, l = 0.0f;
+    floatx16 o[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] = floatx16{};
+
+    for (int t0 = t_lo; t0 < t_hi; t0 += kPT) {
+        const int nt = min(kPT, t_hi - t0);
+        __syncthreads();                     // the previous tile's LDS reads are done
+        // dequantize the tile: item = (token, 8-channel chunk); rows past nt are zero
+        for (int it = tid; it < kPT * C8; it += kWaves * 64) {
+            const int t = it / C8, c = it - t * C8;
+            float xk[8] = {}, xv[8] = {};
+            if (t < nt) {
+                dq::k_values8<KK>(a, bh, t0 + t, c, xk);
+                dq::v_values8<VK>(a, bh, t0 + t, c, xv);
+            }
+            half8 kh8, kl8;
+            split_half8(xk, kh8, kl8);
+            *reinterpret_cast<half8*>(&k_lds[t][8 * c]) = kh8;
+            *reinterpret_cast<half8*>(&kl_lds[t][8 * c]) = kl8;
+            const int col = v_col(t);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v_lds[8 * c + j][col] = (_Float16)xv[j];
+        }
+        __syncthreads();
+
+        // S^T for this wave's 32 rows: two 32-token blocks
+        floatx16 s[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            s[blk] = floatx16{};
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                const half8 ka = *reinterpret_cast<const half8*>(&k_lds[blk * 32 + l32][q * 16 + kh * 8]);
+                const half8 kl = *reinterpret_cast<const half8*>(&kl_lds[blk * 32 + l32][q * 16 + kh * 8]);
+                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, qf[q], s[blk], 0, 0, 0);
+                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qfl[q], s[blk], 0, 0, 0);
+                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[q], s[blk], 0, 0, 0);
+            }
+        }
+        // mask (past the split or the row's last visible slot) and online softmax
+        float mt = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int tok = t0 + blk * 32 + acc_row(v, kh);
+                const float x = (tok < t_hi && tok <= lim) ? s[blk][v] : -INFINITY;
+                s[blk][v] = x;
+                mt = fmaxf(mt, x);
+            }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        const float m_new = fmaxf(m, mt);
+        const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // nothing visible yet
+        const float alpha = exp2f(m - m_use);
+        float ps = 0.0f;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = exp2f(s[blk][v] - m_use);
+                s[blk][v] = p;
+                ps += p;
+            }
+        ps += __shfl_xor(ps, 32);
+        l = l * alpha + ps;
+        m = m_new;
+#pragma unroll
+        for (int d = 0; d < ND; ++d) o[d] *= alpha;
+        // P^T fragments: K-step st takes accumulator elements 8 (st & 1) .. +7 of block st >> 1
+        half8 pf[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pf[st][j] = (_Float16)s[st >> 1][8 * (st & 1) + j];
+        // O^T += V^T P^T
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const half8 va = *reinterpret_cast<const half8*>(&v_lds[d * 32 + l32][16 * st + 8 * kh]);
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[st], o[d], 0, 0, 0);
+            }
+    }
+
+    // unnormalized partials of the split: o[dim], and (m, l) of the row
+    if (row_ok) {
+        const int ns = a.n_splits;
+        float* wo = a.ws_o + (grow * ns + split) * D;
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) wo[d * 32 + acc_row(v, kh)] = o[d][v];
+        if (kh == 0) {
+            a.ws_ml[(grow * ns + split) * 2 + 0] = m;
+            a.ws_ml[(grow * ns + split) * 2 + 1] = l;
+        }
+    }
+}
+
+template <int KK, int VK>
+hipError_t launch_prefill_kv(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
+    dim3 grid((unsigned)a.n_splits, (unsigned)(a.Hkv * n_rb), (unsigned)a.B);
+    switch (a.D) {
+        case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        default: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+    }
+    return hipGetLastError();
+}
+
+template <int KK>
+hipError_t launch_prefill_k(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
+    return a.v_kind == KVQ_PLAIN ? launch_prefill_kv<KK, KVQ_PLAIN>(a, n_q, n_rb, causal, s)
+                                 : launch_prefill_kv<KK, KVQ_TOK_AFFINE>(a, n_q, n_rb, causal, s);
+}
+
+}  // namespace
+
+// Split count before rounding the split length: about 512 workgroups, each
+// split at least two tiles long, at most 1024 splits.  The planned count
+// never exceeds it, and it grows with T, so its value at the capacity bounds
+// every plan of that cache (the workspace size).
+int prefill_max_splits(int B, int Hkv, int Hq, int n_q, int T) {
+    const int R = (Hq / Hkv) * n_q;
+    const int64_t units = (int64_t)B * Hkv * ((R + kRows - 1) / kRows);
+    int64_t ns = (512 + units - 1) / units;
+    const int64_t max_ns = ((int64_t)T + 2 * kPT - 1) / (2 * kPT);
+    if (ns > max_ns) ns = max_ns;
+    if (ns > 1024) ns = 1024;
+    if (ns < 1) ns = 1;
+    return (int)ns;
+}
+
+// Row blocks per kv-head and token splits (at most prefill_max_splits).
+void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, int* n_rb, int* n_splits, int* split_len) {
+    const int R = (Hq / Hkv) * n_q;
+    *n_rb = (R + kRows - 1) / kRows;
+    const int64_t ns = prefill_max_splits(B, Hkv, Hq, n_q, T);
+    int len = (int)(((int64_t)T + ns - 1) / ns);
+    len = ((len + kPT - 1) / kPT) * kPT;
+    *split_len = len;
+    *n_splits = (T + len - 1) / len;
+    if (*n_splits < 1) *n_splits = 1;
+}
+
+hipError_t launch_prefill_attention(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
+    hipError_t e;
+    switch (a.k_kind) {
+        case KVQ_PLAIN: e = launch_prefill_k<KVQ_PLAIN>(a, n_q, n_rb, causal, s); break;
+        case KVQ_KIVI_CH: e = launch_prefill_k<KVQ_KIVI_CH>(a, n_q, n_rb, causal, s); break;
+        case KVQ_TOK_AFFINE: e = launch_prefill_k<KVQ_TOK_AFFINE>(a, n_q, n_rb, causal, s); break;
+        default: e = launch_prefill_k<KVQ_TOK_SYM4>(a, n_q, n_rb, causal, s); break;
+    }
+    if (e != hipSuccess) return e;
+    return launch_decode_combine(a.ws_o, a.ws_ml, a.out, (int64_t)a.B * a.Hq * n_q, a.D, a.n_splits, s);
+}
+
+}  // namespace kvq

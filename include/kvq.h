@@ -227,6 +227,25 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache
                                 float sm_scale, float* out,
                                 void* ws, size_t ws_bytes, void* stream);
 
+/* Multi-query attention over the cache: a prefill chunk of n_q queries per
+ * head ([P4] s.5: the fused-attention microbenchmark shape, 128 queries with
+ * GQA 4:1 over a long cache, where attention is a dense contraction).  Row
+ * (b, hq, i) is the decode of query i of head hq over the cache's slots
+ * [0, T) (T = n_stored), or with causal = 1 -- the chunk's own rows being
+ * the cache's last n_q slots -- over slots [0, T - n_q + i].
+ *   q    device [B][Hq][n_q][D] (q_dtype), before any position rotation
+ *   out  device [B][Hq][n_q][D] fp32
+ *   ws   at least kvq_prefill_workspace_bytes(layout, Hq, n_q) bytes
+ * Keys and values are dequantized to fp16 per 64-token tile for the matrix
+ * cores; scores, softmax and accumulation are fp32.  Errors as
+ * kvq_decode_attention, plus KVQ_ERR_INVALID_ARG for n_q < 1, causal not
+ * 0/1 or a causal chunk longer than the cache; KVQ_ERR_UNSUPPORTED for
+ * B > 65535 or more than 65535 row blocks of 256 rows.                      */
+size_t kvq_prefill_workspace_bytes(const kvq_layout* layout, int32_t n_q_heads, int32_t n_q);
+kvq_status kvq_prefill_attention(const kvq_layout* layout, const kvq_cache* cache, const void* q,
+                                 int32_t q_dtype, int32_t n_q_heads, int32_t n_q, float sm_scale,
+                                 int32_t causal, float* out, void* ws, size_t ws_bytes, void* stream);
+
 /* RoPE on read for StreamingLLM re-positioning ([P1] "RoPE caveat": keys
  * are stored before the rotary embedding and rotated when read, at their
  * slot index in the compressed cache, so sink and window keys sit at

@@ -336,6 +336,27 @@ def test_rope_validation_without_gpu():
     assert call(q=MIS) == K.KVQ_ERR_ALIGNMENT
 
 
+def test_prefill_attention_validation_without_gpu():
+    lib = K.lib()
+    L = c5_layout(batch=1, capacity=32768)
+    ws = K.kvq_prefill_workspace_bytes(L, 32, 128)
+    assert ws >= 32 * 128 * (128 + 2) * 4                 # at least one split's partials
+    assert K.kvq_prefill_workspace_bytes(L, 30, 128) == 0  # Hq not a multiple of Hkv
+    c = fake_cache(L, n_stored=100)
+
+    def call(n_q=128, causal=0, ws_bytes=ws, q=FAKE, Hq=32):
+        cl = L.c()
+        return lib.kvq_prefill_attention(ctypes.byref(cl), ctypes.byref(c), q, K.KVQ_BF16, Hq, n_q, 0.0, causal,
+                                         FAKE, FAKE, ws_bytes, None)
+    assert call(n_q=0) == K.KVQ_ERR_INVALID_ARG
+    assert call(causal=2) == K.KVQ_ERR_INVALID_ARG
+    assert call(n_q=101, causal=1) == K.KVQ_ERR_INVALID_ARG     # the chunk is longer than the cache
+    assert call(ws_bytes=ws - 1) == K.KVQ_ERR_WORKSPACE
+    assert call(q=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert call(Hq=30) == K.KVQ_ERR_INVALID_ARG
+    assert call(Hq=80) == K.KVQ_ERR_UNSUPPORTED                 # more than 8 query heads per kv-head
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(K, "_lib", None)

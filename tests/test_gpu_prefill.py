@@ -1,0 +1,94 @@
+"""GPU parity for multi-query (prefill-chunk) attention over the packed cache
+([P4] s.5: the fused-attention microbenchmark shape -- 128 queries per head,
+GQA 4:1 -- where attention is a dense contraction on the matrix cores).
+
+Row (b, hq, i) is the oracle's fp64 decode of query i over the whole cache
+or, causally, over the slots up to the chunk's own row.  The kernel feeds the
+matrix cores fp16 keys, values, queries and probabilities with fp32
+accumulation; the bar is the attention tolerance, 2e-3 relative to each
+row's largest output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import evicted_kv_cache_amd as K
+import synth
+from oracle.cache import OracleCache, prefill_attention
+
+from _gpu import attn_err, layouts, say, to_dev
+from test_gpu_parity import build_pair, make_case
+
+pytestmark = pytest.mark.gpu
+TOL = 2e-3
+
+
+def gen_q(w, B, Hq, Hkv, n_q, seed):
+    """Queries [B][Hq][n_q][D] in the workload dtype, from the window-query streams."""
+    G = Hq // Hkv
+    wl = synth.workload(w.name, head_dim=w.head_dim, n_kv_heads=Hkv, n_q_heads=Hq, config_id=700 + seed)
+    npdt = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[w.dtype]
+    q = np.empty((B, Hq, n_q, w.head_dim), npdt)
+    for b in range(B):
+        for h in range(Hkv):
+            q[b, h * G:(h + 1) * G] = synth.query_window(wl, b, h, n_q, G)
+    return q
+
+
+@pytest.mark.parametrize("name,n_q,causal", [
+    ("affine4_g64_bf16", 37, False),     # ragged row block, two heads per block
+    ("affine4_g64_bf16", 128, True),     # the microbenchmark row count, causal chunk
+    ("kivi4_llama3b", 128, True),        # KIVI keys with an open residual group
+    ("sym4_centered", 64, False),
+    ("affine8_d64", 5, True),            # head_dim 64, GQA 2
+    ("plain_f32", 200, False),           # head_dim 32, fp32 cache
+    ("kivi2_llama3b", 33, True),
+])
+def test_prefill_attention_parity(name, n_q, causal):
+    w, pl, ol, k, v, _q, bias, cfg = make_case(name)
+    say("prefill attention", name, n_q, causal)
+    c, o = build_pair(pl, ol, k, v, w.dtype, cfg.get("chunks"), k_bias=bias)
+    Hq = cfg.get("Hq", pl.n_kv_heads * w.group)
+    q = gen_q(w, pl.batch, Hq, pl.n_kv_heads, n_q, seed=n_q)
+    out = K.kvq_prefill_attention(pl, c, to_dev(q, w.dtype), causal=causal)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = prefill_attention(o, q, w.dtype, causal=causal)
+    err = attn_err(got, ref)
+    say(f"  prefill attention error {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL, err
+
+
+def test_prefill_single_query_is_the_decode():
+    w, pl, ol, k, v, _q, bias, cfg = make_case("affine4_g64_bf16")
+    c, o = build_pair(pl, ol, k, v, w.dtype, cfg.get("chunks"))
+    q = gen_q(w, pl.batch, 32, 8, 1, seed=3)
+    say("prefill single query")
+    a = K.kvq_prefill_attention(pl, c, to_dev(q, w.dtype)).cpu().numpy()[:, :, 0]
+    d = K.kvq_decode_attention(pl, c, to_dev(np.ascontiguousarray(q[:, :, 0]), w.dtype)).cpu().numpy()
+    ref = o.decode(np.ascontiguousarray(q[:, :, 0]), w.dtype)
+    assert attn_err(a, ref) <= TOL and attn_err(d, ref) <= TOL
+
+
+def test_prefill_microbenchmark_shape_sampled():
+    """B = 1, 32 query / 8 kv-heads x 128, T = 32768 (4-bit affine g64 K and V,
+    bf16), 128 causal queries: sampled rows against the oracle."""
+    w = synth.workload("affine4_g64")
+    B, T, n_q = 1, 32768, 128
+    k, v, _ = synth.full(w, batch=B, threads=16)
+    pl, ol = layouts(batch=B, n_kv_heads=8, head_dim=128, capacity=T, k_kind="tok_affine", k_bits=4,
+                     k_group=64, v_kind="tok_affine", v_bits=4, v_group=64, in_dtype="bf16")
+    say("prefill attention full size", B, T, n_q)
+    c, o = build_pair(pl, ol, k, v, "bf16")
+    q = gen_q(w, B, 32, 8, n_q, seed=9)
+    out = K.kvq_prefill_attention(pl, c, to_dev(q, "bf16"), causal=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    from oracle import decode_head, widen
+    qf = widen(q, "bf16")
+    for hq, i in [(0, 0), (5, 17), (13, 64), (22, 100), (31, 127)]:
+        kv, vv = o.views(0, hq // 4)
+        ref = decode_head(kv, vv, T - n_q + i + 1, qf[0, hq, i], 1.0 / np.sqrt(128))
+        err = float(np.abs(got[0, hq, i] - ref).max() / np.abs(ref).max())
+        say(f"  row ({hq}, {i}) error {err:.3e}")
+        assert err <= TOL
