@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_MFMA_F16_TFLOPS = 2500.0      # dense fp16 matrix-core peak
 FAST_SRC = os.path.join(ROOT, "evicted_kv_cache_amd", "csrc", "decode_fast.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_affine4_g64_traffic.json")
 
@@ -129,7 +130,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--rows", default="ACDB", help="extra rows to time (subset of ACDB)")
+    ap.add_argument("--rows", default="ACDBE", help="extra rows to time (subset of ACDBE)")
     ap.add_argument("--mode", default="full", choices=["full", "decode", "copy"],
                     help="decode: only the timed decode steps (for counter runs); "
                          "copy: a plain 2 GiB device copy (bandwidth probe / counter calibration)")
@@ -317,6 +318,32 @@ def main():
                 "us": round(usb, 2), "algorithmic_bytes": nb, "GB/s": round(nb / usb / 1e3, 1),
                 "frac_hbm": round(nb / usb / 1e3 / PEAK_HBM_GBS, 4)}
             del gb, cb, outb, wsb
+
+    # ---- row E: multi-query (prefill-chunk) attention over the cache, the
+    # microbenchmark shape of 128 causal queries per head with 32/8 heads x 128
+    # over a 4-bit affine g64 cache; matrix-core bound (algorithmic FLOPs:
+    # 2 per multiply-add of QK^T and PV over the visible slots)
+    if "E" in args.rows:
+        we = synth.workload("affine4_g64")
+        n_q = 128
+        for Te in (2048, 32768):
+            ke, ve, _ = synth.full(we, T=Te, batch=1, threads=max(1, min(16, os.cpu_count() or 1)))
+            Le = K.Layout(**{**L.__dict__, "batch": 1, "capacity": Te})
+            ce = K.Cache(Le)
+            K.kvq_quantize_append(Le, ce, bf16(ke), bf16(ve))
+            del ke, ve
+            rng = np.random.default_rng(Te)
+            qe = torch.from_numpy(rng.standard_normal((1, Hq, n_q, D), dtype=np.float32)).to(dev).to(torch.bfloat16)
+            oe = torch.empty((1, Hq, n_q, D), dtype=torch.float32, device=dev)
+            wse = torch.empty(max(K.kvq_prefill_workspace_bytes(Le, Hq, n_q), 16), dtype=torch.uint8, device=dev)
+            mse = time_stream(lambda: K.kvq_prefill_attention(Le, ce, qe, causal=True, out=oe, ws=wse), 20, 3, torch)
+            flops = 4 * D * Hq * (n_q * (Te - n_q) + n_q * (n_q + 1) // 2)
+            tf = flops / mse / 1e9
+            rows[f"E_prefill_attention_T{Te}"] = {
+                "workload": f"{we.name} B=1 Hq/Hkv={Hq}/{Hkv} D={D} T={Te}, {n_q} causal queries per head",
+                "us": round(mse * 1e3, 2), "algorithmic_flops": flops, "TFLOP/s": round(tf, 1),
+                "frac_mfma_fp16": round(tf / PEAK_MFMA_F16_TFLOPS, 4)}
+            del ce, oe, wse
 
     cpu = None
     if not args.no_cpu_baseline:

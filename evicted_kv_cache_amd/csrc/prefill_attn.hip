@@ -52,6 +52,12 @@ __device__ __forceinline__ int v_col(int t) {
     return 16 * s + 8 * ((r & 7) >> 2) + 4 * (r >> 3) + (r & 3);
 }
 
+__device__ __forceinline__ int wave_min(int v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
+    return v;
+}
+
 __device__ __forceinline__ half8 to_half8(const float x[8]) {
     half8 h;
 #pragma unroll
@@ -85,9 +91,16 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     const int64_t bh = (int64_t)b * a.Hkv + hk;
     const int T = a.T;
 
-    __shared__ __align__(16) _Float16 k_lds[kPT][D + kPad];      // keys, fp16 high part
-    __shared__ __align__(16) _Float16 kl_lds[kPT][D + kPad];     // keys, rounding residual
-    __shared__ __align__(16) _Float16 v_lds[D][kPT + kPad];
+    // LDS: keys (fp16 high part and rounding residual, token-major) and the
+    // transposed value tile; after the last tile the same space holds each
+    // wave's output block for a row-major write-out
+    constexpr int kKeyHalfs = kPT * (D + kPad);
+    constexpr int kTileHalfs = 2 * kKeyHalfs + D * (kPT + kPad);
+    constexpr int kOutHalfs = kWaves * 32 * 33 * 2;          // [wave][32 rows][32 dims + pad] fp32
+    __shared__ __align__(16) _Float16 lds[kTileHalfs > kOutHalfs ? kTileHalfs : kOutHalfs];
+    _Float16 (*k_lds)[D + kPad] = reinterpret_cast<_Float16 (*)[D + kPad]>(lds);
+    _Float16 (*kl_lds)[D + kPad] = reinterpret_cast<_Float16 (*)[D + kPad]>(lds + kKeyHalfs);
+    _Float16 (*v_lds)[kPT + kPad] = reinterpret_cast<_Float16 (*)[kPT + kPad]>(lds + 2 * kKeyHalfs);
 
     // this lane's query row: fragments for every K-step, scaled to base-2 logits
     const int r = rb * kRows + wave * 32 + l32;
@@ -112,16 +125,38 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = floatx16{};
 
+    // Each thread owns kItems (token, 8-channel chunk) items of a tile.  The
+    // codes and metadata of tile t + 1 are fetched into registers before tile
+    // t is computed, so their memory latency overlaps the matrix work; they
+    // are unpacked into LDS after it.
+    constexpr int kItems = (kPT * C8 + kWaves * 64 - 1) / (kWaves * 64);
+    dq::Pre8 pk[kItems], pv[kItems];
+    auto fetch = [&](int tb) {
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const int it = tid + j * kWaves * 64;
+            const int t = it / C8, c = it - t * C8;
+            if (it < kPT * C8 && tb + t < t_hi) {
+                dq::k_fetch8<KK>(a, bh, tb + t, c, pk[j]);
+                dq::v_fetch8<VK>(a, bh, tb + t, c, pv[j]);
+            }
+        }
+    };
+    if (t_lo < t_hi) fetch(t_lo);
+
     for (int t0 = t_lo; t0 < t_hi; t0 += kPT) {
         const int nt = min(kPT, t_hi - t0);
         __syncthreads();                     // the previous tile's LDS reads are done
-        // dequantize the tile: item = (token, 8-channel chunk); rows past nt are zero
-        for (int it = tid; it < kPT * C8; it += kWaves * 64) {
+        // unpack the prefetched tile into LDS; rows past nt are zero
+#pragma unroll
+        for (int j = 0; j < kItems; ++j) {
+            const int it = tid + j * kWaves * 64;
+            if (it >= kPT * C8) break;
             const int t = it / C8, c = it - t * C8;
             float xk[8] = {}, xv[8] = {};
             if (t < nt) {
-                dq::k_values8<KK>(a, bh, t0 + t, c, xk);
-                dq::v_values8<VK>(a, bh, t0 + t, c, xv);
+                dq::k_finish8<KK>(a, bh, t0 + t, c, pk[j], xk);
+                dq::v_finish8<VK>(a, bh, t0 + t, c, pv[j], xv);
             }
             half8 kh8, kl8;
             split_half8(xk, kh8, kl8);
@@ -129,9 +164,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             *reinterpret_cast<half8*>(&kl_lds[t][8 * c]) = kl8;
             const int col = v_col(t);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v_lds[8 * c + j][col] = (_Float16)xv[j];
+            for (int jj = 0; jj < 8; ++jj) v_lds[8 * c + jj][col] = (_Float16)xv[jj];
         }
         __syncthreads();
+        if (t0 + kPT < t_hi) fetch(t0 + kPT);
 
         // S^T for this wave's 32 rows: two 32-token blocks
         floatx16 s[2];
@@ -147,35 +183,50 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
                 s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[q], s[blk], 0, 0, 0);
             }
         }
-        // mask (past the split or the row's last visible slot) and online softmax
+        // mask (past the split or the row's last visible slot) -- only tiles
+        // that reach either boundary for some row of the wave need it
+        const int lim_min = __builtin_amdgcn_readfirstlane(wave_min(row_ok ? lim : T - 1));
         float mt = -INFINITY;
+        if (t0 + kPT <= t_hi && t0 + kPT - 1 <= lim_min) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+            for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int tok = t0 + blk * 32 + acc_row(v, kh);
-                const float x = (tok < t_hi && tok <= lim) ? s[blk][v] : -INFINITY;
-                s[blk][v] = x;
-                mt = fmaxf(mt, x);
-            }
+                for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[blk][v]);
+        } else {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int tok = t0 + blk * 32 + acc_row(v, kh);
+                    const float x = (tok < t_hi && tok <= lim) ? s[blk][v] : -INFINITY;
+                    s[blk][v] = x;
+                    mt = fmaxf(mt, x);
+                }
+        }
+        // online softmax, base 2; the running max only moves when a row sees a
+        // larger logit, and only then are the output accumulators rescaled
         mt = fmaxf(mt, __shfl_xor(mt, 32));
         const float m_new = fmaxf(m, mt);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // nothing visible yet
-        const float alpha = exp2f(m - m_use);
         float ps = 0.0f;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                const float p = exp2f(s[blk][v] - m_use);
+                // v_exp_f32: arguments are <= 0, results below 2^-126 flush to 0
+                const float p = __builtin_amdgcn_exp2f(s[blk][v] - m_use);
                 s[blk][v] = p;
                 ps += p;
             }
         ps += __shfl_xor(ps, 32);
-        l = l * alpha + ps;
-        m = m_new;
+        if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+            const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+            l *= alpha;
 #pragma unroll
-        for (int d = 0; d < ND; ++d) o[d] *= alpha;
+            for (int d = 0; d < ND; ++d) o[d] *= alpha;
+        }
+        l += ps;
+        m = m_new;
         // P^T fragments: K-step st takes accumulator elements 8 (st & 1) .. +7 of block st >> 1
         half8 pf[4];
 #pragma unroll
@@ -192,18 +243,35 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             }
     }
 
-    // unnormalized partials of the split: o[dim], and (m, l) of the row
-    if (row_ok) {
-        const int ns = a.n_splits;
-        float* wo = a.ws_o + (grow * ns + split) * D;
+    // unnormalized partials of the split: o[dim] and (m, l) of each row.  The
+    // accumulators hold O^T (lane = row); each 32-dim block goes through LDS
+    // so that rows are written as contiguous 128-byte runs.
+    const int ns = a.n_splits;
+    float (*tr)[33] = reinterpret_cast<float (*)[33]>(lds) + wave * 32;      // [32 rows][32 dims + pad]
+    const int wr = lane >> 1, wh = lane & 1;                                // row, 16-dim half it writes
+    const int r_w = rb * kRows + wave * 32 + wr;
+    int64_t grow_w = 0;
+    if (r_w < R) {
+        const int hw = r_w / n_q, iw = r_w - hw * n_q;
+        grow_w = ((int64_t)b * a.Hq + hk * G + hw) * n_q + iw;
+    }
 #pragma unroll
-        for (int d = 0; d < ND; ++d)
+    for (int d = 0; d < ND; ++d) {
+        __syncthreads();                     // previous block's reads (and the last tile's) are done
 #pragma unroll
-            for (int v = 0; v < 16; ++v) wo[d * 32 + acc_row(v, kh)] = o[d][v];
-        if (kh == 0) {
-            a.ws_ml[(grow * ns + split) * 2 + 0] = m;
-            a.ws_ml[(grow * ns + split) * 2 + 1] = l;
+        for (int v = 0; v < 16; ++v) tr[l32][acc_row(v, kh)] = o[d][v];
+        __syncthreads();
+        if (r_w < R) {
+            float4* dst = reinterpret_cast<float4*>(a.ws_o + (grow_w * ns + split) * D + d * 32 + wh * 16);
+#pragma unroll
+            for (int k4 = 0; k4 < 4; ++k4)
+                dst[k4] = make_float4(tr[wr][wh * 16 + 4 * k4], tr[wr][wh * 16 + 4 * k4 + 1],
+                                      tr[wr][wh * 16 + 4 * k4 + 2], tr[wr][wh * 16 + 4 * k4 + 3]);
         }
+    }
+    if (row_ok && kh == 0) {
+        a.ws_ml[(grow * ns + split) * 2 + 0] = m;
+        a.ws_ml[(grow * ns + split) * 2 + 1] = l;
     }
 }
 
