@@ -136,7 +136,7 @@ def main():
                          "copy: a plain 2 GiB device copy (bandwidth probe / counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (asked for {args.gpus}); this build has no "
+        print(f"bench.py measures one GPU only (asked for {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
 
