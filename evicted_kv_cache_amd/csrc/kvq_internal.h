@@ -154,8 +154,10 @@ struct SnapArgs {
     // observation rows of (b, h): obs + (b * H + h) * obs_stride + r * D, r < n_rows
     const uint16_t* obs; int64_t obs_stride; int n_rows;
     float* scores; int32_t* kept; uint16_t* k_out; uint16_t* v_out;
-    float* stats;          // [B][H][n_chunks][n_rows][2]
-    int B, H, S, D, w, n_sink, budget, n_chunks;
+    float* stats;          // [B][H][n_stat][n_rows][2]
+    int B, H, S, D, w, n_sink, budget;
+    int n_chunks;          // 128-key chunks (scores grid)
+    int n_stat, stat_f, stat_reps;   // stats partials per row; set by the launcher
     int64_t kv_stride;     // elements between (b, h) slices of k and v
     int64_t out_stride;    // elements between (b, h) slices of k_out and v_out
     // optional: positions gathered with the rows (pos_in null: the row index)

@@ -8,19 +8,23 @@
 //
 // The w x S logit block is a dense fp16 contraction, computed with
 // v_mfma_f32_32x32x16_f16 in two passes over the keys: pass 1 (stats) gives
-// each window row's max and exp-sum per chunk of 128 keys (keys as MFMA rows,
-// so the per-window-row reductions stay inside a lane), pass 2 (scores)
-// merges the chunk stats and recomputes the logits with window rows as MFMA
-// rows, so each key's sum over window rows stays inside a lane.  Recomputing
-// the block is cheaper than storing the w x S fp32 logits.
+// each window row's max and exp-sum over a stats chunk (keys as MFMA rows, so
+// the per-window-row reductions stay inside a lane; a chunk is one to four
+// 128-key sub-chunks, more only past 32768 keys, so that at most 64 partials
+// per row are left), pass 2 (scores) merges the chunk stats and recomputes the
+// logits with window rows as MFMA rows, so each key's sum over window rows
+// stays inside a lane.  Recomputing the block is cheaper than storing the
+// w x S fp32 logits.
 //
 // Selection works on order-preserving 32-bit keys of the fp32 scores, one
-// workgroup per head: for S <= 16384 the keys stay in registers and the
+// workgroup per head: for S <= 32768 the keys stay in registers and the
 // threshold (k-th largest key) is found by nested 4096-bucket LDS histograms
-// over the candidate key range; longer sequences use an MSB-first radix
-// select (4 passes of 8 bits, LDS histograms).  Ties at the threshold go to the lower positions, and the
-// kept set is emitted in ascending order through block prefix scans.  No
-// floating-point atomics are used, so results are reproducible.
+// over the candidate key range, finished by ranking the keys of the
+// threshold bucket directly once it holds at most 64; longer sequences use an
+// MSB-first radix select (4 passes of 8 bits, LDS histograms).  Ties at the
+// threshold go to the lower positions, and the kept set is emitted in
+// ascending order through block prefix scans.  No floating-point atomics are
+// used, so results are reproducible.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -30,9 +34,11 @@ namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kChunk = 128;          // keys per block (4 waves x 32)
 constexpr int kMaxWindow = 128;
+constexpr int kStatTarget = 64;      // stats partials per window row (more only past S = 4 * 64 * 128)
 
 __device__ __forceinline__ half8 load_half8(const uint16_t* p) {
     return __builtin_bit_cast(half8, *reinterpret_cast<const uint4*>(p));
@@ -41,7 +47,12 @@ __device__ __forceinline__ half8 load_half8(const uint16_t* p) {
 // acc row index (within a 32-row tile) of accumulator element v for lane half kh.
 __device__ __forceinline__ int acc_row(int v, int kh) { return 8 * (v >> 2) + 4 * kh + (v & 3); }
 
-template <int D>
+// Pass 1: the (max, exp-sum) of every window row over one stats chunk of
+// F * a.stat_reps consecutive 128-key sub-chunks (each wave takes 32 keys of
+// a sub-chunk, keys as MFMA rows, so the per-window-row reductions stay
+// inside a lane).  Sub-chunks are merged online; long sequences take several
+// sub-chunks per workgroup so that the scores pass merges few partials.
+template <int D, int F>
 __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -51,52 +62,76 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
     const uint16_t* K = a.k + ((int64_t)b * a.H + h) * a.kv_stride;
     const uint16_t* O = a.obs + ((int64_t)b * a.H + h) * a.obs_stride;   // observation rows
     const float c = 1.4426950408889634f / sqrtf((float)D);
-    const int key_base = chunk * kChunk + wave * 32;
     __shared__ float sm[4][kMaxWindow], sl[4][kMaxWindow];
-
-    const int key = key_base + l32;
-    // this lane's key fragments, loaded once: all loads in flight together
     constexpr int NK = D / 16;
-    half8 A[NK];
+    constexpr int NT = kMaxWindow / 32;
+    // running (max, sum) of window row nt * 32 + l32, both lane halves alike
+    float M[NT], L[NT];
 #pragma unroll
-    for (int q = 0; q < NK; ++q) {
-        A[q] = half8{};
-        if (key < S) A[q] = load_half8(K + (int64_t)key * D + q * 16 + kh * 8);
-    }
-    for (int nt = 0; nt * 32 < wc; ++nt) {
-        const int wr = nt * 32 + l32;
-        half8 Bv[NK];
+    for (int nt = 0; nt < NT; ++nt) { M[nt] = -INFINITY; L[nt] = 0.0f; }
+
+    for (int rep = 0; rep < a.stat_reps; ++rep) {
+        const int sub0 = (chunk * a.stat_reps + rep) * F;     // first 128-key sub-chunk of this step
+        // this lane's key fragments of all F sub-chunks: all loads in flight together
+        half8 A[F][NK];
 #pragma unroll
-        for (int q = 0; q < NK; ++q) {
-            Bv[q] = half8{};
-            if (wr < wc) Bv[q] = load_half8(O + (int64_t)wr * D + q * 16 + kh * 8);
+        for (int f = 0; f < F; ++f) {
+            const int key = (sub0 + f) * kChunk + wave * 32 + l32;
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                A[f][q] = half8{};
+                if (key < S) A[f][q] = load_half8(K + (int64_t)key * D + q * 16 + kh * 8);
+            }
         }
-        floatx16 acc = {};
 #pragma unroll
-        for (int q = 0; q < NK; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[q], Bv[q], acc, 0, 0, 0);
-        // acc[v] = logit(key_base + acc_row(v, kh), window row wr)
-        float mx = -INFINITY;
+        for (int nt = 0; nt < NT; ++nt) {
+            if (nt * 32 >= wc) break;
+            const int wr = nt * 32 + l32;
+            half8 Bv[NK];
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            if (key_base + acc_row(v, kh) < S) mx = fmaxf(mx, acc[v] * c);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        float sum = 0.0f;
+            for (int q = 0; q < NK; ++q) {
+                Bv[q] = half8{};
+                if (wr < wc) Bv[q] = load_half8(O + (int64_t)wr * D + q * 16 + kh * 8);
+            }
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            if (key_base + acc_row(v, kh) < S) sum += exp2f(acc[v] * c - mx);
-        sum += __shfl_xor(sum, 32);
-        if (kh == 0 && wr < wc) { sm[wave][wr] = mx; sl[wave][wr] = sum; }
+            for (int f = 0; f < F; ++f) {
+                const int key_base = (sub0 + f) * kChunk + wave * 32;
+                if (key_base >= S) break;                  // uniform: the rest is past the end
+                floatx16 acc = {};
+#pragma unroll
+                for (int q = 0; q < NK; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[f][q], Bv[q], acc, 0, 0, 0);
+                // acc[v] = logit(key_base + acc_row(v, kh), window row wr)
+                float mx = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (key_base + acc_row(v, kh) < S) mx = fmaxf(mx, acc[v] * c);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float Mn = fmaxf(M[nt], mx);           // finite: key_base < S
+                float sum = 0.0f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (key_base + acc_row(v, kh) < S) sum += exp2f(acc[v] * c - Mn);
+                sum += __shfl_xor(sum, 32);
+                L[nt] = (M[nt] == -INFINITY ? 0.0f : L[nt] * exp2f(M[nt] - Mn)) + sum;
+                M[nt] = Mn;
+            }
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int wr = nt * 32 + l32;
+        if (kh == 0 && wr < wc) { sm[wave][wr] = M[nt]; sl[wave][wr] = L[nt]; }
     }
     __syncthreads();
     if (tid < wc) {
-        float M = -INFINITY;
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, sm[w][tid]);
-        float L = 0.0f;
+        float Mx = -INFINITY;
+        for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, sm[w][tid]);
+        float Lx = 0.0f;
         for (int w = 0; w < 4; ++w)
-            if (sm[w][tid] > -INFINITY) L += sl[w][tid] * exp2f(sm[w][tid] - M);
-        float* st = a.stats + ((((int64_t)b * a.H + h) * a.n_chunks + chunk) * wc + tid) * 2;
-        st[0] = M;
-        st[1] = L;
+            if (sm[w][tid] > -INFINITY) Lx += sl[w][tid] * exp2f(sm[w][tid] - Mx);
+        float* st = a.stats + ((((int64_t)b * a.H + h) * a.n_stat + chunk) * wc + tid) * 2;
+        st[0] = Mx;
+        st[1] = Lx;
     }
 }
 
@@ -111,8 +146,22 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     const uint16_t* O = a.obs + ((int64_t)b * a.H + h) * a.obs_stride;   // observation rows
     const float c = 1.4426950408889634f / sqrtf((float)D);
     __shared__ float Mrow[kMaxWindow], invL[kMaxWindow];
-    // this lane's key fragments, loaded before the stats merge so that both
-    // memory latencies overlap
+    // Loads in the order they are needed: the first batch of chunk stats
+    // (their merge runs while the key and window fragments are in flight),
+    // then this lane's key fragments, then the first window tile.
+    const int tpr = wc <= 32 ? 8 : (wc <= 64 ? 4 : 2);     // threads per window row in the merge
+    const int r = tid / tpr, j = tid % tpr;
+    const float* st = a.stats + (((int64_t)b * a.H + h) * a.n_stat * wc + r) * 2;
+    float2 ml[8];
+    auto load_stats = [&](int ch0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int ch = ch0 + u * tpr;
+            ml[u] = (r < wc && ch < a.n_stat) ? *reinterpret_cast<const float2*>(st + (int64_t)ch * wc * 2)
+                                              : make_float2(-INFINITY, 0.0f);
+        }
+    };
+    load_stats(j);
     const int key = chunk * kChunk + wave * 32 + l32;
     constexpr int NK = D / 16;
     half8 Bk[NK];
@@ -121,7 +170,6 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
         Bk[q] = half8{};
         if (key < S) Bk[q] = load_half8(K + (int64_t)key * D + q * 16 + kh * 8);
     }
-    // first window tile's fragments, also before the merge
     half8 A[NK];
 #pragma unroll
     for (int q = 0; q < NK; ++q) {
@@ -130,29 +178,24 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
     }
     {
         // merge the per-chunk (max, sum) of every window row: tpr threads per
-        // row stride over the chunks, then combine with lane shuffles
-        const int tpr = wc <= 32 ? 8 : (wc <= 64 ? 4 : 2);
-        const int r = tid / tpr, j = tid % tpr;
+        // row stride over the chunks (eight at a time, one common max per
+        // batch), then combine with lane shuffles
         float M = -INFINITY, L = 0.0f;
-        if (r < wc) {
-            const float* st = a.stats + (((int64_t)b * a.H + h) * a.n_chunks * wc + r) * 2;
-            // chunks j, j + tpr, ...: eight loads in flight before they are merged
-            for (int ch0 = j; ch0 < a.n_chunks; ch0 += 8 * tpr) {
-                float2 ml[8];
+        for (int ch0 = j;;) {
+            float mb = M;
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int ch = ch0 + u * tpr;
-                    ml[u] = ch < a.n_chunks ? *reinterpret_cast<const float2*>(st + (int64_t)ch * wc * 2)
-                                            : make_float2(-INFINITY, 0.0f);
-                }
+            for (int u = 0; u < 8; ++u) mb = fmaxf(mb, ml[u].x);
+            if (mb > -INFINITY) {
+                float Ln = M == -INFINITY ? 0.0f : L * exp2f(M - mb);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float m2 = ml[u].x, l2 = ml[u].y;
-                    const float Mn = fmaxf(M, m2);
-                    L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
-                    M = Mn;
-                }
+                for (int u = 0; u < 8; ++u)
+                    if (ml[u].x > -INFINITY) Ln += ml[u].y * exp2f(ml[u].x - mb);
+                L = Ln;
+                M = mb;
             }
+            ch0 += 8 * tpr;
+            if (ch0 >= a.n_stat) break;
+            load_stats(ch0);
         }
         for (int off = 1; off < tpr; off <<= 1) {
             const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(L, off);
@@ -381,7 +424,8 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
     }
     __shared__ __align__(16) uint32_t hist[kSelBuckets];
     __shared__ __align__(16) uint32_t tot16[4][16];
-    __shared__ uint32_t pick[2];
+    __shared__ uint32_t pick[2][3];             // bucket, keys above it, keys in it
+    __shared__ uint32_t cand[64], cand_rank[64], cand_n, fin[2];
     uint32_t key[KPT];
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     {
@@ -389,8 +433,17 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(sc), (short)0, S * 4, 0x00020000);
         uint32_t raw[KPT];
+        if ((S & 3) == 0) {
+            // every 16-byte group is wholly inside or wholly past the end
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (tid * KPT + i) * 4, 0, 0);
+            for (int i = 0; i < KPT; i += 4) {
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (tid * KPT + i) * 4, 0, 0);
+                raw[i] = x.x; raw[i + 1] = x.y; raw[i + 2] = x.z; raw[i + 3] = x.w;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) raw[i] = __builtin_amdgcn_raw_buffer_load_b32(rs, (tid * KPT + i) * 4, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const int j = tid * KPT + i;
@@ -408,6 +461,8 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
         kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
     }
     if (lane == 0) { tot16[0][wave] = kmin; tot16[1][wave] = kmax; }
+    if (tid < 64) cand_rank[tid] = 0u;
+    if (tid == 0) cand_n = 0u;
     __syncthreads();
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
@@ -417,13 +472,11 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
     const uint32_t range = hi - lo;               // <= 0xFFFFFFFE: real keys are >= 0x007FFFFF
     uint32_t lim = range + 1u;
     int shift = range == 0u ? 0 : max(0, 32 - __clz((int)range) - kSelBits);   // range < 2^(shift + kSelBits)
+    // Three barriers per level: after the histogram, inside the scan, after
+    // the pick.  Each thread reads (and then clears) only its own buckets, so
+    // clearing them for the next level needs no barrier of its own; the pick
+    // and the scan's wave totals alternate between two slots.
     for (int level = 0;; ++level) {
-        if (level > 0) {
-            // zero for this level (the previous level's reads ended at a barrier)
-#pragma unroll
-            for (int q = 0; q < kSelPer / 4; ++q) h4[tid * (kSelPer / 4) + q] = make_uint4(0u, 0u, 0u, 0u);
-            __syncthreads();
-        }
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
             const uint32_t off = key[i] - base;       // keys below base wrap to large values
@@ -437,6 +490,7 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
         for (int q = 0; q < kSelPer / 4; ++q) {
             const uint4 x = h4[top / 4 + q];
             cnt[4 * q] = x.x; cnt[4 * q + 1] = x.y; cnt[4 * q + 2] = x.z; cnt[4 * q + 3] = x.w;
+            h4[top / 4 + q] = make_uint4(0u, 0u, 0u, 0u);
         }
         uint32_t v = 0;
 #pragma unroll
@@ -447,18 +501,59 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
             uint32_t run = excl;
 #pragma unroll
             for (int q = kSelPer - 1; q >= 0; --q) {      // descending buckets
-                if (run < krem && run + cnt[q] >= krem) { pick[0] = (uint32_t)(top + q); pick[1] = run; }
+                if (run < krem && run + cnt[q] >= krem) {
+                    pick[level & 1][0] = (uint32_t)(top + q);
+                    pick[level & 1][1] = run;
+                    pick[level & 1][2] = cnt[q];
+                }
                 run += cnt[q];
             }
         }
         __syncthreads();
-        const uint32_t bucket = pick[0], above = pick[1];
+        const uint32_t bucket = pick[level & 1][0], above = pick[level & 1][1], n_in = pick[level & 1][2];
         base += bucket << shift;
         krem -= above;
         if (shift == 0) break;                    // the bucket is one key value
+        if (n_in <= 64u) {
+            // Few keys in the bucket [base, base + 2^shift): gather them and
+            // rank them directly.  Wave w compares every candidate with
+            // candidates 4w .. 4w+3; the counts (greater | equal << 16) meet
+            // in LDS, and tau is the candidate with greater < krem <= greater + equal.
+            const uint32_t width = 1u << shift;
+#pragma unroll
+            for (int i = 0; i < KPT; ++i) {
+                if (key[i] != 0u && key[i] - base < width) {
+                    const uint32_t slot = atomicAdd(&cand_n, 1u);
+                    if (slot < 64u) cand[slot] = key[i];
+                }
+            }
+            __syncthreads();
+            const uint32_t ci = (uint32_t)lane, j0 = 4u * (uint32_t)wave;
+            if (ci < n_in && j0 < n_in) {
+                const uint32_t x = cand[ci];
+                uint32_t gt = 0, eq = 0;
+#pragma unroll
+                for (uint32_t u = 0; u < 4; ++u) {
+                    if (j0 + u < n_in) {
+                        const uint32_t y = cand[j0 + u];
+                        gt += (y > x);
+                        eq += (y == x);
+                    }
+                }
+                atomicAdd(&cand_rank[ci], gt | (eq << 16));
+            }
+            __syncthreads();
+            if ((uint32_t)tid < n_in) {
+                const uint32_t r = cand_rank[tid], gt = r & 0xFFFFu, eq = r >> 16;
+                if (gt < krem && gt + eq >= krem) { fin[0] = cand[tid]; fin[1] = krem - gt; }
+            }
+            __syncthreads();
+            base = fin[0];
+            krem = fin[1];
+            break;
+        }
         lim = 1u << shift;
         shift = max(0, shift - kSelBits);
-        __syncthreads();                          // everyone has read pick / hist
     }
     const uint32_t tau = base;                    // k-th largest key; krem keys equal to it are kept
     uint32_t n_gt = 0, n_eq = 0;
@@ -470,7 +565,7 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
     }
     uint32_t tot;
     const uint32_t packed = n_gt | (n_eq << 16);
-    __syncthreads();                              // tot16 rows are reused below
+    // tot16[0] (the key minima) was last read before the first level
     const uint32_t excl = scan1024(packed, tot16[0], &tot);
     uint32_t a_run = excl & 0xFFFFu, e_run = excl >> 16;
 #pragma unroll
@@ -565,12 +660,29 @@ hipError_t launch_snapkv_pool(const float* in, float* out, int64_t rows, int S, 
     return hipGetLastError();
 }
 
+// Stats chunking: F 128-key sub-chunks per step and stat_reps steps per
+// workgroup, so that at most kStatTarget partials per window row are left
+// for the scores pass to merge (F <= 4 keeps the fragments in registers).
+static void stat_plan(SnapArgs& a) {
+    const int n128 = a.n_chunks;
+    int f = 1;
+    while (f < 4 && (n128 + f - 1) / f > kStatTarget) f *= 2;
+    const int per = f * kStatTarget;                          // sub-chunks covered by one rep
+    a.stat_f = f;
+    a.stat_reps = n128 > per ? (n128 + per - 1) / per : 1;
+    a.n_stat = (n128 + f * a.stat_reps - 1) / (f * a.stat_reps);
+}
+
 template <int D>
-static hipError_t launch_scores_d(const SnapArgs& a, hipStream_t s) {
-    dim3 grid((unsigned)a.n_chunks, (unsigned)a.H, (unsigned)a.B);
-    hipLaunchKernelGGL((snap_stats_kernel<D>), grid, dim3(256), 0, s, a);
+static hipError_t launch_scores_d(SnapArgs a, hipStream_t s) {
+    stat_plan(a);
+    dim3 sgrid((unsigned)a.n_stat, (unsigned)a.H, (unsigned)a.B);
+    if (a.stat_f == 1) hipLaunchKernelGGL((snap_stats_kernel<D, 1>), sgrid, dim3(256), 0, s, a);
+    else if (a.stat_f == 2) hipLaunchKernelGGL((snap_stats_kernel<D, 2>), sgrid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((snap_stats_kernel<D, 4>), sgrid, dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    dim3 grid((unsigned)a.n_chunks, (unsigned)a.H, (unsigned)a.B);
     hipLaunchKernelGGL((snap_scores_kernel<D>), grid, dim3(256), 0, s, a);
     return hipGetLastError();
 }
@@ -588,6 +700,9 @@ hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_
                            n_sink, budget, kept);
     else if (S <= kSelThreads * 16)
         hipLaunchKernelGGL((snap_select_reg_kernel<16>), dim3((unsigned)(B * H)), dim3(kSelThreads), 0, s, scores, S,
+                           n_sink, budget, kept);
+    else if (S <= kSelThreads * 32)
+        hipLaunchKernelGGL((snap_select_reg_kernel<32>), dim3((unsigned)(B * H)), dim3(kSelThreads), 0, s, scores, S,
                            n_sink, budget, kept);
     else
         hipLaunchKernelGGL(snap_select_radix_kernel, dim3((unsigned)(B * H)), dim3(1024), 0, s, scores, S,

@@ -84,6 +84,9 @@ def test_snapkv_defaults_full_size():
     (1, 2, 129, 64, 128, 0, 64),      # no sinks, widest window, one key past a chunk
     (1, 1, 1, 64, 4, 4, 4),           # a single key
     (3, 2, 1000, 128, 64, 4, 100),    # two MFMA row tiles
+    (1, 2, 10000, 128, 32, 4, 512),   # stats: 2 chunks of 128 keys per workgroup
+    (1, 1, 20000, 64, 40, 4, 512),    # stats: 4 chunks per workgroup, two row tiles
+    (1, 1, 40000, 32, 16, 4, 512),    # stats: two steps of 4 chunks; radix select
 ])
 def test_snapkv_edge_shapes(B, H, S, D, w, sink, budget):
     k, v = gen_kv(B, H, S, D, seed=S + D + w)
@@ -107,8 +110,12 @@ def test_snapkv_identical_keys_keep_the_first_positions():
     (8193, 4, 512, 0),        # 16 keys per thread
     (12000, 4, 700, 5),
     (16384, 4, 512, 0),
-    (20000, 4, 512, 0),       # radix select over global keys
+    (20000, 4, 512, 0),       # 32 keys per thread
     (20000, 0, 1000, 9),
+    (20001, 4, 512, 0),       # 32 keys per thread, 4-byte loads
+    (32768, 4, 512, 3),
+    (40000, 4, 512, 0),       # radix select over global keys
+    (40001, 0, 1000, 9),
 ])
 def test_select_from_scores_bit_exact(S, sink, budget, levels):
     rng = np.random.default_rng(S + budget + levels)
