@@ -11,13 +11,15 @@
 //   O^T += V^T P^T   (head_dim x 32 query rows per wave, K-dim = 64 tokens)
 //
 // with v_mfma_f32_32x32x16_f16.  The workgroup dequantizes each tile once into
-// LDS as fp16 (keys token-major, values transposed) for all its waves.  Keys
-// and queries are each held as an fp16 pair (x_hi + x_lo, x_lo the rounding
-// residual), and the scores take K_hi Q_hi + K_lo Q_hi + K_hi Q_lo, so the
-// logits are fp32-accurate even where large keys (outlier channels) would
-// make a single fp16 rounding move the softmax; values and probabilities
-// enter the second product as single fp16 (their rounding stays relative to
-// the output).  The
+// LDS as fp16 (keys token-major, values transposed) for all its waves, into
+// one of two buffers, so the next tile is unpacked while the current one is
+// computed.  Keys are held as an fp16 pair (x_hi + x_lo, x_lo the rounding
+// residual); an fp16 or bf16 query row is scaled by a power of two into fp16
+// exactly, so the scores take K_hi Q + K_lo Q (an fp32 query is a pair as
+// well: K_hi Q_hi + K_lo Q_hi + K_hi Q_lo).  The logits are fp32-accurate
+// even where large keys (outlier channels) would make a single fp16
+// rounding move the softmax; values and probabilities enter the second
+// product as single fp16 (their rounding stays relative to the output).  The
 // online softmax runs in fp32 on the score accumulators, where each lane holds
 // one query column.  Tokens are handed to the second product in the order the
 // score accumulators hold them, and the value tile is stored in that order,
@@ -76,7 +78,12 @@ __device__ __forceinline__ void split_half8(const float x[8], half8& hi, half8& 
 // Block (split, hk * n_rb + rb, b): query rows [rb * kRows, +kRows) of kv-head
 // hk's group (row r = h * n_q + i: query head hk * G + h, query i), tokens of
 // the split.  Causal rows see slots t <= T - n_q + i.
-template <int KK, int VK, int D>
+//
+// QX: the query is fp16 or bf16.  Each row is then scaled by a power of two
+// into fp16 exactly, the scores need only K_hi Q + K_lo Q, and the row's
+// factor (softmax scale times the power of two) is applied to the fp32
+// scores.  Otherwise (fp32 queries) the query is an fp16 pair as the keys are.
+template <int KK, int VK, int D, bool QX>
 __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
     constexpr int NK = D / 16;               // K-steps of the score product
     constexpr int ND = D / 32;               // 32-row blocks of the output
@@ -91,33 +98,60 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     const int64_t bh = (int64_t)b * a.Hkv + hk;
     const int T = a.T;
 
-    // LDS: keys (fp16 high part and rounding residual, token-major) and the
-    // transposed value tile; after the last tile the same space holds each
-    // wave's output block for a row-major write-out
+    // LDS: two tile buffers, each keys (fp16 high part and rounding residual,
+    // token-major) and the transposed value tile; after the last tile the
+    // same space holds each wave's output block for a row-major write-out
     constexpr int kKeyHalfs = kPT * (D + kPad);
     constexpr int kTileHalfs = 2 * kKeyHalfs + D * (kPT + kPad);
     constexpr int kOutHalfs = kWaves * 32 * 33 * 2;          // [wave][32 rows][32 dims + pad] fp32
-    __shared__ __align__(16) _Float16 lds[kTileHalfs > kOutHalfs ? kTileHalfs : kOutHalfs];
-    _Float16 (*k_lds)[D + kPad] = reinterpret_cast<_Float16 (*)[D + kPad]>(lds);
-    _Float16 (*kl_lds)[D + kPad] = reinterpret_cast<_Float16 (*)[D + kPad]>(lds + kKeyHalfs);
-    _Float16 (*v_lds)[kPT + kPad] = reinterpret_cast<_Float16 (*)[kPT + kPad]>(lds + 2 * kKeyHalfs);
+    __shared__ __align__(16) _Float16 lds[2 * kTileHalfs > kOutHalfs ? 2 * kTileHalfs : kOutHalfs];
+    auto k_lds = [&](int buf) { return reinterpret_cast<_Float16 (*)[D + kPad]>(lds + buf * kTileHalfs); };
+    auto kl_lds = [&](int buf) {
+        return reinterpret_cast<_Float16 (*)[D + kPad]>(lds + buf * kTileHalfs + kKeyHalfs);
+    };
+    auto v_lds = [&](int buf) {
+        return reinterpret_cast<_Float16 (*)[kPT + kPad]>(lds + buf * kTileHalfs + 2 * kKeyHalfs);
+    };
 
-    // this lane's query row: fragments for every K-step, scaled to base-2 logits
+    // this lane's query row: fragments for every K-step
     const int r = rb * kRows + wave * 32 + l32;
     const bool row_ok = r < R;
     const int h = row_ok ? r / n_q : 0, i = row_ok ? r - (r / n_q) * n_q : 0;
     const int64_t grow = ((int64_t)b * a.Hq + hk * G + h) * n_q + i;     // global query row
     half8 qf[NK], qfl[NK];
+    float qc = 1.0f;                         // factor from score accumulators to base-2 logits
+    if constexpr (QX) {
+        float amax = 0.0f;
 #pragma unroll
-    for (int q = 0; q < NK; ++q) {
-        float x[8] = {};
-        if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
+        for (int q = 0; q < NK; ++q) {
+            float x[8] = {};
+            if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] *= a.scale_log2;
-        split_half8(x, qf[q], qfl[q]);
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        int ex = 0;
+        if (amax > 0.0f) frexpf(amax, &ex);                  // amax in [2^(ex-1), 2^ex)
+        const float up = ldexpf(1.0f, 15 - ex);              // largest |q| -> [2^14, 2^15)
+        qc = ldexpf(a.scale_log2, ex - 15);
+#pragma unroll
+        for (int q = 0; q < NK; ++q) {
+            float x[8] = {};
+            if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) qf[q][j] = (_Float16)(x[j] * up);
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < NK; ++q) {
+            float x[8] = {};
+            if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] *= a.scale_log2;
+            split_half8(x, qf[q], qfl[q]);
+        }
     }
     const int lim = causal ? T - n_q + i : T - 1;   // last visible slot
-
     const int t_lo = split * a.split_len;
     const int t_hi = min(T, t_lo + a.split_len);
     float m = -INFINITY, l = 0.0f;
@@ -125,10 +159,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
 #pragma unroll
     for (int d = 0; d < ND; ++d) o[d] = floatx16{};
 
-    // Each thread owns kItems (token, 8-channel chunk) items of a tile.  The
-    // codes and metadata of tile t + 1 are fetched into registers before tile
-    // t is computed, so their memory latency overlaps the matrix work; they
-    // are unpacked into LDS after it.
+    // Each thread owns kItems (token, 8-channel chunk) items of a tile.  Tile
+    // t + 1 is unpacked into the other LDS buffer while tile t is computed,
+    // and the codes and metadata of tile t + 2 are fetched into registers
+    // behind it: one barrier per tile.
     constexpr int kItems = (kPT * C8 + kWaves * 64 - 1) / (kWaves * 64);
     dq::Pre8 pk[kItems], pv[kItems];
     auto fetch = [&](int tb) {
@@ -142,12 +176,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             }
         }
     };
-    if (t_lo < t_hi) fetch(t_lo);
-
-    for (int t0 = t_lo; t0 < t_hi; t0 += kPT) {
-        const int nt = min(kPT, t_hi - t0);
-        __syncthreads();                     // the previous tile's LDS reads are done
-        // unpack the prefetched tile into LDS; rows past nt are zero
+    // unpack the fetched tile at tb into buffer buf; rows past the split are zero
+    auto unpack = [&](int tb, int buf) {
+        const int nt = min(kPT, t_hi - tb);
+        _Float16 (*kd)[D + kPad] = k_lds(buf);
+        _Float16 (*kld)[D + kPad] = kl_lds(buf);
+        _Float16 (*vd)[kPT + kPad] = v_lds(buf);
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
             const int it = tid + j * kWaves * 64;
@@ -155,20 +189,31 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             const int t = it / C8, c = it - t * C8;
             float xk[8] = {}, xv[8] = {};
             if (t < nt) {
-                dq::k_finish8<KK>(a, bh, t0 + t, c, pk[j], xk);
-                dq::v_finish8<VK>(a, bh, t0 + t, c, pv[j], xv);
+                dq::k_finish8<KK>(a, bh, tb + t, c, pk[j], xk);
+                dq::v_finish8<VK>(a, bh, tb + t, c, pv[j], xv);
             }
             half8 kh8, kl8;
             split_half8(xk, kh8, kl8);
-            *reinterpret_cast<half8*>(&k_lds[t][8 * c]) = kh8;
-            *reinterpret_cast<half8*>(&kl_lds[t][8 * c]) = kl8;
+            *reinterpret_cast<half8*>(&kd[t][8 * c]) = kh8;
+            *reinterpret_cast<half8*>(&kld[t][8 * c]) = kl8;
             const int col = v_col(t);
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) v_lds[8 * c + jj][col] = (_Float16)xv[jj];
+            for (int jj = 0; jj < 8; ++jj) vd[8 * c + jj][col] = (_Float16)xv[jj];
         }
-        __syncthreads();
-        if (t0 + kPT < t_hi) fetch(t0 + kPT);
+    };
+    if (t_lo < t_hi) {
+        fetch(t_lo);
+        unpack(t_lo, 0);
+        if (t_lo + kPT < t_hi) fetch(t_lo + kPT);
+    }
+    __syncthreads();
 
+    const int lim_min = __builtin_amdgcn_readfirstlane(wave_min(row_ok ? lim : T - 1));
+    int buf = 0;
+    for (int t0 = t_lo; t0 < t_hi; t0 += kPT, buf ^= 1) {
+        _Float16 (*kd)[D + kPad] = k_lds(buf);
+        _Float16 (*kld)[D + kPad] = kl_lds(buf);
+        _Float16 (*vd)[kPT + kPad] = v_lds(buf);
         // S^T for this wave's 32 rows: two 32-token blocks
         floatx16 s[2];
 #pragma unroll
@@ -176,29 +221,36 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             s[blk] = floatx16{};
 #pragma unroll
             for (int q = 0; q < NK; ++q) {
-                const half8 ka = *reinterpret_cast<const half8*>(&k_lds[blk * 32 + l32][q * 16 + kh * 8]);
-                const half8 kl = *reinterpret_cast<const half8*>(&kl_lds[blk * 32 + l32][q * 16 + kh * 8]);
+                const half8 ka = *reinterpret_cast<const half8*>(&kd[blk * 32 + l32][q * 16 + kh * 8]);
+                const half8 kl = *reinterpret_cast<const half8*>(&kld[blk * 32 + l32][q * 16 + kh * 8]);
                 s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, qf[q], s[blk], 0, 0, 0);
-                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qfl[q], s[blk], 0, 0, 0);
+                if constexpr (!QX) s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qfl[q], s[blk], 0, 0, 0);
                 s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[q], s[blk], 0, 0, 0);
             }
         }
+        // the next tile goes into the other buffer while the products run
+        if (t0 + kPT < t_hi) {
+            unpack(t0 + kPT, buf ^ 1);
+            if (t0 + 2 * kPT < t_hi) fetch(t0 + 2 * kPT);
+        }
         // mask (past the split or the row's last visible slot) -- only tiles
         // that reach either boundary for some row of the wave need it
-        const int lim_min = __builtin_amdgcn_readfirstlane(wave_min(row_ok ? lim : T - 1));
         float mt = -INFINITY;
         if (t0 + kPT <= t_hi && t0 + kPT - 1 <= lim_min) {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[blk][v]);
+                for (int v = 0; v < 16; ++v) {
+                    if constexpr (QX) s[blk][v] *= qc;
+                    mt = fmaxf(mt, s[blk][v]);
+                }
         } else {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int tok = t0 + blk * 32 + acc_row(v, kh);
-                    const float x = (tok < t_hi && tok <= lim) ? s[blk][v] : -INFINITY;
+                    const float x = (tok < t_hi && tok <= lim) ? s[blk][v] * qc : -INFINITY;
                     s[blk][v] = x;
                     mt = fmaxf(mt, x);
                 }
@@ -238,9 +290,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         for (int d = 0; d < ND; ++d)
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                const half8 va = *reinterpret_cast<const half8*>(&v_lds[d * 32 + l32][16 * st + 8 * kh]);
+                const half8 va = *reinterpret_cast<const half8*>(&vd[d * 32 + l32][16 * st + 8 * kh]);
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[st], o[d], 0, 0, 0);
             }
+        __syncthreads();                     // this buffer is read, the other one written
     }
 
     // unnormalized partials of the split: o[dim] and (m, l) of each row.  The
@@ -257,7 +310,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     }
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-        __syncthreads();                     // previous block's reads (and the last tile's) are done
+        if (d > 0) __syncthreads();          // previous block's reads are done (the loop ended in one)
 #pragma unroll
         for (int v = 0; v < 16; ++v) tr[l32][acc_row(v, kh)] = o[d][v];
         __syncthreads();
@@ -275,15 +328,21 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     }
 }
 
-template <int KK, int VK>
-hipError_t launch_prefill_kv(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
+template <int KK, int VK, bool QX>
+hipError_t launch_prefill_kvq(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)(a.Hkv * n_rb), (unsigned)a.B);
     switch (a.D) {
-        case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
-        case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
-        default: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32, QX>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64, QX>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        default: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
     }
     return hipGetLastError();
+}
+
+template <int KK, int VK>
+hipError_t launch_prefill_kv(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
+    return a.q_dtype == KVQ_F32 ? launch_prefill_kvq<KK, VK, false>(a, n_q, n_rb, causal, s)
+                                : launch_prefill_kvq<KK, VK, true>(a, n_q, n_rb, causal, s);
 }
 
 template <int KK>
