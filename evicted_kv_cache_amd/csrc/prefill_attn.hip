@@ -75,6 +75,22 @@ __device__ __forceinline__ void split_half8(const float x[8], half8& hi, half8& 
     }
 }
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Loads of `bytes` (2, 4 or 8) bytes at a buffer offset; past the buffer's end they read zero.
+__device__ __forceinline__ void bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t off, int bytes, dq::Pre8& p) {
+    if (bytes == 2) {
+        p.c0 = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    } else if (bytes == 4) {
+        p.c0 = __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    } else {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+        p.c0 = w.x; p.c1 = w.y;
+    }
+}
+
 // Block (split, hk * n_rb + rb, b): query rows [rb * kRows, +kRows) of kv-head
 // hk's group (row r = h * n_q + i: query head hk * G + h, query i), tokens of
 // the split.  Causal rows see slots t <= T - n_q + i.
@@ -165,14 +181,50 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     // behind it: one barrier per tile.
     constexpr int kItems = (kPT * C8 + kWaves * 64 - 1) / (kWaves * 64);
     dq::Pre8 pk[kItems], pv[kItems];
+    // Per-token layouts put every item of a tile at a fixed byte offset from
+    // the tile's first slot: each tile only rebuilds buffer resources (scalar
+    // work) sized to its valid rows.
+    constexpr bool kTokK = KK == KVQ_TOK_AFFINE || KK == KVQ_TOK_SYM4;
+    constexpr bool kTokV = VK == KVQ_TOK_AFFINE;
+    const int kb = KK == KVQ_TOK_SYM4 ? 4 : a.k_bits;                 // code bytes per 8 channels
+    const int k_row_b = D * kb / 8;
+    const int k_meta_b = KK == KVQ_TOK_SYM4 ? (D / 32) * 2 : (kTokK ? (D / a.k_group) * 4 : 0);
+    const int v_row_b = D * a.v_bits / 8;
+    const int v_meta_b = kTokV ? (D / a.v_group) * 4 : 0;
     auto fetch = [&](int tb) {
+        const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(min(kPT, t_hi - tb));
+        const int64_t slot0 = bh * a.cap + tb;
+        if constexpr (kTokK) {
+            const __amdgpu_buffer_rsrc_t rk = rsrc(static_cast<const uint8_t*>(a.k_codes) + slot0 * k_row_b, nt * k_row_b);
+            const __amdgpu_buffer_rsrc_t rm = rsrc(static_cast<const uint8_t*>(a.k_meta) + slot0 * k_meta_b, nt * k_meta_b);
 #pragma unroll
-        for (int j = 0; j < kItems; ++j) {
-            const int it = tid + j * kWaves * 64;
-            const int t = it / C8, c = it - t * C8;
-            if (it < kPT * C8 && tb + t < t_hi) {
-                dq::k_fetch8<KK>(a, bh, tb + t, c, pk[j]);
-                dq::v_fetch8<VK>(a, bh, tb + t, c, pv[j]);
+            for (int j = 0; j < kItems; ++j) {
+                const int it = tid + j * kWaves * 64;
+                if (it >= kPT * C8) break;
+                const int t = it / C8, c = it - t * C8;
+                bload_codes(rk, (uint32_t)(t * k_row_b + c * kb), kb, pk[j]);
+                pk[j].meta = KK == KVQ_TOK_SYM4
+                                 ? __builtin_amdgcn_raw_buffer_load_b16(rm, (t * (D / 32) + (8 * c) / 32) * 2, 0, 0)
+                                 : __builtin_amdgcn_raw_buffer_load_b32(rm, (t * (D / a.k_group) + (8 * c) / a.k_group) * 4, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kItems; ++j) {
+                const int it = tid + j * kWaves * 64;
+                const int t = it / C8, c = it - t * C8;
+                if (it < kPT * C8 && tb + t < t_hi) dq::k_fetch8<KK>(a, bh, tb + t, c, pk[j]);
+            }
+        }
+        if constexpr (kTokV) {
+            const __amdgpu_buffer_rsrc_t rv = rsrc(static_cast<const uint8_t*>(a.v_codes) + slot0 * v_row_b, nt * v_row_b);
+            const __amdgpu_buffer_rsrc_t rm = rsrc(static_cast<const uint8_t*>(a.v_meta) + slot0 * v_meta_b, nt * v_meta_b);
+#pragma unroll
+            for (int j = 0; j < kItems; ++j) {
+                const int it = tid + j * kWaves * 64;
+                if (it >= kPT * C8) break;
+                const int t = it / C8, c = it - t * C8;
+                bload_codes(rv, (uint32_t)(t * v_row_b + c * a.v_bits), a.v_bits, pv[j]);
+                pv[j].meta = __builtin_amdgcn_raw_buffer_load_b32(rm, (t * (D / a.v_group) + (8 * c) / a.v_group) * 4, 0, 0);
             }
         }
     };
@@ -235,29 +287,27 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         }
         // mask (past the split or the row's last visible slot) -- only tiles
         // that reach either boundary for some row of the wave need it
+        // (the row factor qc > 0 is applied to the max and inside the exponent)
         float mt = -INFINITY;
         if (t0 + kPT <= t_hi && t0 + kPT - 1 <= lim_min) {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    if constexpr (QX) s[blk][v] *= qc;
-                    mt = fmaxf(mt, s[blk][v]);
-                }
+                for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[blk][v]);
         } else {
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int tok = t0 + blk * 32 + acc_row(v, kh);
-                    const float x = (tok < t_hi && tok <= lim) ? s[blk][v] * qc : -INFINITY;
+                    const float x = (tok < t_hi && tok <= lim) ? s[blk][v] : -INFINITY;
                     s[blk][v] = x;
                     mt = fmaxf(mt, x);
                 }
         }
         // online softmax, base 2; the running max only moves when a row sees a
         // larger logit, and only then are the output accumulators rescaled
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        mt = fmaxf(mt, __shfl_xor(mt, 32)) * qc;
         const float m_new = fmaxf(m, mt);
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // nothing visible yet
         float ps = 0.0f;
@@ -266,7 +316,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 // v_exp_f32: arguments are <= 0, results below 2^-126 flush to 0
-                const float p = __builtin_amdgcn_exp2f(s[blk][v] - m_use);
+                const float p = __builtin_amdgcn_exp2f(fmaf(s[blk][v], qc, -m_use));
                 s[blk][v] = p;
                 ps += p;
             }
