@@ -41,10 +41,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Generic split-T decode for every layout (D <= 128, up to 8 query heads
 // per kv-head).  Per 64-token tile the block dequantizes K and V into LDS as
 // fp32 (8 consecutive channels per work item: one code load and one
-// metadata load; keys stored transposed), computes the logits (thread =
-// token x head slot, consecutive lanes read consecutive keys), updates the
-// online softmax per head, and accumulates P V (thread = channel x token
-// range, so each value is read once for all heads).
+// metadata load; both token-major, keys with a 4-float row pad so that
+// consecutive tokens fall in different banks), computes the logits (thread =
+// token x head slot, 16-byte key reads), updates the online softmax per head,
+// and accumulates P V (thread = channel x token range, so each value is read
+// once for all heads).
 template <int KK, int VK, int D>
 __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -55,7 +56,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     const int64_t bh = (int64_t)b * a.Hkv + hk;
 
     __shared__ __align__(16) float q_s[kMaxGroup][kMaxD];
-    __shared__ float k_s[kMaxD * kTile];      // transposed: [channel][token]
+    constexpr int KS = D + 4;                 // key row stride (floats)
+    __shared__ __align__(16) float k_s[kTile * (kMaxD + 4)];   // [token][KS]; also the final reduction
     __shared__ __align__(16) float v_s[kTile * kMaxD];
     __shared__ __align__(16) float p_s[kMaxGroup][kTile];
     __shared__ float m_s[kMaxGroup], l_s[kMaxGroup], alpha_s[kMaxGroup];
@@ -97,28 +99,43 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
     // QK role: token t, head slot (heads slot and slot + 4)
     const int qt = tid & 63, slot = tid >> 6;
 
+    // keys: thread = token (tid % 64) x channel chunks tid / 64 + 4 r, so
+    // consecutive lanes write consecutive tokens of the transposed tile;
+    // values: consecutive lanes take consecutive channel chunks of a token.
+    // The codes and metadata of the next tile are fetched into registers
+    // while the current one is computed (the fetch/finish form of the
+    // dequantization); kinds without codes load in the finish stage.
+    const int kt = tid & 63;
+    dq::Pre8 pk[kItems], pv[kItems];
+    auto fetch = [&](int tb) {
+        const int ntb = min(kTile, t_end - tb);
+#pragma unroll
+        for (int r = 0; r < kItems; ++r) {
+            if (kt < ntb) dq::k_fetch8<KK>(a, bh, tb + kt, (tid >> 6) + 4 * r, pk[r]);
+            const int it = tid + 256 * r, vt = it / c8, vc = it - vt * c8;
+            if (vt < ntb) dq::v_fetch8<VK>(a, bh, tb + vt, vc, pv[r]);
+        }
+    };
+    if (t_begin < t_end) fetch(t_begin);
+
     for (int t0 = t_begin; t0 < t_end; t0 += kTile) {
         const int nt = min(kTile, t_end - t0);
         __syncthreads();                    // previous tile's reads of k_s / v_s / p_s are done
-        // keys: thread = token (tid % 64) x channel chunks tid / 64 + 4 r, so
-        // consecutive lanes write consecutive tokens of the transposed tile;
-        // values: consecutive lanes take consecutive channel chunks of a token.
-        // All loads of the tile are issued before any value is stored.
         {
             float xk[kItems][8], xv[kItems][8];
-            const int kt = tid & 63;
 #pragma unroll
             for (int r = 0; r < kItems; ++r) {
-                if (kt < nt) k_values8<KK>(a, bh, t0 + kt, (tid >> 6) + 4 * r, xk[r]);
+                if (kt < nt) dq::k_finish8<KK>(a, bh, t0 + kt, (tid >> 6) + 4 * r, pk[r], xk[r]);
                 const int it = tid + 256 * r, vt = it / c8, vc = it - vt * c8;
-                if (vt < nt) v_values8<VK>(a, bh, t0 + vt, vc, xv[r]);
+                if (vt < nt) dq::v_finish8<VK>(a, bh, t0 + vt, vc, pv[r], xv[r]);
             }
+            if (t0 + kTile < t_end) fetch(t0 + kTile);
 #pragma unroll
             for (int r = 0; r < kItems; ++r) {
                 if (kt < nt) {
                     const int c = (tid >> 6) + 4 * r;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) k_s[(8 * c + i) * kTile + kt] = xk[r][i];
+                    *reinterpret_cast<float4*>(&k_s[kt * KS + 8 * c]) = make_float4(xk[r][0], xk[r][1], xk[r][2], xk[r][3]);
+                    *reinterpret_cast<float4*>(&k_s[kt * KS + 8 * c + 4]) = make_float4(xk[r][4], xk[r][5], xk[r][6], xk[r][7]);
                 }
                 const int it = tid + 256 * r, vt = it / c8, vc = it - vt * c8;
                 if (vt < nt) {
@@ -135,9 +152,9 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
                 const int t = idx & 63, j = idx >> 6;
                 if (t < nt) {
                     const float2 r = rope[(int64_t)(t0 + t) * hd + j];
-                    const float x0 = k_s[j * kTile + t], x1 = k_s[(j + hd) * kTile + t];
-                    k_s[j * kTile + t] = x0 * r.x - x1 * r.y;
-                    k_s[(j + hd) * kTile + t] = x0 * r.y + x1 * r.x;
+                    const float x0 = k_s[t * KS + j], x1 = k_s[t * KS + j + hd];
+                    k_s[t * KS + j] = x0 * r.x - x1 * r.y;
+                    k_s[t * KS + j + hd] = x0 * r.y + x1 * r.x;
                 }
             }
             __syncthreads();
@@ -145,18 +162,26 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
         {
             float lg0 = 0.0f, lg1 = 0.0f;
             const int h0 = slot, h1 = slot + 4;
-            if (qt < nt) {
+            if (qt >= nt) {
+                lg0 = lg1 = -INFINITY;
+            } else if (gq > 4) {
 #pragma unroll 4
                 for (int d = 0; d < D; d += 4) {
                     const float4 qa = *reinterpret_cast<const float4*>(&q_s[h0][d]);
                     const float4 qb = *reinterpret_cast<const float4*>(&q_s[h1][d]);
-                    const float k0 = k_s[d * kTile + qt], k1 = k_s[(d + 1) * kTile + qt];
-                    const float k2 = k_s[(d + 2) * kTile + qt], k3 = k_s[(d + 3) * kTile + qt];
+                    const float4 kk = *reinterpret_cast<const float4*>(&k_s[qt * KS + d]);
+                    const float k0 = kk.x, k1 = kk.y, k2 = kk.z, k3 = kk.w;
                     lg0 = fmaf(qa.x, k0, lg0); lg0 = fmaf(qa.y, k1, lg0); lg0 = fmaf(qa.z, k2, lg0); lg0 = fmaf(qa.w, k3, lg0);
                     lg1 = fmaf(qb.x, k0, lg1); lg1 = fmaf(qb.y, k1, lg1); lg1 = fmaf(qb.z, k2, lg1); lg1 = fmaf(qb.w, k3, lg1);
                 }
-            } else {
-                lg0 = lg1 = -INFINITY;
+            } else if (h0 < gq) {
+                // at most 4 query heads: one per wave, the second slot is idle
+#pragma unroll 4
+                for (int d = 0; d < D; d += 4) {
+                    const float4 qa = *reinterpret_cast<const float4*>(&q_s[h0][d]);
+                    const float4 kk = *reinterpret_cast<const float4*>(&k_s[qt * KS + d]);
+                    lg0 = fmaf(qa.x, kk.x, lg0); lg0 = fmaf(qa.y, kk.y, lg0); lg0 = fmaf(qa.z, kk.z, lg0); lg0 = fmaf(qa.w, kk.w, lg0);
+                }
             }
             if (h0 < gq) p_s[h0][qt] = lg0;
             if (h1 < gq) p_s[h1][qt] = lg1;
