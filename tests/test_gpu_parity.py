@@ -93,6 +93,15 @@ CASES = {
     "affine8_d64": dict(w="affine4_g64", B=3, H=2, T=600, Hq=4, D=64,
                         lay=dict(k_kind="tok_affine", k_bits=8, k_group=32, v_kind="tok_affine",
                                  v_bits=4, v_group=32, in_dtype="bf16")),
+    # KIVI int4 with 8 query heads per kv-head (both head slots of the scores)
+    "kivi4_gqa8": dict(w="llama3b_kivi_int4", B=1, H=2, T=700, Hq=16,
+                       lay=dict(k_kind="kivi_ch", k_bits=4, k_group=32, v_kind="tok_affine",
+                                v_bits=4, v_group=32, in_dtype="f16"),
+                       chunks=[(0, 100), (100, 700)]),
+    # 4-bit affine K and V at head_dim 64 with 6 query heads per kv-head
+    "affine4_d64_gqa6": dict(w="affine4_g64", B=2, H=2, T=333, Hq=12, D=64,
+                             lay=dict(k_kind="tok_affine", k_bits=4, k_group=64, v_kind="tok_affine",
+                                      v_bits=4, v_group=32, in_dtype="bf16")),
     # KIVI-2bit: per-channel 2-bit K over 32-token groups, 2-bit V groups of 32
     "kivi2_llama3b": dict(w="llama3b_kivi_int4", B=1, H=8, T=1000,
                           lay=dict(k_kind="kivi_ch", k_bits=2, k_group=32, v_kind="tok_affine",
