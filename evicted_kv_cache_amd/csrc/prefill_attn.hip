@@ -99,8 +99,19 @@ __device__ __forceinline__ void bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t o
 // into fp16 exactly, the scores need only K_hi Q + K_lo Q, and the row's
 // factor (softmax scale times the power of two) is applied to the fp32
 // scores.  Otherwise (fp32 queries) the query is an fp16 pair as the keys are.
-template <int KK, int VK, int D, bool QX>
+//
+// C4: per-token 4-bit keys and values.  The code widths are then constants,
+// so each tile's fetch is one straight run of loads whose results are first
+// used one tile later (with widths known only at run time, the branches
+// around the loads cost a wait on each of them).
+template <int KK, int VK, int D, bool QX, bool C4>
 __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
+    static_assert(!C4 || ((KK == KVQ_TOK_AFFINE || KK == KVQ_TOK_SYM4) && VK == KVQ_TOK_AFFINE),
+                  "constant code widths: per-token layouts");
+    if constexpr (C4) {
+        a.k_bits = 4;
+        a.v_bits = 4;
+    }
     constexpr int NK = D / 16;               // K-steps of the score product
     constexpr int ND = D / 32;               // 32-row blocks of the output
     constexpr int C8 = D / 8;                // 8-channel chunks per row
@@ -378,21 +389,30 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     }
 }
 
-template <int KK, int VK, bool QX>
+template <int KK, int VK, bool QX, bool C4>
 hipError_t launch_prefill_kvq(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)(a.Hkv * n_rb), (unsigned)a.B);
     switch (a.D) {
-        case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32, QX>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
-        case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64, QX>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
-        default: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32, QX, C4>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64, QX, C4>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        default: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
     }
     return hipGetLastError();
 }
 
+template <int KK, int VK, bool QX>
+hipError_t launch_prefill_kvq_c(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
+    if constexpr ((KK == KVQ_TOK_AFFINE || KK == KVQ_TOK_SYM4) && VK == KVQ_TOK_AFFINE) {
+        if ((KK == KVQ_TOK_SYM4 || a.k_bits == 4) && a.v_bits == 4)
+            return launch_prefill_kvq<KK, VK, QX, true>(a, n_q, n_rb, causal, s);
+    }
+    return launch_prefill_kvq<KK, VK, QX, false>(a, n_q, n_rb, causal, s);
+}
+
 template <int KK, int VK>
 hipError_t launch_prefill_kv(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
-    return a.q_dtype == KVQ_F32 ? launch_prefill_kvq<KK, VK, false>(a, n_q, n_rb, causal, s)
-                                : launch_prefill_kvq<KK, VK, true>(a, n_q, n_rb, causal, s);
+    return a.q_dtype == KVQ_F32 ? launch_prefill_kvq_c<KK, VK, false>(a, n_q, n_rb, causal, s)
+                                : launch_prefill_kvq_c<KK, VK, true>(a, n_q, n_rb, causal, s);
 }
 
 template <int KK>
