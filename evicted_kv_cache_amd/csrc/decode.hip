@@ -46,8 +46,18 @@ __device__ __forceinline__ float wave_sum(float v) {
 // token x head slot, 16-byte key reads), updates the online softmax per head,
 // and accumulates P V (thread = channel x token range, so each value is read
 // once for all heads).
-template <int KK, int VK, int D>
+//
+// C4: 4-bit key and value codes.  The widths are then constants, so a tile's
+// fetch is a straight run of loads whose results are first used one tile
+// later (with widths known only at run time, the branches around the loads
+// cost a wait on each of them).
+template <int KK, int VK, int D, bool C4>
 __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
+    static_assert(!C4 || (KK != KVQ_PLAIN && VK == KVQ_TOK_AFFINE), "constant code widths: coded layouts");
+    if constexpr (C4) {
+        a.k_bits = 4;
+        a.v_bits = 4;
+    }
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     constexpr int c8 = D / 8;
@@ -310,15 +320,23 @@ __global__ __launch_bounds__(256) void zero_kernel(float* p, size_t n) {
     if (i < n) p[i] = 0.0f;
 }
 
-template <int KK, int VK>
-hipError_t launch_generic_kv(const DecodeArgs& a, hipStream_t s) {
+template <int KK, int VK, bool C4>
+hipError_t launch_generic_kvc(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
     switch (a.D) {
-        case 32: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 32>), grid, dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 64>), grid, dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 128>), grid, dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 32, C4>), grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 64, C4>), grid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL((decode_generic_kernel<KK, VK, 128, C4>), grid, dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
+}
+
+template <int KK, int VK>
+hipError_t launch_generic_kv(const DecodeArgs& a, hipStream_t s) {
+    if constexpr (KK != KVQ_PLAIN && VK == KVQ_TOK_AFFINE) {
+        if ((KK == KVQ_TOK_SYM4 || a.k_bits == 4) && a.v_bits == 4) return launch_generic_kvc<KK, VK, true>(a, s);
+    }
+    return launch_generic_kvc<KK, VK, false>(a, s);
 }
 
 template <int KK>
