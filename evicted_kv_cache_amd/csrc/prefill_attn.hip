@@ -96,9 +96,12 @@ __device__ __forceinline__ void bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t o
 // the split.  Causal rows see slots t <= T - n_q + i.
 //
 // QX: the query is fp16 or bf16.  Each row is then scaled by a power of two
-// into fp16 exactly, the scores need only K_hi Q + K_lo Q, and the row's
-// factor (softmax scale times the power of two) is applied to the fp32
-// scores.  Otherwise (fp32 queries) the query is an fp16 pair as the keys are.
+// so that its largest element lies in [2^14, 2^15): every element down to
+// 2^-28 of the largest is exact in fp16 (smaller ones, far below the fp32
+// rounding of the dot product, may lose low bits), the scores need only
+// K_hi Q + K_lo Q, and the row's factor (softmax scale times the power of
+// two) is applied to the fp32 scores.  Otherwise (fp32 queries) the query is
+// an fp16 pair as the keys are.
 //
 // C4: per-token 4-bit keys and values.  The code widths are then constants,
 // so each tile's fetch is one straight run of loads whose results are first
