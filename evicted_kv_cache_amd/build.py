@@ -8,6 +8,10 @@ Every HIP source is compiled separately with hipcc and linked into
                              call fmaf explicitly
   -target-feature -packed-fp32-ops
                              no compiler-generated packed fp32 instructions
+
+Sources that hold inline asm are also compiled to device assembly, which
+``asm_check.scan`` reads for asm statements placed where the hardware needs
+wait states the compiler does not insert for them; a hit fails the build.
 """
 from __future__ import annotations
 
@@ -49,11 +53,31 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _check_asm(src: str, verbose: bool) -> None:
+    from .asm_check import scan
+    out = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".device.s")
+    cmd = [HIPCC, *FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed for {src}:\n{r.stderr}")
+    with open(out) as f:
+        hits = scan(f.read())
+    if hits:
+        raise RuntimeError(f"{src}: inline asm right after a transcendental instruction it depends on "
+                           f"(needs a wait state the compiler does not add):\n" + "\n".join(hits[:20]))
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
+    asm_srcs = [s for s in srcs if "asm(" in open(os.path.join(CSRC, s)).read()]
+    with ThreadPoolExecutor(min(8, len(srcs) + len(asm_srcs))) as ex:
+        checks = [ex.submit(_check_asm, s, verbose) for s in asm_srcs]
         objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        for c in checks:
+            c.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

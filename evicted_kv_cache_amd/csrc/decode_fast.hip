@@ -43,8 +43,19 @@
 // * Tails need no clamping: loads go through buffer resources whose size is
 //   the valid part of the tile, and out-of-range loads return zero.  Only the
 //   last tile of a split can hold invalid tokens; it alone masks its logits.
+// * KIVI keys ("KIVI" page: per-channel 4-bit keys over 32-token groups with
+//   the open group in full precision) use the same tiles, softmax and value
+//   path with 1-4 query heads per kv-head.  A channel's scale and zero live in
+//   the table row of the token's group, so the factoring above does not
+//   apply: each wave stages the table rows of a tile's first and last tokens
+//   in LDS (a tile spans at most those two in an unevicted cache), every lane
+//   dequantizes its token's 32 channels in fp32 (k = u s + z) and multiplies
+//   them by the exact fp16 query with mixed-precision FMAs.  Tokens whose row
+//   is neither staged row, and tokens of the open group, take a per-lane path
+//   that reads their row or residual from memory.
 #include <math.h>
 
+#include "dequant8.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -58,6 +69,7 @@ constexpr int kRowB = kD / 2;   // bytes of 4-bit K codes per token
 // K code formats of the fast path
 constexpr int kKAff4 = 0;       // per-token affine groups: (scale, zero) fp16 pairs
 constexpr int kKSym4 = 1;       // symmetric blocks of 32: one fp16 scale d, value (u - 8) d
+constexpr int kKKivi = 2;       // KIVI: per-channel (scale, zero) in the table row of the token's group
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -79,16 +91,29 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
     half2_t h = {(_Float16)lo, (_Float16)hi};
     return __builtin_bit_cast(uint32_t, h);
 }
-// (low fp16 half of h) * y in one v_fma_mix_f32 with a +0 addend (a -0
-// product comes out as +0, which no caller distinguishes)
-__device__ __forceinline__ float mul_lo(uint32_t h, float y) {
+// acc + (low / high fp16 half of h) * x in one v_fma_mix_f32.  Written out so
+// that the compiler keeps the packed pair as the operand instead of hoisting
+// loop-invariant widenings into separate registers.  The compiler does not
+// add wait states around inline asm: never feed these a fresh transcendental
+// result (v_exp_f32 and the like); the build checks the assembly for it.
+__device__ __forceinline__ float fma_lo(uint32_t h, float x, float acc) {
     float r;
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(y));
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x), "v"(acc));
+    return r;
+}
+__device__ __forceinline__ float fma_hi(uint32_t h, float x, float acc) {
+    float r;
+    asm("v_fma_mix_f32 %0, %1, %2, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(x), "v"(acc));
     return r;
 }
 // fp16 halves of a packed pair, widened (folds into v_fma_mix_f32 operands)
 __device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(half2_t, u).x; }
 __device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit_cast(half2_t, u).y; }
+// (low fp16 half of h) * y: one v_fma_mix_f32 with a +0 addend (a -0
+// product comes out as +0, which no caller distinguishes).  Plain code, not
+// inline asm: its operands are often fresh v_exp_f32 results, and only code
+// the compiler emits itself gets the wait states such a read needs.
+__device__ __forceinline__ float mul_lo(uint32_t h, float y) { return __builtin_fmaf(f16lo(h), y, 0.0f); }
 // DPP quad rotations: value of lane (l - k) mod 4 within the lane's quad.
 template <int K>
 __device__ __forceinline__ float quad_from_minus(float v) {
@@ -140,13 +165,20 @@ struct TileLoads {
     uint32_t kmo[2];     // K (scale, zero) of the other 64-channel half's group (K groups of 64)
     VMeta<NVG> vm;
     uint32_t v[4][2][VW];  // V code words (8 channels) of tokens ph+4j and ph+4j+16
+    // KIVI keys: table rows of tokens t, t+16; this lane's 8 bytes of the two
+    // staged rows (the rows of the tile's first and last coded tokens, r0, r1)
+    int32_t krow[2];
+    u32x2 stg[2];
+    int r0, r1;
 };
 
-// KF: K format (kKAff4 or kKSym4, whose blocks are GK = 32 channels);
+// KF: K format (kKAff4, kKSym4 whose blocks are GK = 32 channels, or kKKivi
+// with GK = 32 unused);
 // GK, GV: channels per K / V group (32, 64 or 128); VB: bits per V code (4 or 8).
 template <int QDT, int KF, int GK, int VB, int GV>
 __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     static_assert(KF == kKAff4 || GK == 32, "symmetric K blocks are 32 channels");
+    constexpr bool kKivi = KF == kKKivi;
     constexpr int NKG = kD / GK;      // K groups per row
     constexpr int NVG = kD / GV;      // V groups per row
     constexpr int VW = VB / 4;        // V code words per token and lane
@@ -172,6 +204,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     const int tile0 = (n_tiles * wave) / kWaves, tile1 = (n_tiles * (wave + 1)) / kWaves;
 
     __shared__ uint32_t wbuf[kWaves][16][NVG][kGQ];           // fp16 weight pairs of a tile
+    __shared__ __align__(16) uint32_t kst[kKivi ? kWaves : 1][2][kD];   // KIVI: staged table rows
     __shared__ float comb_o[kWaves][kGQ][kD];
     __shared__ float comb_ml[kWaves][kGQ][2];
 
@@ -192,10 +225,13 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     const int vg_c = (8 * c) / GV;
 
     // ---- query: fp16 pairs for this lane's quarter, scaled by 2^-e (shared by the group)
-    const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + hk * kGQ) * kD;
+    // (gq query heads share the kv-head; heads gq .. 3 hold zeros and are not written)
+    const int gq = a.Hq / a.Hkv;
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + hk * gq) * kD;
     float qmax = 0.0f;
 #pragma unroll
-    for (int h = 0; h < kGQ; ++h)
+    for (int h = 0; h < kGQ; ++h) {
+        if (h >= gq) continue;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const uint4 x = *reinterpret_cast<const uint4*>(q16 + h * kD + 32 * q4 + 8 * k);
@@ -204,6 +240,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             for (int i = 0; i < 4; ++i)
                 qmax = fmaxf(qmax, fmaxf(fabsf(q_elem<QDT>(e4[i] & 0xFFFFu)), fabsf(q_elem<QDT>(e4[i] >> 16))));
         }
+    }
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
     // scale so the largest |q| lands in [2^14, 2^15): exact fp16 for bf16/fp16 inputs
@@ -212,6 +249,8 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     const float qscale = ldexpf(1.0f, -qexp);
     // register j of this lane holds query head (q4 + j) % 4, so that the four
     // quarter partials of head h meet in lane quarter h by quad rotations only
+    // (affine / symmetric K: channel pairs (8k+i, 8k+i+4) as the nibble masks
+    // lay them out, high nibbles pre-divided by 16; KIVI K: pairs (8k+2i, 8k+2i+1))
     uint32_t qv[kGQ][16];
     float qsum[kGQ];
 #pragma unroll
@@ -220,25 +259,35 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint4 xx = *reinterpret_cast<const uint4*>(q16 + h * kD + 32 * q4 + 8 * k);
-            const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
             float x[8];
+            if (h < gq) {
+                const uint4 xx = *reinterpret_cast<const uint4*>(q16 + h * kD + 32 * q4 + 8 * k);
+                const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = q_elem<QDT>(e4[i] & 0xFFFFu);
-                x[2 * i + 1] = q_elem<QDT>(e4[i] >> 16);
+                for (int i = 0; i < 4; ++i) {
+                    x[2 * i] = q_elem<QDT>(e4[i] & 0xFFFFu);
+                    x[2 * i + 1] = q_elem<QDT>(e4[i] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) x[i] = 0.0f;
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) s += x[i];
-            qv[j][4 * k + 0] = pack_f16(x[0] * qscale, x[4] * qscale);
-            qv[j][4 * k + 1] = pack_f16(x[1] * qscale * 0.0625f, x[5] * qscale * 0.0625f);
-            qv[j][4 * k + 2] = pack_f16(x[2] * qscale, x[6] * qscale);
-            qv[j][4 * k + 3] = pack_f16(x[3] * qscale * 0.0625f, x[7] * qscale * 0.0625f);
+            if constexpr (kKivi) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) qv[j][4 * k + i] = pack_f16(x[2 * i] * qscale, x[2 * i + 1] * qscale);
+            } else {
+                qv[j][4 * k + 0] = pack_f16(x[0] * qscale, x[4] * qscale);
+                qv[j][4 * k + 1] = pack_f16(x[1] * qscale * 0.0625f, x[5] * qscale * 0.0625f);
+                qv[j][4 * k + 2] = pack_f16(x[2] * qscale, x[6] * qscale);
+                qv[j][4 * k + 3] = pack_f16(x[3] * qscale * 0.0625f, x[7] * qscale * 0.0625f);
+            }
         }
         qsum[j] = s;
     }
-    // logit (base 2) = cexp (s 2^(qexp+24) (q' . u') + z qsum)
-    const float kC = ldexpf(a.scale_log2, qexp + 24);
+    // logit (base 2) = cexp (s 2^(qexp+24) (q' . u') + z qsum); KIVI: scale_log2 2^qexp (q' . k)
+    const float kC = ldexpf(a.scale_log2, kKivi ? qexp : qexp + 24);
     // per head: z * qsum / 2^(qexp+24), so that logit = kC (s (q' . u') + z qsk)
     float qsk[kGQ];
 #pragma unroll
@@ -270,6 +319,9 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kVRowB;
     const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + bh * a.cap * NKG * kKMetaB;
     const uint32_t* vmeta = static_cast<const uint32_t*>(a.v_meta) + bh * a.cap * NVG;
+    // KIVI: the (batch, kv-head)'s table [rows][kD] of (scale, zero) fp16 pairs
+    const int rows_t = kKivi ? a.cap / a.Gt + 3 : 0;
+    const uint8_t* ktab = static_cast<const uint8_t*>(a.k_meta) + (kKivi ? bh * rows_t * kD * 4 : 0);
 
     float m_lane = -INFINITY;     // running max of head q4
     float l_lane = 0.0f;          // running sum of head q4 (this lane's tokens)
@@ -288,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         // kept in a scalar register so the buffer descriptors stay uniform
         const uint32_t nv = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kTileT, t_hi - tb)));
         const __amdgpu_buffer_rsrc_t rk = rsrc(kcodes + (int64_t)tb * kRowB, nv * kRowB);
-        const __amdgpu_buffer_rsrc_t rkm = rsrc(kmeta + (int64_t)tb * NKG * kKMetaB, nv * NKG * kKMetaB);
+        const __amdgpu_buffer_rsrc_t rkm = rsrc(kmeta + (int64_t)tb * NKG * kKMetaB, kKivi ? 0u : nv * NKG * kKMetaB);
         const __amdgpu_buffer_rsrc_t rvm = rsrc(vmeta + (int64_t)tb * NVG, nv * NVG * 4);
         const __amdgpu_buffer_rsrc_t rv = rsrc(vcodes + (int64_t)tb * kVRowB, nv * kVRowB);
 #pragma unroll
@@ -309,7 +361,11 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = t16 + 16 * p;
             L.k[p] = bload128(rk, tok * kRowB + 16 * q4);
-            if constexpr (KF == kKSym4) {
+            if constexpr (kKivi) {
+                // the token's table row (slots past the tile's valid part read 0)
+                const __amdgpu_buffer_rsrc_t rrow = rsrc(a.k_row + tb, nv * 4);
+                L.krow[p] = (int32_t)bload32(rrow, tok * 4);
+            } else if constexpr (KF == kKSym4) {
                 L.km[p] = bload16(rkm, (tok * NKG + kg) * 2);
             } else {
                 L.km[p] = bload32(rkm, (tok * NKG + kg) * 4);
@@ -325,6 +381,22 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                 L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y; L.vm.m[p][2] = x.z; L.vm.m[p][3] = x.w;
             }
         }
+        if constexpr (kKivi) {
+            // the table rows of the tile's first and last coded tokens, staged
+            // through registers: lane l loads channels 2l, 2l+1 of each (the
+            // table buffer covers the whole table, so any row index is safe)
+            const int nq = max(0, min(tb + (int)nv, a.n_quant) - tb);
+            int r0 = 0, r1 = 0;
+            if (nq > 0) {
+                r0 = a.k_row[tb];
+                r1 = a.k_row[tb + nq - 1];
+            }
+            L.r0 = __builtin_amdgcn_readfirstlane(r0);
+            L.r1 = __builtin_amdgcn_readfirstlane(r1);
+            const __amdgpu_buffer_rsrc_t rtab = rsrc(ktab, (uint32_t)rows_t * kD * 4);
+            L.stg[0] = bload64(rtab, (uint32_t)L.r0 * kD * 4 + 8 * lane);
+            L.stg[1] = bload64(rtab, (uint32_t)L.r1 * kD * 4 + 8 * lane);
+        }
     };
 
     auto process = [&](const TileLoads<NVG, VW>& L, int tile, auto tail) {
@@ -332,6 +404,83 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         const int tb = t_lo + tile * kTileT;
         // -------------------------------------------- QK^T, two passes (t16, t16 + 16)
         float xs[2];
+        if constexpr (kKivi) {
+            // stage the two table rows; kst[wave][r][c] = (scale, zero) of channel c
+            *reinterpret_cast<u32x2*>(&kst[wave][0][2 * lane]) = L.stg[0];
+            *reinterpret_cast<u32x2*>(&kst[wave][1][2 * lane]) = L.stg[1];
+            __builtin_amdgcn_wave_barrier();
+            // every token of the wave valid-and-coded with a staged row: the common case
+            bool fast = true;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int t = tb + t16 + 16 * p;
+                const bool staged = L.krow[p] == L.r0 || L.krow[p] == L.r1;
+                fast = fast && (t >= t_hi || (t < a.n_quant && staged));
+            }
+            const bool all_fast = __builtin_amdgcn_ballot_w64(!fast) == 0;
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const int t = tb + t16 + 16 * p;
+                const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
+                // register j: query head (q4 + j) % 4 over this quarter; eight
+                // channels at a time, exact fp16 x fp32 products
+                float part[kGQ];
+#pragma unroll
+                for (int j = 0; j < kGQ; ++j) part[j] = 0.0f;
+                auto chunk = [&](int k, const float xk[8]) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int j = 0; j < kGQ; ++j)
+#pragma unroll
+                        for (int i = 0; i < 8; i += 2) {
+                            part[j] = fma_lo(qv[j][4 * k + i / 2], xk[i], part[j]);
+                            part[j] = fma_hi(qv[j][4 * k + i / 2], xk[i + 1], part[j]);
+                        }
+                };
+                // keys of channels 8k .. 8k+7 of the quarter: k = u s + z from the row's (scale, zero) pairs
+                auto deq = [&](int k, const uint32_t m[8], float xk[8]) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) xk[i] = fmaf((float)((kw[k] >> (4 * i)) & 0xFu), f16lo(m[i]), f16hi(m[i]));
+                };
+                if (all_fast) {
+                    const uint32_t* row = &kst[wave][L.krow[p] == L.r0 ? 0 : 1][32 * q4];
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint4 m0 = *reinterpret_cast<const uint4*>(row + 8 * k);
+                        const uint4 m1 = *reinterpret_cast<const uint4*>(row + 8 * k + 4);
+                        const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+                        float xk[8];
+                        deq(k, m, xk);
+                        chunk(k, xk);
+                    }
+                } else {
+                    // per lane: past the split (zeros), the open group (the
+                    // full-precision residual), a staged row, or a row in memory
+                    const bool staged = L.krow[p] == L.r0 || L.krow[p] == L.r1;
+                    const uint32_t* row = staged ? &kst[wave][L.krow[p] == L.r0 ? 0 : 1][32 * q4]
+                                                 : reinterpret_cast<const uint32_t*>(ktab) + (int64_t)L.krow[p] * kD + 32 * q4;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        float xk[8];
+                        if (t >= t_hi) {
+#pragma unroll
+                            for (int i = 0; i < 8; ++i) xk[i] = 0.0f;
+                        } else if (t >= a.n_quant) {
+                            dq::load8(a.k_resid, (bh * a.Gt + (t - a.n_quant)) * kD + 32 * q4 + 8 * k, a.in_dtype, xk);
+                        } else {
+                            const uint4 m0 = *reinterpret_cast<const uint4*>(row + 8 * k);
+                            const uint4 m1 = *reinterpret_cast<const uint4*>(row + 8 * k + 4);
+                            const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+                            deq(k, m, xk);
+                        }
+                        chunk(k, xk);
+                    }
+                }
+                const float xl = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
+                                  quad_from_minus<3>(part[3])) * kC;
+                if constexpr (kTail) xs[p] = t < t_hi ? xl : -INFINITY;
+                else xs[p] = xl;
+            }
+        } else {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             float dsum[kGQ];
@@ -375,6 +524,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             }
             if constexpr (kTail) xs[p] = (tb + t16 + 16 * p < t_hi) ? x : -INFINITY;
             else xs[p] = x;
+        }
         }
 
         // -------------------------------------------- online softmax (rescale on a new max)
@@ -522,6 +672,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     const int ns = a.n_splits;
     for (int idx = threadIdx.x; idx < kGQ * kD; idx += 256) {
         const int h = idx / kD, d = idx % kD;
+        if (h >= gq) continue;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb_ml[w][h][0]);
@@ -533,7 +684,7 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
             num = fmaf(f, comb_o[w][h][d], num);
             den = fmaf(f, comb_ml[w][h][1], den);
         }
-        const int64_t row = (int64_t)b * a.Hq + hk * kGQ + h;
+        const int64_t row = (int64_t)b * a.Hq + hk * gq + h;
         if (ns == 1) {
             a.out[row * kD + d] = num / den;
         } else {
@@ -548,14 +699,18 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 
 }  // namespace
 
-// Fast path applies to: per-token 4-bit affine or symmetric K and affine 4/8-bit
-// V, D = 128, 4 query heads per kv-head, bf16 or fp16 queries, no RoPE on read
-// (a per-key rotation would undo the factored scale).
+// Fast path applies to affine 4/8-bit V, D = 128, bf16 or fp16 queries and no
+// RoPE on read, with either per-token 4-bit affine or symmetric K and 4 query
+// heads per kv-head (a per-key rotation would undo the factored scale), or
+// KIVI 4-bit K and 1-4 query heads per kv-head.
 bool decode_fast_applies(const DecodeArgs& a) {
-    const bool k_ok = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4;
+    const bool tok_k = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4;
+    const bool kivi_k = a.k_kind == KVQ_KIVI_CH && a.k_bits == 4;
     const bool v_ok = a.v_kind == KVQ_TOK_AFFINE && (a.v_bits == 4 || a.v_bits == 8);
-    return k_ok && v_ok && a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) &&
-           !a.rope;
+    const bool heads_ok =
+        tok_k ? a.Hq == kGQ * a.Hkv : (a.Hq % a.Hkv == 0 && a.Hq >= a.Hkv && a.Hq <= kGQ * a.Hkv);
+    return (tok_k || kivi_k) && heads_ok && v_ok && a.D == kD &&
+           (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) && !a.rope;
 }
 
 // Split plan: one workgroup per (batch, kv-head) when that fills the chip
@@ -592,6 +747,7 @@ static hipError_t launch_fast_k(const DecodeArgs& a, hipStream_t s) {
 
 template <int QDT>
 static hipError_t launch_fast_q(const DecodeArgs& a, hipStream_t s) {
+    if (a.k_kind == KVQ_KIVI_CH) return launch_fast_k<QDT, kKKivi, 32>(a, s);
     if (a.k_kind == KVQ_TOK_SYM4) return launch_fast_k<QDT, kKSym4, 32>(a, s);
     switch (a.k_group) {
         case 32: return launch_fast_k<QDT, kKAff4, 32>(a, s);

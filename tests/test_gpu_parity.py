@@ -362,6 +362,28 @@ def test_periodic_eviction_and_batch_eviction_kivi4():
     assert_same_state(dst, ob.evict(3, 64))
 
 
+@pytest.mark.parametrize("G,vb,vg,qdt", [(3, 4, 32, "f16"), (1, 8, 128, "bf16"), (4, 4, 64, "f16"),
+                                          (2, 4, 128, "bf16")])
+def test_kivi_fast_decode(G, vb, vg, qdt):
+    """KIVI 4-bit keys at head_dim 128 with 1-4 query heads per kv-head (the
+    fast decode's KIVI path): a ragged cache whose last group is still open,
+    then the same cache after StreamingLLM compaction (sink 5, window 700),
+    whose tiles mix table rows and read some rows per lane."""
+    w = synth.workload("llama3b_kivi_int4")
+    B, H, T = 1, 2, 2221
+    k, v, q = gen(w, B, H, T, H * G)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind="kivi_ch", k_bits=4, k_group=32,
+                     v_kind="tok_affine", v_bits=vb, v_group=vg, in_dtype="f16")
+    say("kivi fast decode", G, vb, vg, qdt)
+    c, o = build_pair(pl, ol, k, v, "f16", chunks=[(0, 1000), (1000, T)])
+    qq = q if qdt == "f16" else synth.cast(synth.widen(q, "f16"), "bf16")
+    check_decode(pl, c, o, qq, qdt)
+    dst = K.Cache(pl)
+    assert K.kvq_evict_streaming(pl, c, dst, 5, 700) == K.KVQ_OK
+    torch.cuda.synchronize()
+    check_decode(pl, dst, o.evict(5, 700), qq, qdt)
+
+
 def test_quantize_codes_on_rounding_boundaries():
     """Quotients exactly on, and one ulp either side of, half-integers (where a
     reciprocal-based quotient could round differently): codes stay bit-exact."""
