@@ -34,7 +34,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_MFMA_F16_TFLOPS = 2500.0      # dense fp16 matrix-core peak
-FAST_SRC = os.path.join(ROOT, "evicted_kv_cache_amd", "csrc", "decode_fast.hip")
+# source of the kernel the step launches (the traffic counters are only
+# reported while they were taken on this source)
+DECODE_SRC = os.path.join(ROOT, "evicted_kv_cache_amd", "csrc", "decode_mfma.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_affine4_g64_traffic.json")
 
 
@@ -78,7 +80,7 @@ def load_traffic():
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_sha256_16") != source_hash(FAST_SRC):
+    if t.get("source_sha256_16") != source_hash(DECODE_SRC):
         return None
     return t.get("bytes_per_launch")
 
@@ -361,7 +363,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 q / u4 codes, fp32 accumulate",
+        "dtype": "bf16 q / u4 codes, fp16 MFMA operands (exact), fp32 accumulate",
         "data": "synthetic (seeded N(0,1), synth.affine4_g64)",
         "config": {"workload": w.name, "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "head_dim": D, "seq_len": T, "k_format": "tok_affine u4 g64 fp16 scale+zero",
@@ -371,7 +373,7 @@ def main():
                    "algorithmic_bytes_per_step": nbytes},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_tok4_kernel<bf16, 64, 64> (one launch per step)"},
+                     "kernel": "decode_mfma_kernel<bf16, 64, 64> (one launch per step)"},
         "cpu_baseline": cpu,
         "rows": rows,
     }

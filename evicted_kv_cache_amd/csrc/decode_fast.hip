@@ -758,6 +758,7 @@ static hipError_t launch_fast_q(const DecodeArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) {
+    if (decode_mfma_applies(a)) return launch_decode_mfma(a, s);
     if (a.q_dtype == KVQ_BF16) return launch_fast_q<KVQ_BF16>(a, s);
     return launch_fast_q<KVQ_F16>(a, s);
 }

@@ -1,0 +1,417 @@
+// decode_mfma.hip -- decode attention for per-token affine 4-bit K and V
+// (mlx-lm style groups, "Low-bit KV caches on MLX", s.1) at head_dim 128 and
+// 4 query heads per kv-head, with both products on the matrix cores
+// (gfx950, v_mfma_f32_16x16x32_f16).
+//
+// Same work split as the VALU decode in decode_fast.hip: 4 waves per
+// (batch, kv-head[, token split]), each streaming 32-token tiles with its own
+// online softmax, merged through LDS (token splits merge in a combine
+// kernel).  What changes is where the multiply-adds run.  A 4-bit code left
+// in place under a mask is an fp16 subnormal (u 2^-24 for a low nibble,
+// u 2^-20 for a high one), and the matrix cores multiply subnormal fp16
+// operands exactly, so the codes feed the MFMA B operand with one AND each.
+// Lane l below is (r, n) = (l >> 4, l & 15).
+//
+// * Scores, per 16-token block: C = A B over the 128 channels in 4 MFMAs of
+//   32 channels.  B column n is token n; lane (r, n) supplies channels
+//   32r .. 32r+31 of it (one 16-byte load).  A row i = 4qq + h holds query
+//   head h restricted to channel quarter qq (zero elsewhere), so C row
+//   (qq, h) is the partial dot product of head h over quarter qq, and lane
+//   (r, n) ends with the quarter-r partials of all four heads for token n.
+//   Each lane applies its token's (scale, zero) of the quarter's group:
+//     q . k = sum_qq [ s (q . u)_qq + z (sum q)_qq ]
+//   and two cross-row exchanges sum the quarters, leaving lane (r, n) with
+//   the logit of head r for token n.  The query is held as fp16 scaled by a
+//   power of two (exact for bf16 and fp16 queries), high-nibble channels
+//   pre-divided by 16.
+// * Softmax: lane (h, n) owns head h for tokens n and n + 16 of the tile,
+//   with a lazily rescaled running max as in the VALU decode, and writes the
+//   fp16 weight pairs w^ = fp16(p s) per V group to LDS.
+// * Values: O = W V over the tile's 32 tokens in one MFMA per code byte
+//   position and kind.  W row i = 4g + h holds head h's weights for V group
+//   g (one 16-byte LDS read per lane); V column n is code word n (channels
+//   8n .. 8n+7), and one v_perm_b32 per token pair gives the whole bytes
+//   b = u_2k + 16 u_2k+1 of tokens (t, t + 16) as subnormal fp16 pairs, one
+//   AND their low nibbles.  The high-nibble channel is (byte sum - low sum)
+//   / 16 at the end.  Only the rows of a column's own V group are kept.  The
+//   zero points and the rounding of the weights are accounted exactly in
+//   fp32 as in the VALU decode:
+//     o = sum_t w^_t u_t + sum_t p_t (z_t + 8 s_t) - 8 sum_t w^_t
+// * Loads go through buffer resources sized to the valid part of a tile, so
+//   tail tokens read zeros; the last tile of a split masks their logits.
+#include <math.h>
+
+#include "bufload.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+using buf::u32x4;
+
+constexpr int kD = 128;
+constexpr int kGQ = 4;          // query heads per kv-head
+constexpr int kTileT = 32;      // tokens per wave tile
+constexpr int kWaves = 4;
+constexpr int kRowB = kD / 2;   // bytes of 4-bit codes per token (K and V)
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma16(u32x4 a, u32x4 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0,
+                                                  0);
+}
+__device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+__device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
+    half2_t h = {(_Float16)lo, (_Float16)hi};
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ float f16lo(uint32_t u) { return (float)__builtin_bit_cast(half2_t, u).x; }
+__device__ __forceinline__ float f16hi(uint32_t u) { return (float)__builtin_bit_cast(half2_t, u).y; }
+template <int QDT>
+__device__ __forceinline__ float q_elem(uint32_t bits16) {
+    if constexpr (QDT == KVQ_BF16) return bf16_bits_to_f32(bits16);
+    else return f16_bits_to_f32(bits16);
+}
+template <bool B>
+struct Flag { static constexpr bool value = B; };
+
+// The four code-word nibble masks as the B operand of one 32-channel MFMA:
+// fp16 slots (c0, c4, c1, c5, c2, c6, c3, c7) of the word's eight channels,
+// odd channels 16x (their query slots carry 1/16).
+__device__ __forceinline__ u32x4 nibble_operand(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    return u32x4{w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u};
+}
+
+// Loads of one lane for one tile, issued a tile ahead of their use.
+template <int NVG>
+struct MTile {
+    u32x4 k[2];          // K codes of channels 32r .. 32r+31, tokens n and n + 16
+    uint32_t km[2];      // K (scale, zero) of that quarter's group, tokens n and n + 16
+    uint32_t vm[2][NVG]; // V (scale, zero) per group, tokens n and n + 16
+    uint32_t v[4][2];    // V code word n of tokens 4r + j and 4r + j + 16
+};
+
+// GK, GV: channels per K / V group (32, 64 or 128).
+template <int QDT, int GK, int GV>
+__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr int NKG = kD / GK;
+    constexpr int NVG = kD / GV;
+    constexpr float kVCenter = 8.0f;                 // V codes are centered on 8
+    constexpr uint32_t kVCenterNeg = 0xC800C800u;    // fp16 (-8, -8)
+
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int n = lane & 15, r = lane >> 4;
+    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int64_t bh = (int64_t)b * a.Hkv + hk;
+    const int t_lo = split * a.split_len;
+    const int t_hi = min(a.T, t_lo + a.split_len);
+    const int n_tiles = (t_hi - t_lo + kTileT - 1) / kTileT;
+    const int tile0 = (n_tiles * wave) / kWaves, tile1 = (n_tiles * (wave + 1)) / kWaves;
+
+    __shared__ __align__(16) uint32_t wbuf[kWaves][NVG][kGQ][16];   // fp16 weight pairs (t, t + 16)
+    __shared__ float comb_o[kWaves][kGQ][kD];
+    __shared__ float comb_ml[kWaves][kGQ][2];
+
+    // ---- query: lane (r, n) reads channels 32r .. 32r+31 of head n & 3
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + hk * kGQ) * kD;
+    float x[32];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint4 xx = *reinterpret_cast<const uint4*>(q16 + (n & 3) * kD + 32 * r + 8 * k);
+        const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[8 * k + 2 * i] = q_elem<QDT>(e4[i] & 0xFFFFu);
+            x[8 * k + 2 * i + 1] = q_elem<QDT>(e4[i] >> 16);
+        }
+    }
+    float qmax = 0.0f, qpart = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        qmax = fmaxf(qmax, fabsf(x[i]));
+        qpart += x[i];
+    }
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+    // scale so the largest |q| lands in [2^14, 2^15): exact fp16 for bf16/fp16 inputs
+    int qexp = 0;
+    if (qmax > 0.0f) { frexpf(qmax, &qexp); qexp -= 15; }
+    const float qscale = ldexpf(1.0f, -qexp);
+    // A operands of the score MFMAs: row n = (quarter n >> 2, head n & 3) is
+    // nonzero only in the lanes of its own quarter (r == n >> 2)
+    const bool own = (n >> 2) == r;
+    u32x4 qa[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const float* xc = x + 8 * c;
+        const float s = own ? qscale : 0.0f, s16 = s * 0.0625f;
+        qa[c] = u32x4{pack_f16(xc[0] * s, xc[4] * s), pack_f16(xc[1] * s16, xc[5] * s16),
+                      pack_f16(xc[2] * s, xc[6] * s), pack_f16(xc[3] * s16, xc[7] * s16)};
+    }
+    // zero-point terms: sum of head h's query over quarter r (lane (r, h) holds it), / 2^(qexp + 24)
+    float qsk[kGQ];
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) qsk[h] = ldexpf(__shfl(qpart, 16 * r + h), -(qexp + 24));
+    // logit (base 2) = kC sum_quarters (s C + z qsk)
+    const float kC = ldexpf(a.scale_log2, qexp + 24);
+    const int kg = (32 * r) / GK;   // K group of this lane's quarter
+
+    const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
+    const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kRowB;
+    const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + bh * a.cap * NKG * 4;
+    const uint8_t* vmeta = static_cast<const uint8_t*>(a.v_meta) + bh * a.cap * NVG * 4;
+
+    float m_lane = -INFINITY;     // running max of head r
+    float l_lane = 0.0f;          // running sum of head r over this lane's tokens
+    float corr[NVG];              // head r, per V group: sum p (z + 8 s) - 8 sum w^
+#pragma unroll
+    for (int g = 0; g < NVG; ++g) corr[g] = 0.0f;
+    // PV: row (g = r, h = i) of column n, per code byte k: whole bytes and low nibbles (scaled 2^-24)
+    f4 accw[4], accl[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        accw[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+        accl[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    auto load_tile = [&](int tile, MTile<NVG>& L) {
+        const int tb = t_lo + tile * kTileT;
+        // valid tokens in the tile (0 past the end: those loads return zeros),
+        // in a scalar register so that the descriptors stay uniform
+        const uint32_t nv = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kTileT, t_hi - tb)));
+        const __amdgpu_buffer_rsrc_t rk = buf::rsrc(kcodes + (int64_t)tb * kRowB, nv * kRowB);
+        const __amdgpu_buffer_rsrc_t rkm = buf::rsrc(kmeta + (int64_t)tb * NKG * 4, nv * NKG * 4);
+        const __amdgpu_buffer_rsrc_t rvm = buf::rsrc(vmeta + (int64_t)tb * NVG * 4, nv * NVG * 4);
+        const __amdgpu_buffer_rsrc_t rv = buf::rsrc(vcodes + (int64_t)tb * kRowB, nv * kRowB);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) L.v[j][e] = buf::load32(rv, (4 * r + j + 16 * e) * kRowB + 4 * n);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t tok = n + 16 * p;
+            L.k[p] = buf::load128(rk, tok * kRowB + 16 * r);
+            L.km[p] = buf::load32(rkm, (tok * NKG + kg) * 4);
+            if constexpr (NVG == 1) {
+                L.vm[p][0] = buf::load32(rvm, tok * 4);
+            } else if constexpr (NVG == 2) {
+                const buf::u32x2 v2 = buf::load64(rvm, tok * 8);
+                L.vm[p][0] = v2.x; L.vm[p][1] = v2.y;
+            } else {
+                const u32x4 v4 = buf::load128(rvm, tok * 16);
+                L.vm[p][0] = v4.x; L.vm[p][1] = v4.y; L.vm[p][2] = v4.z; L.vm[p][3] = v4.w;
+            }
+        }
+    };
+
+    auto process = [&](const MTile<NVG>& L, int tile, auto tail) {
+        constexpr bool kTail = decltype(tail)::value;     // the tile may hold invalid tokens
+        const int tb = t_lo + tile * kTileT;
+        // -------------------------------------------- scores of tokens n and n + 16
+        float xs[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            f4 cq = f4{0.0f, 0.0f, 0.0f, 0.0f};
+            const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) cq = mfma16(qa[c], nibble_operand(kw[c]), cq);
+            // quarter r of the four heads: s C + z qsk
+            const float sk = f16lo(L.km[p]), zk = f16hi(L.km[p]);
+            float y[kGQ];
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h) y[h] = fmaf(sk, cq[h], zk * qsk[h]);
+            // sum the quarters: rows r and r ^ 2 first (keeping the heads of
+            // this row pair), then r and r ^ 1 (keeping head r)
+            const bool hi = (r >> 1) != 0, odd = (r & 1) != 0;
+            const float z0 = (hi ? y[2] : y[0]) + __shfl_xor(hi ? y[0] : y[2], 32);
+            const float z1 = (hi ? y[3] : y[1]) + __shfl_xor(hi ? y[1] : y[3], 32);
+            const float xh = (odd ? z1 : z0) + __shfl_xor(odd ? z0 : z1, 16);
+            const float xl = xh * kC;
+            if constexpr (kTail) xs[p] = (tb + n + 16 * p < t_hi) ? xl : -INFINITY;
+            else xs[p] = xl;
+        }
+
+        // -------------------------------------------- online softmax (rescale on a new max)
+        const bool grow = (xs[0] > m_lane) || (xs[1] > m_lane);
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            float mt = fmaxf(xs[0], xs[1]);
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+            const float m_new = fmaxf(m_lane, mt);
+            const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);
+            m_lane = m_new;
+            l_lane *= alpha;
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) corr[g] *= alpha;
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h) {
+                // row h owns head h
+                const float ah =
+                    __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 16 * h));
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    accw[k][h] *= ah;
+                    accl[k][h] *= ah;
+                }
+            }
+        }
+        // v_exp_f32: weights below 2^-126 of the running max may flush to zero
+        const float p0 = __builtin_amdgcn_exp2f(xs[0] - m_lane);
+        const float p1 = __builtin_amdgcn_exp2f(xs[1] - m_lane);
+        l_lane += p0 + p1;
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) {
+            const uint32_t m0 = L.vm[0][g], m1 = L.vm[1][g];
+            const uint32_t pair = pack_f16(__builtin_fmaf(f16lo(m0), p0, 0.0f), __builtin_fmaf(f16lo(m1), p1, 0.0f));
+            float cg = corr[g];
+            cg = fmaf(p0, fmaf(kVCenter, f16lo(m0), f16hi(m0)), cg);
+            cg = fmaf(p1, fmaf(kVCenter, f16lo(m1), f16hi(m1)), cg);
+            corr[g] = dot2_f16(pair, kVCenterNeg /* (-8, -8) */, cg);
+            wbuf[wave][g][r][n] = pair;
+        }
+        __builtin_amdgcn_wave_barrier();
+
+        // -------------------------------------------- values
+        // A: row n = (group n >> 2, head n & 3), tokens (4r + j, 4r + j + 16) for j < 4
+        u32x4 aw = u32x4{0u, 0u, 0u, 0u};
+        if ((n >> 2) < NVG) aw = *reinterpret_cast<const u32x4*>(&wbuf[wave][n >> 2][n & 3][4 * r]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            u32x4 bw, bl;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // byte k of word n for tokens 4r + j and 4r + j + 16
+                const uint32_t P = __builtin_amdgcn_perm(L.v[j][1], L.v[j][0], 0x0C040C00u + 0x00010001u * k);
+                bw[j] = P;
+                bl[j] = P & 0x000F000Fu;
+            }
+            accw[k] = mfma16(aw, bw, accw[k]);
+            accl[k] = mfma16(aw, bl, accl[k]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // two load buffers in ping-pong: the next tile's loads are in flight while
+    // the current tile is computed; only the split's last tile can be partial
+    MTile<NVG> A, B2;
+    const int full_end = min(tile1, (t_hi - t_lo) / kTileT);
+    int tile = tile0;
+    load_tile(tile, A);
+    for (; tile + 1 < full_end; tile += 2) {
+        load_tile(tile + 1, B2);
+        process(A, tile, Flag<false>{});
+        load_tile(tile + 2, A);
+        process(B2, tile + 1, Flag<false>{});
+    }
+    if (tile < full_end) {
+        process(A, tile, Flag<false>{});
+        ++tile;
+        if (tile < tile1) load_tile(tile, A);
+    }
+    if (tile < tile1) process(A, tile, Flag<true>{});
+
+    // ---------------------------------------------------- wave-level reduction
+    // head r sums over the row's tokens
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        l_lane += __shfl_xor(l_lane, off);
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) corr[g] += __shfl_xor(corr[g], off);
+    }
+    // column n (channels 8n .. 8n+7) is kept in the row of its own V group
+    const int gw = (8 * n) / GV;
+#pragma unroll
+    for (int h = 0; h < kGQ; ++h) {
+        // correction of head h (row h) for V group r
+        float cv = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) {
+            const float cg = __shfl(corr[g], 16 * h);
+            cv = (g == r) ? cg : cv;
+        }
+        if (r == gw) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float lo = accl[k][h], whole = accw[k][h];
+                comb_o[wave][h][8 * n + 2 * k] = lo * 16777216.0f + cv;                   // 2^24
+                comb_o[wave][h][8 * n + 2 * k + 1] = (whole - lo) * 1048576.0f + cv;      // 2^24 / 16
+            }
+        }
+    }
+    if (n == 0) {
+        comb_ml[wave][r][0] = m_lane;
+        comb_ml[wave][r][1] = l_lane;
+    }
+    __syncthreads();
+    // ---------------------------------------------------- merge the 4 waves
+    const int ns = a.n_splits;
+    for (int idx = threadIdx.x; idx < kGQ * kD; idx += 256) {
+        const int h = idx / kD, d = idx % kD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb_ml[w][h][0]);
+        float num = 0.0f, den = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = comb_ml[w][h][0];
+            const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
+            num = fmaf(f, comb_o[w][h][d], num);
+            den = fmaf(f, comb_ml[w][h][1], den);
+        }
+        const int64_t row = (int64_t)b * a.Hq + hk * kGQ + h;
+        if (ns == 1) {
+            a.out[row * kD + d] = num / den;
+        } else {
+            a.ws_o[(row * ns + split) * kD + d] = num;
+            if (d == 0) {
+                a.ws_ml[(row * ns + split) * 2 + 0] = M;
+                a.ws_ml[(row * ns + split) * 2 + 1] = den;
+            }
+        }
+    }
+}
+
+template <int QDT, int GK>
+hipError_t launch_mfma_v(const DecodeArgs& a, hipStream_t s) {
+    dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
+    switch (a.v_group) {
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<QDT, GK, 32>), grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_mfma_kernel<QDT, GK, 64>), grid, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_mfma_kernel<QDT, GK, 128>), grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <int QDT>
+hipError_t launch_mfma_q(const DecodeArgs& a, hipStream_t s) {
+    switch (a.k_group) {
+        case 32: return launch_mfma_v<QDT, 32>(a, s);
+        case 64: return launch_mfma_v<QDT, 64>(a, s);
+        case 128: return launch_mfma_v<QDT, 128>(a, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+// Applies to per-token affine 4-bit K and V at head_dim 128, 4 query heads
+// per kv-head, bf16 or fp16 queries, no RoPE on read.  It shares the split
+// plan of the VALU decode (decode_fast_plan).
+bool decode_mfma_applies(const DecodeArgs& a) {
+    return a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4 && a.v_kind == KVQ_TOK_AFFINE && a.v_bits == 4 &&
+           a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) && !a.rope;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+    if (a.q_dtype == KVQ_BF16) return launch_mfma_q<KVQ_BF16>(a, s);
+    return launch_mfma_q<KVQ_F16>(a, s);
+}
+
+}  // namespace kvq

@@ -132,6 +132,10 @@ hipError_t launch_prefill_attention(const DecodeArgs& a, int n_q, int n_rb, int 
 bool decode_fast_applies(const DecodeArgs& a);
 void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
+// Matrix-core decode for per-token affine 4-bit K and V (a case of the fast
+// path: same plan, launched by launch_decode_fast).
+bool decode_mfma_applies(const DecodeArgs& a);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Hq, int D, int cap);
 void decode_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
 

@@ -9,7 +9,7 @@ device copy of known size.
   python -m evicted_kv_cache_amd.profiling stats  <kernel_stats.csv> --cmd "<command>"
   python -m evicted_kv_cache_amd.profiling counters <counter_collection.csv> [...] --cmd "<command>"
   python -m evicted_kv_cache_amd.profiling traffic --fetch F.csv --write W.csv \
-      --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --kernel decode_tok4 \
+      --copy-fetch CF.csv --copy-write CW.csv --copy-bytes N --kernel decode_mfma \
       [--source file.hip] [--cmd "<command>" ...]
 
 Host-side tooling only: it runs nothing on the GPU.
