@@ -1,7 +1,9 @@
-// decode_mfma.hip -- decode attention for per-token affine 4-bit K and V
-// (mlx-lm style groups, "Low-bit KV caches on MLX", s.1) at head_dim 128 and
-// 4 query heads per kv-head, with both products on the matrix cores
-// (gfx950, v_mfma_f32_16x16x32_f16).
+// decode_mfma.hip -- decode attention for per-token 4-bit K (affine groups,
+// mlx-lm style, "Low-bit KV caches on MLX", s.1; or symmetric blocks of 32,
+// "kv-cache: optional per-channel K-cache mean-centering for Q4_0") and
+// per-token affine 4- or 8-bit V at head_dim 128 and 4 query heads per
+// kv-head, with both products on the matrix cores (gfx950,
+// v_mfma_f32_16x16x32_f16).
 //
 // Same work split as the VALU decode in decode_fast.hip: 4 waves per
 // (batch, kv-head[, token split]), each streaming 32-token tiles with its own
@@ -29,14 +31,18 @@
 //   fp16 weight pairs w^ = fp16(p s) per V group to LDS.
 // * Values: O = W V over the tile's 32 tokens in one MFMA per code byte
 //   position and kind.  W row i = 4g + h holds head h's weights for V group
-//   g (one 16-byte LDS read per lane); V column n is code word n (channels
-//   8n .. 8n+7), and one v_perm_b32 per token pair gives the whole bytes
-//   b = u_2k + 16 u_2k+1 of tokens (t, t + 16) as subnormal fp16 pairs, one
-//   AND their low nibbles.  The high-nibble channel is (byte sum - low sum)
-//   / 16 at the end.  Only the rows of a column's own V group are kept.  The
-//   zero points and the rounding of the weights are accounted exactly in
-//   fp32 as in the VALU decode:
-//     o = sum_t w^_t u_t + sum_t p_t (z_t + 8 s_t) - 8 sum_t w^_t
+//   g (one 16-byte LDS read per lane); V column n is code word n (4-bit:
+//   channels 8n .. 8n+7), and one v_perm_b32 per token pair gives the whole
+//   bytes b = u_2k + 16 u_2k+1 of tokens (t, t + 16) as subnormal fp16
+//   pairs, one AND their low nibbles.  The high-nibble channel is (byte sum -
+//   low sum) / 16 at the end.  8-bit codes are whole bytes already: words n
+//   and n + 16 (channels 4n .. 4n+3 and 64 + 4n ..) give one MFMA per byte.
+//   Only the rows of a column's own V group are kept.  The zero points and
+//   the rounding of the weights are accounted exactly in fp32 as in the VALU
+//   decode (c = 8 for 4-bit codes, 128 for 8-bit):
+//     o = sum_t w^_t u_t + sum_t p_t (z_t + c s_t) - c sum_t w^_t
+// * Symmetric K blocks (value (u - 8) d) are the affine case with s = d and
+//   z = -8 d.
 // * Loads go through buffer resources sized to the valid part of a tile, so
 //   tail tokens read zeros; the last tile of a split masks their logits.
 #include <math.h>
@@ -53,7 +59,9 @@ constexpr int kD = 128;
 constexpr int kGQ = 4;          // query heads per kv-head
 constexpr int kTileT = 32;      // tokens per wave tile
 constexpr int kWaves = 4;
-constexpr int kRowB = kD / 2;   // bytes of 4-bit codes per token (K and V)
+constexpr int kRowB = kD / 2;   // bytes of 4-bit K codes per token
+constexpr int kKAff4 = 0;       // per-token affine K groups: (scale, zero) fp16 pairs
+constexpr int kKSym4 = 1;       // symmetric K blocks of 32: one fp16 scale d, value (u - 8) d
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -89,21 +97,27 @@ __device__ __forceinline__ u32x4 nibble_operand(uint32_t w) {
 }
 
 // Loads of one lane for one tile, issued a tile ahead of their use.
-template <int NVG>
+// VH: V code words per token and lane (1 at 4 bits, 2 at 8).
+template <int NVG, int VH>
 struct MTile {
     u32x4 k[2];          // K codes of channels 32r .. 32r+31, tokens n and n + 16
-    uint32_t km[2];      // K (scale, zero) of that quarter's group, tokens n and n + 16
+    uint32_t km[2];      // K (scale, zero) of that quarter's group (symmetric: d), tokens n and n + 16
     uint32_t vm[2][NVG]; // V (scale, zero) per group, tokens n and n + 16
-    uint32_t v[4][2];    // V code word n of tokens 4r + j and 4r + j + 16
+    uint32_t v[4][2][VH];  // V code words n (and n + 16) of tokens 4r + j and 4r + j + 16
 };
 
-// GK, GV: channels per K / V group (32, 64 or 128).
-template <int QDT, int GK, int GV>
+// KF: K format (kKAff4, or kKSym4 with GK = 32); GK, GV: channels per K / V
+// group (32, 64 or 128); VB: bits per V code (4 or 8).
+template <int QDT, int KF, int GK, int VB, int GV>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+    static_assert(KF == kKAff4 || GK == 32, "symmetric K blocks are 32 channels");
     constexpr int NKG = kD / GK;
     constexpr int NVG = kD / GV;
-    constexpr float kVCenter = 8.0f;                 // V codes are centered on 8
-    constexpr uint32_t kVCenterNeg = 0xC800C800u;    // fp16 (-8, -8)
+    constexpr int VH = VB / 4;
+    constexpr int kVRowB = kD * VB / 8;              // bytes of V codes per token
+    constexpr int kKMetaB = KF == kKSym4 ? 2 : 4;    // bytes per K group and token
+    constexpr float kVCenter = VB == 4 ? 8.0f : 128.0f;                       // V codes are centered on this
+    constexpr uint32_t kVCenterNeg = VB == 4 ? 0xC800C800u : 0xD800D800u;     // fp16 (-c, -c)
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int n = lane & 15, r = lane >> 4;
@@ -163,8 +177,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int kg = (32 * r) / GK;   // K group of this lane's quarter
 
     const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
-    const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kRowB;
-    const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + bh * a.cap * NKG * 4;
+    const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kVRowB;
+    const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + bh * a.cap * NKG * kKMetaB;
     const uint8_t* vmeta = static_cast<const uint8_t*>(a.v_meta) + bh * a.cap * NVG * 4;
 
     float m_lane = -INFINITY;     // running max of head r
@@ -172,32 +186,35 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     float corr[NVG];              // head r, per V group: sum p (z + 8 s) - 8 sum w^
 #pragma unroll
     for (int g = 0; g < NVG; ++g) corr[g] = 0.0f;
-    // PV: row (g = r, h = i) of column n, per code byte k: whole bytes and low nibbles (scaled 2^-24)
-    f4 accw[4], accl[4];
+    // PV: row (g = r, h = i) of column n, scaled 2^-24.  4-bit codes: acc[k]
+    // the whole bytes k, acc[4 + k] their low nibbles; 8-bit: acc[4 hb + k]
+    // byte k of word n + 16 hb
+    f4 acc[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        accw[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-        accl[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
+    for (int k = 0; k < 8; ++k) acc[k] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    auto load_tile = [&](int tile, MTile<NVG>& L) {
+    auto load_tile = [&](int tile, MTile<NVG, VH>& L) {
         const int tb = t_lo + tile * kTileT;
         // valid tokens in the tile (0 past the end: those loads return zeros),
         // in a scalar register so that the descriptors stay uniform
         const uint32_t nv = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kTileT, t_hi - tb)));
         const __amdgpu_buffer_rsrc_t rk = buf::rsrc(kcodes + (int64_t)tb * kRowB, nv * kRowB);
-        const __amdgpu_buffer_rsrc_t rkm = buf::rsrc(kmeta + (int64_t)tb * NKG * 4, nv * NKG * 4);
+        const __amdgpu_buffer_rsrc_t rkm = buf::rsrc(kmeta + (int64_t)tb * NKG * kKMetaB, nv * NKG * kKMetaB);
         const __amdgpu_buffer_rsrc_t rvm = buf::rsrc(vmeta + (int64_t)tb * NVG * 4, nv * NVG * 4);
-        const __amdgpu_buffer_rsrc_t rv = buf::rsrc(vcodes + (int64_t)tb * kRowB, nv * kRowB);
+        const __amdgpu_buffer_rsrc_t rv = buf::rsrc(vcodes + (int64_t)tb * kVRowB, nv * kVRowB);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int e = 0; e < 2; ++e) L.v[j][e] = buf::load32(rv, (4 * r + j + 16 * e) * kRowB + 4 * n);
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int hb = 0; hb < VH; ++hb)
+                    L.v[j][e][hb] = buf::load32(rv, (4 * r + j + 16 * e) * kVRowB + 4 * (n + 16 * hb));
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = n + 16 * p;
             L.k[p] = buf::load128(rk, tok * kRowB + 16 * r);
-            L.km[p] = buf::load32(rkm, (tok * NKG + kg) * 4);
+            if constexpr (KF == kKSym4) L.km[p] = buf::load16(rkm, (tok * NKG + kg) * 2);
+            else L.km[p] = buf::load32(rkm, (tok * NKG + kg) * 4);
             if constexpr (NVG == 1) {
                 L.vm[p][0] = buf::load32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
@@ -210,7 +227,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
-    auto process = [&](const MTile<NVG>& L, int tile, auto tail) {
+    auto process = [&](const MTile<NVG, VH>& L, int tile, auto tail) {
         constexpr bool kTail = decltype(tail)::value;     // the tile may hold invalid tokens
         const int tb = t_lo + tile * kTileT;
         // -------------------------------------------- scores of tokens n and n + 16
@@ -222,7 +239,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) cq = mfma16(qa[c], nibble_operand(kw[c]), cq);
             // quarter r of the four heads: s C + z qsk
-            const float sk = f16lo(L.km[p]), zk = f16hi(L.km[p]);
+            const float sk = f16lo(L.km[p]);
+            const float zk = KF == kKSym4 ? -8.0f * sk : f16hi(L.km[p]);
             float y[kGQ];
 #pragma unroll
             for (int h = 0; h < kGQ; ++h) y[h] = fmaf(sk, cq[h], zk * qsk[h]);
@@ -255,10 +273,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                 const float ah =
                     __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 16 * h));
 #pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    accw[k][h] *= ah;
-                    accl[k][h] *= ah;
-                }
+                for (int k = 0; k < 8; ++k) acc[k][h] *= ah;
             }
         }
         // v_exp_f32: weights below 2^-126 of the running max may flush to zero
@@ -282,24 +297,31 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         u32x4 aw = u32x4{0u, 0u, 0u, 0u};
         if ((n >> 2) < NVG) aw = *reinterpret_cast<const u32x4*>(&wbuf[wave][n >> 2][n & 3][4 * r]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            u32x4 bw, bl;
+        for (int hb = 0; hb < VH; ++hb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // byte k of word n for tokens 4r + j and 4r + j + 16
-                const uint32_t P = __builtin_amdgcn_perm(L.v[j][1], L.v[j][0], 0x0C040C00u + 0x00010001u * k);
-                bw[j] = P;
-                bl[j] = P & 0x000F000Fu;
+            for (int k = 0; k < 4; ++k) {
+                u32x4 bw, bl;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    // byte k of the word for tokens 4r + j and 4r + j + 16
+                    const uint32_t P =
+                        __builtin_amdgcn_perm(L.v[j][1][hb], L.v[j][0][hb], 0x0C040C00u + 0x00010001u * k);
+                    bw[j] = P;
+                    bl[j] = P & 0x000F000Fu;
+                }
+                if constexpr (VB == 4) {
+                    acc[k] = mfma16(aw, bw, acc[k]);
+                    acc[4 + k] = mfma16(aw, bl, acc[4 + k]);
+                } else {
+                    acc[4 * hb + k] = mfma16(aw, bw, acc[4 * hb + k]);
+                }
             }
-            accw[k] = mfma16(aw, bw, accw[k]);
-            accl[k] = mfma16(aw, bl, accl[k]);
-        }
         __builtin_amdgcn_wave_barrier();
     };
 
     // two load buffers in ping-pong: the next tile's loads are in flight while
     // the current tile is computed; only the split's last tile can be partial
-    MTile<NVG> A, B2;
+    MTile<NVG, VH> A, B2;
     const int full_end = min(tile1, (t_hi - t_lo) / kTileT);
     int tile = tile0;
     load_tile(tile, A);
@@ -324,8 +346,6 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < NVG; ++g) corr[g] += __shfl_xor(corr[g], off);
     }
-    // column n (channels 8n .. 8n+7) is kept in the row of its own V group
-    const int gw = (8 * n) / GV;
 #pragma unroll
     for (int h = 0; h < kGQ; ++h) {
         // correction of head h (row h) for V group r
@@ -335,12 +355,24 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
             const float cg = __shfl(corr[g], 16 * h);
             cv = (g == r) ? cg : cv;
         }
-        if (r == gw) {
+        // a column is kept in the row of its own V group
+        if constexpr (VB == 4) {
+            if (r == (8 * n) / GV) {      // channels 8n .. 8n+7
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float lo = accl[k][h], whole = accw[k][h];
-                comb_o[wave][h][8 * n + 2 * k] = lo * 16777216.0f + cv;                   // 2^24
-                comb_o[wave][h][8 * n + 2 * k + 1] = (whole - lo) * 1048576.0f + cv;      // 2^24 / 16
+                for (int k = 0; k < 4; ++k) {
+                    const float whole = acc[k][h], lo = acc[4 + k][h];
+                    comb_o[wave][h][8 * n + 2 * k] = lo * 16777216.0f + cv;                   // 2^24
+                    comb_o[wave][h][8 * n + 2 * k + 1] = (whole - lo) * 1048576.0f + cv;      // 2^24 / 16
+                }
+            }
+        } else {
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int c0 = 4 * (n + 16 * hb);     // channels c0 .. c0 + 3
+                if (r == c0 / GV) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) comb_o[wave][h][c0 + k] = acc[4 * hb + k][h] * 16777216.0f + cv;
+                }
             }
         }
     }
@@ -377,36 +409,45 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     }
 }
 
-template <int QDT, int GK>
+template <int QDT, int KF, int GK, int VB>
 hipError_t launch_mfma_v(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
     switch (a.v_group) {
-        case 32: hipLaunchKernelGGL((decode_mfma_kernel<QDT, GK, 32>), grid, dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((decode_mfma_kernel<QDT, GK, 64>), grid, dim3(256), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((decode_mfma_kernel<QDT, GK, 128>), grid, dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 32>), grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 64>), grid, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 128>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+template <int QDT, int KF, int GK>
+hipError_t launch_mfma_k(const DecodeArgs& a, hipStream_t s) {
+    return a.v_bits == 8 ? launch_mfma_v<QDT, KF, GK, 8>(a, s) : launch_mfma_v<QDT, KF, GK, 4>(a, s);
+}
+
 template <int QDT>
 hipError_t launch_mfma_q(const DecodeArgs& a, hipStream_t s) {
+    if (a.k_kind == KVQ_TOK_SYM4) return launch_mfma_k<QDT, kKSym4, 32>(a, s);
     switch (a.k_group) {
-        case 32: return launch_mfma_v<QDT, 32>(a, s);
-        case 64: return launch_mfma_v<QDT, 64>(a, s);
-        case 128: return launch_mfma_v<QDT, 128>(a, s);
+        case 32: return launch_mfma_k<QDT, kKAff4, 32>(a, s);
+        case 64: return launch_mfma_k<QDT, kKAff4, 64>(a, s);
+        case 128: return launch_mfma_k<QDT, kKAff4, 128>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
 
 }  // namespace
 
-// Applies to per-token affine 4-bit K and V at head_dim 128, 4 query heads
-// per kv-head, bf16 or fp16 queries, no RoPE on read.  It shares the split
-// plan of the VALU decode (decode_fast_plan).
+// Applies to per-token 4-bit K (affine groups or symmetric blocks) and
+// affine 4- or 8-bit V at head_dim 128, 4 query heads per kv-head, bf16 or
+// fp16 queries, no RoPE on read (a per-key rotation would undo the factored
+// scale).  It shares the split plan of the VALU decode (decode_fast_plan).
 bool decode_mfma_applies(const DecodeArgs& a) {
-    return a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4 && a.v_kind == KVQ_TOK_AFFINE && a.v_bits == 4 &&
-           a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) && !a.rope;
+    const bool k_ok = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4;
+    const bool v_ok = a.v_kind == KVQ_TOK_AFFINE && (a.v_bits == 4 || a.v_bits == 8);
+    return k_ok && v_ok && a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) &&
+           !a.rope;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
