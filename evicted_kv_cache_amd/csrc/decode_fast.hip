@@ -1,58 +1,45 @@
-// decode_fast.hip -- bandwidth-tuned decode attention for per-token 4-bit K
-// (affine groups, mlx-lm style, "Low-bit KV caches on MLX", s.1; or symmetric
-// blocks of 32, "kv-cache: optional per-channel K-cache mean-centering for
-// Q4_0") and per-token affine 4- or 8-bit V, at head_dim 128 and 4 query heads
-// per kv-head (gfx950).
+// decode_fast.hip -- decode attention for KIVI keys ("StreamingLLM + KIVI",
+// "KIVI": per-channel 4-bit keys over 32-token groups, the open group kept in
+// full precision) and per-token affine 4- or 8-bit values ("Low-bit KV caches
+// on MLX", s.1) at head_dim 128 and 1-4 query heads per kv-head, on the VALU
+// (gfx950).  Per-token 4-bit keys run on the matrix cores instead
+// (decode_mfma.hip); both kernels use the split plan and the dispatch below.
 //
 // Decode streams the whole cache once per step ("Low-bit KV caches on MLX",
-// s.5: decode spends its time reading the cache).  At 4.5 bits per element
-// and 4 query heads per kv-head the VALU has ~2.8 lane-ops per cached element
-// at the HBM roofline, so the kernel is built around keeping per-element
-// VALU work minimal:
+// s.5: decode spends its time reading the cache):
 //
 // * Workgroup = 4 waves on one (batch, kv-head[, token split]); each wave
 //   owns a contiguous run of 32-token tiles with its own online softmax; the
 //   waves merge through LDS (token splits merge in a combine kernel).
-// * Codes become fp16 operands with one AND: a nibble left in place is the
-//   fp16 subnormal u * 2^-24 (low nibble of a byte) or u * 2^-20 (high
-//   nibble); v_dot2_f32_f16 multiplies subnormals exactly, so each
-//   instruction does two exact MACs into fp32 and the power-of-two scales are
-//   folded into the query (x 1/16 for high nibbles) or applied at the end.
 // * QK^T: lane (token t, quarter of head_dim) reads 16 bytes of codes per
-//   token; the query is held as fp16 pairs scaled by a power of two shared by
-//   the head group (exact for bf16/fp16 queries).  The group's scale s and zero
-//   z are factored out of the dot product:  q . k = s (q . u) + z sum(q).
-//   The four quarter partials are reduced over the lane quad with DPP adds
-//   that leave lane quarter h with query head h.  With K groups of at least
-//   64 channels the reduce runs in two steps: within each 64-channel half
-//   (one scale, applied once to the pair sum), then across the halves; the
-//   zero-point terms z sum(q) of both groups are added after the reduce.
+//   token.  A channel's scale and zero live in the table row of the token's
+//   group, so they cannot be factored out of the dot product: each wave
+//   stages the table rows of a tile's first and last tokens in LDS (a tile
+//   spans at most those two in an unevicted cache), every lane dequantizes
+//   its token's 32 channels in fp32 (k = u s + z) and multiplies them by the
+//   query with mixed-precision FMAs.  The query is held as fp16 pairs scaled
+//   by a power of two shared by the head group (exact for bf16/fp16 queries).
+//   Tokens whose row is neither staged row, and tokens of the open group,
+//   take a per-lane path that reads their row or residual from memory.  The
+//   four quarter partials of a head meet in lane quarter h by DPP rotations.
 // * Softmax: lane (t, h) computes p for head h of tokens t and t+16 (one
 //   exp each) and writes the fp16 weight pair (p_t s_t, p_t+16 s_t+16) to
 //   LDS; the running max is rescaled only when a wave sees a larger logit,
 //   so weights stay <= 1 and never overflow fp16.
-// * PV: lane (phase, 8-channel chunk) reads the codes of tokens t and t+16;
-//   one v_perm_b32 per byte position gives the pair of whole bytes
-//   (b_t, b_t+16), b = u_2k + 16 u_2k+1, as fp16 subnormals, and one AND its
-//   low nibbles; v_dot2_f32_f16 with the weight pair does two token MACs on
-//   each, and the high-nibble channel is (byte sum - low sum) / 16 at the end.
-//   The zero points and the fp16 rounding of the weights are accounted
-//   exactly in fp32:
-//     o = sum_t w^_t u_t + sum_t p_t (z_t + 8 s_t) - 8 sum_t w^_t
-//   so rounding a weight only perturbs w (u - 8).
+// * PV: lane (phase, 8-channel chunk) reads the codes of tokens t and t+16.
+//   A 4-bit code left in place under a mask is an fp16 subnormal, which
+//   v_dot2_f32_f16 multiplies exactly: one v_perm_b32 per byte position
+//   gives the pair of whole bytes (b_t, b_t+16), b = u_2k + 16 u_2k+1, and
+//   one AND its low nibbles; v_dot2_f32_f16 with the weight pair does two
+//   token MACs on each, and the high-nibble channel is (byte sum - low sum)
+//   / 16 at the end (8-bit codes: the whole bytes are the codes).  The zero
+//   points and the fp16 rounding of the weights are accounted exactly in
+//   fp32 (c = 8 for 4-bit codes, 128 for 8-bit):
+//     o = sum_t w^_t u_t + sum_t p_t (z_t + c s_t) - c sum_t w^_t
+//   so rounding a weight only perturbs w (u - c).
 // * Tails need no clamping: loads go through buffer resources whose size is
 //   the valid part of the tile, and out-of-range loads return zero.  Only the
 //   last tile of a split can hold invalid tokens; it alone masks its logits.
-// * KIVI keys ("KIVI" page: per-channel 4-bit keys over 32-token groups with
-//   the open group in full precision) use the same tiles, softmax and value
-//   path with 1-4 query heads per kv-head.  A channel's scale and zero live in
-//   the table row of the token's group, so the factoring above does not
-//   apply: each wave stages the table rows of a tile's first and last tokens
-//   in LDS (a tile spans at most those two in an unevicted cache), every lane
-//   dequantizes its token's 32 channels in fp32 (k = u s + z) and multiplies
-//   them by the exact fp16 query with mixed-precision FMAs.  Tokens whose row
-//   is neither staged row, and tokens of the open group, take a per-lane path
-//   that reads their row or residual from memory.
 #include <math.h>
 
 #include "dequant8.h"
@@ -66,10 +53,6 @@ constexpr int kGQ = 4;          // query heads per kv-head
 constexpr int kTileT = 32;      // tokens per wave tile
 constexpr int kWaves = 4;
 constexpr int kRowB = kD / 2;   // bytes of 4-bit K codes per token
-// K code formats of the fast path
-constexpr int kKAff4 = 0;       // per-token affine groups: (scale, zero) fp16 pairs
-constexpr int kKSym4 = 1;       // symmetric blocks of 32: one fp16 scale d, value (u - 8) d
-constexpr int kKKivi = 2;       // KIVI: per-channel (scale, zero) in the table row of the token's group
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -78,13 +61,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
                                   false);
-}
-// First product of a chain: v_dot2_f32_f16 with an inline zero accumulator
-// (the tied-accumulator form would need a separate move of zero).
-__device__ __forceinline__ float dot2_f16_first(uint32_t a, uint32_t b) {
-    float r;
-    asm("v_dot2_f32_f16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
-    return r;
 }
 // Round-to-nearest-even pack of two fp32 into an fp16 pair.
 __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
@@ -121,12 +97,6 @@ __device__ __forceinline__ float quad_from_minus(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
 }
 
-// DPP quad exchange: value of lane l ^ X (X = 1 or 2) within the lane's quad.
-template <int X>
-__device__ __forceinline__ float quad_xor(float v) {
-    constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;   // quad_perm [1,0,3,2] / [2,3,0,1]
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
-}
 template <bool B>
 struct Flag { static constexpr bool value = B; };
 
@@ -135,9 +105,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_
 }
 __device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
-__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 __device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
@@ -161,37 +128,23 @@ struct VMeta { uint32_t m[2][NVG]; };   // (scale, zero) of tokens t, t+16 per V
 template <int NVG, int VW>
 struct TileLoads {
     u32x4 k[2];          // codes of the lane's quarter for tokens t and t+16
-    uint32_t km[2];      // K (scale, zero) of the quarter's group (sym4: the scale d), tokens t, t+16
-    uint32_t kmo[2];     // K (scale, zero) of the other 64-channel half's group (K groups of 64)
     VMeta<NVG> vm;
     uint32_t v[4][2][VW];  // V code words (8 channels) of tokens ph+4j and ph+4j+16
-    // KIVI keys: table rows of tokens t, t+16; this lane's 8 bytes of the two
-    // staged rows (the rows of the tile's first and last coded tokens, r0, r1)
+    // table rows of tokens t, t+16; this lane's 8 bytes of the two staged
+    // rows (the rows of the tile's first and last coded tokens, r0, r1)
     int32_t krow[2];
     u32x2 stg[2];
     int r0, r1;
 };
 
-// KF: K format (kKAff4, kKSym4 whose blocks are GK = 32 channels, or kKKivi
-// with GK = 32 unused);
-// GK, GV: channels per K / V group (32, 64 or 128); VB: bits per V code (4 or 8).
-template <int QDT, int KF, int GK, int VB, int GV>
-__global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
-    static_assert(KF == kKAff4 || GK == 32, "symmetric K blocks are 32 channels");
-    constexpr bool kKivi = KF == kKKivi;
-    constexpr int NKG = kD / GK;      // K groups per row
+// GV: channels per V group (32, 64 or 128); VB: bits per V code (4 or 8).
+template <int QDT, int VB, int GV>
+__global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
     constexpr int NVG = kD / GV;      // V groups per row
     constexpr int VW = VB / 4;        // V code words per token and lane
     constexpr int kVRowB = kD * VB / 8;   // bytes of V codes per token
     constexpr float kVCenter = VB == 4 ? 8.0f : 128.0f;          // codes are centered on this
     constexpr uint32_t kVCenterNeg = VB == 4 ? 0xC800C800u : 0xD800D800u;   // fp16 (-c, -c)
-    constexpr int kKMetaB = KF == kKSym4 ? 2 : 4;                 // bytes per K group and token
-    // When each 64-channel half of head_dim lies in one K group (GK >= 64),
-    // the four quarter partials of a head are reduced in two steps: first
-    // within the half (same scale, applied once to the pair sum), then across
-    // the halves.  With GK = 32 every quarter is scaled before one 3-step
-    // rotation reduce.
-    constexpr bool kHalfReduce = GK >= 64;
 
     // the wave index is uniform across the wave; say so, so that tile bases and
     // buffer descriptors stay in scalar registers
@@ -204,22 +157,13 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     const int tile0 = (n_tiles * wave) / kWaves, tile1 = (n_tiles * (wave + 1)) / kWaves;
 
     __shared__ uint32_t wbuf[kWaves][16][NVG][kGQ];           // fp16 weight pairs of a tile
-    __shared__ __align__(16) uint32_t kst[kKivi ? kWaves : 1][2][kD];   // KIVI: staged table rows
+    __shared__ __align__(16) uint32_t kst[kWaves][2][kD];     // staged table rows
     __shared__ float comb_o[kWaves][kGQ][kD];
     __shared__ float comb_ml[kWaves][kGQ][2];
 
     // QK role: token t16 (and t16 + 16), quarter q4 of head_dim; after the
     // reduce-scatter the lane owns query head hq = q4.
     const int t16 = lane >> 2, q4 = lane & 3;
-    const int kg = (32 * q4) / GK;                          // K group of the quarter
-    // query head held in dot register j.  Half reduce: register order
-    // [q4, q4^2, q4^1, q4^3], so that step 1 (partner q4^1) adds registers
-    // (0, 2) and (1, 3) of the two lanes and step 2 (partner q4^2) leaves
-    // head q4 in lane quarter q4.  Rotation reduce: head (q4 + j) % 4.
-    auto head_of = [&](int j) {
-        if constexpr (kHalfReduce) return q4 ^ (j == 1 ? 2 : j == 2 ? 1 : j);
-        else return (q4 + j) & 3;
-    };
     // PV role: phase ph (tokens ph + 4j, j < 4, and +16), chunk c (channels 8c..8c+7)
     const int ph = lane >> 4, c = lane & 15;
     const int vg_c = (8 * c) / GV;
@@ -248,15 +192,12 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
     if (qmax > 0.0f) { frexpf(qmax, &qexp); qexp -= 15; }
     const float qscale = ldexpf(1.0f, -qexp);
     // register j of this lane holds query head (q4 + j) % 4, so that the four
-    // quarter partials of head h meet in lane quarter h by quad rotations only
-    // (affine / symmetric K: channel pairs (8k+i, 8k+i+4) as the nibble masks
-    // lay them out, high nibbles pre-divided by 16; KIVI K: pairs (8k+2i, 8k+2i+1))
+    // quarter partials of head h meet in lane quarter h by quad rotations
+    // only; channel pairs (8k+2i, 8k+2i+1)
     uint32_t qv[kGQ][16];
-    float qsum[kGQ];
 #pragma unroll
     for (int j = 0; j < kGQ; ++j) {
-        const int h = head_of(j);
-        float s = 0.0f;
+        const int h = (q4 + j) & 3;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             float x[8];
@@ -273,55 +214,18 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                 for (int i = 0; i < 8; ++i) x[i] = 0.0f;
             }
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s += x[i];
-            if constexpr (kKivi) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) qv[j][4 * k + i] = pack_f16(x[2 * i] * qscale, x[2 * i + 1] * qscale);
-            } else {
-                qv[j][4 * k + 0] = pack_f16(x[0] * qscale, x[4] * qscale);
-                qv[j][4 * k + 1] = pack_f16(x[1] * qscale * 0.0625f, x[5] * qscale * 0.0625f);
-                qv[j][4 * k + 2] = pack_f16(x[2] * qscale, x[6] * qscale);
-                qv[j][4 * k + 3] = pack_f16(x[3] * qscale * 0.0625f, x[7] * qscale * 0.0625f);
-            }
+            for (int i = 0; i < 4; ++i) qv[j][4 * k + i] = pack_f16(x[2 * i] * qscale, x[2 * i + 1] * qscale);
         }
-        qsum[j] = s;
     }
-    // logit (base 2) = cexp (s 2^(qexp+24) (q' . u') + z qsum); KIVI: scale_log2 2^qexp (q' . k)
-    const float kC = ldexpf(a.scale_log2, kKivi ? qexp : qexp + 24);
-    // per head: z * qsum / 2^(qexp+24), so that logit = kC (s (q' . u') + z qsk)
-    float qsk[kGQ];
-#pragma unroll
-    for (int h = 0; h < kGQ; ++h) qsk[h] = ldexpf(qsum[h], -(qexp + 24));
-    float qsk8[kGQ];              // symmetric K: the zero point -8 d, as -8 qsk
-#pragma unroll
-    for (int h = 0; h < kGQ; ++h) qsk8[h] = -8.0f * qsk[h];
-    // half reduce: the zero-point term of head q4 is added after the reduce,
-    // as z_own qz_own + z_other qz_other with qz = scale_log2 * (sum of q over
-    // the K group) for the group of this lane's half and the other group
-    float qz_own = 0.0f, qz_oth = 0.0f;
-    if constexpr (kHalfReduce) {
-        const uint16_t* qh = q16 + q4 * kD;
-#pragma unroll
-        for (int k = 0; k < kD / 8; ++k) {
-            const uint4 xx = *reinterpret_cast<const uint4*>(qh + 8 * k);
-            const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
-            float t = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t += q_elem<QDT>(e4[i] & 0xFFFFu) + q_elem<QDT>(e4[i] >> 16);
-            if ((8 * k) / GK == kg) qz_own += t;
-            else qz_oth += t;
-        }
-        qz_own *= a.scale_log2;
-        qz_oth *= a.scale_log2;
-    }
+    // logit (base 2) = scale_log2 2^qexp (q' . k)
+    const float kC = ldexpf(a.scale_log2, qexp);
 
     const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
     const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kVRowB;
-    const uint8_t* kmeta = static_cast<const uint8_t*>(a.k_meta) + bh * a.cap * NKG * kKMetaB;
     const uint32_t* vmeta = static_cast<const uint32_t*>(a.v_meta) + bh * a.cap * NVG;
-    // KIVI: the (batch, kv-head)'s table [rows][kD] of (scale, zero) fp16 pairs
-    const int rows_t = kKivi ? a.cap / a.Gt + 3 : 0;
-    const uint8_t* ktab = static_cast<const uint8_t*>(a.k_meta) + (kKivi ? bh * rows_t * kD * 4 : 0);
+    // the (batch, kv-head)'s table [rows][kD] of (scale, zero) fp16 pairs
+    const int rows_t = a.cap / a.Gt + 3;
+    const uint8_t* ktab = static_cast<const uint8_t*>(a.k_meta) + bh * rows_t * kD * 4;
 
     float m_lane = -INFINITY;     // running max of head q4
     float l_lane = 0.0f;          // running sum of head q4 (this lane's tokens)
@@ -340,7 +244,6 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         // kept in a scalar register so the buffer descriptors stay uniform
         const uint32_t nv = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kTileT, t_hi - tb)));
         const __amdgpu_buffer_rsrc_t rk = rsrc(kcodes + (int64_t)tb * kRowB, nv * kRowB);
-        const __amdgpu_buffer_rsrc_t rkm = rsrc(kmeta + (int64_t)tb * NKG * kKMetaB, kKivi ? 0u : nv * NKG * kKMetaB);
         const __amdgpu_buffer_rsrc_t rvm = rsrc(vmeta + (int64_t)tb * NVG, nv * NVG * 4);
         const __amdgpu_buffer_rsrc_t rv = rsrc(vcodes + (int64_t)tb * kVRowB, nv * kVRowB);
 #pragma unroll
@@ -361,16 +264,9 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = t16 + 16 * p;
             L.k[p] = bload128(rk, tok * kRowB + 16 * q4);
-            if constexpr (kKivi) {
-                // the token's table row (slots past the tile's valid part read 0)
-                const __amdgpu_buffer_rsrc_t rrow = rsrc(a.k_row + tb, nv * 4);
-                L.krow[p] = (int32_t)bload32(rrow, tok * 4);
-            } else if constexpr (KF == kKSym4) {
-                L.km[p] = bload16(rkm, (tok * NKG + kg) * 2);
-            } else {
-                L.km[p] = bload32(rkm, (tok * NKG + kg) * 4);
-                if constexpr (GK == 64) L.kmo[p] = bload32(rkm, (tok * NKG + (kg ^ 1)) * 4);
-            }
+            // the token's table row (slots past the tile's valid part read 0)
+            const __amdgpu_buffer_rsrc_t rrow = rsrc(a.k_row + tb, nv * 4);
+            L.krow[p] = (int32_t)bload32(rrow, tok * 4);
             if constexpr (NVG == 1) {
                 L.vm.m[p][0] = bload32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
@@ -381,22 +277,20 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
                 L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y; L.vm.m[p][2] = x.z; L.vm.m[p][3] = x.w;
             }
         }
-        if constexpr (kKivi) {
-            // the table rows of the tile's first and last coded tokens, staged
-            // through registers: lane l loads channels 2l, 2l+1 of each (the
-            // table buffer covers the whole table, so any row index is safe)
-            const int nq = max(0, min(tb + (int)nv, a.n_quant) - tb);
-            int r0 = 0, r1 = 0;
-            if (nq > 0) {
-                r0 = a.k_row[tb];
-                r1 = a.k_row[tb + nq - 1];
-            }
-            L.r0 = __builtin_amdgcn_readfirstlane(r0);
-            L.r1 = __builtin_amdgcn_readfirstlane(r1);
-            const __amdgpu_buffer_rsrc_t rtab = rsrc(ktab, (uint32_t)rows_t * kD * 4);
-            L.stg[0] = bload64(rtab, (uint32_t)L.r0 * kD * 4 + 8 * lane);
-            L.stg[1] = bload64(rtab, (uint32_t)L.r1 * kD * 4 + 8 * lane);
+        // the table rows of the tile's first and last coded tokens, staged
+        // through registers: lane l loads channels 2l, 2l+1 of each (the
+        // table buffer covers the whole table, so any row index is safe)
+        const int nq = max(0, min(tb + (int)nv, a.n_quant) - tb);
+        int r0 = 0, r1 = 0;
+        if (nq > 0) {
+            r0 = a.k_row[tb];
+            r1 = a.k_row[tb + nq - 1];
         }
+        L.r0 = __builtin_amdgcn_readfirstlane(r0);
+        L.r1 = __builtin_amdgcn_readfirstlane(r1);
+        const __amdgpu_buffer_rsrc_t rtab = rsrc(ktab, (uint32_t)rows_t * kD * 4);
+        L.stg[0] = bload64(rtab, (uint32_t)L.r0 * kD * 4 + 8 * lane);
+        L.stg[1] = bload64(rtab, (uint32_t)L.r1 * kD * 4 + 8 * lane);
     };
 
     auto process = [&](const TileLoads<NVG, VW>& L, int tile, auto tail) {
@@ -404,127 +298,80 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
         const int tb = t_lo + tile * kTileT;
         // -------------------------------------------- QK^T, two passes (t16, t16 + 16)
         float xs[2];
-        if constexpr (kKivi) {
-            // stage the two table rows; kst[wave][r][c] = (scale, zero) of channel c
-            *reinterpret_cast<u32x2*>(&kst[wave][0][2 * lane]) = L.stg[0];
-            *reinterpret_cast<u32x2*>(&kst[wave][1][2 * lane]) = L.stg[1];
-            __builtin_amdgcn_wave_barrier();
-            // every token of the wave valid-and-coded with a staged row: the common case
-            bool fast = true;
+        // stage the two table rows; kst[wave][r][c] = (scale, zero) of channel c
+        *reinterpret_cast<u32x2*>(&kst[wave][0][2 * lane]) = L.stg[0];
+        *reinterpret_cast<u32x2*>(&kst[wave][1][2 * lane]) = L.stg[1];
+        __builtin_amdgcn_wave_barrier();
+        // every token of the wave valid-and-coded with a staged row: the common case
+        bool fast = true;
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int t = tb + t16 + 16 * p;
+        for (int p = 0; p < 2; ++p) {
+            const int t = tb + t16 + 16 * p;
+            const bool staged = L.krow[p] == L.r0 || L.krow[p] == L.r1;
+            fast = fast && (t >= t_hi || (t < a.n_quant && staged));
+        }
+        const bool all_fast = __builtin_amdgcn_ballot_w64(!fast) == 0;
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int t = tb + t16 + 16 * p;
+            const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
+            // register j: query head (q4 + j) % 4 over this quarter; eight
+            // channels at a time, exact fp16 x fp32 products
+            float part[kGQ];
+#pragma unroll
+            for (int j = 0; j < kGQ; ++j) part[j] = 0.0f;
+            auto chunk = [&](int k, const float xk[8]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int j = 0; j < kGQ; ++j)
+#pragma unroll
+                    for (int i = 0; i < 8; i += 2) {
+                        part[j] = fma_lo(qv[j][4 * k + i / 2], xk[i], part[j]);
+                        part[j] = fma_hi(qv[j][4 * k + i / 2], xk[i + 1], part[j]);
+                    }
+            };
+            // keys of channels 8k .. 8k+7 of the quarter: k = u s + z from the row's (scale, zero) pairs
+            auto deq = [&](int k, const uint32_t m[8], float xk[8]) __attribute__((always_inline)) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xk[i] = fmaf((float)((kw[k] >> (4 * i)) & 0xFu), f16lo(m[i]), f16hi(m[i]));
+            };
+            if (all_fast) {
+                const uint32_t* row = &kst[wave][L.krow[p] == L.r0 ? 0 : 1][32 * q4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint4 m0 = *reinterpret_cast<const uint4*>(row + 8 * k);
+                    const uint4 m1 = *reinterpret_cast<const uint4*>(row + 8 * k + 4);
+                    const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+                    float xk[8];
+                    deq(k, m, xk);
+                    chunk(k, xk);
+                }
+            } else {
+                // per lane: past the split (zeros), the open group (the
+                // full-precision residual), a staged row, or a row in memory
                 const bool staged = L.krow[p] == L.r0 || L.krow[p] == L.r1;
-                fast = fast && (t >= t_hi || (t < a.n_quant && staged));
-            }
-            const bool all_fast = __builtin_amdgcn_ballot_w64(!fast) == 0;
+                const uint32_t* row = staged ? &kst[wave][L.krow[p] == L.r0 ? 0 : 1][32 * q4]
+                                             : reinterpret_cast<const uint32_t*>(ktab) + (int64_t)L.krow[p] * kD + 32 * q4;
 #pragma unroll
-            for (int p = 0; p < 2; ++p) {
-                const int t = tb + t16 + 16 * p;
-                const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
-                // register j: query head (q4 + j) % 4 over this quarter; eight
-                // channels at a time, exact fp16 x fp32 products
-                float part[kGQ];
+                for (int k = 0; k < 4; ++k) {
+                    float xk[8];
+                    if (t >= t_hi) {
 #pragma unroll
-                for (int j = 0; j < kGQ; ++j) part[j] = 0.0f;
-                auto chunk = [&](int k, const float xk[8]) __attribute__((always_inline)) {
-#pragma unroll
-                    for (int j = 0; j < kGQ; ++j)
-#pragma unroll
-                        for (int i = 0; i < 8; i += 2) {
-                            part[j] = fma_lo(qv[j][4 * k + i / 2], xk[i], part[j]);
-                            part[j] = fma_hi(qv[j][4 * k + i / 2], xk[i + 1], part[j]);
-                        }
-                };
-                // keys of channels 8k .. 8k+7 of the quarter: k = u s + z from the row's (scale, zero) pairs
-                auto deq = [&](int k, const uint32_t m[8], float xk[8]) __attribute__((always_inline)) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) xk[i] = fmaf((float)((kw[k] >> (4 * i)) & 0xFu), f16lo(m[i]), f16hi(m[i]));
-                };
-                if (all_fast) {
-                    const uint32_t* row = &kst[wave][L.krow[p] == L.r0 ? 0 : 1][32 * q4];
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
+                        for (int i = 0; i < 8; ++i) xk[i] = 0.0f;
+                    } else if (t >= a.n_quant) {
+                        dq::load8(a.k_resid, (bh * a.Gt + (t - a.n_quant)) * kD + 32 * q4 + 8 * k, a.in_dtype, xk);
+                    } else {
                         const uint4 m0 = *reinterpret_cast<const uint4*>(row + 8 * k);
                         const uint4 m1 = *reinterpret_cast<const uint4*>(row + 8 * k + 4);
                         const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-                        float xk[8];
                         deq(k, m, xk);
-                        chunk(k, xk);
                     }
-                } else {
-                    // per lane: past the split (zeros), the open group (the
-                    // full-precision residual), a staged row, or a row in memory
-                    const bool staged = L.krow[p] == L.r0 || L.krow[p] == L.r1;
-                    const uint32_t* row = staged ? &kst[wave][L.krow[p] == L.r0 ? 0 : 1][32 * q4]
-                                                 : reinterpret_cast<const uint32_t*>(ktab) + (int64_t)L.krow[p] * kD + 32 * q4;
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        float xk[8];
-                        if (t >= t_hi) {
-#pragma unroll
-                            for (int i = 0; i < 8; ++i) xk[i] = 0.0f;
-                        } else if (t >= a.n_quant) {
-                            dq::load8(a.k_resid, (bh * a.Gt + (t - a.n_quant)) * kD + 32 * q4 + 8 * k, a.in_dtype, xk);
-                        } else {
-                            const uint4 m0 = *reinterpret_cast<const uint4*>(row + 8 * k);
-                            const uint4 m1 = *reinterpret_cast<const uint4*>(row + 8 * k + 4);
-                            const uint32_t m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-                            deq(k, m, xk);
-                        }
-                        chunk(k, xk);
-                    }
-                }
-                const float xl = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
-                                  quad_from_minus<3>(part[3])) * kC;
-                if constexpr (kTail) xs[p] = t < t_hi ? xl : -INFINITY;
-                else xs[p] = xl;
-            }
-        } else {
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            float dsum[kGQ];
-            const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t w = kw[k];
-                const uint32_t w8 = w >> 8;
-                const uint32_t u0 = w & 0x000F000Fu, u1 = w & 0x00F000F0u;     // (n0,n4), (n1,n5)
-                const uint32_t u2 = w8 & 0x000F000Fu, u3 = w8 & 0x00F000F0u;   // (n2,n6), (n3,n7)
-#pragma unroll
-                for (int h = 0; h < kGQ; ++h) {
-                    dsum[h] = k == 0 ? dot2_f16_first(u0, qv[h][0]) : dot2_f16(u0, qv[h][4 * k + 0], dsum[h]);
-                    dsum[h] = dot2_f16(u1, qv[h][4 * k + 1], dsum[h]);
-                    dsum[h] = dot2_f16(u2, qv[h][4 * k + 2], dsum[h]);
-                    dsum[h] = dot2_f16(u3, qv[h][4 * k + 3], dsum[h]);
+                    chunk(k, xk);
                 }
             }
-            float x;
-            if constexpr (kHalfReduce) {
-                // step 1 within the half, scale of the half's group, step 2 across halves
-                const float h0 = mul_lo(L.km[p], dsum[0] + quad_xor<1>(dsum[2]));
-                const float h1 = mul_lo(L.km[p], dsum[1] + quad_xor<1>(dsum[3]));
-                const float sum = h0 + quad_xor<2>(h1);
-                float zt = f16hi(L.km[p]) * qz_own;
-                if constexpr (GK == 64) zt = fmaf(f16hi(L.kmo[p]), qz_oth, zt);
-                x = fmaf(sum, kC, zt);
-            } else {
-                float part[kGQ];
-                if constexpr (KF == kKSym4) {
-                    // zero point -8 d:  d (q'.u') - 8 d qsk
-#pragma unroll
-                    for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16lo(L.km[p]) * qsk8[h]);
-                } else {
-#pragma unroll
-                    for (int h = 0; h < kGQ; ++h) part[h] = fmaf(f16lo(L.km[p]), dsum[h], f16hi(L.km[p]) * qsk[h]);
-                }
-                // head q4 of this token: part[0] here plus part[k] of lane quarter q4 - k
-                x = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
-                     quad_from_minus<3>(part[3])) * kC;
-            }
-            if constexpr (kTail) xs[p] = (tb + t16 + 16 * p < t_hi) ? x : -INFINITY;
-            else xs[p] = x;
-        }
+            const float xl = (part[0] + quad_from_minus<1>(part[1]) + quad_from_minus<2>(part[2]) +
+                              quad_from_minus<3>(part[3])) * kC;
+            if constexpr (kTail) xs[p] = t < t_hi ? xl : -INFINITY;
+            else xs[p] = xl;
         }
 
         // -------------------------------------------- online softmax (rescale on a new max)
@@ -699,17 +546,16 @@ __global__ __launch_bounds__(256, 2) void decode_tok4_kernel(DecodeArgs a) {
 
 }  // namespace
 
-// Fast path applies to affine 4/8-bit V, D = 128, bf16 or fp16 queries and no
-// RoPE on read, with either per-token 4-bit affine or symmetric K and 4 query
-// heads per kv-head (a per-key rotation would undo the factored scale), or
-// KIVI 4-bit K and 1-4 query heads per kv-head.
+// The fast decode covers D = 128, bf16 or fp16 queries, affine 4- or 8-bit V
+// and no RoPE on read, with per-token 4-bit K (affine groups or symmetric
+// blocks, 4 query heads per kv-head: decode_mfma.hip; a per-key rotation
+// would undo the factored scale) or KIVI 4-bit K (1-4 query heads per
+// kv-head: this file).
 bool decode_fast_applies(const DecodeArgs& a) {
-    const bool tok_k = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4;
-    const bool kivi_k = a.k_kind == KVQ_KIVI_CH && a.k_bits == 4;
+    if (decode_mfma_applies(a)) return true;
     const bool v_ok = a.v_kind == KVQ_TOK_AFFINE && (a.v_bits == 4 || a.v_bits == 8);
-    const bool heads_ok =
-        tok_k ? a.Hq == kGQ * a.Hkv : (a.Hq % a.Hkv == 0 && a.Hq >= a.Hkv && a.Hq <= kGQ * a.Hkv);
-    return (tok_k || kivi_k) && heads_ok && v_ok && a.D == kD &&
+    const bool heads_ok = a.Hq % a.Hkv == 0 && a.Hq >= a.Hkv && a.Hq <= kGQ * a.Hkv;
+    return a.k_kind == KVQ_KIVI_CH && a.k_bits == 4 && v_ok && heads_ok && a.D == kD &&
            (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) && !a.rope;
 }
 
@@ -728,39 +574,27 @@ void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len) {
     *n_splits = (T + len - 1) / len;
 }
 
-template <int QDT, int KF, int GK, int VB>
-static hipError_t launch_fast_v(const DecodeArgs& a, hipStream_t s) {
+template <int QDT, int VB>
+static hipError_t launch_kivi_v(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
     switch (a.v_group) {
-        case 32: hipLaunchKernelGGL((decode_tok4_kernel<QDT, KF, GK, VB, 32>), grid, dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((decode_tok4_kernel<QDT, KF, GK, VB, 64>), grid, dim3(256), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((decode_tok4_kernel<QDT, KF, GK, VB, 128>), grid, dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((decode_kivi_kernel<QDT, VB, 32>), grid, dim3(256), 0, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_kivi_kernel<QDT, VB, 64>), grid, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_kivi_kernel<QDT, VB, 128>), grid, dim3(256), 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-template <int QDT, int KF, int GK>
-static hipError_t launch_fast_k(const DecodeArgs& a, hipStream_t s) {
-    return a.v_bits == 8 ? launch_fast_v<QDT, KF, GK, 8>(a, s) : launch_fast_v<QDT, KF, GK, 4>(a, s);
-}
-
 template <int QDT>
-static hipError_t launch_fast_q(const DecodeArgs& a, hipStream_t s) {
-    if (a.k_kind == KVQ_KIVI_CH) return launch_fast_k<QDT, kKKivi, 32>(a, s);
-    if (a.k_kind == KVQ_TOK_SYM4) return launch_fast_k<QDT, kKSym4, 32>(a, s);
-    switch (a.k_group) {
-        case 32: return launch_fast_k<QDT, kKAff4, 32>(a, s);
-        case 64: return launch_fast_k<QDT, kKAff4, 64>(a, s);
-        case 128: return launch_fast_k<QDT, kKAff4, 128>(a, s);
-        default: return hipErrorInvalidValue;
-    }
+static hipError_t launch_kivi_q(const DecodeArgs& a, hipStream_t s) {
+    return a.v_bits == 8 ? launch_kivi_v<QDT, 8>(a, s) : launch_kivi_v<QDT, 4>(a, s);
 }
 
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) {
     if (decode_mfma_applies(a)) return launch_decode_mfma(a, s);
-    if (a.q_dtype == KVQ_BF16) return launch_fast_q<KVQ_BF16>(a, s);
-    return launch_fast_q<KVQ_F16>(a, s);
+    if (a.q_dtype == KVQ_BF16) return launch_kivi_q<KVQ_BF16>(a, s);
+    return launch_kivi_q<KVQ_F16>(a, s);
 }
 
 }  // namespace kvq
