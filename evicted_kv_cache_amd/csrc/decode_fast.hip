@@ -564,7 +564,9 @@ bool decode_fast_applies(const DecodeArgs& a) {
 void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len) {
     const int units = B * Hkv;
     int ns = (512 + units - 1) / units;
-    const int min_len = kWaves * kTileT * 4;       // at least 4 tiles per wave
+    // at least 2 tiles per wave, so that each wave's second tile loads while
+    // its first is computed (the best latency for small batches)
+    const int min_len = kWaves * kTileT * 2;
     const int max_ns = (T + min_len - 1) / min_len;
     if (ns > max_ns) ns = max_ns;
     if (ns < 1) ns = 1;
