@@ -204,6 +204,40 @@ def test_fast_decode_k_formats_and_8bit_v(k_kind, kg, vb, vg):
     check_decode(pl, c, o, synth.cast(synth.widen(q, "f16"), "bf16"), "bf16")
 
 
+@pytest.mark.parametrize("k_kind,kg,vb,vg,dt", [
+    ("tok_affine", 32, 4, 128, "bf16"), ("tok_affine", 64, 4, 64, "f16"), ("tok_sym4", 32, 8, 64, "f16"),
+])
+def test_matrix_core_decode_extremes(k_kind, kg, vb, vg, dt):
+    """Per-token 4-bit K with 4 query heads per kv-head (the matrix-core
+    decode) on inputs at the edges of its exactness argument: keys with x100
+    outlier channels and a constant block, values with constant rows and a
+    channel at +-4, query heads that span 2^-24 .. 2^4, are zero, or hold one
+    large element among tiny ones, and a kv-head whose whole query group is
+    zero.  T = 97: three full tiles and a partial one."""
+    rng = np.random.default_rng(1234)
+    B, H, T, D, Hq = 1, 2, 97, 128, 8
+    k = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    k[..., 5] *= 100.0
+    k[..., 70] *= 100.0
+    k[..., 96:] = 0.75
+    v = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    v[:, :, ::7, :] = 3.0
+    v[..., 0] = np.where(np.arange(T) % 2 == 0, -4.0, 4.0)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float32)
+    q[0, 1] = np.ldexp(np.where(rng.random(D) < 0.5, -1.0, 1.0), rng.integers(-24, 5, D))
+    q[0, 2] = 0.0
+    q[0, 3] *= 1e-6
+    q[0, 3, 17] = 8.0
+    q[0, 4:8] = 0.0
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=D, capacity=T, k_kind=k_kind, k_bits=4, k_group=kg,
+                     v_kind="tok_affine", v_bits=vb, v_group=vg, in_dtype=dt)
+    say("matrix-core decode extremes", k_kind, kg, vb, vg, dt)
+    c, o = build_pair(pl, ol, synth.cast(k, dt), synth.cast(v, dt), dt)
+    assert_same_state(c, o)
+    for qdt in ("bf16", "f16"):
+        check_decode(pl, c, o, synth.cast(q, qdt), qdt)
+
+
 def test_empty_cache_decodes_to_zeros():
     pl, ol = layouts(batch=2, n_kv_heads=2, head_dim=64, capacity=10, in_dtype="f16",
                      k_group=64, v_group=64)
