@@ -505,9 +505,7 @@ static kvq_status snap_run(const SnapRun& r, hipStream_t s) {
             return KVQ_ERR_HIP;
         rank = pooled;
     }
-    if (launch_snapkv_select(rank, r.B, r.H, r.S, r.n_sink, r.budget, r.kept, s) != hipSuccess)
-        return KVQ_ERR_HIP;
-    if (launch_snapkv_gather(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    if (launch_snapkv_select_gather(a, rank, s) != hipSuccess) return KVQ_ERR_HIP;
     return KVQ_OK;
 }
 

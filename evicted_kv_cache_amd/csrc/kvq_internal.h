@@ -178,6 +178,9 @@ hipError_t launch_snapkv_chunk_copy(const void* k_chunk, const void* v_chunk, vo
 hipError_t launch_snapkv_select(const float* scores, int B, int H, int S, int n_sink, int budget,
                                 int32_t* kept, hipStream_t s);
 hipError_t launch_snapkv_gather(const SnapArgs& a, hipStream_t s);
+// Top-k of `rank` and the gather of the kept rows (one launch where the keys fit
+// in registers and at most 4096 rows are kept, else select then gather).
+hipError_t launch_snapkv_select_gather(const SnapArgs& a, const float* rank, hipStream_t s);
 
 hipError_t launch_zero_f32(float* p, size_t n, hipStream_t s);
 

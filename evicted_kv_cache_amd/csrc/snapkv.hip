@@ -407,19 +407,23 @@ __device__ __forceinline__ uint32_t scan1024(uint32_t v, uint32_t* tot16, uint32
     return before + x - v;
 }
 
+// Top-k of one (batch, head) row of scores sc[0, S) by the whole block, with
+// the keys in registers (S <= kSelThreads * KPT): the kept indices in
+// ascending order go to `kept` and, when given, to `kept_lds`.
 template <int KPT>
-__global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const float* scores, int S, int n_sink,
-                                                                      int budget, int32_t* kept_all) {
-    const int64_t bh = blockIdx.x;
+__device__ __forceinline__ void select_reg(const float* sc, int S, int n_sink, int budget, int32_t* kept,
+                                           int32_t* kept_lds) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n_keep = min(budget, S);
     const int n_s = min(n_sink, n_keep);
     const int k = n_keep - n_s;
     const int C = S - n_s;
-    const float* sc = scores + bh * S;
-    int32_t* kept = kept_all + bh * n_keep;
+    auto emit = [&](uint32_t out, int j) {
+        if (kept) kept[out] = j;
+        if (kept_lds) kept_lds[out] = j;
+    };
     if (k == C || k == 0) {                       // all candidates, or sinks only
-        for (int i = tid; i < n_keep; i += blockDim.x) kept[i] = i;
+        for (int i = tid; i < n_keep; i += blockDim.x) emit((uint32_t)i, i);
         return;
     }
     __shared__ __align__(16) uint32_t hist[kSelBuckets];
@@ -574,15 +578,53 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
         if (j >= S) break;
         if (j < n_s || key[i] > tau) {
             const uint32_t out = a_run + min(e_run, krem);
-            if (out < (uint32_t)n_keep) kept[out] = j;
+            if (out < (uint32_t)n_keep) emit(out, j);
             ++a_run;
         } else if (key[i] == tau) {
             if (e_run < krem) {
                 const uint32_t out = a_run + e_run;
-                if (out < (uint32_t)n_keep) kept[out] = j;
+                if (out < (uint32_t)n_keep) emit(out, j);
             }
             ++e_run;
         }
+    }
+}
+
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const float* scores, int S, int n_sink,
+                                                                      int budget, int32_t* kept_all) {
+    const int64_t bh = blockIdx.x;
+    const int n_keep = min(budget, S);
+    select_reg<KPT>(scores + bh * S, S, n_sink, budget, kept_all + bh * n_keep, nullptr);
+}
+
+// Select and gather in one launch: n_rep blocks per (batch, head) each run
+// the same selection (block rep 0 writes the kept indices), then copy their
+// share of the kept K and V rows (and positions).  The selection is
+// latency-bound and the copy is short, so the repeats cost nothing and the
+// gather's own launch disappears.
+constexpr int kFuseMaxKeep = 4096;
+template <int KPT>
+__global__ __launch_bounds__(kSelThreads) void snap_select_gather_kernel(SnapArgs a, const float* rank, int n_rep) {
+    __shared__ int32_t keptl[kFuseMaxKeep];
+    const int64_t bh = blockIdx.x / n_rep;
+    const int rep = (int)(blockIdx.x - bh * n_rep);
+    const int n_keep = min(a.budget, a.S);
+    select_reg<KPT>(rank + bh * a.S, a.S, a.n_sink, a.budget, rep == 0 ? a.kept + bh * n_keep : nullptr, keptl);
+    __syncthreads();
+    const int upr = a.D / 8;                      // 16-byte units per fp16 row
+    const int units = n_keep * upr;
+    const int per = (units + n_rep - 1) / n_rep;
+    const int u1 = min(units, (rep + 1) * per);
+    for (int x = rep * per + (int)threadIdx.x; x < u1; x += kSelThreads) {
+        const int rl = x / upr, u = x - rl * upr;
+        const int j = keptl[rl];
+        const int64_t src = (bh * a.kv_stride + (int64_t)j * a.D) / 8 + u;
+        const int64_t dst = (bh * a.out_stride + (int64_t)rl * a.D) / 8 + u;
+        reinterpret_cast<uint4*>(a.k_out)[dst] = reinterpret_cast<const uint4*>(a.k)[src];
+        reinterpret_cast<uint4*>(a.v_out)[dst] = reinterpret_cast<const uint4*>(a.v)[src];
+        if (u == 0 && a.pos_out)
+            a.pos_out[bh * a.pos_out_rows + rl] = a.pos_in ? a.pos_in[bh * a.pos_in_rows + j] : j;
     }
 }
 
@@ -721,6 +763,26 @@ hipError_t launch_snapkv_chunk_copy(const void* k_chunk, const void* v_chunk, vo
                        static_cast<const uint4*>(k_chunk), static_cast<const uint4*>(v_chunk),
                        static_cast<uint4*>(k_state), static_cast<uint4*>(v_state), pos_state, rows, n, upr, cap,
                        row0, first_pos);
+    return hipGetLastError();
+}
+
+hipError_t launch_snapkv_select_gather(const SnapArgs& a, const float* rank, hipStream_t s) {
+    const int n_keep = a.budget < a.S ? a.budget : a.S;
+    if (n_keep > kFuseMaxKeep || a.S > kSelThreads * 32) {
+        const hipError_t e = launch_snapkv_select(rank, a.B, a.H, a.S, a.n_sink, a.budget, a.kept, s);
+        if (e != hipSuccess) return e;
+        return launch_snapkv_gather(a, s);
+    }
+    // about one 16-byte unit of K and of V per thread and block
+    int n_rep = (n_keep * (a.D / 8) + kSelThreads - 1) / kSelThreads;
+    n_rep = n_rep < 1 ? 1 : (n_rep > 32 ? 32 : n_rep);
+    const dim3 grid((unsigned)(a.B * a.H * n_rep));
+    if (a.S <= kSelThreads * 8)
+        hipLaunchKernelGGL((snap_select_gather_kernel<8>), grid, dim3(kSelThreads), 0, s, a, rank, n_rep);
+    else if (a.S <= kSelThreads * 16)
+        hipLaunchKernelGGL((snap_select_gather_kernel<16>), grid, dim3(kSelThreads), 0, s, a, rank, n_rep);
+    else
+        hipLaunchKernelGGL((snap_select_gather_kernel<32>), grid, dim3(kSelThreads), 0, s, a, rank, n_rep);
     return hipGetLastError();
 }
 
