@@ -5,10 +5,11 @@
 // kv-head, with both products on the matrix cores (gfx950,
 // v_mfma_f32_16x16x32_f16).
 //
-// Same work split as the VALU decode in decode_fast.hip: 4 waves per
-// (batch, kv-head[, token split]), each streaming 32-token tiles with its own
-// online softmax, merged through LDS (token splits merge in a combine
-// kernel).  What changes is where the multiply-adds run.  A 4-bit code left
+// Work split: 4 waves per (batch, kv-head[, token split]), each with its own
+// online softmax over every fourth 32-token tile of the split (so the four
+// waves of a workgroup stream one region of the cache together, which keeps
+// fewer DRAM streams open than four separate runs), merged through LDS
+// (token splits merge in a combine kernel).  What changes is where the multiply-adds run.  A 4-bit code left
 // in place under a mask is an fp16 subnormal (u 2^-24 for a low nibble,
 // u 2^-20 for a high one), and the matrix cores multiply subnormal fp16
 // operands exactly, so the codes feed the MFMA B operand with one AND each.
@@ -126,7 +127,6 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int t_lo = split * a.split_len;
     const int t_hi = min(a.T, t_lo + a.split_len);
     const int n_tiles = (t_hi - t_lo + kTileT - 1) / kTileT;
-    const int tile0 = (n_tiles * wave) / kWaves, tile1 = (n_tiles * (wave + 1)) / kWaves;
 
     __shared__ __align__(16) uint32_t wbuf[kWaves][NVG][kGQ][16];   // fp16 weight pairs (t, t + 16)
     __shared__ float comb_o[kWaves][kGQ][kD];
@@ -319,24 +319,29 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         __builtin_amdgcn_wave_barrier();
     };
 
-    // two load buffers in ping-pong: the next tile's loads are in flight while
-    // the current tile is computed; only the split's last tile can be partial
+    // this wave's tiles wave, wave + 4, ...; two load buffers in ping-pong:
+    // the next tile's loads are in flight while the current tile is computed
+    // (a prefetch past the split reads zeros and is never used); only the
+    // split's last tile can be partial
     MTile<NVG, VH> A, B2;
-    const int full_end = min(tile1, (t_hi - t_lo) / kTileT);
-    int tile = tile0;
-    load_tile(tile, A);
-    for (; tile + 1 < full_end; tile += 2) {
-        load_tile(tile + 1, B2);
-        process(A, tile, Flag<false>{});
-        load_tile(tile + 2, A);
-        process(B2, tile + 1, Flag<false>{});
+    const int n_full = (t_hi - t_lo) / kTileT;
+    const int n_mine = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
+    const int n_mine_full = n_full > wave ? (n_full - wave + kWaves - 1) / kWaves : 0;
+    auto tl = [&](int i) { return wave + kWaves * i; };
+    int i = 0;
+    if (n_mine > 0) load_tile(tl(0), A);
+    for (; i + 1 < n_mine_full; i += 2) {
+        load_tile(tl(i + 1), B2);
+        process(A, tl(i), Flag<false>{});
+        load_tile(tl(i + 2), A);
+        process(B2, tl(i + 1), Flag<false>{});
     }
-    if (tile < full_end) {
-        process(A, tile, Flag<false>{});
-        ++tile;
-        if (tile < tile1) load_tile(tile, A);
+    if (i < n_mine_full) {
+        process(A, tl(i), Flag<false>{});
+        ++i;
+        if (i < n_mine) load_tile(tl(i), A);
     }
-    if (tile < tile1) process(A, tile, Flag<true>{});
+    if (i < n_mine) process(A, tl(i), Flag<true>{});
 
     // ---------------------------------------------------- wave-level reduction
     // head r sums over the row's tokens
