@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 
     float m_lane = -INFINITY;     // running max of head r
     float l_lane = 0.0f;          // running sum of head r over this lane's tokens
-    float corr[NVG];              // head r, per V group: sum p (z + 8 s) - 8 sum w^
+    float corr[NVG];              // head r, per V group: sum p (z + c s) - c sum w^
 #pragma unroll
     for (int g = 0; g < NVG; ++g) corr[g] = 0.0f;
     // PV: row (g = r, h = i) of column n, scaled 2^-24.  4-bit codes: acc[k]
