@@ -426,14 +426,16 @@ hipError_t launch_prefill_k(const DecodeArgs& a, int n_q, int n_rb, int causal, 
 
 }  // namespace
 
-// Split count before rounding the split length: about 512 workgroups, each
+// Split count before rounding the split length: about 256 workgroups, each
 // split at least two tiles long, at most 1024 splits.  The planned count
 // never exceeds it, and it grows with T, so its value at the capacity bounds
 // every plan of that cache (the workspace size).
 int prefill_max_splits(int B, int Hkv, int Hq, int n_q, int T) {
     const int R = (Hq / Hkv) * n_q;
     const int64_t units = (int64_t)B * Hkv * ((R + kRows - 1) / kRows);
-    int64_t ns = (512 + units - 1) / units;
+    // one round of workgroups: each holds two tile buffers (about 106 KB of
+    // LDS at head_dim 128), so one fits per CU and 256 cover the chip
+    int64_t ns = (256 + units - 1) / units;
     const int64_t max_ns = ((int64_t)T + 2 * kPT - 1) / (2 * kPT);
     if (ns > max_ns) ns = max_ns;
     if (ns > 1024) ns = 1024;
