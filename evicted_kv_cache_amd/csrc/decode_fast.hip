@@ -42,6 +42,7 @@
 //   last tile of a split can hold invalid tokens; it alone masks its logits.
 #include <math.h>
 
+#include "bufload.h"
 #include "dequant8.h"
 #include "kvq_internal.h"
 
@@ -54,9 +55,11 @@ constexpr int kTileT = 32;      // tokens per wave tile
 constexpr int kWaves = 4;
 constexpr int kRowB = kD / 2;   // bytes of 4-bit K codes per token
 
+using buf::rsrc;
+using buf::u32x2;
+using buf::u32x4;
+
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float dot2_f16(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
@@ -99,19 +102,6 @@ __device__ __forceinline__ float quad_from_minus(float v) {
 
 template <bool B>
 struct Flag { static constexpr bool value = B; };
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ uint32_t bload32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
-}
-__device__ __forceinline__ u32x2 bload64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
-}
-__device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
-}
 
 // Query element as fp32.
 template <int QDT>
@@ -253,9 +243,9 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
             for (int e = 0; e < 2; ++e) {
                 const uint32_t off = (tt + 16 * e) * kVRowB + 4 * VW * c;
                 if constexpr (VW == 1) {
-                    L.v[j][e][0] = bload32(rv, off);
+                    L.v[j][e][0] = buf::load32(rv, off);
                 } else {
-                    const u32x2 x = bload64(rv, off);
+                    const u32x2 x = buf::load64(rv, off);
                     L.v[j][e][0] = x.x; L.v[j][e][1] = x.y;
                 }
             }
@@ -263,17 +253,17 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = t16 + 16 * p;
-            L.k[p] = bload128(rk, tok * kRowB + 16 * q4);
+            L.k[p] = buf::load128(rk, tok * kRowB + 16 * q4);
             // the token's table row (slots past the tile's valid part read 0)
             const __amdgpu_buffer_rsrc_t rrow = rsrc(a.k_row + tb, nv * 4);
-            L.krow[p] = (int32_t)bload32(rrow, tok * 4);
+            L.krow[p] = (int32_t)buf::load32(rrow, tok * 4);
             if constexpr (NVG == 1) {
-                L.vm.m[p][0] = bload32(rvm, tok * 4);
+                L.vm.m[p][0] = buf::load32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
-                const u32x2 x = bload64(rvm, tok * 8);
+                const u32x2 x = buf::load64(rvm, tok * 8);
                 L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y;
             } else {
-                const u32x4 x = bload128(rvm, tok * 16);
+                const u32x4 x = buf::load128(rvm, tok * 16);
                 L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y; L.vm.m[p][2] = x.z; L.vm.m[p][3] = x.w;
             }
         }
@@ -289,8 +279,8 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
         L.r0 = __builtin_amdgcn_readfirstlane(r0);
         L.r1 = __builtin_amdgcn_readfirstlane(r1);
         const __amdgpu_buffer_rsrc_t rtab = rsrc(ktab, (uint32_t)rows_t * kD * 4);
-        L.stg[0] = bload64(rtab, (uint32_t)L.r0 * kD * 4 + 8 * lane);
-        L.stg[1] = bload64(rtab, (uint32_t)L.r1 * kD * 4 + 8 * lane);
+        L.stg[0] = buf::load64(rtab, (uint32_t)L.r0 * kD * 4 + 8 * lane);
+        L.stg[1] = buf::load64(rtab, (uint32_t)L.r1 * kD * 4 + 8 * lane);
     };
 
     auto process = [&](const TileLoads<NVG, VW>& L, int tile, auto tail) {

@@ -28,6 +28,7 @@
 // decode's log-sum-exp combine merges.
 #include <math.h>
 
+#include "bufload.h"
 #include "dequant8.h"
 #include "kvq_internal.h"
 
@@ -75,9 +76,7 @@ __device__ __forceinline__ void split_half8(const float x[8], half8& hi, half8& 
     }
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
+using buf::rsrc;
 // Loads of `bytes` (2, 4 or 8) bytes at a buffer offset; past the buffer's end they read zero.
 __device__ __forceinline__ void bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t off, int bytes, dq::Pre8& p) {
     if (bytes == 2) {
