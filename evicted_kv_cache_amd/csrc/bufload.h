@@ -28,5 +28,22 @@ __device__ __forceinline__ u32x4 load128(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
 }
 
+// The same loads with the non-temporal cache policy (nt), for data read
+// once per launch (the cache streams of a decode step): they do not displace
+// reused lines from L2 and the infinity cache.
+constexpr int kNonTemporal = 2;
+__device__ __forceinline__ uint32_t stream16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, kNonTemporal);
+}
+__device__ __forceinline__ uint32_t stream32(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, kNonTemporal);
+}
+__device__ __forceinline__ u32x2 stream64(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, kNonTemporal);
+}
+__device__ __forceinline__ u32x4 stream128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kNonTemporal);
+}
+
 }  // namespace buf
 }  // namespace kvq

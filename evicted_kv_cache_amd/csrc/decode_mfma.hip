@@ -46,6 +46,8 @@
 //   z = -8 d.
 // * Loads go through buffer resources sized to the valid part of a tile, so
 //   tail tokens read zeros; the last tile of a split masks their logits.
+//   They carry the non-temporal cache policy: the cache is read once per
+//   step.
 #include <math.h>
 
 #include "bufload.h"
@@ -208,20 +210,20 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
             for (int e = 0; e < 2; ++e)
 #pragma unroll
                 for (int hb = 0; hb < VH; ++hb)
-                    L.v[j][e][hb] = buf::load32(rv, (4 * r + j + 16 * e) * kVRowB + 4 * (n + 16 * hb));
+                    L.v[j][e][hb] = buf::stream32(rv, (4 * r + j + 16 * e) * kVRowB + 4 * (n + 16 * hb));
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = n + 16 * p;
-            L.k[p] = buf::load128(rk, tok * kRowB + 16 * r);
-            if constexpr (KF == kKSym4) L.km[p] = buf::load16(rkm, (tok * NKG + kg) * 2);
-            else L.km[p] = buf::load32(rkm, (tok * NKG + kg) * 4);
+            L.k[p] = buf::stream128(rk, tok * kRowB + 16 * r);
+            if constexpr (KF == kKSym4) L.km[p] = buf::stream16(rkm, (tok * NKG + kg) * 2);
+            else L.km[p] = buf::stream32(rkm, (tok * NKG + kg) * 4);
             if constexpr (NVG == 1) {
-                L.vm[p][0] = buf::load32(rvm, tok * 4);
+                L.vm[p][0] = buf::stream32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
-                const buf::u32x2 v2 = buf::load64(rvm, tok * 8);
+                const buf::u32x2 v2 = buf::stream64(rvm, tok * 8);
                 L.vm[p][0] = v2.x; L.vm[p][1] = v2.y;
             } else {
-                const u32x4 v4 = buf::load128(rvm, tok * 16);
+                const u32x4 v4 = buf::stream128(rvm, tok * 16);
                 L.vm[p][0] = v4.x; L.vm[p][1] = v4.y; L.vm[p][2] = v4.z; L.vm[p][3] = v4.w;
             }
         }

@@ -61,6 +61,8 @@ __device__ __forceinline__ RowRemap row_remap(const int32_t* k_row, int n, int s
 // copies the shorter rows (per-token metadata) and the slot's position (per
 // (b, h) position rows; for shared positions (0, 0, i) moves pos[i]), and
 // (0, 0, i) moves k_row[i].  Consecutive threads touch consecutive units.
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void gather_kernel(EvictArgs a, int upr) {
     const int m = a.sink + a.window;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -77,8 +79,10 @@ __global__ __launch_bounds__(256) void gather_kernel(EvictArgs a, int upr) {
         const uint8_t* src = static_cast<const uint8_t*>(a.src[k]) + (bh * a.cap + si) * rb;
         uint8_t* dst = static_cast<uint8_t*>(a.dst[k]) + (bh * a.cap + i) * rb;
         if ((rb & 15) == 0) {
+            // each row is read and written once: non-temporal on both sides
             if (u * 16 < rb)
-                *reinterpret_cast<uint4*>(dst + u * 16) = *reinterpret_cast<const uint4*>(src + u * 16);
+                __builtin_nontemporal_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(src + u * 16)),
+                                            reinterpret_cast<u32x4v*>(dst + u * 16));
         } else if (u == 0) {
             copy_row(src, dst, rb);
         }
