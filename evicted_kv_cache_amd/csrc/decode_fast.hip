@@ -40,6 +40,8 @@
 // * Tails need no clamping: loads go through buffer resources whose size is
 //   the valid part of the tile, and out-of-range loads return zero.  Only the
 //   last tile of a split can hold invalid tokens; it alone masks its logits.
+//   Codes and per-token metadata, read once per step, load with the
+//   non-temporal cache policy; table rows and positions use the default.
 #include <math.h>
 
 #include "bufload.h"
@@ -243,9 +245,9 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
             for (int e = 0; e < 2; ++e) {
                 const uint32_t off = (tt + 16 * e) * kVRowB + 4 * VW * c;
                 if constexpr (VW == 1) {
-                    L.v[j][e][0] = buf::load32(rv, off);
+                    L.v[j][e][0] = buf::stream32(rv, off);
                 } else {
-                    const u32x2 x = buf::load64(rv, off);
+                    const u32x2 x = buf::stream64(rv, off);
                     L.v[j][e][0] = x.x; L.v[j][e][1] = x.y;
                 }
             }
@@ -253,17 +255,17 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = t16 + 16 * p;
-            L.k[p] = buf::load128(rk, tok * kRowB + 16 * q4);
+            L.k[p] = buf::stream128(rk, tok * kRowB + 16 * q4);
             // the token's table row (slots past the tile's valid part read 0)
             const __amdgpu_buffer_rsrc_t rrow = rsrc(a.k_row + tb, nv * 4);
             L.krow[p] = (int32_t)buf::load32(rrow, tok * 4);
             if constexpr (NVG == 1) {
-                L.vm.m[p][0] = buf::load32(rvm, tok * 4);
+                L.vm.m[p][0] = buf::stream32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
-                const u32x2 x = buf::load64(rvm, tok * 8);
+                const u32x2 x = buf::stream64(rvm, tok * 8);
                 L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y;
             } else {
-                const u32x4 x = buf::load128(rvm, tok * 16);
+                const u32x4 x = buf::stream128(rvm, tok * 16);
                 L.vm.m[p][0] = x.x; L.vm.m[p][1] = x.y; L.vm.m[p][2] = x.z; L.vm.m[p][3] = x.w;
             }
         }
