@@ -37,7 +37,10 @@
 //   bytes b = u_2k + 16 u_2k+1 of tokens (t, t + 16) as subnormal fp16
 //   pairs, one AND their low nibbles.  The high-nibble channel is (byte sum -
 //   low sum) / 16 at the end.  8-bit codes are whole bytes already: words n
-//   and n + 16 (channels 4n .. 4n+3 and 64 + 4n ..) give one MFMA per byte.
+//   and n + 16 (channels 4n .. 4n+3 and 64 + 4n ..) give one MFMA per byte;
+//   their tile is fetched with 16-byte loads and staged in LDS, from where
+//   each lane reads its words (16 single-dword fetches per lane and tile
+//   would cost more).
 //   Only the rows of a column's own V group are kept.  The zero points and
 //   the rounding of the weights are accounted exactly in fp32 as in the VALU
 //   decode (c = 8 for 4-bit codes, 128 for 8-bit):
@@ -107,6 +110,7 @@ struct MTile {
     uint32_t km[2];      // K (scale, zero) of that quarter's group (symmetric: d), tokens n and n + 16
     uint32_t vm[2][NVG]; // V (scale, zero) per group, tokens n and n + 16
     uint32_t v[4][2][VH];  // V code words n (and n + 16) of tokens 4r + j and 4r + j + 16
+    u32x4 vraw[4];         // 8-bit V codes of the tile, 16-byte units lane + 64 q
 };
 
 // KF: K format (kKAff4, or kKSym4 with GK = 32); GK, GV: channels per K / V
@@ -131,6 +135,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int n_tiles = (t_hi - t_lo + kTileT - 1) / kTileT;
 
     __shared__ __align__(16) uint32_t wbuf[kWaves][NVG][kGQ][16];   // fp16 weight pairs (t, t + 16)
+    __shared__ __align__(16) uint32_t vst[VB == 8 ? kWaves : 1][kTileT][36];     // 8-bit V code rows (32 words + pad)
     __shared__ float comb_o[kWaves][kGQ][kD];
     __shared__ float comb_ml[kWaves][kGQ][2];
 
@@ -204,6 +209,10 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         const __amdgpu_buffer_rsrc_t rkm = buf::rsrc(kmeta + (int64_t)tb * NKG * kKMetaB, nv * NKG * kKMetaB);
         const __amdgpu_buffer_rsrc_t rvm = buf::rsrc(vmeta + (int64_t)tb * NVG * 4, nv * NVG * 4);
         const __amdgpu_buffer_rsrc_t rv = buf::rsrc(vcodes + (int64_t)tb * kVRowB, nv * kVRowB);
+        if constexpr (VB == 8) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) L.vraw[q] = buf::stream128(rv, 16 * (lane + 64 * q));
+        } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -211,6 +220,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int hb = 0; hb < VH; ++hb)
                     L.v[j][e][hb] = buf::stream32(rv, (4 * r + j + 16 * e) * kVRowB + 4 * (n + 16 * hb));
+        }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = n + 16 * p;
@@ -295,6 +305,30 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         __builtin_amdgcn_wave_barrier();
 
         // -------------------------------------------- values
+        uint32_t vw[4][2][VH];
+        if constexpr (VB == 8) {
+            // stage the tile's codes (unit u: token u / 8, words 4 (u % 8) ..) and
+            // read words n and n + 16 of tokens 4r + j and 4r + j + 16
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int u = lane + 64 * q;
+                *reinterpret_cast<u32x4*>(&vst[wave][u >> 3][4 * (u & 7)]) = L.vraw[q];
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int hb = 0; hb < VH; ++hb) vw[j][e][hb] = vst[wave][4 * r + j + 16 * e][n + 16 * hb];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 2; ++e)
+#pragma unroll
+                    for (int hb = 0; hb < VH; ++hb) vw[j][e][hb] = L.v[j][e][hb];
+        }
         // A: row n = (group n >> 2, head n & 3), tokens (4r + j, 4r + j + 16) for j < 4
         u32x4 aw = u32x4{0u, 0u, 0u, 0u};
         if ((n >> 2) < NVG) aw = *reinterpret_cast<const u32x4*>(&wbuf[wave][n >> 2][n & 3][4 * r]);
@@ -307,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                 for (int j = 0; j < 4; ++j) {
                     // byte k of the word for tokens 4r + j and 4r + j + 16
                     const uint32_t P =
-                        __builtin_amdgcn_perm(L.v[j][1][hb], L.v[j][0][hb], 0x0C040C00u + 0x00010001u * k);
+                        __builtin_amdgcn_perm(vw[j][1][hb], vw[j][0][hb], 0x0C040C00u + 0x00010001u * k);
                     bw[j] = P;
                     bl[j] = P & 0x000F000Fu;
                 }
