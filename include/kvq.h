@@ -90,6 +90,11 @@ typedef enum { KVQ_PLAIN = 0, KVQ_KIVI_CH = 1, KVQ_TOK_AFFINE = 2, KVQ_TOK_SYM4 
  *       Dequantized value: u * scale + zero.            ([P1] formula, eps 1e-5)
  *   symmetric block of 32: x' = x - bias; d = fp16(max(1e-5, max|x'| / 7));
  *       code u = clamp(rint(x' / d), -8, 7) + 8;  value (u - 8) * d.
+ * Inputs must be finite.  K/V rows holding NaN or +-Inf, or a k_bias that
+ * makes x - bias overflow, are outside this specification: the call still
+ * completes and writes only the slots and table rows it appends, but the
+ * codes and metadata of the groups that hold such values are unspecified,
+ * and so is attention over them.
  * Codes are stored packed: 8-bit codes one per byte; 4-bit codes two per
  * byte with element 2i in the low nibble of byte i; 2-bit codes (KIVI-2bit,
  * [P2] "SnapKV-adapted" table; [P4] s.1 mx.quantize widths) four per byte,
@@ -210,7 +215,7 @@ size_t kvq_decode_workspace_bytes(const kvq_layout* layout, int32_t n_q_heads);
 
 /* Decode attention for one query token per sequence ([P4] s.1: scores
  * against the packed keys, softmax, weighted sum of the packed values; no
- * full-precision copy of the cache is made; [P4] s.5: split over the token
+ * dequantized buffer of K or V is ever written; [P4] s.5: split over the token
  * axis for long caches).
  *   out[b][hq][:] = sum_t softmax_t(sm_scale * q[b][hq] . k_t) v_t
  * over the n_stored slots of kv-head hk = hq / (n_q_heads / Hkv), where k_t,

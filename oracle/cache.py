@@ -117,7 +117,7 @@ class OracleCache:
             self.pos[..., sl] = self.next_pos + np.arange(n, dtype=np.int32)
         else:
             self.pos[..., sl] = np.asarray(positions, dtype=np.int32)
-        # V: per token, at write time ([P1]: "Computed once per new token").
+        # V: per token, at write time ([P1] "KIVI": one (scale, zero) per token, fixed once written).
         if L.v_kind == "plain":
             self.v_plain[:, :, sl] = v_new
         else:

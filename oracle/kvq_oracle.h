@@ -100,7 +100,7 @@ void kvo_decode_head_rope(const kvo_view* K, const kvo_view* V, int T,
                           double* out);
 
 /* ---- D1: SnapKV observation-window scores (fp64) ------------------------ *
- * [P2] "How it works" step 1: softmax(K[-w:] K^T / sqrt(D)) mean-pooled over
+ * [P2] "How it works" step 1: the row softmax of the last w keys against all keys (scaled by 1/sqrt(D)), averaged over
  * the window; w clamped to S.  K: [S][D] fp32.  score: [S].                   */
 void kvo_snapkv_scores(const float* K, int S, int D, int w, double* score);
 

@@ -22,8 +22,20 @@ MUTANTS = {
     "offset_first": ("float y = rintf(ratio);", "float y = rintf(ratio + (float)(-(1 << (bits - 1)))) + (float)(1 << (bits - 1));"),
     # eps guard dropped
     "no_eps": ("if (s < KVO_EPS) s = KVO_EPS;", ""),
-    # codes against the fp32 scale instead of the stored fp16 scale
-    "unrounded_scale": ("*scale16 = kvo_f32_to_f16(s);", "*scale16 = kvo_f32_to_f16(s * 1.0009765625f);"),
+    # stored scale one fp16 ulp too large (0.1% above the rounded scale)
+    "inflated_stored_scale": ("*scale16 = kvo_f32_to_f16(s);", "*scale16 = kvo_f32_to_f16(s * 1.0009765625f);"),
+    # affine codes against the fp32 scale before rounding instead of the stored fp16 scale
+    "codes_vs_fp32_scale": [
+        ("static const float KVO_EPS = 1e-5f;", "static const float KVO_EPS = 1e-5f;\nstatic float kvo_last_s;"),
+        ("*scale16 = kvo_f32_to_f16(s);", "*scale16 = kvo_f32_to_f16(s);\n    kvo_last_s = s;"),
+        ("float s = kvo_f16_to_f32(scale16);", "float s = kvo_last_s; (void)scale16;"),
+    ],
+    # symmetric codes rounded half away from zero instead of half to even
+    "sym4_round_half_away": ("float y = rintf(xc[i] / df);", "float y = roundf(xc[i] / df);"),
+    # symmetric eps floor dropped (an all-zero block divides by zero)
+    "sym4_no_eps": ("if (dd < KVO_EPS) dd = KVO_EPS;", ""),
+    # symmetric codes against the fp32 d before rounding instead of the stored fp16 d
+    "sym4_codes_vs_fp32_scale": ("float df = kvo_f16_to_f32(d16);", "float df = dd;"),
     # fp16 conversion truncates instead of rounding
     "f16_truncate": ("double n = nearbyint(a / quantum);", "double n = floor(a / quantum);"),
     # symmetric quantizer divides by 8 instead of 7
@@ -57,11 +69,15 @@ MUTANTS = {
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_reject_mutant(name, tmp_path):
-    old, new = MUTANTS[name]
+    edits = MUTANTS[name]
+    if isinstance(edits, tuple):
+        edits = [edits]
     src = open(SRC).read()
-    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    for old, new in edits:
+        assert src.count(old) >= 1, f"mutation anchor for {name} not found: {old!r}"
+        src = src.replace(old, new)
     mut = tmp_path / "kvq_oracle.c"
-    mut.write_text(src.replace(old, new))
+    mut.write_text(src)
     lib = str(tmp_path / "libmut.so")
     obuild.build(src=str(mut), out=lib)
     env = dict(os.environ, KVQ_ORACLE_LIB=lib)

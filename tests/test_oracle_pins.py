@@ -187,6 +187,84 @@ def test_sym4_error_bound_and_range():
     assert u.min() >= 0 and u.max() <= 15
 
 
+# Half-even rounding of k + 1/2, written out: the even one of k and k + 1
+# (the ties that fit under max |x'/d| = 7).
+SYM4_TIES = {-7: -6, -6: -6, -5: -4, -4: -4, -3: -2, -2: -2, -1: 0,
+             0: 0, 1: 2, 2: 2, 3: 4, 4: 4, 5: 6, 6: 6}
+
+
+def test_sym4_ties_round_half_even():
+    """[P3] "The idea" (symmetric, no zero point) with the rint of the
+    specification: a block whose max |x'| is 7/8 has d = 1/8 exactly, so
+    x' = (k + 1/2)/8 is a tie k + 1/2 and must go to the even neighbour
+    (round-half-away would give k + 1 for k >= 0 and k for k < 0).  The same
+    ties after centering by a bias on the 1/16 grid (x - bias exact)."""
+    ks = sorted(SYM4_TIES)                                      # -7 .. 6
+    vals = [7.0, -7.0, 0.0, 0.0] + [k + 0.5 for k in ks] + [k + 0.5 for k in ks[::-1]]
+    want = [7, -7, 0, 0] + [SYM4_TIES[k] for k in ks] + [SYM4_TIES[k] for k in ks[::-1]]
+    assert len(vals) == 32
+    x = np.tile(np.array(vals) / 8, 4)[None].astype(np.float32)   # one row, 4 blocks
+    u, sc = oracle.quant_sym4(x, None)
+    assert np.all(sc == 0x3000)                                 # fp16 bits of 1/8
+    assert np.array_equal(u[0], np.tile(np.array(want) + 8, 4).astype(np.uint8))
+    bias = (np.arange(128) % 37 - 18).astype(np.float32) / 16
+    xb = (x + bias).astype(np.float32)
+    assert np.array_equal((xb - bias).astype(np.float32), x)     # exact on this grid
+    ub, scb = oracle.quant_sym4(xb, bias)
+    assert np.array_equal(ub, u) and np.array_equal(scb, sc)
+
+
+def test_sym4_zero_block_takes_eps_scale():
+    """[P1] "The bug class the previous attempt hit" (class 1: a degenerate
+    range must not divide by zero) reached through [P3]'s subtraction: a key
+    equal to the bias is an all-zero centered block, so d = fp16(1e-5) (the
+    subnormal 168 * 2^-24) and every code is 8 (q = 0).  Blocks with
+    max |x'| below 7e-5 also take the eps scale; their codes follow x'/d."""
+    bias = (np.arange(128, dtype=np.float32) - 60) / 8
+    x = np.tile(bias, (3, 1)).astype(np.float32)
+    x[1, 32:64] += np.float32(2.0 ** -20)     # one tiny block: x'/d = 2^-20 / (168 * 2^-24) = 16/168
+    x[2, 64:96] += np.float32(2.0 ** -14)     # max |x'| / 7 = 8.7e-6 < eps; x'/d = 1024/168 = 6.1 -> 6
+    u, sc = oracle.quant_sym4(x, bias)
+    assert sc.shape == (3, 4)
+    assert np.all(sc == 168)
+    want = np.full((3, 128), 8, np.uint8)
+    want[2, 64:96] = 14
+    assert np.array_equal(u, want)
+    u0, sc0 = oracle.quant_sym4(np.zeros((2, 64), np.float32), None)
+    assert np.all(sc0 == 168) and np.all(u0 == 8)
+
+
+def test_quant_codes_use_the_stored_fp16_scale():
+    """O3/O9: codes are taken against the scale as stored (fp16), not the fp32
+    value before rounding.  Each input below sits between the two quotients'
+    rounding boundary, so the two readings give different codes.
+
+    Affine int4: range 1.5 -> s32 = 0.1, stored s = fp16(0.1) = 0.0999755859375
+    (below s32); x = 1.4498 gives x/s = 14.5015 against the stored scale
+    (code 15) but 14.498 against s32 (code 14).
+    Q4_0: max |x'| = 1 -> d32 = 1/7, stored d = 1170/8192 = 0.142822265625;
+    x' = 2.5 * (d + d32)/2 gives x'/d just above 2.5 (q = 3, code 11) and
+    x'/d32 just below (q = 2, code 10)."""
+    g = np.zeros(32, np.float32)
+    g[1] = 1.5
+    g[2] = np.float32(1.4498)
+    s16 = np.float64(np.float16(0.1))
+    assert s16 == 0.0999755859375
+    assert float(g[2]) / s16 > 14.5 > float(g[2]) / 0.1
+    u, meta = oracle.quant_tok_affine(g[None], G=32, bits=4)
+    assert meta[0, 0, 0] == np.float16(0.1).view(np.uint16)
+    assert u[0, 2] == 15
+    d16 = 1170 / 8192
+    assert np.float64(np.float16(np.float32(1) / np.float32(7))) == d16
+    blk = np.zeros(32, np.float32)
+    blk[0] = 1.0
+    blk[1] = np.float32(2.5 * (d16 + 1 / 7) / 2)
+    assert float(blk[1]) / d16 > 2.5 > float(blk[1]) * 7
+    us, ss = oracle.quant_sym4(blk[None], None)
+    assert oracle.f16_bits_to_f32(ss)[0, 0] == np.float32(d16)
+    assert us[0, 0] == 15 and us[0, 1] == 11
+
+
 # --------------------------------------------------------------------------
 # decode attention
 # --------------------------------------------------------------------------
