@@ -23,9 +23,12 @@
 //   take a per-lane path that reads their row or residual from memory.  The
 //   four quarter partials of a head meet in lane quarter h by DPP rotations.
 // * Softmax: lane (t, h) computes p for head h of tokens t and t+16 (one
-//   exp each) and writes the fp16 weight pair (p_t s_t, p_t+16 s_t+16) to
+//   exp each) and writes the fp16 weight pair (p_t s_t, p_t+16 s_t+16) 2^E to
 //   LDS; the running max is rescaled only when a wave sees a larger logit,
-//   so weights stay <= 1 and never overflow fp16.
+//   so p <= 1.  The power of two 2^E follows the largest V scale the wave
+//   has seen (the accumulators are rescaled when it changes), so weights
+//   neither overflow nor fall into fp16's subnormal range when V is small;
+//   it is taken out exactly at the end.
 // * PV: lane (phase, 8-channel chunk) reads the codes of tokens t and t+16.
 //   A 4-bit code left in place under a mask is an fp16 subnormal, which
 //   v_dot2_f32_f16 multiplies exactly: one v_perm_b32 per byte position
@@ -221,6 +224,13 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
 
     float m_lane = -INFINITY;     // running max of head q4
     float l_lane = 0.0f;          // running sum of head q4 (this lane's tokens)
+    // fp16 weights are p s 2^wexp: wexp follows the largest V scale the wave
+    // has seen (vsmax 2^wexp in [2^13, 2^14)), so with p <= 1 no weight
+    // overflows, and any weight above 2^-27 of vsmax stays a normal fp16
+    // with full relative precision.  acc and corr are in these units.
+    float vsmax = 0.0f;
+    int wexp = 0;
+    float wmul = 1.0f;            // 2^wexp
     float corr[NVG];              // head q4, per V group
 #pragma unroll
     for (int g = 0; g < NVG; ++g) corr[g] = 0.0f;
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
         // stage the two table rows; kst[wave][r][c] = (scale, zero) of channel c
         *reinterpret_cast<u32x2*>(&kst[wave][0][2 * lane]) = L.stg[0];
         *reinterpret_cast<u32x2*>(&kst[wave][1][2 * lane]) = L.stg[1];
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
         // every token of the wave valid-and-coded with a staged row: the common case
         bool fast = true;
 #pragma unroll
@@ -386,21 +396,43 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
                 for (int i = 0; i < 8; ++i) acc[h][i] *= ah;
             }
         }
+        // -------------------------------------------- weight scale (rescale on a new largest V scale)
+        // lanes of equal q4 hold the V scales of all the tile's tokens
+        float sl = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) sl = fmaxf(sl, fmaxf(f16lo(L.vm.m[0][g]), f16lo(L.vm.m[1][g])));
+        if (__builtin_amdgcn_ballot_w64(sl > vsmax) != 0) {
+#pragma unroll
+            for (int off = 4; off < 64; off <<= 1) sl = fmaxf(sl, __shfl_xor(sl, off));
+            vsmax = fmaxf(vsmax, sl);
+            int e;
+            frexpf(vsmax, &e);                        // vsmax in [2^(e-1), 2^e)
+            const float f = ldexpf(1.0f, 14 - e - wexp);
+            wexp = 14 - e;
+            wmul = ldexpf(1.0f, wexp);
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) corr[g] *= f;
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[h][i] *= f;
+        }
         // v_exp_f32: weights below 2^-126 of the running max may flush to zero
         const float p0 = __builtin_amdgcn_exp2f(xs[0] - m_lane);
         const float p1 = __builtin_amdgcn_exp2f(xs[1] - m_lane);
         l_lane += p0 + p1;
+        const float pw0 = p0 * wmul, pw1 = p1 * wmul;   // exact: a power of two
 #pragma unroll
         for (int g = 0; g < NVG; ++g) {
             const uint32_t m0 = L.vm.m[0][g], m1 = L.vm.m[1][g];
-            const uint32_t pair = pack_f16(mul_lo(m0, p0), mul_lo(m1, p1));
+            const uint32_t pair = pack_f16(mul_lo(m0, pw0), mul_lo(m1, pw1));
             float cg = corr[g];
-            cg = fmaf(p0, fmaf(kVCenter, f16lo(m0), f16hi(m0)), cg);
-            cg = fmaf(p1, fmaf(kVCenter, f16lo(m1), f16hi(m1)), cg);
+            cg = fmaf(pw0, fmaf(kVCenter, f16lo(m0), f16hi(m0)), cg);
+            cg = fmaf(pw1, fmaf(kVCenter, f16lo(m1), f16hi(m1)), cg);
             corr[g] = dot2_f16(pair, kVCenterNeg /* (-c, -c) */, cg);
             wbuf[wave][t16][g][q4] = pair;
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
 
         // -------------------------------------------- PV
 #pragma unroll
@@ -430,7 +462,7 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) acc[h][i] = dot2_f16(wpair[h], cp[i], acc[h][i]);
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
     };
 
     // two load buffers in ping-pong: the next tile's loads are in flight while
@@ -468,17 +500,19 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
             v += __shfl_xor(v, 32);
             acc[h][i] = v;
         }
+    // undo the code scale 2^-24 and the weight scale 2^wexp (exact)
+    const float unit = ldexpf(1.0f, 24 - wexp), unit16 = ldexpf(1.0f, 20 - wexp), unitc = ldexpf(1.0f, -wexp);
 #pragma unroll
     for (int h = 0; h < kGQ; ++h)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const float lo = acc[h][2 * k], whole = acc[h][2 * k + 1];
             if constexpr (VB == 4) {
-                acc[h][2 * k] = lo * 16777216.0f;                   // 2^24
-                acc[h][2 * k + 1] = (whole - lo) * 1048576.0f;      // 2^24 / 16
+                acc[h][2 * k] = lo * unit;
+                acc[h][2 * k + 1] = (whole - lo) * unit16;      // / 16
             } else {
-                acc[h][2 * k] = lo * 16777216.0f;
-                acc[h][2 * k + 1] = whole * 16777216.0f;
+                acc[h][2 * k] = lo * unit;
+                acc[h][2 * k + 1] = whole * unit;
             }
         }
     // head q4 sums over the lane's tokens: reduce over lanes with equal q4
@@ -499,7 +533,7 @@ __global__ __launch_bounds__(256, 2) void decode_kivi_kernel(DecodeArgs a) {
         }
         if (lane < 16) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) comb_o[wave][h][c * 8 + i] = acc[h][i] + cv;
+            for (int i = 0; i < 8; ++i) comb_o[wave][h][c * 8 + i] = fmaf(cv, unitc, acc[h][i]);
         }
     }
     if (lane < kGQ) {

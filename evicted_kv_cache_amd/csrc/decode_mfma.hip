@@ -29,7 +29,11 @@
 //   pre-divided by 16.
 // * Softmax: lane (h, n) owns head h for tokens n and n + 16 of the tile,
 //   with a lazily rescaled running max as in the VALU decode, and writes the
-//   fp16 weight pairs w^ = fp16(p s) per V group to LDS.
+//   fp16 weight pairs w^ = fp16(p s 2^E) per V group to LDS.  E is the wave's
+//   weight exponent: it follows the largest V scale seen so far (rescaling
+//   the accumulators when it changes, as for a new running max), so that
+//   small V scales do not push the weights into fp16's subnormal range,
+//   and it is taken out exactly at the end.
 // * Values: O = W V over the tile's 32 tokens in one MFMA per code byte
 //   position and kind.  W row i = 4g + h holds head h's weights for V group
 //   g (one 16-byte LDS read per lane); V column n is code word n (4-bit:
@@ -190,7 +194,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 
     float m_lane = -INFINITY;     // running max of head r
     float l_lane = 0.0f;          // running sum of head r over this lane's tokens
-    float corr[NVG];              // head r, per V group: sum p (z + c s) - c sum w^
+    // fp16 weights are p s 2^wexp: wexp follows the largest V scale the wave
+    // has seen (vsmax 2^wexp in [2^13, 2^14)), so with p <= 1 no weight
+    // overflows, and any weight above 2^-27 of vsmax stays a normal fp16
+    // with full relative precision.  acc and corr are in these units.
+    float vsmax = 0.0f;
+    int wexp = 0;
+    float wmul = 1.0f;            // 2^wexp
+    float corr[NVG];              // head r, per V group: (sum p (z + c s) - c sum w^) 2^wexp
 #pragma unroll
     for (int g = 0; g < NVG; ++g) corr[g] = 0.0f;
     // PV: row (g = r, h = i) of column n, scaled 2^-24.  4-bit codes: acc[k]
@@ -288,21 +299,41 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                 for (int k = 0; k < 8; ++k) acc[k][h] *= ah;
             }
         }
+        // -------------------------------------------- weight scale (rescale on a new largest V scale)
+        // the lanes of a row hold the V scales of all the tile's tokens
+        float sl = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NVG; ++g) sl = fmaxf(sl, fmaxf(f16lo(L.vm[0][g]), f16lo(L.vm[1][g])));
+        if (__builtin_amdgcn_ballot_w64(sl > vsmax) != 0) {
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) sl = fmaxf(sl, __shfl_xor(sl, off));
+            vsmax = fmaxf(vsmax, sl);
+            int e;
+            frexpf(vsmax, &e);                        // vsmax in [2^(e-1), 2^e)
+            const float f = ldexpf(1.0f, 14 - e - wexp);
+            wexp = 14 - e;
+            wmul = ldexpf(1.0f, wexp);
+#pragma unroll
+            for (int g = 0; g < NVG; ++g) corr[g] *= f;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc[k] *= f;
+        }
         // v_exp_f32: weights below 2^-126 of the running max may flush to zero
         const float p0 = __builtin_amdgcn_exp2f(xs[0] - m_lane);
         const float p1 = __builtin_amdgcn_exp2f(xs[1] - m_lane);
         l_lane += p0 + p1;
+        const float pw0 = p0 * wmul, pw1 = p1 * wmul;   // exact: a power of two
 #pragma unroll
         for (int g = 0; g < NVG; ++g) {
             const uint32_t m0 = L.vm[0][g], m1 = L.vm[1][g];
-            const uint32_t pair = pack_f16(__builtin_fmaf(f16lo(m0), p0, 0.0f), __builtin_fmaf(f16lo(m1), p1, 0.0f));
+            const uint32_t pair = pack_f16(__builtin_fmaf(f16lo(m0), pw0, 0.0f), __builtin_fmaf(f16lo(m1), pw1, 0.0f));
             float cg = corr[g];
-            cg = fmaf(p0, fmaf(kVCenter, f16lo(m0), f16hi(m0)), cg);
-            cg = fmaf(p1, fmaf(kVCenter, f16lo(m1), f16hi(m1)), cg);
+            cg = fmaf(pw0, fmaf(kVCenter, f16lo(m0), f16hi(m0)), cg);
+            cg = fmaf(pw1, fmaf(kVCenter, f16lo(m1), f16hi(m1)), cg);
             corr[g] = dot2_f16(pair, kVCenterNeg /* (-8, -8) */, cg);
             wbuf[wave][g][r][n] = pair;
         }
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
 
         // -------------------------------------------- values
         uint32_t vw[4][2][VH];
@@ -314,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                 const int u = lane + 64 * q;
                 *reinterpret_cast<u32x4*>(&vst[wave][u >> 3][4 * (u & 7)]) = L.vraw[q];
             }
-            __builtin_amdgcn_wave_barrier();
+            wave_lds_sync();
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -352,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                     acc[4 * hb + k] = mfma16(aw, bw, acc[4 * hb + k]);
                 }
             }
-        __builtin_amdgcn_wave_barrier();
+        wave_lds_sync();
     };
 
     // this wave's tiles wave, wave + 4, ...; two load buffers in ping-pong:
@@ -387,6 +418,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
         for (int g = 0; g < NVG; ++g) corr[g] += __shfl_xor(corr[g], off);
     }
+    // undo the code scale 2^-24 and the weight scale 2^wexp (exact)
+    const float unit = ldexpf(1.0f, 24 - wexp), unit16 = ldexpf(1.0f, 20 - wexp), unitc = ldexpf(1.0f, -wexp);
 #pragma unroll
     for (int h = 0; h < kGQ; ++h) {
         // correction of head h (row h) for V group r
@@ -402,8 +435,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const float whole = acc[k][h], lo = acc[4 + k][h];
-                    comb_o[wave][h][8 * n + 2 * k] = lo * 16777216.0f + cv;                   // 2^24
-                    comb_o[wave][h][8 * n + 2 * k + 1] = (whole - lo) * 1048576.0f + cv;      // 2^24 / 16
+                    comb_o[wave][h][8 * n + 2 * k] = fmaf(lo, unit, cv * unitc);
+                    comb_o[wave][h][8 * n + 2 * k + 1] = fmaf(whole - lo, unit16, cv * unitc);   // / 16
                 }
             }
         } else {
@@ -412,7 +445,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                 const int c0 = 4 * (n + 16 * hb);     // channels c0 .. c0 + 3
                 if (r == c0 / GV) {
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) comb_o[wave][h][c0 + k] = acc[4 * hb + k][h] * 16777216.0f + cv;
+                    for (int k = 0; k < 4; ++k) comb_o[wave][h][c0 + k] = fmaf(acc[4 * hb + k][h], unit, cv * unitc);
                 }
             }
         }

@@ -53,6 +53,17 @@ __device__ __forceinline__ void load4_as_f32(const void* p, int64_t i, float v[4
 
 __host__ __device__ constexpr int dtype_bytes(int dt) { return dt == KVQ_F32 ? 4 : 2; }
 
+// Exchange through LDS between the lanes of one wave: the stores before the
+// call are visible to the loads after it.  The fences order the LDS accesses
+// for the compiler (the wave barrier alone does not touch memory); at
+// wavefront scope they emit no wait, since one wave's LDS operations complete
+// in order.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Quantization constants of the specification (kvq.h): eps = 1e-5.
 constexpr float kEps = 1e-5f;
 
