@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 # ---- enums (mirror include/kvq.h) -------------------------------------------
 KVQ_OK, KVQ_NOOP = 0, 1
 KVQ_ERR_INVALID_ARG, KVQ_ERR_UNSUPPORTED, KVQ_ERR_CAPACITY = -1, -2, -3
-KVQ_ERR_ALIGNMENT, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP = -4, -5, -6
+KVQ_ERR_ALIGNMENT, KVQ_ERR_WORKSPACE, KVQ_ERR_HIP, KVQ_ERR_SCRATCH = -4, -5, -6, -7
 KVQ_F32, KVQ_F16, KVQ_BF16 = 0, 1, 2
 KVQ_PLAIN, KVQ_KIVI_CH, KVQ_TOK_AFFINE, KVQ_TOK_SYM4 = 0, 1, 2, 3
 KVQ_CENTER_K, KVQ_TEST_CENTER_ANY, KVQ_POS_PER_HEAD = 0x1, 0x2, 0x4
@@ -43,7 +43,7 @@ EXPORTS = ("kvq_cache_sizes", "kvq_cache_reset", "kvq_quantize_append",
            "kvq_snapkv_select_ex", "kvq_snapkv_pool_scores", "kvq_quantize_append_at",
            "kvq_snapkv_chunk_workspace_bytes", "kvq_snapkv_prefill_chunk", "kvq_rope_table",
            "kvq_decode_attention_rope", "kvq_prefill_workspace_bytes", "kvq_prefill_attention",
-           "kvq_status_string", "kvq_version")
+           "kvq_decode_attention_noalloc", "kvq_status_string", "kvq_version")
 
 
 class KvqError(RuntimeError):
@@ -101,6 +101,7 @@ def lib():
         L.kvq_decode_workspace_bytes.restype = sz
         L.kvq_decode_workspace_bytes.argtypes = [P, i32]
         L.kvq_decode_attention.argtypes = [P, P, P, i32, i32, f32, P, P, sz, P]
+        L.kvq_decode_attention_noalloc.argtypes = [P, P, P, i32, i32, f32, P, P]
         L.kvq_evict_streaming.argtypes = [P, P, P, i32, i32, P]
         L.kvq_snapkv_workspace_bytes.restype = sz
         L.kvq_snapkv_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
@@ -277,6 +278,23 @@ def kvq_decode_attention(layout: Layout, cache: Cache, q, sm_scale: float = 0.0,
                                       ws.data_ptr(), ws.numel() * ws.element_size(),
                                       _stream(stream)),
            "kvq_decode_attention")
+    return out
+
+
+def kvq_decode_attention_noalloc(layout: Layout, cache: Cache, q, sm_scale: float = 0.0, out=None,
+                                 stream=None):
+    """kvq_decode_attention without a workspace: the library's fixed per-GPU
+    scratch holds the split partials.  q: [B][Hq][D]; returns out [B][Hq][D] fp32."""
+    torch = _torch()
+    assert q.is_contiguous()
+    B, Hq, D = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    cl = layout.c()
+    _check(lib().kvq_decode_attention_noalloc(ctypes.byref(cl), ctypes.byref(cache.c), q.data_ptr(),
+                                              _qdtype(q), Hq, float(sm_scale), out.data_ptr(),
+                                              _stream(stream)),
+           "kvq_decode_attention_noalloc")
     return out
 
 

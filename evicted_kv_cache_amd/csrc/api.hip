@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 using namespace kvq;
@@ -145,6 +147,7 @@ const char* kvq_status_string(kvq_status s) {
         case KVQ_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
         case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
         case KVQ_ERR_HIP: return "HIP runtime or launch error";
+        case KVQ_ERR_SCRATCH: return "request exceeds the fixed scratch of the no-allocation call";
     }
     return "unknown status";
 }
@@ -249,17 +252,10 @@ size_t kvq_decode_workspace_bytes(const kvq_layout* L, int32_t n_q_heads) {
     return decode_workspace_bytes(L->batch, n_q_heads, L->head_dim, L->capacity);
 }
 
-static kvq_status decode_impl(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
-                              int32_t n_q_heads, float sm_scale, const float* rope, int32_t q_pos, float* out,
-                              void* ws, size_t ws_bytes, void* stream) {
-    hipStream_t s = static_cast<hipStream_t>(stream);
+// Kernel arguments and split plan of one decode (workspace pointers unset).
+static DecodeArgs decode_args(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
+                              int32_t n_q_heads, float sm_scale, const float* rope, int32_t q_pos, float* out) {
     const int D = L->head_dim;
-    if (c->n_stored == 0)
-        return hip_status(launch_zero_f32(out, (size_t)L->batch * n_q_heads * D, s));
-    const size_t need = decode_workspace_bytes(L->batch, n_q_heads, D, L->capacity);
-    if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
-    if (!aligned16(ws)) return KVQ_ERR_ALIGNMENT;
-
     DecodeArgs a{};
     a.k_codes = c->k_codes; a.k_meta = c->k_meta; a.k_resid = c->k_resid;
     a.v_codes = c->v_codes; a.v_meta = c->v_meta; a.k_row = c->k_row;
@@ -274,9 +270,34 @@ static kvq_status decode_impl(const kvq_layout* L, const kvq_cache* c, const voi
     a.scale_log2 = scale * 1.4426950408889634f;
     if (decode_fast_applies(a)) decode_fast_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
     else decode_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
+    return a;
+}
+
+// Split partials the launch writes: B Hq n_splits (D + 2) fp32, none when the
+// fast kernels run unsplit (they then write the output directly).
+static size_t decode_partial_bytes(const DecodeArgs& a) {
+    if (a.n_splits == 1 && decode_fast_applies(a)) return 0;
+    return (size_t)a.B * a.Hq * a.n_splits * (a.D + 2) * sizeof(float);
+}
+
+static kvq_status decode_launch(DecodeArgs& a, void* ws, hipStream_t s) {
     a.ws_o = static_cast<float*>(ws);
-    a.ws_ml = a.ws_o + (size_t)a.B * a.Hq * a.n_splits * D;
+    a.ws_ml = a.ws_o + (size_t)a.B * a.Hq * a.n_splits * a.D;
     return hip_status(launch_decode(a, s));
+}
+
+static kvq_status decode_impl(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
+                              int32_t n_q_heads, float sm_scale, const float* rope, int32_t q_pos, float* out,
+                              void* ws, size_t ws_bytes, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int D = L->head_dim;
+    if (c->n_stored == 0)
+        return hip_status(launch_zero_f32(out, (size_t)L->batch * n_q_heads * D, s));
+    const size_t need = decode_workspace_bytes(L->batch, n_q_heads, D, L->capacity);
+    if (!ws || ws_bytes < need) return KVQ_ERR_WORKSPACE;
+    if (!aligned16(ws)) return KVQ_ERR_ALIGNMENT;
+    DecodeArgs a = decode_args(L, c, q, q_dtype, n_q_heads, sm_scale, rope, q_pos, out);
+    return decode_launch(a, ws, s);
 }
 
 static kvq_status decode_check(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,
@@ -298,6 +319,51 @@ kvq_status kvq_decode_attention(const kvq_layout* L, const kvq_cache* c, const v
     kvq_status st = decode_check(L, c, q, q_dtype, n_q_heads, sm_scale, out);
     if (st != KVQ_OK) return st;
     return decode_impl(L, c, q, q_dtype, n_q_heads, sm_scale, nullptr, 0, out, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------- no-allocation decode
+// The split partials of kvq_decode_attention_noalloc live in this fixed
+// array (KVQ_NOALLOC_SCRATCH_BYTES), one copy per GPU the library runs on.
+// Host code never uses the array's name as an address: the device address
+// of each GPU's copy comes from hipGetSymbolAddress, looked up once per
+// device on the first call with that device current.  Partials are written
+// before they are read, so nothing needs clearing between calls.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+static kvq_status noalloc_scratch(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return KVQ_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return KVQ_ERR_UNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return KVQ_ERR_HIP;
+    *ptr = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
+kvq_status kvq_decode_attention_noalloc(const kvq_layout* L, const kvq_cache* c, const void* q,
+                                        int32_t q_dtype, int32_t n_q_heads, float sm_scale, float* out,
+                                        void* stream) {
+    kvq_status st = decode_check(L, c, q, q_dtype, n_q_heads, sm_scale, out);
+    if (st != KVQ_OK) return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (c->n_stored == 0)
+        return hip_status(launch_zero_f32(out, (size_t)L->batch * n_q_heads * L->head_dim, s));
+    DecodeArgs a = decode_args(L, c, q, q_dtype, n_q_heads, sm_scale, nullptr, 0, out);
+    if (decode_partial_bytes(a) > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_SCRATCH;
+    void* ws = nullptr;
+    if ((st = noalloc_scratch(&ws)) != KVQ_OK) return st;
+    return decode_launch(a, ws, s);
 }
 
 kvq_status kvq_decode_attention_rope(const kvq_layout* L, const kvq_cache* c, const void* q, int32_t q_dtype,

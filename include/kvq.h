@@ -21,7 +21,8 @@
  *   - Pointers named in a layout comment as device memory are device pointers
  *     on the current HIP device; the layout/cache/size structs themselves are
  *     host memory.  The caller owns all memory; the library allocates nothing
- *     and keeps no state besides cached device properties.
+ *     and keeps no state besides cached device properties and the fixed
+ *     scratch of kvq_decode_attention_noalloc.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *     and never synchronized; outputs are valid once the stream reaches them.
  *   - Arguments are validated on the host before anything is enqueued.  On an
@@ -53,7 +54,8 @@ typedef enum {
     KVQ_ERR_CAPACITY = -3,      /* append past the cache capacity */
     KVQ_ERR_ALIGNMENT = -4,
     KVQ_ERR_WORKSPACE = -5,     /* workspace missing or too small */
-    KVQ_ERR_HIP = -6            /* a HIP launch or runtime call failed */
+    KVQ_ERR_HIP = -6,           /* a HIP launch or runtime call failed */
+    KVQ_ERR_SCRATCH = -7        /* needs more than the fixed scratch of a no-allocation call */
 } kvq_status;
 
 /* Element types of K/V inputs, queries and PLAIN storage. */
@@ -231,6 +233,27 @@ kvq_status kvq_decode_attention(const kvq_layout* layout, const kvq_cache* cache
                                 const void* q, int32_t q_dtype, int32_t n_q_heads,
                                 float sm_scale, float* out,
                                 void* ws, size_t ws_bytes, void* stream);
+
+/* kvq_decode_attention without a caller workspace, for callers that cannot
+ * allocate device memory (code under stream capture, tight serving loops,
+ * harnesses that forbid allocation).  The split partials live in a fixed
+ * scratch array of KVQ_NOALLOC_SCRATCH_BYTES bytes that the library holds on
+ * each GPU it runs on until the process ends; its address is looked up once
+ * per device, on the first call with that device current.  Nothing is
+ * allocated or freed by the call itself.
+ *   Arguments, layout and results as kvq_decode_attention.
+ *   The scratch is shared by every call on one GPU and keeps the last call's
+ *   partials: calls that overlap on one GPU (different streams, or several
+ *   host threads) race and must be ordered by the caller.
+ * Errors as kvq_decode_attention (never KVQ_ERR_WORKSPACE), plus
+ * KVQ_ERR_SCRATCH when the split partials of this call (B * n_q_heads *
+ * splits * (head_dim + 2) fp32) exceed the scratch: every layout of the
+ * per-token 4-bit-key or KIVI 4-bit-key kernels fits, the LDS-tiled kernel
+ * of the other layouts fits while B * n_q_heads <= 16129 at head_dim 128.  */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const kvq_cache* cache,
+                                        const void* q, int32_t q_dtype, int32_t n_q_heads,
+                                        float sm_scale, float* out, void* stream);
 
 /* Multi-query attention over the cache: a prefill chunk of n_q queries per
  * head ([P4] s.5: the fused-attention microbenchmark shape, 128 queries with

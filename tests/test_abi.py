@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in (0, 1, -1, -2, -3, -4, -5, -6):
+    for code in (0, 1, -1, -2, -3, -4, -5, -6, -7):
         assert K.status_string(code) and K.status_string(code) != "unknown status"
     assert K.status_string(-99) == "unknown status"
 
@@ -177,6 +177,29 @@ def test_decode_validation_without_gpu():
     assert call_decode(L, c, 32, q=MIS) == K.KVQ_ERR_ALIGNMENT
     assert call_decode(L, c, 32, qdt=7) == K.KVQ_ERR_INVALID_ARG
     assert call_decode(L, c, 32, scale=float("nan")) == K.KVQ_ERR_INVALID_ARG
+
+
+def call_decode_noalloc(L, c, hq, q=FAKE, out=FAKE, qdt=K.KVQ_BF16, scale=0.0):
+    cl = L.c()
+    return K.lib().kvq_decode_attention_noalloc(ctypes.byref(cl), ctypes.byref(c), q, qdt, hq,
+                                                ctypes.c_float(scale), out, None)
+
+
+def test_decode_noalloc_validation_without_gpu():
+    """The no-allocation decode validates like kvq_decode_attention and
+    rejects, before touching the device, a call whose split partials exceed
+    the fixed scratch (8 MiB): the LDS-tiled kernel writes B * Hq * splits *
+    (D + 2) fp32, here 4096 * 64 * 130 * 4 B at one split."""
+    L = c5_layout(batch=2, capacity=1000)
+    c = fake_cache(L, n_stored=500)
+    assert call_decode_noalloc(L, c, 12) == K.KVQ_ERR_INVALID_ARG
+    assert call_decode_noalloc(L, c, 8 * 9) == K.KVQ_ERR_UNSUPPORTED
+    assert call_decode_noalloc(L, c, 32, q=MIS) == K.KVQ_ERR_ALIGNMENT
+    assert call_decode_noalloc(L, c, 32, qdt=7) == K.KVQ_ERR_INVALID_ARG
+    assert call_decode_noalloc(L, c, 32, scale=float("nan")) == K.KVQ_ERR_INVALID_ARG
+    big = c5_layout(batch=4096, capacity=64, k_kind="kivi_ch", k_bits=8, k_group=32, v_bits=8,
+                    v_group=128)
+    assert call_decode_noalloc(big, fake_cache(big, n_stored=40, n_quant=32), 64) == K.KVQ_ERR_SCRATCH
 
 
 def call_evict(L, src, dst, sink, window):
