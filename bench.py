@@ -51,6 +51,49 @@ def decode_algorithmic_bytes(B, Hkv, Hq, D, T, bits, group, q_bytes=2):
     return B * Hkv * T * per_token_head + B * Hq * D * q_bytes + B * Hq * D * 4
 
 
+MALL_BYTES = 256 << 20
+ROTATE_BYTES = 512 << 20           # input copies cycled by the cold timings: twice the MALL
+
+
+def time_rotating(fns, reps, torch):
+    """Per-call ms of calls whose inputs are distinct copies (fns[i] reads copy
+    i), replayed from one captured HIP graph: a copy comes round again only
+    after ROTATE_BYTES (> 2x the 256 MB MALL) of other inputs were read, so
+    each call reads its inputs from HBM ("cold")."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for f in fns:
+            f()
+    ms = time_stream(g.replay, reps, 2, torch) / len(fns)
+    del g
+    return ms
+
+
+def n_copies(nbytes):
+    return max(2, math.ceil(ROTATE_BYTES / nbytes))
+
+
+def host_cpu():
+    """(os.cpu_count(), CPUs this process may run on, /proc/cpuinfo model name)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        avail = os.cpu_count() or 1
+    return os.cpu_count() or 1, avail, model
+
+
 def time_stream(fn, steps, warmup, torch):
     """Average ms per call of fn over `steps` calls, with HIP events on the current stream."""
     for _ in range(warmup):
@@ -93,7 +136,8 @@ def cpu_baseline(w, target_s=12.0):
     from oracle.cache import Layout as OLayout
     from oracle.cache import OracleCache
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    host_cpus, avail, model = host_cpu()
+    threads = max(1, min(16, avail))
     e = w.extra
 
     def slice_cache(b, h):
@@ -119,11 +163,14 @@ def cpu_baseline(w, target_s=12.0):
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(lambda oc: oc[0].decode(oc[1], w.dtype, threads=1), caches))
     dt = time.perf_counter() - t0
-    nbytes = decode_algorithmic_bytes(1, 1, w.group, w.head_dim, w.seq_len, e["k_bits"], e["k_group"]) * n
+    per_slice = decode_algorithmic_bytes(1, 1, w.group, w.head_dim, w.seq_len, e["k_bits"], e["k_group"])
+    nbytes = per_slice * n
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": round(per_slice / one / 1e9, 5),
+            "host_cpus": host_cpus, "cpus_available": avail, "cpu_model": model,
             "sample": f"{n} of {w.batch * w.n_kv_heads} (batch, kv-head) slices of the headline "
                       f"workload ({n * w.group} query heads over T={w.seq_len}), fp64 decode, "
-                      f"{dt:.1f} s wall on {threads} threads"}
+                      f"{dt:.1f} s wall on {threads} threads (one thread: {one:.2f} s per slice)"}
 
 
 def main():
@@ -267,14 +314,25 @@ def main():
         vo = torch.empty_like(ko)
         wsb = torch.empty(K.kvq_snapkv_workspace_bytes(Bs, Hs, Ss, Ds, ex["obs_window"]),
                           dtype=torch.uint8, device=dev)
-        msd = time_stream(lambda: K.kvq_snapkv_select(ksd, vsd, ex["obs_window"], ex["n_sink"],
-                                                      ex["budget"], sc, kept, ko, vo, wsb),
-                          200, 10, torch)
+        def snap(kk, vv):
+            return lambda: K.kvq_snapkv_select(kk, vv, ex["obs_window"], ex["n_sink"], ex["budget"],
+                                               sc, kept, ko, vo, wsb)
+        msw = time_stream(snap(ksd, vsd), 200, 10, torch)
+        ncp = n_copies(ks.nbytes + vs.nbytes)
+        copies = [(ksd.clone(), vsd.clone()) for _ in range(ncp)]
+        msd = time_rotating([snap(a, b) for a, b in copies], 20, torch)
+        del copies
         sbytes = ks.nbytes + 2 * n_keep * Hs * Ds * 2 * 2 + sc.numel() * 4 + kept.numel() * 4
         rows["D_snapkv"] = {"workload": f"{ws_.name} S={Ss} w={ex['obs_window']} sink={ex['n_sink']} "
                                         f"budget={ex['budget']} Hkv={Hs} D={Ds}",
                             "us": round(msd * 1e3, 2), "scores/s": round(Hs * Ss / (msd * 1e-3), 1),
-                            "GB/s": round(sbytes / msd / 1e6, 1)}
+                            "algorithmic_bytes": sbytes,
+                            "GB/s": round(sbytes / msd / 1e6, 1),
+                            "frac_hbm": round(sbytes / msd / 1e6 / PEAK_HBM_GBS, 4),
+                            "timing": f"cold: graph replay over {ncp} copies of K and V "
+                                      f"({ncp * (ks.nbytes + vs.nbytes) >> 20} MiB)",
+                            "us_warm": round(msw * 1e3, 2),
+                            "GB/s_warm": round(sbytes / msw / 1e6, 1)}
 
     # ---- row B, other decode workloads: Q4_0-style centered K + int8 V (B=16,
     # T=16384; HBM-bound) and a Llama-3.2-3B-shaped KIVI int4 layer (B=1,
@@ -297,17 +355,23 @@ def main():
                           v_bits=eb["v_bits"], v_group=eb["v_group"], in_dtype=wb.dtype, flags=flags)
             cb = K.Cache(Lb, k_bias=bias)
             K.kvq_quantize_append(Lb, cb, kdb, vdb)
-            del kdb, vdb
             outb = torch.empty((Bb, Hqb, Db), dtype=torch.float32, device=dev)
             wsb = torch.empty(max(K.kvq_decode_workspace_bytes(Lb, Hqb), 16), dtype=torch.uint8, device=dev)
             stepb = lambda: K.kvq_decode_attention(Lb, cb, qb, out=outb, ws=wsb)
-            stepb()
-            torch.cuda.synchronize()
-            gb = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gb):
-                for _ in range(10):
-                    stepb()
-            usb = time_stream(gb.replay, 10, 2, torch) / 10 * 1e3
+            # warm: the same cache 10 times per replayed graph
+            usw = time_rotating([stepb] * 10, 10, torch) * 1e3
+            # cold: identical caches (appended from the same inputs) in rotation
+            cache_bytes = sum(x.numel() for x in (cb.k_codes, cb.k_meta, cb.v_codes, cb.v_meta) if x is not None)
+            ncp = n_copies(cache_bytes)
+            caches = [cb]
+            for _ in range(ncp - 1):
+                cx = K.Cache(Lb, k_bias=bias)
+                K.kvq_quantize_append(Lb, cx, kdb, vdb)
+                caches.append(cx)
+            del kdb, vdb
+            usb = time_rotating([(lambda cc=cc: K.kvq_decode_attention(Lb, cc, qb, out=outb, ws=wsb))
+                                 for cc in caches], 10, torch) * 1e3
+            del caches
             qo = Bb * Hqb * Db * (2 + 4)
             if eb["k_kind"] == "tok_sym4":     # codes + fp16 block scales; int8 V + (scale, zero)
                 nb = Bb * Hb * Tb * (Db // 2 + (Db // 32) * 2 + Db * eb["v_bits"] // 8 + (Db // eb["v_group"]) * 4) + qo
@@ -318,8 +382,10 @@ def main():
                 "workload": f"{wname} B={Bb} Hq/Hkv={Hqb}/{Hb} D={Db} T={Tb} K {eb['k_kind']} "
                             f"{eb['k_bits']}-bit, V affine {eb['v_bits']}-bit",
                 "us": round(usb, 2), "algorithmic_bytes": nb, "GB/s": round(nb / usb / 1e3, 1),
-                "frac_hbm": round(nb / usb / 1e3 / PEAK_HBM_GBS, 4)}
-            del gb, cb, outb, wsb
+                "frac_hbm": round(nb / usb / 1e3 / PEAK_HBM_GBS, 4),
+                "timing": f"cold: graph replay over {ncp} identical caches ({ncp * cache_bytes >> 20} MiB)",
+                "us_warm": round(usw, 2), "GB/s_warm": round(nb / usw / 1e3, 1)}
+            del cb, outb, wsb
 
     # ---- row E: multi-query (prefill-chunk) attention over the cache, the
     # microbenchmark shape of 128 causal queries per head with 32/8 heads x 128
@@ -346,6 +412,22 @@ def main():
                 "us": round(mse * 1e3, 2), "algorithmic_flops": flops, "TFLOP/s": round(tf, 1),
                 "frac_mfma_fp16": round(tf / PEAK_MFMA_F16_TFLOPS, 4)}
             del ce, oe, wse
+
+    # bandwidth probes on the same device: a 2 GiB device copy (read + write)
+    # and a 2 GiB read (a sum reduction), both torch library kernels
+    probes = None
+    if args.mode == "full":
+        n = 1 << 31
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        msc = time_stream(lambda: dst.copy_(src), 10, 3, torch)
+        msr = time_stream(lambda: torch.sum(src), 10, 3, torch)
+        del src, dst
+        probes = {"copy_GB/s": round(2 * n / msc / 1e6, 1), "read_GB/s": round(n / msr / 1e6, 1),
+                  "what": "torch copy_ of 2 GiB (read + write bytes) and torch.sum over 2 GiB (read bytes)"}
+        probes["step_frac_of_copy_probe"] = round(gbs / probes["copy_GB/s"], 4)
+        probes["step_frac_of_read_probe"] = round(gbs / probes["read_GB/s"], 4)
+        log(f"probes: copy {probes['copy_GB/s']} GB/s, read {probes['read_GB/s']} GB/s")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -375,6 +457,7 @@ def main():
                      "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "decode_mfma_kernel<bf16, 64, 64> (one launch per step)"},
         "cpu_baseline": cpu,
+        "bandwidth_probes": probes,
         "rows": rows,
     }
     print(json.dumps(result), flush=True)
