@@ -12,7 +12,8 @@ workloads and reported under "rows":
   D  SnapKV prefill selection (8 kv-heads x 128, S = 8192, window 32,
      sink 4, budget 512): scores/s
   B  decode on the other cache formats: Q4_0-style centered K + int8 V
-     (batch 16, T = 16384) and a KIVI int4 Llama-3.2-3B layer (T = 8192)
+     (batch 16, T = 16384), a KIVI int4 Llama-3.2-3B layer (T = 8192) and
+     the same layer shape at batch 16, T = 16384
 Inputs are seeded synthetic data (synth) already resident in HBM when the
 timed region starts.  Times come from HIP events on the stream the kernels
 run on.  The CPU oracle is timed on a bounded sample as the CPU baseline.
@@ -339,8 +340,9 @@ def main():
     # T=8192; latency-bound).  Device time per step from a replayed graph of
     # 10 steps, so host marshalling is not in the timed region.
     if "B" in args.rows:
-        for wname in ("q4_0_centered", "llama3b_kivi_int4"):
-            wb = synth.workload(wname)
+        for wname, over in (("q4_0_centered", {}), ("llama3b_kivi_int4", {}),
+                            ("llama3b_kivi_int4", {"batch": 16, "seq_len": 16384})):
+            wb = synth.workload(wname, **over)
             eb = wb.extra
             Bb, Hb, Hqb, Db, Tb = wb.batch, wb.n_kv_heads, wb.n_q_heads, wb.head_dim, wb.seq_len
             kh, vh, qh = synth.full(wb, threads=max(1, min(16, os.cpu_count() or 1)))
@@ -378,7 +380,7 @@ def main():
             else:                              # KIVI: codes + one table row per 32 tokens; int4 V
                 nb = Bb * Hb * (Tb * Db * eb["k_bits"] // 8 + (Tb // eb["k_group"]) * Db * 4 +
                                 Tb * Db * eb["v_bits"] // 8 + Tb * (Db // eb["v_group"]) * 4) + qo
-            rows[f"B_decode_{wname}"] = {
+            rows[f"B_decode_{wname}" + (f"_B{Bb}_T{Tb}" if over else "")] = {
                 "workload": f"{wname} B={Bb} Hq/Hkv={Hqb}/{Hb} D={Db} T={Tb} K {eb['k_kind']} "
                             f"{eb['k_bits']}-bit, V affine {eb['v_bits']}-bit",
                 "us": round(usb, 2), "algorithmic_bytes": nb, "GB/s": round(nb / usb / 1e3, 1),

@@ -28,7 +28,7 @@ LIB = os.path.join(PKG, "libkvq.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_fast.hip", "decode_mfma.hip", "prefill_attn.hip", "evict.hip",
+SOURCES = ["api.hip", "quantize.hip", "decode.hip", "decode_mfma.hip", "prefill_attn.hip", "evict.hip",
            "snapkv.hip"]
 
 FLAGS = [

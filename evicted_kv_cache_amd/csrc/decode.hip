@@ -11,7 +11,7 @@
 // ("kv-cache: optional per-channel K-cache mean-centering", "Why this is safe").
 //
 // This file holds the generic kernel that serves every layout.  The
-// bandwidth-tuned kernels for per-token 4-bit layouts live in decode_fast.hip.
+// bandwidth-tuned kernels for 4-bit-key layouts live in decode_mfma.hip.
 #include <math.h>
 
 #include "dequant8.h"

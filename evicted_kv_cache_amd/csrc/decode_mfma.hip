@@ -58,6 +58,7 @@
 #include <math.h>
 
 #include "bufload.h"
+#include "dequant8.h"
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -72,6 +73,7 @@ constexpr int kWaves = 4;
 constexpr int kRowB = kD / 2;   // bytes of 4-bit K codes per token
 constexpr int kKAff4 = 0;       // per-token affine K groups: (scale, zero) fp16 pairs
 constexpr int kKSym4 = 1;       // symmetric K blocks of 32: one fp16 scale d, value (u - 8) d
+constexpr int kKKivi = 2;       // KIVI per-channel K: (scale, zero) per channel from the token's group row
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -115,13 +117,16 @@ struct MTile {
     uint32_t vm[2][NVG]; // V (scale, zero) per group, tokens n and n + 16
     uint32_t v[4][2][VH];  // V code words n (and n + 16) of tokens 4r + j and 4r + j + 16
     u32x4 vraw[4];         // 8-bit V codes of the tile, 16-byte units lane + 64 q
+    int32_t krow[2];       // KIVI: table rows of tokens n and n + 16
+    buf::u32x2 stg[2];     // KIVI: this lane's 8 bytes of table rows r0, r1
+    int r0, r1;            // KIVI: rows of the tile's first and last coded tokens
 };
 
-// KF: K format (kKAff4, or kKSym4 with GK = 32); GK, GV: channels per K / V
-// group (32, 64 or 128); VB: bits per V code (4 or 8).
+// KF: K format (kKAff4; kKSym4 or kKKivi with GK = 32); GK, GV: channels
+// per K / V group (32, 64 or 128); VB: bits per V code (4 or 8).
 template <int QDT, int KF, int GK, int VB, int GV>
 __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
-    static_assert(KF == kKAff4 || GK == 32, "symmetric K blocks are 32 channels");
+    static_assert(KF == kKAff4 || GK == 32, "symmetric and KIVI keys take GK = 32");
     constexpr int NKG = kD / GK;
     constexpr int NVG = kD / GV;
     constexpr int VH = VB / 4;
@@ -142,13 +147,23 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     __shared__ __align__(16) uint32_t vst[VB == 8 ? kWaves : 1][kTileT][36];     // 8-bit V code rows (32 words + pad)
     __shared__ float comb_o[kWaves][kGQ][kD];
     __shared__ float comb_ml[kWaves][kGQ][2];
+    // KIVI keys: the staged table rows r0, r1 ((scale, zero) per channel),
+    // the A operands built from one of them ([hi | lo][head][channel chunk]),
+    // and the query of all heads for tokens that take the per-lane path
+    constexpr int KW = KF == kKKivi ? kWaves : 1;
+    __shared__ __align__(16) uint32_t kst[KW][2][kD];
+    __shared__ __align__(16) u32x4 abuf[KW][2][kGQ][16];
+    __shared__ __align__(16) float qbuf[KF == kKKivi ? kGQ : 1][kD];
 
     // ---- query: lane (r, n) reads channels 32r .. 32r+31 of head n & 3
-    const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + hk * kGQ) * kD;
+    // (gq query heads per kv-head; the rows of heads gq .. 3 are zero)
+    const int gq = a.Hq / a.Hkv;
+    const uint16_t* q16 = static_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + hk * gq) * kD;
     float x[32];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-        const uint4 xx = *reinterpret_cast<const uint4*>(q16 + (n & 3) * kD + 32 * r + 8 * k);
+        uint4 xx = make_uint4(0u, 0u, 0u, 0u);
+        if ((n & 3) < gq) xx = *reinterpret_cast<const uint4*>(q16 + (n & 3) * kD + 32 * r + 8 * k);
         const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -186,6 +201,32 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     // logit (base 2) = kC sum_quarters (s C + z qsk)
     const float kC = ldexpf(a.scale_log2, qexp + 24);
     const int kg = (32 * r) / GK;   // K group of this lane's quarter
+
+    // KIVI: lane l builds the A operands of head l >> 4 over channels
+    // 8 (l & 15) .. +7 (qx8); eq: qmax < 2^eq
+    float qx8[8];
+    int eq = 0;
+    const uint32_t* ktab = nullptr;
+    int rows_t = 0;
+    if constexpr (KF == kKKivi) {
+        const int hh = lane >> 4, c8 = 8 * (lane & 15);
+        uint4 xx = make_uint4(0u, 0u, 0u, 0u);
+        if (hh < gq) xx = *reinterpret_cast<const uint4*>(q16 + hh * kD + c8);
+        const uint32_t e4[4] = {xx.x, xx.y, xx.z, xx.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            qx8[2 * i] = q_elem<QDT>(e4[i] & 0xFFFFu);
+            qx8[2 * i + 1] = q_elem<QDT>(e4[i] >> 16);
+        }
+        if (qmax > 0.0f) frexpf(qmax, &eq);
+        if (wave == 0 && n < kGQ) {
+#pragma unroll
+            for (int i = 0; i < 32; ++i) qbuf[n][32 * r + i] = x[i];
+        }
+        __syncthreads();
+        rows_t = a.cap / a.Gt + 3;
+        ktab = static_cast<const uint32_t*>(a.k_meta) + bh * rows_t * kD;
+    }
 
     const uint8_t* kcodes = static_cast<const uint8_t*>(a.k_codes) + bh * a.cap * kRowB;
     const uint8_t* vcodes = static_cast<const uint8_t*>(a.v_codes) + bh * a.cap * kVRowB;
@@ -232,12 +273,31 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                 for (int hb = 0; hb < VH; ++hb)
                     L.v[j][e][hb] = buf::stream32(rv, (4 * r + j + 16 * e) * kVRowB + 4 * (n + 16 * hb));
         }
+        if constexpr (KF == kKKivi) {
+            // each token's table row (past the tile's valid part: 0), and the
+            // rows of its first and last coded tokens, staged through registers
+            // (lane l: channels 2l, 2l + 1; the table resource covers every row)
+            const __amdgpu_buffer_rsrc_t rrow = buf::rsrc(a.k_row + tb, nv * 4);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) L.krow[p] = (int32_t)buf::load32(rrow, (n + 16 * p) * 4);
+            const int nq = max(0, min(tb + (int)nv, a.n_quant) - tb);
+            int q0 = 0, q1 = 0;
+            if (nq > 0) {
+                q0 = a.k_row[tb];
+                q1 = a.k_row[tb + nq - 1];
+            }
+            L.r0 = __builtin_amdgcn_readfirstlane(q0);
+            L.r1 = __builtin_amdgcn_readfirstlane(q1);
+            const __amdgpu_buffer_rsrc_t rtab = buf::rsrc(ktab, (uint32_t)rows_t * kD * 4);
+            L.stg[0] = buf::load64(rtab, (uint32_t)L.r0 * kD * 4 + 8 * lane);
+            L.stg[1] = buf::load64(rtab, (uint32_t)L.r1 * kD * 4 + 8 * lane);
+        }
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t tok = n + 16 * p;
             L.k[p] = buf::stream128(rk, tok * kRowB + 16 * r);
             if constexpr (KF == kKSym4) L.km[p] = buf::stream16(rkm, (tok * NKG + kg) * 2);
-            else L.km[p] = buf::stream32(rkm, (tok * NKG + kg) * 4);
+            else if constexpr (KF == kKAff4) L.km[p] = buf::stream32(rkm, (tok * NKG + kg) * 4);
             if constexpr (NVG == 1) {
                 L.vm[p][0] = buf::stream32(rvm, tok * 4);
             } else if constexpr (NVG == 2) {
@@ -250,30 +310,163 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         }
     };
 
+    // KIVI keys.  A 16-token block whose coded tokens share a table row g
+    // runs on the matrix cores: with the row's (s, z) per channel,
+    //   q . k = sum_c (q_c s_c) u_c + sum_c q_c z_c,
+    // so the A operand is q o s, held as an exact fp16 pair hi + lo (q and s
+    // carry at most 11 significant bits each, so q_c s_c has at most 22 and
+    // hi takes the top 11, lo the rest), scaled by 2^E so that the largest
+    // element stays below 2^15; odd channels carry a further 1/16 for the
+    // high-nibble operand.  The tile's first and last coded tokens name the
+    // two staged rows; tokens of another row or of the open group (the
+    // full-precision residual) take a per-lane path.
+    auto kivi_scores = [&](const MTile<NVG, VH>& L, int tb, float (&y)[2][kGQ]) __attribute__((always_inline)) {
+        *reinterpret_cast<buf::u32x2*>(&kst[wave][0][2 * lane]) = L.stg[0];
+        *reinterpret_cast<buf::u32x2*>(&kst[wave][1][2 * lane]) = L.stg[1];
+        wave_lds_sync();
+        // 0: coded with row r0; 1: coded with row r1 (!= r0); 2: the per-lane
+        // path; 3: past the split (codes read as zero, logit masked)
+        int cls[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const int t = tb + n + 16 * p;
+            cls[p] = t >= t_hi ? 3 : t >= a.n_quant ? 2 : L.krow[p] == L.r0 ? 0 : L.krow[p] == L.r1 ? 1 : 2;
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h) y[p][h] = 0.0f;
+        }
+        const uint32_t kw[2][4] = {{L.k[0].x, L.k[0].y, L.k[0].z, L.k[0].w},
+                                   {L.k[1].x, L.k[1].y, L.k[1].z, L.k[1].w}};
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            if (__builtin_amdgcn_ballot_w64(cls[0] == g || cls[1] == g) == 0) continue;
+            // A operands of row g: lane l takes head l >> 4, channels 8 ci .. 8 ci + 7
+            const int hh = lane >> 4, ci = lane & 15;
+            const uint4 m0 = *reinterpret_cast<const uint4*>(&kst[wave][g][8 * ci]);
+            const uint4 m1 = *reinterpret_cast<const uint4*>(&kst[wave][g][8 * ci + 4]);
+            const uint32_t mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+            float smax = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) smax = fmaxf(smax, f16lo(mm[i]));
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) smax = fmaxf(smax, __shfl_xor(smax, off));
+            int es = 0;
+            frexpf(smax, &es);                    // |q s| < 2^(eq + es)
+            const int E = 15 - eq - es;
+            const float se = ldexpf(1.0f, E), so = ldexpf(1.0f, E - 4);
+            float hv[8], lv[8];
+            float qzp = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = qx8[i] * f16lo(mm[i]) * ((i & 1) ? so : se);   // exact
+                hv[i] = (float)(_Float16)v;
+                lv[i] = v - hv[i];                                            // exact
+                qzp = fmaf(qx8[i], f16hi(mm[i]), qzp);
+            }
+            // fp16 slot order of nibble_operand: channels (0, 4, 1, 5, 2, 6, 3, 7)
+            abuf[wave][0][hh][ci] = u32x4{pack_f16(hv[0], hv[4]), pack_f16(hv[1], hv[5]), pack_f16(hv[2], hv[6]),
+                                          pack_f16(hv[3], hv[7])};
+            abuf[wave][1][hh][ci] = u32x4{pack_f16(lv[0], lv[4]), pack_f16(lv[1], lv[5]), pack_f16(lv[2], lv[6]),
+                                          pack_f16(lv[3], lv[7])};
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) qzp += __shfl_xor(qzp, off);   // q . z of head hh
+            float qz[kGQ];
+#pragma unroll
+            for (int h = 0; h < kGQ; ++h)
+                qz[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qzp), 16 * h));
+            wave_lds_sync();
+            u32x4 ah[4], al[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                ah[c] = own ? abuf[wave][0][n & 3][4 * r + c] : u32x4{0u, 0u, 0u, 0u};
+                al[c] = own ? abuf[wave][1][n & 3][4 * r + c] : u32x4{0u, 0u, 0u, 0u};
+            }
+            wave_lds_sync();                      // abuf is rebuilt for the next row
+            const float fu = ldexpf(1.0f, 24 - E);
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                const bool mem = cls[p] == g;
+                f4 cq = f4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const u32x4 bw = mem ? nibble_operand(kw[p][c]) : u32x4{0u, 0u, 0u, 0u};
+                    cq = mfma16(ah[c], bw, cq);
+                    cq = mfma16(al[c], bw, cq);
+                }
+                if (mem) {
+#pragma unroll
+                    for (int h = 0; h < kGQ; ++h) y[p][h] = fmaf(cq[h], fu, r == 0 ? qz[h] : 0.0f);
+                }
+            }
+        }
+        if (__builtin_amdgcn_ballot_w64(cls[0] == 2 || cls[1] == 2) != 0) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                if (cls[p] != 2) continue;
+                // keys of channels 32r .. 32r+31: the residual row, or u s + z from the token's row
+                const int t = tb + n + 16 * p;
+                float kv[32];
+                if (t >= a.n_quant) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k)
+                        dq::load8(a.k_resid, (bh * a.Gt + (t - a.n_quant)) * kD + 32 * r + 8 * k, a.in_dtype,
+                                  kv + 8 * k);
+                } else {
+                    const uint32_t* row = ktab + (int64_t)L.krow[p] * kD + 32 * r;
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const uint4 m0 = *reinterpret_cast<const uint4*>(row + 8 * k);
+                        const uint4 m1 = *reinterpret_cast<const uint4*>(row + 8 * k + 4);
+                        const uint32_t mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            kv[8 * k + i] = fmaf((float)((kw[p][k] >> (4 * i)) & 0xFu), f16lo(mm[i]), f16hi(mm[i]));
+                    }
+                }
+#pragma unroll
+                for (int h = 0; h < kGQ; ++h) {
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) acc = fmaf(qbuf[h][32 * r + i], kv[i], acc);
+                    y[p][h] = acc;
+                }
+            }
+        }
+    };
+
     auto process = [&](const MTile<NVG, VH>& L, int tile, auto tail) {
         constexpr bool kTail = decltype(tail)::value;     // the tile may hold invalid tokens
         const int tb = t_lo + tile * kTileT;
         // -------------------------------------------- scores of tokens n and n + 16
+        // y[p][h]: quarter r of head h's dot product for token n + 16 p
+        float y[2][kGQ];
+        if constexpr (KF == kKKivi) {
+            kivi_scores(L, tb, y);
+        } else {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) {
+                f4 cq = f4{0.0f, 0.0f, 0.0f, 0.0f};
+                const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) cq = mfma16(qa[c], nibble_operand(kw[c]), cq);
+                // quarter r of the four heads: s C + z qsk
+                const float sk = f16lo(L.km[p]);
+                const float zk = KF == kKSym4 ? -8.0f * sk : f16hi(L.km[p]);
+#pragma unroll
+                for (int h = 0; h < kGQ; ++h) y[p][h] = fmaf(sk, cq[h], zk * qsk[h]);
+            }
+        }
+        // scaled units (per-token formats) or plain q . k (KIVI) to base-2 logits
+        const float kCx = KF == kKKivi ? a.scale_log2 : kC;
         float xs[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            f4 cq = f4{0.0f, 0.0f, 0.0f, 0.0f};
-            const uint32_t kw[4] = {L.k[p].x, L.k[p].y, L.k[p].z, L.k[p].w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) cq = mfma16(qa[c], nibble_operand(kw[c]), cq);
-            // quarter r of the four heads: s C + z qsk
-            const float sk = f16lo(L.km[p]);
-            const float zk = KF == kKSym4 ? -8.0f * sk : f16hi(L.km[p]);
-            float y[kGQ];
-#pragma unroll
-            for (int h = 0; h < kGQ; ++h) y[h] = fmaf(sk, cq[h], zk * qsk[h]);
             // sum the quarters: rows r and r ^ 2 first (keeping the heads of
             // this row pair), then r and r ^ 1 (keeping head r)
             const bool hi = (r >> 1) != 0, odd = (r & 1) != 0;
-            const float z0 = (hi ? y[2] : y[0]) + __shfl_xor(hi ? y[0] : y[2], 32);
-            const float z1 = (hi ? y[3] : y[1]) + __shfl_xor(hi ? y[1] : y[3], 32);
+            const float z0 = (hi ? y[p][2] : y[p][0]) + __shfl_xor(hi ? y[p][0] : y[p][2], 32);
+            const float z1 = (hi ? y[p][3] : y[p][1]) + __shfl_xor(hi ? y[p][1] : y[p][3], 32);
             const float xh = (odd ? z1 : z0) + __shfl_xor(odd ? z0 : z1, 16);
-            const float xl = xh * kC;
+            const float xl = xh * kCx;
             if constexpr (kTail) xs[p] = (tb + n + 16 * p < t_hi) ? xl : -INFINITY;
             else xs[p] = xl;
         }
@@ -459,6 +652,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int ns = a.n_splits;
     for (int idx = threadIdx.x; idx < kGQ * kD; idx += 256) {
         const int h = idx / kD, d = idx % kD;
+        if (h >= gq) continue;
         float M = -INFINITY;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb_ml[w][h][0]);
@@ -470,7 +664,7 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
             num = fmaf(f, comb_o[w][h][d], num);
             den = fmaf(f, comb_ml[w][h][1], den);
         }
-        const int64_t row = (int64_t)b * a.Hq + hk * kGQ + h;
+        const int64_t row = (int64_t)b * a.Hq + hk * gq + h;
         if (ns == 1) {
             a.out[row * kD + d] = num / den;
         } else {
@@ -503,6 +697,7 @@ hipError_t launch_mfma_k(const DecodeArgs& a, hipStream_t s) {
 template <int QDT>
 hipError_t launch_mfma_q(const DecodeArgs& a, hipStream_t s) {
     if (a.k_kind == KVQ_TOK_SYM4) return launch_mfma_k<QDT, kKSym4, 32>(a, s);
+    if (a.k_kind == KVQ_KIVI_CH) return launch_mfma_k<QDT, kKKivi, 32>(a, s);
     switch (a.k_group) {
         case 32: return launch_mfma_k<QDT, kKAff4, 32>(a, s);
         case 64: return launch_mfma_k<QDT, kKAff4, 64>(a, s);
@@ -513,20 +708,43 @@ hipError_t launch_mfma_q(const DecodeArgs& a, hipStream_t s) {
 
 }  // namespace
 
-// Applies to per-token 4-bit K (affine groups or symmetric blocks) and
-// affine 4- or 8-bit V at head_dim 128, 4 query heads per kv-head, bf16 or
-// fp16 queries, no RoPE on read (a per-key rotation would undo the factored
-// scale).  It shares the split plan of the VALU decode (decode_fast_plan).
+// Applies to 4-bit K -- per-token affine groups, symmetric blocks, or KIVI
+// per-channel groups -- with affine 4- or 8-bit V at head_dim 128, 1 to 4
+// query heads per kv-head, bf16 or fp16 queries and no RoPE on read (a
+// per-key rotation would undo the factored scales).
 bool decode_mfma_applies(const DecodeArgs& a) {
-    const bool k_ok = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4;
+    const bool k_ok = (a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4) || a.k_kind == KVQ_TOK_SYM4 ||
+                      (a.k_kind == KVQ_KIVI_CH && a.k_bits == 4);
     const bool v_ok = a.v_kind == KVQ_TOK_AFFINE && (a.v_bits == 4 || a.v_bits == 8);
-    return k_ok && v_ok && a.D == kD && a.Hq == kGQ * a.Hkv && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) &&
-           !a.rope;
+    const bool heads_ok = a.Hq % a.Hkv == 0 && a.Hq >= a.Hkv && a.Hq <= kGQ * a.Hkv;
+    return k_ok && v_ok && heads_ok && a.D == kD && (a.q_dtype == KVQ_BF16 || a.q_dtype == KVQ_F16) && !a.rope;
 }
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
     if (a.q_dtype == KVQ_BF16) return launch_mfma_q<KVQ_BF16>(a, s);
     return launch_mfma_q<KVQ_F16>(a, s);
+}
+
+// The fast path is the matrix-core decode.
+bool decode_fast_applies(const DecodeArgs& a) { return decode_mfma_applies(a); }
+
+hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s) { return launch_decode_mfma(a, s); }
+
+// Split plan: one workgroup per (batch, kv-head) when that fills the chip
+// twice over, otherwise split the tokens so that about 512 workgroups run,
+// with at least 2 tiles per wave, so that each wave's second tile loads
+// while its first is computed (the best latency for small batches).
+void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len) {
+    const int units = B * Hkv;
+    int ns = (512 + units - 1) / units;
+    const int min_len = kWaves * kTileT * 2;
+    const int max_ns = (T + min_len - 1) / min_len;
+    if (ns > max_ns) ns = max_ns;
+    if (ns < 1) ns = 1;
+    int len = (T + ns - 1) / ns;
+    len = ((len + kTileT - 1) / kTileT) * kTileT;
+    *split_len = len;
+    *n_splits = (T + len - 1) / len;
 }
 
 }  // namespace kvq

@@ -140,11 +140,12 @@ hipError_t launch_decode_combine(const float* ws_o, const float* ws_ml, float* o
 void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, int* n_rb, int* n_splits, int* split_len);
 int prefill_max_splits(int B, int Hkv, int Hq, int n_q, int T);
 hipError_t launch_prefill_attention(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s);
+// The fast decode: matrix-core kernels for 4-bit K (per-token affine,
+// symmetric blocks or KIVI per-channel) and affine 4/8-bit V at head_dim
+// 128 with 1-4 query heads per kv-head (decode_mfma.hip).
 bool decode_fast_applies(const DecodeArgs& a);
 void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
-// Matrix-core decode for per-token affine 4-bit K and V (a case of the fast
-// path: same plan, launched by launch_decode_fast).
 bool decode_mfma_applies(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 size_t decode_workspace_bytes(int B, int Hq, int D, int cap);

@@ -534,3 +534,54 @@ def test_streaming_rope_repositioning_kivi_int8_tiny():
     c, o = stream_pair(pl, ol, k, v, "f32", 4, 256)
     table = K.kvq_rope_table(261, 32)
     check_decode_rope(pl, c, o, q, "f32", table, c.n_stored - 1)
+
+
+@pytest.mark.parametrize("gt,G,dt,qdt,vb,vg", [(16, 4, "f16", "f16", 4, 32), (64, 2, "bf16", "bf16", 8, 128),
+                                              (8, 3, "f32", "f16", 4, 64), (128, 1, "f16", "bf16", 8, 32),
+                                              (32, 4, "f32", "bf16", 4, 32)])
+def test_kivi_matrix_core_group_sizes(gt, G, dt, qdt, vb, vg):
+    """KIVI 4-bit keys on the matrix-core decode with token groups of 8 to
+    128: a 32-token tile then holds one group, two (the second staged row)
+    or four (rows beyond the two staged ones take the per-lane path); the
+    open group is read from an fp16, bf16 or fp32 residual.  Then the same
+    cache after StreamingLLM compaction (sink 5, window 700), whose tiles
+    mix table rows of the sink and window runs."""
+    rng = np.random.default_rng(gt * 10 + G)
+    B, H, T, D = 1, 2, 1333, 128
+    k = (rng.standard_normal((B, H, T, D)) * np.where(rng.random(D) < 0.05, 10.0, 1.0)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, D)).astype(np.float32)
+    q = rng.standard_normal((B, H * G, D)).astype(np.float32)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=D, capacity=T, k_kind="kivi_ch", k_bits=4, k_group=gt,
+                     v_kind="tok_affine", v_bits=vb, v_group=vg, in_dtype=dt)
+    say("kivi matrix-core groups", gt, G, dt, qdt, vb, vg)
+    c, o = build_pair(pl, ol, synth.cast(k, dt), synth.cast(v, dt), dt, chunks=[(0, 1), (1, 600), (600, T)])
+    assert_same_state(c, o)
+    qq = synth.cast(q, qdt)
+    check_decode(pl, c, o, qq, qdt)
+    dst = K.Cache(pl)
+    assert K.kvq_evict_streaming(pl, c, dst, 5, 700) == K.KVQ_OK
+    torch.cuda.synchronize()
+    check_decode(pl, dst, o.evict(5, 700), qq, qdt)
+
+
+@pytest.mark.parametrize("k_kind,kg,G,vb,vg", [("tok_affine", 64, 1, 4, 64), ("tok_sym4", 32, 2, 8, 128),
+                                               ("tok_affine", 32, 3, 4, 32)])
+def test_matrix_core_decode_fewer_query_heads(k_kind, kg, G, vb, vg):
+    """Per-token 4-bit keys with 1-3 query heads per kv-head on the
+    matrix-core decode (the rows of the missing heads are zero and never
+    written): ragged length, split over T."""
+    w = synth.workload("q4_0_centered")
+    B, H, T = 2, 2, 1555
+    k, v, q = gen(w, B, H, T, Hq=H * G)
+    bias = np.stack([synth.head_params(w, h)[0] for h in range(H)]).astype(np.float32)
+    flags = K.KVQ_CENTER_K if k_kind == "tok_sym4" else 0
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind=k_kind, k_bits=4, k_group=kg,
+                     v_kind="tok_affine", v_bits=vb, v_group=vg, in_dtype="f16", flags=flags)
+    say("matrix-core fewer heads", k_kind, kg, G, vb, vg)
+    c, o = build_pair(pl, ol, k, v, "f16", chunks=[(0, 700), (700, T)], k_bias=bias if flags else None)
+    out = torch.full((B, H * G, 128), 9.0, device=DEV)
+    K.kvq_decode_attention(pl, c, to_dev(q, "f16"), out=out)
+    torch.cuda.synchronize()
+    err = attn_err(out.cpu().numpy(), o.decode(q, "f16"))
+    say(f"  attention error {err:.3e}")
+    assert err <= TOL
