@@ -585,3 +585,27 @@ def test_matrix_core_decode_fewer_query_heads(k_kind, kg, G, vb, vg):
     err = attn_err(out.cpu().numpy(), o.decode(q, "f16"))
     say(f"  attention error {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("k_kind,G", [("kivi_ch", 3), ("tok_affine", 4)])
+def test_split_decode_repeats_bit_identically(k_kind, G):
+    """A decode split over T (partials merged by log-sum-exp): thirty
+    back-to-back calls, queued without synchronization, give bit-identical
+    outputs that match the oracle."""
+    w = synth.workload("llama3b_kivi_int4")
+    B, H, T = 1, 8, 3001
+    k, v, q = gen(w, B, H, T, Hq=H * G)
+    kg = 32 if k_kind == "kivi_ch" else 64
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind=k_kind, k_bits=4, k_group=kg,
+                     v_kind="tok_affine", v_bits=4, v_group=32, in_dtype="f16")
+    say("split merge repeats", k_kind, G)
+    c, o = build_pair(pl, ol, k, v, "f16")
+    qd = to_dev(q, "f16")
+    outs = [K.kvq_decode_attention(pl, c, qd) for _ in range(30)]
+    torch.cuda.synchronize()
+    first = outs[0].cpu().numpy()
+    for x in outs[1:]:
+        assert np.array_equal(x.cpu().numpy().view(np.uint32), first.view(np.uint32))
+    err = attn_err(first, o.decode(q, "f16"))
+    say(f"  attention error {err:.3e}")
+    assert err <= TOL
