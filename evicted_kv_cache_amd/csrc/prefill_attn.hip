@@ -205,7 +205,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     const int v_row_b = D * a.v_bits / 8;
     const int v_meta_b = kTokV ? (D / a.v_group) * 4 : 0;
     auto fetch = [&](int tb) {
-        const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(min(kPT, t_hi - tb));
+        // rows of the tile inside the split (0 past its end: every load then reads zero)
+        const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kPT, t_hi - tb)));
         const int64_t slot0 = bh * a.cap + tb;
         if constexpr (kTokK) {
             const __amdgpu_buffer_rsrc_t rk = rsrc(static_cast<const uint8_t*>(a.k_codes) + slot0 * k_row_b, nt * k_row_b);
@@ -253,7 +254,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             if (it >= kPT * C8) break;
             const int t = it / C8, c = it - t * C8;
             float xk[8] = {}, xv[8] = {};
-            if (t < nt) {
+            if (kTokK && kTokV) {
+                // rows past the split were fetched as zero codes and zero
+                // metadata, which dequantize to zero: no branch
+                dq::k_finish8<KK>(a, bh, tb + t, c, pk[j], xk);
+                dq::v_finish8<VK>(a, bh, tb + t, c, pv[j], xv);
+            } else if (t < nt) {
                 dq::k_finish8<KK>(a, bh, tb + t, c, pk[j], xk);
                 dq::v_finish8<VK>(a, bh, tb + t, c, pv[j], xv);
             }
@@ -294,7 +300,13 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             }
         }
         // the next tile goes into the other buffer while the products run
-        if (t0 + kPT < t_hi) {
+        // (without a branch, so that the score products and the unpacking
+        // are one block the scheduler can interleave; past the split's end
+        // the unpack writes zero rows and the fetch reads zeros)
+        if constexpr (kTokK && kTokV) {
+            unpack(t0 + kPT, buf ^ 1);
+            fetch(t0 + 2 * kPT);
+        } else if (t0 + kPT < t_hi) {
             unpack(t0 + kPT, buf ^ 1);
             if (t0 + 2 * kPT < t_hi) fetch(t0 + 2 * kPT);
         }
