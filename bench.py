@@ -116,17 +116,18 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def load_traffic():
+def load_traffic(path=TRAFFIC_FILE, src=DECODE_SRC):
     """HBM traffic per launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source."""
+    were taken on the current kernel source. The sum over the file's kernels
+    when it holds several (one launch of each per call)."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except OSError:
         return None
-    if t.get("source_sha256_16") != source_hash(DECODE_SRC):
+    if t.get("source_sha256_16") != source_hash(src):
         return None
-    return t.get("bytes_per_launch")
+    return t.get("bytes_per_launch") or sum(k["bytes_per_launch"] for k in t["kernels"].values())
 
 
 def cpu_baseline(w, target_s=12.0):
@@ -297,7 +298,11 @@ def main():
         cbytes = 2 * B * Hkv * (sink + window) * row_bytes + 2 * (sink + window) * 4
         rows["C_evict"] = {"workload": f"{w.name} T={T} -> sink {sink} + window {window}",
                            "ms": round(msc, 4), "GB/s": round(cbytes / msc / 1e6, 1),
-                           "frac_hbm": round(cbytes / msc / 1e6 / PEAK_HBM_GBS, 4)}
+                           "frac_hbm": round(cbytes / msc / 1e6 / PEAK_HBM_GBS, 4),
+                           "algorithmic_bytes": cbytes,
+                           "traffic": load_traffic(
+                               os.path.join(ROOT, "profiles", "evict_gather_affine4_g64_traffic.json"),
+                               os.path.join(ROOT, "evicted_kv_cache_amd", "csrc", "evict.hip"))}
         del dst
 
     # ---- row D: SnapKV prefill selection
@@ -328,6 +333,9 @@ def main():
                                         f"budget={ex['budget']} Hkv={Hs} D={Ds}",
                             "us": round(msd * 1e3, 2), "scores/s": round(Hs * Ss / (msd * 1e-3), 1),
                             "algorithmic_bytes": sbytes,
+                            "traffic": load_traffic(
+                                os.path.join(ROOT, "profiles", "snapkv_s8192_traffic.json"),
+                                os.path.join(ROOT, "evicted_kv_cache_amd", "csrc", "snapkv.hip")),
                             "GB/s": round(sbytes / msd / 1e6, 1),
                             "frac_hbm": round(sbytes / msd / 1e6 / PEAK_HBM_GBS, 4),
                             "timing": f"cold: graph replay over {ncp} copies of K and V "
