@@ -54,6 +54,13 @@ def decode_algorithmic_bytes(B, Hkv, Hq, D, T, bits, group, q_bytes=2):
 
 MALL_BYTES = 256 << 20
 ROTATE_BYTES = 512 << 20           # input copies cycled by the cold timings: twice the MALL
+# Sustained load: for the first tens of ms of heavy work after an idle spell
+# the power manager pulls the shader clock down (on an MI355X under the decode:
+# 2.4 GHz to about 1.1 GHz within 5 ms, back to about 2.2 GHz after some 40 ms,
+# flat from then on), so every row first runs its own work untimed for
+# SUSTAIN_MS of device time and is then timed over at least MIN_TIMED_MS.
+SUSTAIN_MS = 80.0
+MIN_TIMED_MS = 30.0
 
 
 def time_rotating(fns, reps, torch):
@@ -95,11 +102,36 @@ def host_cpu():
     return os.cpu_count() or 1, avail, model
 
 
-def time_stream(fn, steps, warmup, torch):
-    """Average ms per call of fn over `steps` calls, with HIP events on the current stream."""
+def sustain(fn, torch, ms_min=SUSTAIN_MS):
+    """Run fn untimed until at least ms_min of device time has passed; return
+    the last batch's ms per call."""
+    s = torch.cuda.current_stream()
+    done, n, per = 0.0, 1, 0.0
+    while done < ms_min:
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(n):
+            fn()
+        b.record(s)
+        torch.cuda.synchronize()
+        t = a.elapsed_time(b)
+        done += t
+        per = t / n
+        n = min(2 * n, 4096)
+    return per
+
+
+def time_stream(fn, steps, warmup, torch, sustain_ms=SUSTAIN_MS, min_timed_ms=MIN_TIMED_MS):
+    """Average ms per call of fn, with HIP events on the current stream: `warmup`
+    calls, then sustain_ms of device time untimed, then max(steps, as many as
+    fill min_timed_ms) timed calls."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    per = sustain(fn, torch, sustain_ms) if sustain_ms > 0 else 0.0
+    if per > 0:
+        steps = max(steps, math.ceil(min_timed_ms / per))
     s = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
@@ -109,6 +141,28 @@ def time_stream(fn, steps, warmup, torch):
     end.record(s)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
+
+
+def time_steps(fn, steps, warmup, torch):
+    """The timed step: exactly `warmup` untimed calls (each bracketed by events,
+    so the clock's settling shows), then exactly `steps` timed calls. Returns
+    (ms per timed call, ms of each warm-up call)."""
+    s = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(warmup + 1)]
+    evs[0].record(s)
+    for i in range(warmup):
+        fn()
+        evs[i + 1].record(s)
+    torch.cuda.synchronize()
+    warm = [evs[i].elapsed_time(evs[i + 1]) for i in range(warmup)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(s)
+    for _ in range(steps):
+        fn()
+    end.record(s)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps, warm
 
 
 def source_hash(path):
@@ -178,8 +232,9 @@ def cpu_baseline(w, target_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first (about 75 ms of decode: the clock has settled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", default="ACDBE", help="extra rows to time (subset of ACDBE)")
     ap.add_argument("--mode", default="full", choices=["full", "decode", "copy"],
@@ -229,19 +284,12 @@ def main():
     del Kh, Vh
     rows = {}
 
-    # ---- row A: prefill quantize-on-write (n_new = T), timed once after a warm-up cache
+    # ---- row A: prefill quantize-on-write (n_new = T) into an emptied cache
     if "A" in args.rows:
-        scratch = K.Cache(L)
-        K.kvq_quantize_append(L, scratch, kd, vd)
-        torch.cuda.synchronize()
-        del scratch
-        s = torch.cuda.current_stream()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(s)
-        K.kvq_quantize_append(L, cache, kd, vd)
-        ev1.record(s)
-        torch.cuda.synchronize()
-        ms = ev0.elapsed_time(ev1)
+        def prefill():
+            K.kvq_cache_reset(cache)               # host counters only: an empty cache
+            K.kvq_quantize_append(L, cache, kd, vd)
+        ms = time_stream(prefill, 1, 1, torch)
         nbytes = 2 * kd.numel() * 2 + 2 * (cache.sizes.k_codes + cache.sizes.k_meta) + T * 4
         rows["A_quantize_prefill"] = {"workload": f"{w.name} prefill n_new={T}", "ms": round(ms, 4),
                                       "GB/s": round(nbytes / ms / 1e6, 1),
@@ -259,7 +307,7 @@ def main():
         K.kvq_decode_attention(L, cache, q, out=out, ws=ws)
 
     log("timing decode")
-    ms = time_stream(step, args.steps, args.warmup, torch)
+    ms, warm = time_steps(step, args.steps, args.warmup, torch)
     nbytes = decode_algorithmic_bytes(B, Hkv, Hq, D, T, e["k_bits"], e["k_group"])
     gbs = nbytes / ms / 1e6
     log(f"decode {ms * 1e3:.1f} us/step  {gbs:.1f} GB/s  {gbs / PEAK_HBM_GBS:.3f} of HBM peak")
@@ -452,6 +500,13 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 5),
+        "warmup_settling": {
+            "what": "us per step over the untimed warm-up steps (run right after the prefill append), "
+                    "by blocks of 50: the shader clock dips under the first tens of ms of sustained "
+                    "decode and settles after about 100 steps",
+            "us_first_20": round(1e3 * sum(warm[:20]) / max(1, len(warm[:20])), 1) if warm else None,
+            "us_per_50": [round(1e3 * sum(warm[i:i + 50]) / len(warm[i:i + 50]), 1)
+                          for i in range(0, len(warm), 50)]},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
