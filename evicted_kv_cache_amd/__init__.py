@@ -43,7 +43,8 @@ EXPORTS = ("kvq_cache_sizes", "kvq_cache_reset", "kvq_quantize_append",
            "kvq_snapkv_select_ex", "kvq_snapkv_pool_scores", "kvq_quantize_append_at",
            "kvq_snapkv_chunk_workspace_bytes", "kvq_snapkv_prefill_chunk", "kvq_rope_table",
            "kvq_decode_attention_rope", "kvq_prefill_workspace_bytes", "kvq_prefill_attention",
-           "kvq_decode_attention_noalloc", "kvq_status_string", "kvq_version")
+           "kvq_decode_attention_noalloc", "kvq_snapkv_set_wait_us", "kvq_status_string",
+           "kvq_version")
 
 
 class KvqError(RuntimeError):
@@ -111,6 +112,8 @@ def lib():
         L.kvq_snapkv_workspace_bytes_ex.argtypes = [P, i32, i32, i32, i32, i32]
         L.kvq_snapkv_select_ex.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, i32, P, P, P, P, P, sz, P]
         L.kvq_snapkv_pool_scores.argtypes = [P, P, i32, i32, i32, i32, P]
+        L.kvq_snapkv_set_wait_us.argtypes = [i32]
+        L.kvq_snapkv_set_wait_us.restype = i32
         L.kvq_quantize_append_at.argtypes = [P, P, P, P, i32, i32, P, i32, i32, P]
         L.kvq_rope_table.argtypes = [P, i32, i32, f32, P]
         L.kvq_prefill_workspace_bytes.restype = sz
@@ -437,6 +440,12 @@ def kvq_snapkv_select_ex(k, v, obs_window: int, n_sink: int, budget: int, q_wind
                                       ws.data_ptr(), ws.numel(), _stream(stream)),
            "kvq_snapkv_select_ex")
     return scores, kept, k_out, v_out
+
+
+def kvq_snapkv_set_wait_us(microseconds: int) -> int:
+    """Bound (us) on the one-read SnapKV scores' wait for the rest of a head;
+    returns the previous bound."""
+    return int(lib().kvq_snapkv_set_wait_us(int(microseconds)))
 
 
 def kvq_snapkv_pool_scores(scores, pool_kernel: int, pooled=None, stream=None):

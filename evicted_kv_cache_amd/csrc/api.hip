@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+#include <chrono>
 #include <mutex>
 
 #include "kvq_internal.h"
@@ -527,6 +529,36 @@ size_t kvq_snapkv_workspace_bytes(int32_t B, int32_t H, int32_t S, int32_t D, in
     return kvq_snapkv_workspace_bytes_ex(nullptr, B, H, S, D, w);
 }
 
+int32_t kvq_snapkv_set_wait_us(int32_t microseconds) {
+    const int32_t prev = g_snap_wait_us;
+    if (microseconds >= 0) g_snap_wait_us = microseconds;
+    return prev;
+}
+
+// Tags of the one-read scores' ready flags: distinct for every call of the
+// process (a flag left by an earlier call, or stale workspace contents, never
+// reads as this call's), never 0 (the cleared value).
+static uint64_t snap_next_tag() {
+    static std::atomic<uint64_t> next{0x9E3779B97F4A7C15ull ^
+                                      (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count()};
+    uint64_t t = next.fetch_add(0x9E3779B97F4A7C15ull) * 0xBF58476D1CE4E5B9ull;
+    return t ? t : 1u;
+}
+
+// The device wall clock's rate (kHz), per device.
+static int64_t wall_clock_khz() {
+    static int64_t cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 100000;
+    if (cached[dev] == 0) {
+        int khz = 0;
+        if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+            khz = 100000;
+        cached[dev] = khz;
+    }
+    return cached[dev];
+}
+
 // One SnapKV pass over S candidate rows per (b, h) (slices kv_stride elements
 // apart): scores, optional pooling, selection into kept, gather into
 // k_out / v_out (slices out_stride apart) with optional positions.  The
@@ -563,7 +595,15 @@ static kvq_status snap_run(const SnapRun& r, hipStream_t s) {
     const size_t sc = ((size_t)r.B * r.H * r.S * sizeof(float) + 255) & ~(size_t)255;
     a.stats = reinterpret_cast<float*>(r.ws);
     a.scores = r.scores ? r.scores : reinterpret_cast<float*>(r.ws + stats);
-    if (launch_snapkv_scores(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    a.flags = reinterpret_cast<uint64_t*>(r.ws + stats + sc + (r.pool > 1 ? sc : 0));
+    if (snapkv_one_read_applies(a)) {
+        a.tag = snap_next_tag();
+        a.wait_ticks = (int64_t)g_snap_wait_us * wall_clock_khz() / 1000;
+        if (launch_snapkv_scores_one_read(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    } else {
+        a.flags = nullptr;
+        if (launch_snapkv_scores(a, s) != hipSuccess) return KVQ_ERR_HIP;
+    }
     const float* rank = a.scores;
     if (r.pool > 1) {
         float* pooled = reinterpret_cast<float*>(r.ws + stats + sc);

@@ -178,10 +178,24 @@ struct SnapArgs {
     int64_t out_stride;    // elements between (b, h) slices of k_out and v_out
     // optional: positions gathered with the rows (pos_in null: the row index)
     const int32_t* pos_in; int32_t* pos_out; int pos_in_rows, pos_out_rows;
+    // one-read scores: per-(b, h, chunk) ready flags (null: the two-pass
+    // scores), the call's tag, keys per chunk and the bounded wait
+    uint64_t* flags; uint64_t tag; int one_chunk, n_one; int64_t wait_ticks;
 };
 size_t snapkv_ws_bytes(int B, int H, int S, int D, int n_rows, bool pooled);
 hipError_t launch_snapkv_pool(const float* in, float* out, int64_t rows, int S, int kernel, hipStream_t s);
 hipError_t launch_snapkv_scores(const SnapArgs& a, hipStream_t s);
+// One-read scores (logits kept in registers across a per-head exchange of the
+// row statistics): true and the launch made when the shape allows it (a.flags
+// set), false to use launch_snapkv_scores.
+bool snapkv_one_read_applies(const SnapArgs& a);
+hipError_t launch_snapkv_scores_one_read(SnapArgs& a, hipStream_t s);
+// Bytes of ready flags the one-read scores need in the workspace (0 when the
+// shape does not allow it).
+size_t snapkv_flag_bytes(int B, int H, int S, int n_rows);
+// Process-wide bound on the one-read wait, in microseconds (tests set 0 to
+// force the recomputing path).
+extern int g_snap_wait_us;
 // Copy chunk rows [B][H][n][D] fp16 into rows [row0, row0 + n) of a state
 // [B][H][cap][D] and set their positions first_pos + i ([B][H][cap] int32).
 hipError_t launch_snapkv_chunk_copy(const void* k_chunk, const void* v_chunk, void* k_state, void* v_state,

@@ -234,6 +234,230 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
         a.scores[((int64_t)b * a.H + h) * S + key] = score / (float)wc;
 }
 
+// ---------------------------------------------------------------- one-read scores
+//
+// The keys are read once.  Workgroup (chunk, h, b) computes the logits of its
+// one_chunk keys against every observation row (keys as MFMA rows, as in
+// pass 1) and keeps them in registers, publishes its per-row (max, exp-sum),
+// waits until every chunk of its head has published, merges the head's
+// statistics and turns its own logits into scores.  The exchange uses
+// agent-coherent stores and loads: a workgroup's partials are stored and
+// complete before its ready flag takes the call's tag.  The wait is bounded:
+// a workgroup that gives up (when not every chunk of the head could be
+// resident at once, for instance) recomputes every chunk's partials itself
+// with the same code, so the statistics, and the scores, are the same bits
+// either way.  The select-gather launch that follows clears the flags.
+
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): this lane's stores have completed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+template <int D, int F, int NT>
+__global__ __launch_bounds__(256) void snap_one_read_kernel(SnapArgs a) {
+    const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int kh = lane >> 5, l32 = lane & 31;
+    const int S = a.S, wc = a.n_rows, n_c = a.n_one, ck = a.one_chunk;
+    const int64_t bh = (int64_t)b * a.H + h;
+    const uint16_t* K = a.k + bh * a.kv_stride;
+    const uint16_t* O = a.obs + bh * a.obs_stride;   // observation rows
+    float* part = a.stats + bh * (int64_t)n_c * wc * 2;   // [n_c][wc] (max, sum)
+    uint64_t* flag = a.flags + bh * n_c;
+    const float c = 1.4426950408889634f / sqrtf((float)D);
+    constexpr int NK = D / 16;
+    __shared__ float sm[4][kMaxWindow], sl[4][kMaxWindow];
+    __shared__ float Mrow[kMaxWindow], invL[kMaxWindow];
+
+    // acc[f][nt][v] = logit(key kb(f) + acc_row(v, kh), observation row nt * 32 + l32)
+    auto key_base = [&](int ch, int f) { return ch * ck + (f * 4 + wave) * 32; };
+    auto logits = [&](int ch, floatx16 (&acc)[F][NT]) {
+        half8 A[F][NK];
+#pragma unroll
+        for (int f = 0; f < F; ++f) {
+            const int key = key_base(ch, f) + l32;
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                A[f][q] = half8{};
+                if (key < S) A[f][q] = load_half8(K + (int64_t)key * D + q * 16 + kh * 8);
+            }
+        }
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int wr = nt * 32 + l32;
+            half8 Bv[NK];
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                Bv[q] = half8{};
+                if (wr < wc) Bv[q] = load_half8(O + (int64_t)wr * D + q * 16 + kh * 8);
+            }
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                floatx16 x = {};
+#pragma unroll
+                for (int q = 0; q < NK; ++q) x = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[f][q], Bv[q], x, 0, 0, 0);
+                acc[f][nt] = x;
+            }
+        }
+    };
+    // (max, exp-sum) of every observation row over chunk ch's keys, stored
+    // agent-coherent into the chunk's partials
+    auto publish = [&](int ch, const floatx16 (&acc)[F][NT]) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            float M = -INFINITY, L = 0.0f;
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                const int kb = key_base(ch, f);
+                if (kb >= S) break;                        // uniform: the rest is past the end
+                float mx = -INFINITY;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (kb + acc_row(v, kh) < S) mx = fmaxf(mx, acc[f][nt][v] * c);
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float Mn = fmaxf(M, mx);
+                float sum = 0.0f;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    if (kb + acc_row(v, kh) < S) sum += exp2f(acc[f][nt][v] * c - Mn);
+                sum += __shfl_xor(sum, 32);
+                L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + sum;
+                M = Mn;
+            }
+            const int wr = nt * 32 + l32;
+            if (kh == 0 && wr < wc) { sm[wave][wr] = M; sl[wave][wr] = L; }
+        }
+        __syncthreads();
+        if (tid < wc) {
+            float Mx = -INFINITY;
+            for (int w = 0; w < 4; ++w) Mx = fmaxf(Mx, sm[w][tid]);
+            float Lx = 0.0f;
+            for (int w = 0; w < 4; ++w)
+                if (sm[w][tid] > -INFINITY) Lx += sl[w][tid] * exp2f(sm[w][tid] - Mx);
+            st_agent(part + ((int64_t)ch * wc + tid) * 2, Mx);
+            st_agent(part + ((int64_t)ch * wc + tid) * 2 + 1, Lx);
+        }
+        __syncthreads();
+    };
+
+    floatx16 acc[F][NT];
+    logits(chunk, acc);
+    publish(chunk, acc);
+    if (tid < wc) wait_vmem();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flag + chunk, a.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool late = false;
+    if (tid < n_c) {
+        const uint64_t t0 = wall_clock64();
+        while (__hip_atomic_load(flag + tid, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.tag) {
+            if ((int64_t)(wall_clock64() - t0) > a.wait_ticks) { late = true; break; }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    }
+    if (__syncthreads_or(late)) {
+        // not every chunk of the head published in time: compute them all here
+        for (int ch = 0; ch < n_c; ++ch) {
+            logits(ch, acc);
+            publish(ch, acc);
+        }
+        if (tid < wc) wait_vmem();
+        __syncthreads();
+        logits(chunk, acc);
+    }
+    {
+        // merge the head's per-chunk (max, sum) of every observation row: tpr
+        // threads per row stride over the chunks (eight at a time, one common
+        // max per batch), then combine with lane shuffles
+        const int tpr = wc <= 32 ? 8 : (wc <= 64 ? 4 : 2);
+        const int r = tid / tpr, j = tid % tpr;
+        float M = -INFINITY, L = 0.0f;
+        for (int ch0 = j; ch0 < n_c; ch0 += 8 * tpr) {
+            float pm[8], pl[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int ch = ch0 + u * tpr;
+                pm[u] = -INFINITY;
+                pl[u] = 0.0f;
+                if (r < wc && ch < n_c) {
+                    pm[u] = ld_agent(part + ((int64_t)ch * wc + r) * 2);
+                    pl[u] = ld_agent(part + ((int64_t)ch * wc + r) * 2 + 1);
+                }
+            }
+            float mb = M;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) mb = fmaxf(mb, pm[u]);
+            if (mb > -INFINITY) {
+                float Ln = M == -INFINITY ? 0.0f : L * exp2f(M - mb);
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (pm[u] > -INFINITY) Ln += pl[u] * exp2f(pm[u] - mb);
+                L = Ln;
+                M = mb;
+            }
+        }
+        for (int off = 1; off < tpr; off <<= 1) {
+            const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(L, off);
+            const float Mn = fmaxf(M, m2);
+            L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
+            M = Mn;
+        }
+        if (r < wc && j == 0) {
+            Mrow[r] = M;
+            invL[r] = 1.0f / L;
+        }
+    }
+    __syncthreads();
+    // scores: each lane sums its observation rows' weights for its 16 keys,
+    // then the 32 lanes of a half add up (reduce-scatter over 16 lanes, then
+    // the two 16-lane groups), leaving key acc_row(l32 & 15, kh) in lane l32
+    float mrow[NT], ilr[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int wr = nt * 32 + l32;
+        mrow[nt] = wr < wc ? Mrow[wr] : 0.0f;
+        ilr[nt] = wr < wc ? invL[wr] : 0.0f;
+    }
+#pragma unroll
+    for (int f = 0; f < F; ++f) {
+        const int kb = key_base(chunk, f);
+        if (kb >= S) break;                                // uniform
+        float x[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            float sacc = 0.0f;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+                if (nt * 32 + l32 < wc) sacc += exp2f(acc[f][nt][v] * c - mrow[nt]) * ilr[nt];
+            x[v] = sacc;
+        }
+        float x8[8], x4[4], x2[2];
+        {
+            const bool hi = (l32 & 8) != 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x8[i] = (hi ? x[i + 8] : x[i]) + __shfl_xor(hi ? x[i] : x[i + 8], 8);
+        }
+        {
+            const bool hi = (l32 & 4) != 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x4[i] = (hi ? x8[i + 4] : x8[i]) + __shfl_xor(hi ? x8[i] : x8[i + 4], 4);
+        }
+        {
+            const bool hi = (l32 & 2) != 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) x2[i] = (hi ? x4[i + 2] : x4[i]) + __shfl_xor(hi ? x4[i] : x4[i + 2], 2);
+        }
+        const bool hi = (l32 & 1) != 0;
+        float sc = (hi ? x2[1] : x2[0]) + __shfl_xor(hi ? x2[0] : x2[1], 1);
+        sc += __shfl_xor(sc, 16);
+        const int key = kb + acc_row(l32 & 15, kh);
+        if (l32 < 16 && key < S) a.scores[bh * S + key] = sc / (float)wc;
+    }
+}
+
 // ---------------------------------------------------------------- selection
 
 __device__ __forceinline__ uint32_t order_key(float s) {
@@ -604,13 +828,22 @@ __global__ __launch_bounds__(kSelThreads) void snap_select_reg_kernel(const floa
 // latency-bound and the copy is short, so the repeats cost nothing and the
 // gather's own launch disappears.
 constexpr int kFuseMaxKeep = 4096;
+// Blocks go to the XCDs in turn (block x on XCD x % 8), so block x =
+// ((bh / 8) n_rep + rep) 8 + bh % 8 puts the n_rep blocks of one (batch,
+// head) on one XCD, where they share its L2 copy of the head's scores; the
+// grid is padded to whole groups of 8 heads.
+constexpr int kXcds = 8;
 template <int KPT>
 __global__ __launch_bounds__(kSelThreads) void snap_select_gather_kernel(SnapArgs a, const float* rank, int n_rep) {
     __shared__ int32_t keptl[kFuseMaxKeep];
-    const int64_t bh = blockIdx.x / n_rep;
-    const int rep = (int)(blockIdx.x - bh * n_rep);
+    const int xcd = (int)(blockIdx.x % kXcds), jx = (int)(blockIdx.x / kXcds);
+    const int rep = jx % n_rep;
+    const int64_t bh = (int64_t)(jx / n_rep) * kXcds + xcd;
+    if (bh >= (int64_t)a.B * a.H) return;         // padding block
     const int n_keep = min(a.budget, a.S);
     select_reg<KPT>(rank + bh * a.S, a.S, a.n_sink, a.budget, rep == 0 ? a.kept + bh * n_keep : nullptr, keptl);
+    if (a.flags && rep == 0)                      // the one-read scores' ready flags, for the next call
+        for (int t = (int)threadIdx.x; t < a.n_one; t += kSelThreads) a.flags[bh * a.n_one + t] = 0u;
     __syncthreads();
     const int upr = a.D / 8;                      // 16-byte units per fp16 row
     const int units = n_keep * upr;
@@ -684,6 +917,15 @@ __global__ __launch_bounds__(256) void snap_pool_kernel(const float* __restrict_
 
 // Workspace: chunk statistics, then scores (used when the caller passes no
 // scores buffer), then pooled scores (when pooling).
+// Ready flags of the one-read scores: one per (b, h, 128-key chunk), which
+// covers every chunking the one-read kernel uses (and grows with S, so a
+// workspace sized for a capacity also holds a call over fewer rows).
+size_t snapkv_flag_bytes(int B, int H, int S, int n_rows) {
+    (void)n_rows;
+    const int n_chunks = (S + kChunk - 1) / kChunk;
+    return ((size_t)B * H * n_chunks * sizeof(uint64_t) + 255) & ~(size_t)255;
+}
+
 size_t snapkv_ws_bytes(int B, int H, int S, int D, int n_rows, bool pooled) {
     (void)D;
     const int n_chunks = (S + kChunk - 1) / kChunk;
@@ -691,7 +933,67 @@ size_t snapkv_ws_bytes(int B, int H, int S, int D, int n_rows, bool pooled) {
     stats = (stats + 255) & ~(size_t)255;
     size_t sc = (size_t)B * H * S * sizeof(float);
     sc = (sc + 255) & ~(size_t)255;
-    return stats + sc + (pooled ? sc : 0);
+    return stats + sc + (pooled ? sc : 0) + snapkv_flag_bytes(B, H, S, n_rows);
+}
+
+int g_snap_wait_us = 200;
+
+// One-read chunking: 256 keys per workgroup (two 32-key sub-chunks per wave)
+// for up to 32 observation rows, 128 keys for more (their logits take 2 or 4
+// row tiles of registers).
+static int one_read_f(int rows) { return rows <= 32 ? 2 : 1; }
+static int one_read_nt(int rows) { return rows <= 32 ? 1 : (rows <= 64 ? 2 : 4); }
+
+template <int D, int F, int NT>
+static int one_read_resident() {
+    // workgroups of this kernel that the whole device holds at once
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] > 0) return cached[dev];
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, snap_one_read_kernel<D, F, NT>, 256, 0) != hipSuccess)
+        return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = per_cu * cus;
+    return cached[dev];
+}
+
+template <int D>
+static int one_read_resident_d(int F, int NT) {
+    if (F == 2) return one_read_resident<D, 2, 1>();
+    return NT == 2 ? one_read_resident<D, 1, 2>() : one_read_resident<D, 1, 4>();
+}
+
+bool snapkv_one_read_applies(const SnapArgs& a) {
+    if (!a.flags) return false;
+    const int n_keep = a.budget < a.S ? a.budget : a.S;
+    // the select-gather launch clears the flags: it must be the fused one
+    if (n_keep > kFuseMaxKeep || a.S > kSelThreads * 32) return false;
+    const int F = one_read_f(a.n_rows), NT = one_read_nt(a.n_rows);
+    const int n_c = (a.S + 128 * F - 1) / (128 * F);
+    if (n_c > 256) return false;
+    const int cap = a.D == 128 ? one_read_resident_d<128>(F, NT)
+                               : (a.D == 64 ? one_read_resident_d<64>(F, NT) : one_read_resident_d<32>(F, NT));
+    return (int64_t)a.B * a.H * n_c <= cap;
+}
+
+template <int D>
+static hipError_t launch_one_read_d(const SnapArgs& a, int F, int NT, hipStream_t s) {
+    const dim3 grid((unsigned)a.n_one, (unsigned)a.H, (unsigned)a.B);
+    if (F == 2) hipLaunchKernelGGL((snap_one_read_kernel<D, 2, 1>), grid, dim3(256), 0, s, a);
+    else if (NT == 2) hipLaunchKernelGGL((snap_one_read_kernel<D, 1, 2>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((snap_one_read_kernel<D, 1, 4>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_snapkv_scores_one_read(SnapArgs& a, hipStream_t s) {
+    const int F = one_read_f(a.n_rows), NT = one_read_nt(a.n_rows);
+    a.one_chunk = 128 * F;
+    a.n_one = (a.S + a.one_chunk - 1) / a.one_chunk;
+    if (a.D == 128) return launch_one_read_d<128>(a, F, NT, s);
+    if (a.D == 64) return launch_one_read_d<64>(a, F, NT, s);
+    return launch_one_read_d<32>(a, F, NT, s);
 }
 
 hipError_t launch_snapkv_pool(const float* in, float* out, int64_t rows, int S, int kernel, hipStream_t s) {
@@ -776,7 +1078,7 @@ hipError_t launch_snapkv_select_gather(const SnapArgs& a, const float* rank, hip
     // about one 16-byte unit of K and of V per thread and block
     int n_rep = (n_keep * (a.D / 8) + kSelThreads - 1) / kSelThreads;
     n_rep = n_rep < 1 ? 1 : (n_rep > 32 ? 32 : n_rep);
-    const dim3 grid((unsigned)(a.B * a.H * n_rep));
+    const dim3 grid((unsigned)((a.B * a.H + kXcds - 1) / kXcds * n_rep * kXcds));
     if (a.S <= kSelThreads * 8)
         hipLaunchKernelGGL((snap_select_gather_kernel<8>), grid, dim3(kSelThreads), 0, s, a, rank, n_rep);
     else if (a.S <= kSelThreads * 16)

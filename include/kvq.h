@@ -338,6 +338,20 @@ kvq_status kvq_snapkv_select(const void* k, const void* v, int32_t batch,
                              float* scores, int32_t* kept, void* k_out, void* v_out,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* How kvq_snapkv_select computes step 1.  Where every (b, h, key chunk)
+ * workgroup fits on the device at once (S <= 32768, n_keep <= 4096), the keys
+ * are read once: each workgroup keeps its chunk's logits in registers while
+ * the chunks of a head exchange their per-row softmax statistics through the
+ * workspace, and the select launch that follows clears the exchange flags
+ * (two launches per call).  Otherwise the logits are computed twice, in a
+ * statistics pass and a scores pass (three launches).  A workgroup waits for
+ * the rest of its head for at most the time set here (default 200 us; it
+ * then recomputes the head's statistics itself, which gives the same
+ * result); 0 makes every late workgroup take that path at once.  Calls that
+ * share one workspace must not overlap.  Returns the previous limit;
+ * negative values are ignored.                                              */
+int32_t kvq_snapkv_set_wait_us(int32_t microseconds);
+
 /* Steps 2-4 of kvq_snapkv_select without the gather, from given scores
  * [B][Hkv][S] fp32 (finite; -0 ranks as +0).  kept: [B][Hkv][n_keep].     */
 kvq_status kvq_snapkv_select_from_scores(const float* scores, int32_t batch,
