@@ -374,11 +374,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
             for (int h = 0; h < kGQ; ++h)
                 qz[h] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qzp), 16 * h));
             wave_lds_sync();
+            // row n = (quarter, head n & 3) carries the head's operand over
+            // every quarter (the scales are folded into it), so each row of
+            // the product is the head's whole dot product
             u32x4 ah[4], al[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                ah[c] = own ? abuf[wave][0][n & 3][4 * r + c] : u32x4{0u, 0u, 0u, 0u};
-                al[c] = own ? abuf[wave][1][n & 3][4 * r + c] : u32x4{0u, 0u, 0u, 0u};
+                ah[c] = abuf[wave][0][n & 3][4 * r + c];
+                al[c] = abuf[wave][1][n & 3][4 * r + c];
             }
             wave_lds_sync();                      // abuf is rebuilt for the next row
             const float fu = ldexpf(1.0f, 24 - E);
@@ -388,20 +391,23 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                 f4 cq = f4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    const u32x4 bw = mem ? nibble_operand(kw[p][c]) : u32x4{0u, 0u, 0u, 0u};
+                    const u32x4 bw = nibble_operand(mem ? kw[p][c] : 0u);   // zero codes: no term
                     cq = mfma16(ah[c], bw, cq);
                     cq = mfma16(al[c], bw, cq);
                 }
                 if (mem) {
 #pragma unroll
-                    for (int h = 0; h < kGQ; ++h) y[p][h] = fmaf(cq[h], fu, r == 0 ? qz[h] : 0.0f);
+                    for (int h = 0; h < kGQ; ++h) y[p][h] = fmaf(cq[h], fu, qz[h]);
                 }
             }
         }
         if (__builtin_amdgcn_ballot_w64(cls[0] == 2 || cls[1] == 2) != 0) {
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
-                if (cls[p] != 2) continue;
+                float part[kGQ];
+#pragma unroll
+                for (int h = 0; h < kGQ; ++h) part[h] = 0.0f;
+                if (cls[p] == 2) {
                 // keys of channels 32r .. 32r+31: the residual row, or u s + z from the token's row
                 const int t = tb + n + 16 * p;
                 float kv[32];
@@ -427,7 +433,18 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
                     float acc = 0.0f;
 #pragma unroll
                     for (int i = 0; i < 32; ++i) acc = fmaf(qbuf[h][32 * r + i], kv[i], acc);
-                    y[p][h] = acc;
+                    part[h] = acc;
+                }
+                }
+                // the whole dot products: add the four quarters (lanes r = 0 .. 3 of the token)
+#pragma unroll
+                for (int h = 0; h < kGQ; ++h) {
+                    part[h] += __shfl_xor(part[h], 16);
+                    part[h] += __shfl_xor(part[h], 32);
+                }
+                if (cls[p] == 2) {
+#pragma unroll
+                    for (int h = 0; h < kGQ; ++h) y[p][h] = part[h];
                 }
             }
         }
@@ -437,7 +454,8 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         constexpr bool kTail = decltype(tail)::value;     // the tile may hold invalid tokens
         const int tb = t_lo + tile * kTileT;
         // -------------------------------------------- scores of tokens n and n + 16
-        // y[p][h]: quarter r of head h's dot product for token n + 16 p
+        // y[p][h]: quarter r of head h's dot product for token n + 16 p (KIVI:
+        // the whole dot product, in every lane)
         float y[2][kGQ];
         if constexpr (KF == kKKivi) {
             kivi_scores(L, tb, y);
@@ -460,12 +478,17 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
         float xs[2];
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            // sum the quarters: rows r and r ^ 2 first (keeping the heads of
-            // this row pair), then r and r ^ 1 (keeping head r)
-            const bool hi = (r >> 1) != 0, odd = (r & 1) != 0;
-            const float z0 = (hi ? y[p][2] : y[p][0]) + __shfl_xor(hi ? y[p][0] : y[p][2], 32);
-            const float z1 = (hi ? y[p][3] : y[p][1]) + __shfl_xor(hi ? y[p][1] : y[p][3], 32);
-            const float xh = (odd ? z1 : z0) + __shfl_xor(odd ? z0 : z1, 16);
+            float xh;
+            if constexpr (KF == kKKivi) {
+                xh = r == 0 ? y[p][0] : (r == 1 ? y[p][1] : (r == 2 ? y[p][2] : y[p][3]));   // head r
+            } else {
+                // sum the quarters: rows r and r ^ 2 first (keeping the heads of
+                // this row pair), then r and r ^ 1 (keeping head r)
+                const bool hi = (r >> 1) != 0, odd = (r & 1) != 0;
+                const float z0 = (hi ? y[p][2] : y[p][0]) + __shfl_xor(hi ? y[p][0] : y[p][2], 32);
+                const float z1 = (hi ? y[p][3] : y[p][1]) + __shfl_xor(hi ? y[p][1] : y[p][3], 32);
+                xh = (odd ? z1 : z0) + __shfl_xor(odd ? z0 : z1, 16);
+            }
             const float xl = xh * kCx;
             if constexpr (kTail) xs[p] = (tb + n + 16 * p < t_hi) ? xl : -INFINITY;
             else xs[p] = xl;
