@@ -263,42 +263,61 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
 constexpr int kCombineMaxSplits = 1024;
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, const float* ws_ml,
                                                              float* out, int D, int ns) {
+    // Every load goes out first: the first kPre partial outputs of this
+    // thread's channel and this thread's (max, sum) pairs; none depends on
+    // the merged max, so the kernel waits for memory once.
+    constexpr int kPre = 32;
     const int64_t row = blockIdx.x;
     const int d = threadIdx.x;
     __shared__ float w_s[kCombineMaxSplits];
     __shared__ float red[2][4];
     const float* ml = ws_ml + row * ns * 2;
+    const float* o = ws_o + row * ns * D + d;
+    float v[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) v[u] = (d < D && u < ns) ? o[(int64_t)u * D] : 0.0f;
+    float2 mlv[kCombineMaxSplits / 128];
+#pragma unroll
+    for (int k = 0; k < kCombineMaxSplits / 128; ++k) {
+        const int sidx = d + 128 * k;
+        mlv[k] = sidx < ns ? reinterpret_cast<const float2*>(ml)[sidx] : make_float2(-INFINITY, 0.0f);
+    }
     float mloc = -INFINITY;
-    for (int s = d; s < ns; s += blockDim.x) mloc = fmaxf(mloc, ml[2 * s]);
+#pragma unroll
+    for (int k = 0; k < kCombineMaxSplits / 128; ++k) mloc = fmaxf(mloc, mlv[k].x);
     mloc = fmaxf(mloc, __shfl_xor(mloc, 1)); mloc = fmaxf(mloc, __shfl_xor(mloc, 2));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 4)); mloc = fmaxf(mloc, __shfl_xor(mloc, 8));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16)); mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
     if ((d & 63) == 0) red[0][d >> 6] = mloc;
     __syncthreads();
-    float M = -INFINITY;
-    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) M = fmaxf(M, red[0][w]);
+    const float M = fmaxf(red[0][0], red[0][1]);
     float dloc = 0.0f;
-    for (int s = d; s < ns; s += blockDim.x) {
-        const float w = exp2f(ml[2 * s] - M);
-        w_s[s] = w;
-        dloc = fmaf(w, ml[2 * s + 1], dloc);
+#pragma unroll
+    for (int k = 0; k < kCombineMaxSplits / 128; ++k) {
+        const int sidx = d + 128 * k;
+        if (sidx < ns) {
+            const float w = exp2f(mlv[k].x - M);
+            w_s[sidx] = w;
+            dloc = fmaf(w, mlv[k].y, dloc);
+        }
     }
     dloc += __shfl_xor(dloc, 1); dloc += __shfl_xor(dloc, 2); dloc += __shfl_xor(dloc, 4);
     dloc += __shfl_xor(dloc, 8); dloc += __shfl_xor(dloc, 16); dloc += __shfl_xor(dloc, 32);
     if ((d & 63) == 0) red[1][d >> 6] = dloc;
     __syncthreads();
-    float den = 0.0f;
-    for (int w = 0; w < (int)(blockDim.x + 63) / 64; ++w) den += red[1][w];
+    const float den = red[1][0] + red[1][1];
     if (d >= D) return;
-    const float* o = ws_o + row * ns * D + d;
     float num = 0.0f;
-    int s = 0;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u)
+        if (u < ns) num = fmaf(w_s[u], v[u], num);
+    int s = kPre;
     for (; s + 8 <= ns; s += 8) {
-        float v[8];
+        float x[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = o[(int64_t)(s + u) * D];
+        for (int u = 0; u < 8; ++u) x[u] = o[(int64_t)(s + u) * D];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) num = fmaf(w_s[s + u], v[u], num);
+        for (int u = 0; u < 8; ++u) num = fmaf(w_s[s + u], x[u], num);
     }
     for (; s < ns; ++s) num = fmaf(w_s[s], o[(int64_t)s * D], num);
     out[row * D + d] = num / den;
