@@ -261,6 +261,8 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(DecodeArgs a) {
 // per-split (m, l) pairs are staged in LDS by the block; the partial outputs
 // are read eight splits at a time.
 constexpr int kCombineMaxSplits = 1024;
+// Log-sum-exp merge of the splits of each row: the partials are unnormalized
+// sums o, weighted exp2(m - M).
 __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, const float* ws_ml,
                                                              float* out, int D, int ns) {
     // Every load goes out first: the first kPre partial outputs of this
@@ -273,9 +275,12 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, 
     __shared__ float red[2][4];
     const float* ml = ws_ml + row * ns * 2;
     const float* o = ws_o + row * ns * D + d;
+    // unconditional loads (a split index past ns reads split ns - 1 and gets weight 0)
     float v[kPre];
+    if (d < D) {
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) v[u] = (d < D && u < ns) ? o[(int64_t)u * D] : 0.0f;
+        for (int u = 0; u < kPre; ++u) v[u] = o[(int64_t)min(u, ns - 1) * D];
+    }
     float2 mlv[kCombineMaxSplits / 128];
 #pragma unroll
     for (int k = 0; k < kCombineMaxSplits / 128; ++k) {
@@ -304,13 +309,13 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, 
     dloc += __shfl_xor(dloc, 1); dloc += __shfl_xor(dloc, 2); dloc += __shfl_xor(dloc, 4);
     dloc += __shfl_xor(dloc, 8); dloc += __shfl_xor(dloc, 16); dloc += __shfl_xor(dloc, 32);
     if ((d & 63) == 0) red[1][d >> 6] = dloc;
+    if (d >= ns && d < kPre) w_s[d] = 0.0f;    // the padding of the prefetch
     __syncthreads();
     const float den = red[1][0] + red[1][1];
     if (d >= D) return;
     float num = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kPre; ++u)
-        if (u < ns) num = fmaf(w_s[u], v[u], num);
+    for (int u = 0; u < kPre; ++u) num = fmaf(w_s[u], v[u], num);
     int s = kPre;
     for (; s + 8 <= ns; s += 8) {
         float x[8];
@@ -321,6 +326,76 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, 
     }
     for (; s < ns; ++s) num = fmaf(w_s[s], o[(int64_t)s * D], num);
     out[row * D + d] = num / den;
+}
+
+// The same merge over fp16 partials o / l (weight exp2(m - M) l), D in {32,
+// 64, 128}.  Thread t takes channel pair t % (D/2) (one 32-bit load per
+// split) of the splits s = t / (D/2) mod 128 / (D/2); the phases meet in LDS.
+__global__ __launch_bounds__(128) void combine_f16_kernel(const uint16_t* ws_o, const float* ws_ml, float* out,
+                                                          int D, int ns) {
+    constexpr int kPre = 16;                      // splits prefetched per thread
+    const int64_t row = blockIdx.x;
+    const int t = threadIdx.x;
+    const int P = D / 2, Q = 128 / P;
+    const int c2 = t % P, q = t / P;
+    __shared__ float w_s[kCombineMaxSplits];
+    __shared__ float red[2][2];
+    __shared__ float2 part[128];
+    const float* ml = ws_ml + row * ns * 2;
+    const uint32_t* o = reinterpret_cast<const uint32_t*>(ws_o + row * ns * D) + c2;     // split s: o[s * P]
+    uint32_t v[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) v[u] = o[(int64_t)min(q + Q * u, ns - 1) * P];
+    float2 mlv[kCombineMaxSplits / 128];
+#pragma unroll
+    for (int k = 0; k < kCombineMaxSplits / 128; ++k) {
+        const int sidx = t + 128 * k;
+        mlv[k] = sidx < ns ? reinterpret_cast<const float2*>(ml)[sidx] : make_float2(-INFINITY, 0.0f);
+    }
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kCombineMaxSplits / 128; ++k) mloc = fmaxf(mloc, mlv[k].x);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 1)); mloc = fmaxf(mloc, __shfl_xor(mloc, 2));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 4)); mloc = fmaxf(mloc, __shfl_xor(mloc, 8));
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 16)); mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    if ((t & 63) == 0) red[0][t >> 6] = mloc;
+    __syncthreads();
+    const float M = fmaxf(red[0][0], red[0][1]);
+    float dloc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kCombineMaxSplits / 128; ++k) {
+        const int sidx = t + 128 * k;
+        if (sidx < ns) {
+            const float wl = exp2f(mlv[k].x - M) * mlv[k].y;
+            w_s[sidx] = wl;
+            dloc += wl;
+        }
+    }
+    dloc += __shfl_xor(dloc, 1); dloc += __shfl_xor(dloc, 2); dloc += __shfl_xor(dloc, 4);
+    dloc += __shfl_xor(dloc, 8); dloc += __shfl_xor(dloc, 16); dloc += __shfl_xor(dloc, 32);
+    if ((t & 63) == 0) red[1][t >> 6] = dloc;
+    __syncthreads();
+    const float den = red[1][0] + red[1][1];
+    float nx = 0.0f, ny = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int sidx = q + Q * u;
+        const float w = sidx < ns ? w_s[sidx] : 0.0f;
+        nx = fmaf(w, (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u] & 0xFFFFu)), nx);
+        ny = fmaf(w, (float)__builtin_bit_cast(_Float16, (uint16_t)(v[u] >> 16)), ny);
+    }
+    for (int sidx = q + Q * kPre; sidx < ns; sidx += Q) {
+        const uint32_t x = o[(int64_t)sidx * P];
+        nx = fmaf(w_s[sidx], (float)__builtin_bit_cast(_Float16, (uint16_t)(x & 0xFFFFu)), nx);
+        ny = fmaf(w_s[sidx], (float)__builtin_bit_cast(_Float16, (uint16_t)(x >> 16)), ny);
+    }
+    part[t] = make_float2(nx, ny);
+    __syncthreads();
+    if (t < P) {
+        float sx = 0.0f, sy = 0.0f;
+        for (int qq = 0; qq < Q; ++qq) { sx += part[qq * P + t].x; sy += part[qq * P + t].y; }
+        reinterpret_cast<float2*>(out + row * D)[t] = make_float2(sx / den, sy / den);
+    }
 }
 
 // (cos, sin) of pos * base^(-2j/D) for pos < n_pos, j < D/2, computed in fp64.
@@ -418,6 +493,14 @@ hipError_t launch_rope_table(float* table, int n_pos, int D, double base, hipStr
     const int64_t n = (int64_t)n_pos * (D / 2);
     hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        reinterpret_cast<float2*>(table), n_pos, D / 2, base);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_combine_f16(const uint16_t* ws_o, const float* ws_ml, float* out, int64_t rows, int D,
+                                     int ns, hipStream_t s) {
+    if (ns > kCombineMaxSplits || rows > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (D != 32 && D != 64 && D != 128) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(combine_f16_kernel, dim3((unsigned)rows), dim3(128), 0, s, ws_o, ws_ml, out, D, ns);
     return hipGetLastError();
 }
 

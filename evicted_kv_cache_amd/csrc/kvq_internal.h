@@ -135,6 +135,9 @@ hipError_t launch_rope_table(float* table, int n_pos, int D, double base, hipStr
 // log-sum-exp merge of per-split partials ws_o [rows][ns][D], ws_ml [rows][ns][2]
 hipError_t launch_decode_combine(const float* ws_o, const float* ws_ml, float* out, int64_t rows, int D, int ns,
                                  hipStream_t s);
+// The same merge over fp16 partials o / l (the multi-query attention's).
+hipError_t launch_decode_combine_f16(const uint16_t* ws_o, const float* ws_ml, float* out, int64_t rows, int D,
+                                     int ns, hipStream_t s);
 // Multi-query attention over the cache (DecodeArgs with T, splits and q as
 // [B][Hq][n_q][D]; out [B][Hq][n_q][D]).
 void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, int* n_rb, int* n_splits, int* split_len);

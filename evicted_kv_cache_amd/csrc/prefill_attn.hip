@@ -147,39 +147,53 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     const bool row_ok = r < R;
     const int h = row_ok ? r / n_q : 0, i = row_ok ? r - (r / n_q) * n_q : 0;
     const int64_t grow = ((int64_t)b * a.Hq + hk * G + h) * n_q + i;     // global query row
+    // the query operands, prepared while the first tile's codes are in flight
     half8 qf[NK], qfl[NK];
     float qc = 1.0f;                         // factor from score accumulators to base-2 logits
-    if constexpr (QX) {
-        float amax = 0.0f;
+    auto prepare_query = [&]() {
+        if constexpr (QX) {
+            // all of the row's loads first (16 bytes each, whatever the type), then the conversions
+            uint4 raw[NK];
 #pragma unroll
-        for (int q = 0; q < NK; ++q) {
-            float x[8] = {};
-            if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
+            for (int q = 0; q < NK; ++q) {
+                raw[q] = make_uint4(0u, 0u, 0u, 0u);
+                if (row_ok) raw[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + grow * D + q * 16 + kh * 8);
+            }
+            const bool f16in = a.q_dtype == KVQ_F16;
+            auto elem = [&](uint32_t bits16) { return f16in ? f16_bits_to_f32(bits16) : bf16_bits_to_f32(bits16); };
+            float amax = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(x[j]));
+            for (int q = 0; q < NK; ++q) {
+                const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    amax = fmaxf(amax, fmaxf(fabsf(elem(w[j] & 0xFFFFu)), fabsf(elem(w[j] >> 16))));
+            }
+            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            int ex = 0;
+            if (amax > 0.0f) frexpf(amax, &ex);                  // amax in [2^(ex-1), 2^ex)
+            const float up = ldexpf(1.0f, 15 - ex);              // largest |q| -> [2^14, 2^15)
+            qc = ldexpf(a.scale_log2, ex - 15);
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    qf[q][2 * j] = (_Float16)(elem(w[j] & 0xFFFFu) * up);
+                    qf[q][2 * j + 1] = (_Float16)(elem(w[j] >> 16) * up);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NK; ++q) {
+                float x[8] = {};
+                if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) x[j] *= a.scale_log2;
+                split_half8(x, qf[q], qfl[q]);
+            }
         }
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        int ex = 0;
-        if (amax > 0.0f) frexpf(amax, &ex);                  // amax in [2^(ex-1), 2^ex)
-        const float up = ldexpf(1.0f, 15 - ex);              // largest |q| -> [2^14, 2^15)
-        qc = ldexpf(a.scale_log2, ex - 15);
-#pragma unroll
-        for (int q = 0; q < NK; ++q) {
-            float x[8] = {};
-            if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) qf[q][j] = (_Float16)(x[j] * up);
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < NK; ++q) {
-            float x[8] = {};
-            if (row_ok) dq::load8(a.q, grow * D + q * 16 + kh * 8, a.q_dtype, x);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] *= a.scale_log2;
-            split_half8(x, qf[q], qfl[q]);
-        }
-    }
+    };
     const int lim = causal ? T - n_q + i : T - 1;   // last visible slot
     const int t_lo = split * a.split_len;
     const int t_hi = min(T, t_lo + a.split_len);
@@ -272,8 +286,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             for (int jj = 0; jj < 8; ++jj) vd[8 * c + jj][col] = (_Float16)xv[jj];
         }
     };
+    if (t_lo < t_hi) fetch(t_lo);
+    prepare_query();
     if (t_lo < t_hi) {
-        fetch(t_lo);
         unpack(t_lo, 0);
         if (t_lo + kPT < t_hi) fetch(t_lo + kPT);
     }
@@ -371,10 +386,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         __syncthreads();                     // this buffer is read, the other one written
     }
 
-    // unnormalized partials of the split: o[dim] and (m, l) of each row.  The
+    // partials of the split: o[dim] / l as fp16 and (m, l) of each row in
+    // fp32 (a row that saw no slot here has l = 0 and writes zeros).  The
     // accumulators hold O^T (lane = row); each 32-dim block goes through LDS
-    // so that rows are written as contiguous 128-byte runs.
+    // so that rows are written as contiguous 64-byte runs.
     const int ns = a.n_splits;
+    const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
     float (*tr)[33] = reinterpret_cast<float (*)[33]>(lds) + wave * 32;      // [32 rows][32 dims + pad]
     const int wr = lane >> 1, wh = lane & 1;                                // row, 16-dim half it writes
     const int r_w = rb * kRows + wave * 32 + wr;
@@ -383,18 +400,23 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         const int hw = r_w / n_q, iw = r_w - hw * n_q;
         grow_w = ((int64_t)b * a.Hq + hk * G + hw) * n_q + iw;
     }
+    uint16_t* ws_h = reinterpret_cast<uint16_t*>(a.ws_o);
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
         if (d > 0) __syncthreads();          // previous block's reads are done (the loop ended in one)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tr[l32][acc_row(v, kh)] = o[d][v];
+        for (int v = 0; v < 16; ++v) tr[l32][acc_row(v, kh)] = o[d][v] * inv_l;
         __syncthreads();
         if (r_w < R) {
-            float4* dst = reinterpret_cast<float4*>(a.ws_o + (grow_w * ns + split) * D + d * 32 + wh * 16);
+            uint32_t hw2[8];
 #pragma unroll
-            for (int k4 = 0; k4 < 4; ++k4)
-                dst[k4] = make_float4(tr[wr][wh * 16 + 4 * k4], tr[wr][wh * 16 + 4 * k4 + 1],
-                                      tr[wr][wh * 16 + 4 * k4 + 2], tr[wr][wh * 16 + 4 * k4 + 3]);
+            for (int k = 0; k < 8; ++k) {
+                _Float16 lo = (_Float16)tr[wr][wh * 16 + 2 * k], hi = (_Float16)tr[wr][wh * 16 + 2 * k + 1];
+                hw2[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
+            }
+            uint4* dst = reinterpret_cast<uint4*>(ws_h + (grow_w * ns + split) * D + d * 32 + wh * 16);
+            dst[0] = make_uint4(hw2[0], hw2[1], hw2[2], hw2[3]);
+            dst[1] = make_uint4(hw2[4], hw2[5], hw2[6], hw2[7]);
         }
     }
     if (row_ok && kh == 0) {
@@ -475,7 +497,8 @@ hipError_t launch_prefill_attention(const DecodeArgs& a, int n_q, int n_rb, int 
         default: e = launch_prefill_k<KVQ_TOK_SYM4>(a, n_q, n_rb, causal, s); break;
     }
     if (e != hipSuccess) return e;
-    return launch_decode_combine(a.ws_o, a.ws_ml, a.out, (int64_t)a.B * a.Hq * n_q, a.D, a.n_splits, s);
+    return launch_decode_combine_f16(reinterpret_cast<const uint16_t*>(a.ws_o), a.ws_ml, a.out,
+                                     (int64_t)a.B * a.Hq * n_q, a.D, a.n_splits, s);
 }
 
 }  // namespace kvq
