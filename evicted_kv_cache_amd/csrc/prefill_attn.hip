@@ -76,6 +76,21 @@ __device__ __forceinline__ void split_half8(const float x[8], half8& hi, half8& 
     }
 }
 
+// The eight 4-bit codes of a code word as floats: even channels are the bytes
+// of w & 0x0F0F0F0F, odd channels those of (w >> 4) & 0x0F0F0F0F (one
+// byte-to-float conversion each).
+__device__ __forceinline__ void nib8(uint32_t w, float u[8]) {
+    const uint32_t e = w & 0x0F0F0F0Fu, o = (w >> 4) & 0x0F0F0F0Fu;
+    u[0] = (float)(e & 0xFFu);
+    u[1] = (float)(o & 0xFFu);
+    u[2] = (float)((e >> 8) & 0xFFu);
+    u[3] = (float)((o >> 8) & 0xFFu);
+    u[4] = (float)((e >> 16) & 0xFFu);
+    u[5] = (float)((o >> 16) & 0xFFu);
+    u[6] = (float)(e >> 24);
+    u[7] = (float)(o >> 24);
+}
+
 using buf::rsrc;
 // Loads of `bytes` (2, 4 or 8) bytes at a buffer offset; past the buffer's end they read zero.
 __device__ __forceinline__ void bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t off, int bytes, dq::Pre8& p) {
@@ -213,6 +228,20 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     // work) sized to its valid rows.
     constexpr bool kTokK = KK == KVQ_TOK_AFFINE || KK == KVQ_TOK_SYM4;
     constexpr bool kTokV = VK == KVQ_TOK_AFFINE;
+    // 4-bit affine keys and values at head_dim 128: a thread's two items are
+    // tokens 2p and 2p + 1 of one 8-channel chunk, whose transposed values
+    // sit in adjacent columns (one 32-bit LDS store per channel)
+    constexpr bool kPair = C4 && KK == KVQ_TOK_AFFINE && D == 128 && kItems == 2;
+    auto item_tc = [&](int j, int& t, int& c) {
+        if constexpr (kPair) {
+            c = tid % C8;
+            t = 2 * (tid / C8) + j;
+        } else {
+            const int it = tid + j * kWaves * 64;
+            t = it / C8;
+            c = it - t * C8;
+        }
+    };
     const int kb = KK == KVQ_TOK_SYM4 ? 4 : a.k_bits;                 // code bytes per 8 channels
     const int k_row_b = D * kb / 8;
     const int k_meta_b = KK == KVQ_TOK_SYM4 ? (D / 32) * 2 : (kTokK ? (D / a.k_group) * 4 : 0);
@@ -227,9 +256,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             const __amdgpu_buffer_rsrc_t rm = rsrc(static_cast<const uint8_t*>(a.k_meta) + slot0 * k_meta_b, nt * k_meta_b);
 #pragma unroll
             for (int j = 0; j < kItems; ++j) {
-                const int it = tid + j * kWaves * 64;
-                if (it >= kPT * C8) break;
-                const int t = it / C8, c = it - t * C8;
+                if (!kPair && tid + j * kWaves * 64 >= kPT * C8) break;
+                int t, c;
+                item_tc(j, t, c);
                 bload_codes(rk, (uint32_t)(t * k_row_b + c * kb), kb, pk[j]);
                 pk[j].meta = KK == KVQ_TOK_SYM4
                                  ? __builtin_amdgcn_raw_buffer_load_b16(rm, (t * (D / 32) + (8 * c) / 32) * 2, 0, 0)
@@ -248,9 +277,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             const __amdgpu_buffer_rsrc_t rm = rsrc(static_cast<const uint8_t*>(a.v_meta) + slot0 * v_meta_b, nt * v_meta_b);
 #pragma unroll
             for (int j = 0; j < kItems; ++j) {
-                const int it = tid + j * kWaves * 64;
-                if (it >= kPT * C8) break;
-                const int t = it / C8, c = it - t * C8;
+                if (!kPair && tid + j * kWaves * 64 >= kPT * C8) break;
+                int t, c;
+                item_tc(j, t, c);
                 bload_codes(rv, (uint32_t)(t * v_row_b + c * a.v_bits), a.v_bits, pv[j]);
                 pv[j].meta = __builtin_amdgcn_raw_buffer_load_b32(rm, (t * (D / a.v_group) + (8 * c) / a.v_group) * 4, 0, 0);
             }
@@ -262,6 +291,38 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         _Float16 (*kd)[D + kPad] = k_lds(buf);
         _Float16 (*kld)[D + kPad] = kl_lds(buf);
         _Float16 (*vd)[kPT + kPad] = v_lds(buf);
+        if constexpr (kPair) {
+            // rows past the split were fetched as zero codes and metadata: zero keys and values
+            const int c = tid % C8, t0 = 2 * (tid / C8);
+            float xv[2][8];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                float u[8];
+                nib8(pk[j].c0, u);
+                const float sk = f16_bits_to_f32(pk[j].meta & 0xFFFFu), zk = f16_bits_to_f32(pk[j].meta >> 16);
+                half8 kh8, kl8;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const float x = fmaf(u[i], sk, zk);
+                    kh8[i] = (_Float16)x;
+                    kl8[i] = (_Float16)(x - (float)kh8[i]);
+                }
+                *reinterpret_cast<half8*>(&kd[t0 + j][8 * c]) = kh8;
+                *reinterpret_cast<half8*>(&kld[t0 + j][8 * c]) = kl8;
+                nib8(pv[j].c0, u);
+                const float sv = f16_bits_to_f32(pv[j].meta & 0xFFFFu), zv = f16_bits_to_f32(pv[j].meta >> 16);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xv[j][i] = fmaf(u[i], sv, zv);
+            }
+            const int col = v_col(t0);                // even; token t0 + 1 is column col + 1
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                const h2 pr = {(_Float16)xv[0][jj], (_Float16)xv[1][jj]};
+                *reinterpret_cast<h2*>(&vd[8 * c + jj][col]) = pr;
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
             const int it = tid + j * kWaves * 64;
