@@ -55,6 +55,12 @@ __device__ __forceinline__ int v_col(int t) {
     return 16 * s + 8 * ((r & 7) >> 2) + 4 * (r >> 3) + (r & 3);
 }
 
+// Physical column of (row, col) in the value tile: the 16-byte chunk index
+// (col bits 3..5) is XORed with (row >> 4) & 7, so the rows 8c + j that one
+// store instruction writes (c = 0..15) spread over the banks, while the
+// 16-byte operand reads of a row stay contiguous.
+__device__ __forceinline__ int vswz(int row, int col) { return col ^ (((row >> 4) & 7) << 3); }
+
 __device__ __forceinline__ int wave_min(int v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             for (int jj = 0; jj < 8; ++jj) {
                 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
                 const h2 pr = {(_Float16)xv[0][jj], (_Float16)xv[1][jj]};
-                *reinterpret_cast<h2*>(&vd[8 * c + jj][col]) = pr;
+                *reinterpret_cast<h2*>(&vd[8 * c + jj][vswz(8 * c + jj, col)]) = pr;
             }
             return;
         }
@@ -344,7 +350,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             *reinterpret_cast<half8*>(&kld[t][8 * c]) = kl8;
             const int col = v_col(t);
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) vd[8 * c + jj][col] = (_Float16)xv[jj];
+            for (int jj = 0; jj < 8; ++jj) vd[8 * c + jj][vswz(8 * c + jj, col)] = (_Float16)xv[jj];
         }
     };
     if (t_lo < t_hi) fetch(t_lo);
@@ -441,7 +447,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         for (int d = 0; d < ND; ++d)
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                const half8 va = *reinterpret_cast<const half8*>(&vd[d * 32 + l32][16 * st + 8 * kh]);
+                const half8 va = *reinterpret_cast<const half8*>(&vd[d * 32 + l32][vswz(d * 32 + l32, 16 * st + 8 * kh)]);
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[st], o[d], 0, 0, 0);
             }
         __syncthreads();                     // this buffer is read, the other one written
