@@ -123,9 +123,11 @@ struct MTile {
 };
 
 // KF: K format (kKAff4; kKSym4 or kKKivi with GK = 32); GK, GV: channels
-// per K / V group (32, 64 or 128); VB: bits per V code (4 or 8).
-template <int QDT, int KF, int GK, int VB, int GV>
-__global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
+// per K / V group (32, 64 or 128); VB: bits per V code (4 or 8); NW: waves
+// per workgroup (4, two workgroups per CU; 8, one, for splits of at most 8
+// tiles, where a wave's second tile would only lengthen the latency chain).
+template <int QDT, int KF, int GK, int VB, int GV, int NW>
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
     static_assert(KF == kKAff4 || GK == 32, "symmetric and KIVI keys take GK = 32");
     constexpr int NKG = kD / GK;
     constexpr int NVG = kD / GV;
@@ -143,14 +145,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     const int t_hi = min(a.T, t_lo + a.split_len);
     const int n_tiles = (t_hi - t_lo + kTileT - 1) / kTileT;
 
-    __shared__ __align__(16) uint32_t wbuf[kWaves][NVG][kGQ][16];   // fp16 weight pairs (t, t + 16)
-    __shared__ __align__(16) uint32_t vst[VB == 8 ? kWaves : 1][kTileT][36];     // 8-bit V code rows (32 words + pad)
-    __shared__ float comb_o[kWaves][kGQ][kD];
-    __shared__ float comb_ml[kWaves][kGQ][2];
+    __shared__ __align__(16) uint32_t wbuf[NW][NVG][kGQ][16];   // fp16 weight pairs (t, t + 16)
+    __shared__ __align__(16) uint32_t vst[VB == 8 ? NW : 1][kTileT][36];     // 8-bit V code rows (32 words + pad)
+    __shared__ float comb_o[NW][kGQ][kD];
+    __shared__ float comb_ml[NW][kGQ][2];
     // KIVI keys: the staged table rows r0, r1 ((scale, zero) per channel),
     // the A operands built from one of them ([hi | lo][head][channel chunk]),
     // and the query of all heads for tokens that take the per-lane path
-    constexpr int KW = KF == kKKivi ? kWaves : 1;
+    constexpr int KW = KF == kKKivi ? NW : 1;
     __shared__ __align__(16) uint32_t kst[KW][2][kD];
     __shared__ __align__(16) u32x4 abuf[KW][2][kGQ][16];
     __shared__ __align__(16) float qbuf[KF == kKKivi ? kGQ : 1][kD];
@@ -608,9 +610,9 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     // split's last tile can be partial
     MTile<NVG, VH> A, B2;
     const int n_full = (t_hi - t_lo) / kTileT;
-    const int n_mine = n_tiles > wave ? (n_tiles - wave + kWaves - 1) / kWaves : 0;
-    const int n_mine_full = n_full > wave ? (n_full - wave + kWaves - 1) / kWaves : 0;
-    auto tl = [&](int i) { return wave + kWaves * i; };
+    const int n_mine = n_tiles > wave ? (n_tiles - wave + NW - 1) / NW : 0;
+    const int n_mine_full = n_full > wave ? (n_full - wave + NW - 1) / NW : 0;
+    auto tl = [&](int i) { return wave + NW * i; };
     int i = 0;
     if (n_mine > 0) load_tile(tl(0), A);
     for (; i + 1 < n_mine_full; i += 2) {
@@ -673,15 +675,15 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     __syncthreads();
     // ---------------------------------------------------- merge the 4 waves
     const int ns = a.n_splits;
-    for (int idx = threadIdx.x; idx < kGQ * kD; idx += 256) {
+    for (int idx = threadIdx.x; idx < kGQ * kD; idx += NW * 64) {
         const int h = idx / kD, d = idx % kD;
         if (h >= gq) continue;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, comb_ml[w][h][0]);
+        for (int w = 0; w < NW; ++w) M = fmaxf(M, comb_ml[w][h][0]);
         float num = 0.0f, den = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float mw = comb_ml[w][h][0];
             const float f = mw == -INFINITY ? 0.0f : exp2f(mw - M);
             num = fmaf(f, comb_o[w][h][d], num);
@@ -700,13 +702,14 @@ __global__ __launch_bounds__(256, 2) void decode_mfma_kernel(DecodeArgs a) {
     }
 }
 
-template <int QDT, int KF, int GK, int VB>
+template <int QDT, int KF, int GK, int VB, int NW>
 hipError_t launch_mfma_v(const DecodeArgs& a, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)a.Hkv, (unsigned)a.B);
+    const dim3 block(NW * 64);
     switch (a.v_group) {
-        case 32: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 32>), grid, dim3(256), 0, s, a); break;
-        case 64: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 64>), grid, dim3(256), 0, s, a); break;
-        case 128: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 128>), grid, dim3(256), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 32, NW>), grid, block, 0, s, a); break;
+        case 64: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 64, NW>), grid, block, 0, s, a); break;
+        case 128: hipLaunchKernelGGL((decode_mfma_kernel<QDT, KF, GK, VB, 128, NW>), grid, block, 0, s, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -714,7 +717,12 @@ hipError_t launch_mfma_v(const DecodeArgs& a, hipStream_t s) {
 
 template <int QDT, int KF, int GK>
 hipError_t launch_mfma_k(const DecodeArgs& a, hipStream_t s) {
-    return a.v_bits == 8 ? launch_mfma_v<QDT, KF, GK, 8>(a, s) : launch_mfma_v<QDT, KF, GK, 4>(a, s);
+    if (a.v_bits == 8) return launch_mfma_v<QDT, KF, GK, 8, 4>(a, s);
+    // KIVI keys in short splits (at most 8 tiles: one per wave of 8): the
+    // latency-bound small-batch case
+    if constexpr (KF == kKKivi)
+        if (a.split_len <= 8 * kTileT) return launch_mfma_v<QDT, KF, GK, 4, 8>(a, s);
+    return launch_mfma_v<QDT, KF, GK, 4, 4>(a, s);
 }
 
 template <int QDT>
