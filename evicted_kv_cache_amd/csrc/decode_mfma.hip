@@ -5,10 +5,11 @@
 // kv-head, with both products on the matrix cores (gfx950,
 // v_mfma_f32_16x16x32_f16).
 //
-// Work split: 4 waves per (batch, kv-head[, token split]), each with its own
-// online softmax over every fourth 32-token tile of the split (so the four
-// waves of a workgroup stream one region of the cache together, which keeps
-// fewer DRAM streams open than four separate runs), merged through LDS
+// Work split: 4 waves per (batch, kv-head[, token split]) (8 for KIVI keys
+// in splits of at most 8 tiles), each with its own online softmax over
+// every fourth (eighth) 32-token tile of the split (so the waves of a
+// workgroup stream one region of the cache together, which keeps fewer DRAM
+// streams open than separate runs), merged through LDS
 // (token splits merge in a combine kernel).  What changes is where the multiply-adds run.  A 4-bit code left
 // in place under a mask is an fp16 subnormal (u 2^-24 for a low nibble,
 // u 2^-20 for a high one), and the matrix cores multiply subnormal fp16
@@ -604,7 +605,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
         wave_lds_sync();
     };
 
-    // this wave's tiles wave, wave + 4, ...; two load buffers in ping-pong:
+    // this wave's tiles wave, wave + NW, ...; two load buffers in ping-pong:
     // the next tile's loads are in flight while the current tile is computed
     // (a prefetch past the split reads zeros and is never used); only the
     // split's last tile can be partial
@@ -673,7 +674,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
         comb_ml[wave][r][1] = l_lane;
     }
     __syncthreads();
-    // ---------------------------------------------------- merge the 4 waves
+    // ---------------------------------------------------- merge the waves
     const int ns = a.n_splits;
     for (int idx = threadIdx.x; idx < kGQ * kD; idx += NW * 64) {
         const int h = idx / kD, d = idx % kD;
