@@ -92,3 +92,30 @@ def test_prefill_microbenchmark_shape_sampled():
         err = float(np.abs(got[0, hq, i] - ref).max() / np.abs(ref).max())
         say(f"  row ({hq}, {i}) error {err:.3e}")
         assert err <= TOL
+
+
+@pytest.mark.parametrize("D,dtype,k_bits,T", [
+    (128, "bf16", 4, 8192),      # 64 splits: 32 past the combine's prefetch (two split phases)
+    (64, "bf16", 8, 12000),      # 93 splits, four phases
+    (32, "f32", 4, 20000),       # 156 splits, eight phases, fp32 queries
+])
+def test_prefill_many_splits(D, dtype, k_bits, T):
+    """One kv-head and four query rows over a long cache: the split plan then
+    takes many short splits, and the fp16 split combine reads the splits past
+    its prefetch in its tail loop.  Every row against the oracle."""
+    B, H, G, n_q = 1, 1, 2, 2
+    w = synth.workload("affine4_g64", head_dim=D, seq_len=T, batch=B, n_kv_heads=H, n_q_heads=H * G,
+                       dtype=dtype)
+    k, v, _ = synth.full(w, threads=16)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=D, capacity=T, k_kind="tok_affine", k_bits=k_bits,
+                     k_group=32, v_kind="tok_affine", v_bits=k_bits, v_group=32, in_dtype=dtype)
+    say("prefill many splits", D, dtype, k_bits, T)
+    c, o = build_pair(pl, ol, k, v, dtype)
+    q = gen_q(w, B, H * G, H, n_q, seed=T)
+    out = K.kvq_prefill_attention(pl, c, to_dev(q, dtype), causal=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = prefill_attention(o, q, dtype, causal=True)
+    err = attn_err(got, ref)
+    say(f"  error {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL, err
