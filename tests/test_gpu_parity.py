@@ -609,3 +609,27 @@ def test_split_decode_repeats_bit_identically(k_kind, G):
     err = attn_err(first, o.decode(q, "f16"))
     say(f"  attention error {err:.3e}")
     assert err <= TOL
+
+
+@pytest.mark.parametrize("wname,D,lay,T", [
+    # matrix-core decode: 64 splits of 256 tokens
+    ("affine4_g64", 128, dict(k_kind="tok_affine", k_bits=4, k_group=64, v_kind="tok_affine", v_bits=4,
+                              v_group=64), 16384),
+    # KIVI keys: 64 splits of 8 tiles, workgroups of 8 waves
+    ("llama3b_kivi_int4", 128, dict(k_kind="kivi_ch", k_bits=4, k_group=32, v_kind="tok_affine", v_bits=4,
+                                    v_group=64), 16384),
+    # generic decode (8-bit codes at head_dim 64)
+    ("affine4_g64", 64, dict(k_kind="tok_affine", k_bits=8, k_group=32, v_kind="tok_affine", v_bits=8,
+                             v_group=32), 6000),
+])
+def test_decode_many_splits(wname, D, lay, T):
+    """One kv-head of four query heads over a long cache: the split plans take
+    many splits, and the combine reads the splits past its prefetch in its
+    tail loop."""
+    B, H, Hq = 1, 1, 4
+    w = synth.workload(wname, head_dim=D)
+    k, v, q = gen(w, B, H, T, Hq)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=D, capacity=T + 37, in_dtype=w.dtype, **lay)
+    say("decode many splits", wname, D, lay["k_kind"], T)
+    c, o = build_pair(pl, ol, k, v, w.dtype)
+    check_decode(pl, c, o, q, w.dtype)
