@@ -42,6 +42,7 @@ constexpr int kPT = 64;          // tokens per tile
 constexpr int kWaves = 8;        // waves per workgroup, 32 query rows each
 constexpr int kRows = 32 * kWaves;
 constexpr int kPad = 8;          // halfs of padding per LDS row (bank spread)
+constexpr float kSlack = 8.0f;   // log2 headroom of the lazily moved softmax reference point
 
 // Row of the 32x32 block held by accumulator element v of lane half kh.
 __device__ __forceinline__ int acc_row(int v, int kh) { return 8 * (v >> 2) + 4 * kh + (v & 3); }
@@ -412,36 +413,42 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
                     mt = fmaxf(mt, x);
                 }
         }
-        // online softmax, base 2; the running max only moves when a row sees a
-        // larger logit, and only then are the output accumulators rescaled
+        // online softmax, base 2.  A row's reference point m moves only when
+        // the row sees a logit more than kSlack above it (and on its first
+        // visible slot); only then are its output accumulators rescaled.  The
+        // probabilities are then at most 2^kSlack, well inside fp16, and the
+        // split's (m, l) stay consistent with its outputs.
         mt = fmaxf(mt, __shfl_xor(mt, 32)) * qc;
-        const float m_new = fmaxf(m, mt);
+        const float m_new = mt > m + kSlack ? mt : m;
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // nothing visible yet
-        float ps = 0.0f;
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                // v_exp_f32: arguments are <= 0, results below 2^-126 flush to 0
-                const float p = __builtin_amdgcn_exp2f(fmaf(s[blk][v], qc, -m_use));
-                s[blk][v] = p;
-                ps += p;
-            }
-        ps += __shfl_xor(ps, 32);
         if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
             const float alpha = __builtin_amdgcn_exp2f(m - m_use);
             l *= alpha;
 #pragma unroll
             for (int d = 0; d < ND; ++d) o[d] *= alpha;
         }
-        l += ps;
         m = m_new;
-        // P^T fragments: K-step st takes accumulator elements 8 (st & 1) .. +7 of block st >> 1
+        // P^T fragments: K-step st takes accumulator elements 8 (st & 1) .. +7
+        // of block st >> 1 (v_exp_f32: results below 2^-126 flush to 0)
         half8 pf[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) pf[st][j] = (_Float16)s[st >> 1][8 * (st & 1) + j];
+            for (int j = 0; j < 8; ++j)
+                pf[st][j] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + j], qc, -m_use));
+        // the row sum takes the fp16 probabilities the value product uses, two per instruction
+        typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+        const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        float ps = 0.0f;
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const half2v pr = {pf[st][2 * j], pf[st][2 * j + 1]};
+                ps = __builtin_amdgcn_fdot2(pr, one2, ps, false);
+            }
+        ps += __shfl_xor(ps, 32);
+        l += ps;
         // O^T += V^T P^T
 #pragma unroll
         for (int d = 0; d < ND; ++d)
