@@ -36,6 +36,7 @@ namespace kvq {
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPT = 64;          // tokens per tile
@@ -128,10 +129,26 @@ __device__ __forceinline__ void bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t o
 // so each tile's fetch is one straight run of loads whose results are first
 // used one tile later (with widths known only at run time, the branches
 // around the loads cost a wait on each of them).
-template <int KK, int VK, int D, bool QX, bool C4>
+//
+// FG > 0: factored scores for 4-bit per-token affine keys with FG groups per
+// row (group 64 or 128 at head_dim 128).  A key is u s_g + z_g, so
+//   q.k = sum_g s_g (q_g . u_g) + sum_g z_g Q_g,    Q_g = sum of q over group g.
+// The key tile holds the codes themselves as MFMA operands: a code left in
+// place under a nibble mask is the fp16 subnormal u 2^-24 (low nibble) or
+// u 2^-20 (high nibble), and the query operand carries the matching channel
+// order and a 1/16 on the high-nibble channels, so every product is exact and
+// only the fp32 accumulation rounds.  One accumulator per group takes the
+// q_g . u_g sums; the zero-point term is one bf16 product per 32-token block
+// (z as an exact bf16 pair, Q_g 2^-24 as an exact bf16 triple); the lane then
+// scales each group's sum by its token's s_g.  There is no key residual and
+// no second key product.
+template <int KK, int VK, int D, bool QX, bool C4, int FG>
 __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
     static_assert(!C4 || ((KK == KVQ_TOK_AFFINE || KK == KVQ_TOK_SYM4) && VK == KVQ_TOK_AFFINE),
                   "constant code widths: per-token layouts");
+    static_assert(FG == 0 || (C4 && QX && KK == KVQ_TOK_AFFINE && D == 128 && FG <= 2),
+                  "factored scores: 4-bit affine keys at head_dim 128, fp16/bf16 queries, 1 or 2 groups per row");
+    constexpr bool kFact = FG > 0;
     if constexpr (C4) {
         a.k_bits = 4;
         a.v_bits = 4;
@@ -163,6 +180,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     auto v_lds = [&](int buf) {
         return reinterpret_cast<_Float16 (*)[kPT + kPad]>(lds + buf * kTileHalfs + 2 * kKeyHalfs);
     };
+    // factored scores: the residual's space holds each token's group scales
+    // (fp16 s_0 | s_1 << 16) and its zero-point operands ([token][group] 8 bf16)
+    auto sc_lds = [&](int buf) { return reinterpret_cast<uint32_t*>(lds + buf * kTileHalfs + kKeyHalfs); };
+    auto zo_lds = [&](int buf) {
+        return reinterpret_cast<uint4 (*)[2]>(lds + buf * kTileHalfs + kKeyHalfs + 2 * kPT);
+    };
 
     // this lane's query row: fragments for every K-step
     const int r = rb * kRows + wave * 32 + l32;
@@ -171,6 +194,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     const int64_t grow = ((int64_t)b * a.Hq + hk * G + h) * n_q + i;     // global query row
     // the query operands, prepared while the first tile's codes are in flight
     half8 qf[NK], qfl[NK];
+    uint4 zq = make_uint4(0u, 0u, 0u, 0u);   // factored: B operand of the zero-point product
     float qc = 1.0f;                         // factor from score accumulators to base-2 logits
     auto prepare_query = [&]() {
         if constexpr (QX) {
@@ -195,15 +219,47 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             int ex = 0;
             if (amax > 0.0f) frexpf(amax, &ex);                  // amax in [2^(ex-1), 2^ex)
             const float up = ldexpf(1.0f, 15 - ex);              // largest |q| -> [2^14, 2^15)
-            qc = ldexpf(a.scale_log2, ex - 15);
+            qc = ldexpf(a.scale_log2, kFact ? ex + 9 : ex - 15); // factored sums carry 2^-24
+            float qsum[2] = {0.0f, 0.0f};        // factored: this lane's half of each group's query sum
 #pragma unroll
             for (int q = 0; q < NK; ++q) {
                 const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+                float x[8];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    qf[q][2 * j] = (_Float16)(elem(w[j] & 0xFFFFu) * up);
-                    qf[q][2 * j + 1] = (_Float16)(elem(w[j] >> 16) * up);
+                    x[2 * j] = elem(w[j] & 0xFFFFu) * up;
+                    x[2 * j + 1] = elem(w[j] >> 16) * up;
                 }
+                if constexpr (kFact) {
+                    // operand element e holds channel {0,4,1,5,2,6,3,7}[e] of the
+                    // chunk; high-nibble channels (odd) arrive 16x larger
+                    constexpr int ch[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qf[q][e] = (_Float16)((ch[e] & 1) ? x[ch[e]] * 0.0625f : x[ch[e]]);
+                    // K-step q covers channels 16q .. 16q + 15, all in group q / (NK / FG)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qsum[FG == 2 && q >= NK / 2 ? 1 : 0] += x[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) qf[q][e] = (_Float16)x[e];
+                }
+            }
+            if constexpr (kFact) {
+                // Lane half kh supplies group kh's term (FG = 2), or the low
+                // half the whole row's (FG = 1); the partner lane holds the
+                // other half of every group's channels.
+                const float send = FG == 2 ? qsum[1 - kh] : qsum[0];
+                const float other = __shfl_xor(send, 32);
+                const float Q = (FG == 2 ? qsum[kh] : qsum[0]) + other;
+                // Q 2^-24 as an exact bf16 triple (truncating splits)
+                const float Qs = Q * 0x1p-24f;
+                const uint32_t hb = __float_as_uint(Qs) & 0xFFFF0000u;
+                const float r1 = Qs - __uint_as_float(hb);
+                const uint32_t mb = __float_as_uint(r1) & 0xFFFF0000u;
+                const float r2 = r1 - __uint_as_float(mb);
+                const uint32_t h = hb >> 16, mdl = mb >> 16, lw = __float_as_uint(r2) >> 16;
+                const bool live = FG == 2 || kh == 0;
+                zq = live ? make_uint4(h | (mdl << 16), lw | (h << 16), mdl | (lw << 16), 0u) : make_uint4(0u, 0u, 0u, 0u);
             }
         } else {
 #pragma unroll
@@ -305,17 +361,37 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 float u[8];
-                nib8(pk[j].c0, u);
-                const float sk = f16_bits_to_f32(pk[j].meta & 0xFFFFu), zk = f16_bits_to_f32(pk[j].meta >> 16);
-                half8 kh8, kl8;
+                if constexpr (kFact) {
+                    // the code word under nibble masks: channels (0,4), (1,5)*16,
+                    // (2,6), (3,7)*16 as fp16 subnormal pairs
+                    const uint32_t w = pk[j].c0, w8 = w >> 8;
+                    *reinterpret_cast<uint4*>(&kd[t0 + j][8 * c]) =
+                        make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u);
+                    constexpr int kCg = 128 / FG / 8;    // 8-channel chunks per group
+                    if (c % kCg == 0) {
+                        // first chunk of group g: the token's s_g, and z_g as an
+                        // exact bf16 pair (zh keeps the top 8 significant bits)
+                        const int g = c / kCg;
+                        reinterpret_cast<uint16_t*>(sc_lds(buf))[2 * (t0 + j) + g] = (uint16_t)(pk[j].meta & 0xFFFFu);
+                        const float z = f16_bits_to_f32(pk[j].meta >> 16);
+                        const uint32_t zhb = __float_as_uint(z) & 0xFFFF0000u;
+                        const uint32_t zh = zhb >> 16, zl = __float_as_uint(z - __uint_as_float(zhb)) >> 16;
+                        zo_lds(buf)[t0 + j][g] = make_uint4(zh | (zh << 16), zh | (zl << 16), zl | (zl << 16), 0u);
+                        if (FG == 1) zo_lds(buf)[t0 + j][1] = make_uint4(0u, 0u, 0u, 0u);
+                    }
+                } else {
+                    nib8(pk[j].c0, u);
+                    const float sk = f16_bits_to_f32(pk[j].meta & 0xFFFFu), zk = f16_bits_to_f32(pk[j].meta >> 16);
+                    half8 kh8, kl8;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const float x = fmaf(u[i], sk, zk);
-                    kh8[i] = (_Float16)x;
-                    kl8[i] = (_Float16)(x - (float)kh8[i]);
+                    for (int i = 0; i < 8; ++i) {
+                        const float x = fmaf(u[i], sk, zk);
+                        kh8[i] = (_Float16)x;
+                        kl8[i] = (_Float16)(x - (float)kh8[i]);
+                    }
+                    *reinterpret_cast<half8*>(&kd[t0 + j][8 * c]) = kh8;
+                    *reinterpret_cast<half8*>(&kld[t0 + j][8 * c]) = kl8;
                 }
-                *reinterpret_cast<half8*>(&kd[t0 + j][8 * c]) = kh8;
-                *reinterpret_cast<half8*>(&kld[t0 + j][8 * c]) = kl8;
                 nib8(pv[j].c0, u);
                 const float sv = f16_bits_to_f32(pv[j].meta & 0xFFFFu), zv = f16_bits_to_f32(pv[j].meta >> 16);
 #pragma unroll
@@ -370,6 +446,41 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         _Float16 (*vd)[kPT + kPad] = v_lds(buf);
         // S^T for this wave's 32 rows: two 32-token blocks
         floatx16 s[2];
+        if constexpr (kFact) {
+            const uint32_t* scl = sc_lds(buf);
+            uint4 (*zo)[2] = zo_lds(buf);
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const uint4 za = zo[blk * 32 + l32][kh];
+                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, za),
+                                                                 __builtin_bit_cast(bf16x8, zq), floatx16{}, 0, 0, 0);
+                // one group at a time: its K-steps into one accumulator, then
+                // each element scaled by its token's s_g (token 8j + 4kh + i of
+                // the block is accumulator element 4j + i)
+#pragma unroll
+                for (int g = 0; g < FG; ++g) {
+                    constexpr int kQ = NK / FG;
+                    floatx16 sg = floatx16{};
+#pragma unroll
+                    for (int q = 0; q < kQ; ++q) {
+                        const half8 ka = *reinterpret_cast<const half8*>(&kd[blk * 32 + l32][(g * kQ + q) * 16 + kh * 8]);
+                        sg = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[g * kQ + q], sg, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint4 sv = *reinterpret_cast<const uint4*>(&scl[blk * 32 + 8 * j + 4 * kh]);
+                        const uint32_t w[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            s[blk][4 * j + i] = fmaf(f16_bits_to_f32(g == 0 ? w[i] & 0xFFFFu : w[i] >> 16), sg[4 * j + i], s[blk][4 * j + i]);
+                    }
+                }
+                // the block's logits are complete here (keeps the next block's
+                // products from running ahead of this block's scaling)
+                asm volatile("" : "+v"(s[blk]));
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        } else
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk) {
             s[blk] = floatx16{};
@@ -386,6 +497,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         // (without a branch, so that the score products and the unpacking
         // are one block the scheduler can interleave; past the split's end
         // the unpack writes zero rows and the fetch reads zeros)
+        if constexpr (kFact) __builtin_amdgcn_sched_barrier(0);
         if constexpr (kTokK && kTokV) {
             unpack(t0 + kPT, buf ^ 1);
             fetch(t0 + 2 * kPT);
@@ -502,10 +614,24 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
 template <int KK, int VK, bool QX, bool C4>
 hipError_t launch_prefill_kvq(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
     dim3 grid((unsigned)a.n_splits, (unsigned)(a.Hkv * n_rb), (unsigned)a.B);
+    const dim3 blk(kWaves * 64);
     switch (a.D) {
-        case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32, QX, C4>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
-        case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64, QX, C4>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
-        default: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4>), grid, dim3(kWaves * 64), 0, s, a, n_q, n_rb, causal); break;
+        case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32, QX, C4, 0>), grid, blk, 0, s, a, n_q, n_rb, causal); break;
+        case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64, QX, C4, 0>), grid, blk, 0, s, a, n_q, n_rb, causal); break;
+        default:
+            if constexpr (C4 && QX && KK == KVQ_TOK_AFFINE) {
+                // factored scores for key groups of 64 or 128 channels
+                if (a.k_group == 64) {
+                    hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4, 2>), grid, blk, 0, s, a, n_q, n_rb, causal);
+                    break;
+                }
+                if (a.k_group == 128) {
+                    hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4, 1>), grid, blk, 0, s, a, n_q, n_rb, causal);
+                    break;
+                }
+            }
+            hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4, 0>), grid, blk, 0, s, a, n_q, n_rb, causal);
+            break;
     }
     return hipGetLastError();
 }

@@ -119,3 +119,35 @@ def test_prefill_many_splits(D, dtype, k_bits, T):
     err = attn_err(got, ref)
     say(f"  error {err:.3e}")
     assert np.all(np.isfinite(got)) and err <= TOL, err
+
+
+@pytest.mark.parametrize("kg,vg,dtype,stress", [
+    (64, 32, "bf16", "outliers"), (64, 64, "bf16", "outliers"), (64, 128, "bf16", "offset"),
+    (128, 32, "bf16", "outliers"), (128, 64, "f16", "outliers"), (128, 128, "bf16", "offset"),
+    (64, 64, "f16", "offset"), (64, 32, "f16", "outliers"),
+])
+def test_prefill_factored_key_groups(kg, vg, dtype, stress):
+    """4-bit per-token affine keys in groups of 64 or 128 channels at head_dim
+    128 take the factored scores (codes as exact operands, per-group scales
+    applied to the sums, zero points as one more product).  Keys with x10
+    outlier channels, or with a large per-channel offset (big zero points whose
+    term cancels most of the code term), against the oracle: causal rows over
+    a ragged cache, two batches x two kv-heads x four query heads."""
+    B, H, G, T, n_q = 2, 2, 4, 1500, 40
+    over = dict(n_outlier_channels=6, outlier_scale=10.0) if stress == "outliers" else dict(k_bias_std=8.0)
+    w = synth.workload("affine4_g64", head_dim=128, seq_len=T, batch=B, n_kv_heads=H, n_q_heads=H * G,
+                       dtype=dtype, **over)
+    k, v, _ = synth.full(w, threads=8)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind="tok_affine", k_bits=4,
+                     k_group=kg, v_kind="tok_affine", v_bits=4, v_group=vg, in_dtype=dtype)
+    say("prefill factored scores", kg, vg, dtype, stress)
+    c, o = build_pair(pl, ol, k, v, dtype)
+    rng = np.random.default_rng([0, 701, kg, vg])
+    q = synth.cast(rng.standard_normal((B, H * G, n_q, 128), dtype=np.float32), dtype)
+    out = K.kvq_prefill_attention(pl, c, to_dev(q, dtype), causal=True)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = prefill_attention(o, q, dtype, causal=True)
+    err = attn_err(got, ref)
+    say(f"  error {err:.3e}")
+    assert np.all(np.isfinite(got)) and err <= TOL, err
