@@ -402,7 +402,7 @@ kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* c, const 
     const int64_t rows = (int64_t)L->batch * n_q_heads * n_q;
     if (rows > INT32_MAX || L->batch > 65535) return KVQ_ERR_UNSUPPORTED;
     const int64_t R = (int64_t)(n_q_heads / L->n_kv_heads) * n_q;
-    if ((int64_t)L->n_kv_heads * ((R + 255) / 256) > 65535) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)L->n_kv_heads * ((R + 127) / 128) > 65535) return KVQ_ERR_UNSUPPORTED;   // grid rows, 128-row blocks
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int D = L->head_dim;
     if (c->n_stored == 0) return hip_status(launch_zero_f32(out, (size_t)rows * D, s));
@@ -421,8 +421,9 @@ kvq_status kvq_prefill_attention(const kvq_layout* L, const kvq_cache* c, const 
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
     a.scale_log2 = scale * 1.4426950408889634f;
     int n_rb = 1;
-    prefill_plan(a.B, a.Hkv, a.Hq, n_q, a.T, &n_rb, &a.n_splits, &a.split_len);
+    prefill_plan(a.B, a.Hkv, a.Hq, n_q, a.T, prefill_factored(a), &n_rb, &a.n_splits, &a.split_len);
     if (a.n_splits > prefill_max_splits(a.B, a.Hkv, a.Hq, n_q, L->capacity)) return KVQ_ERR_WORKSPACE;
+    if ((int64_t)a.n_splits * a.Hkv * n_rb * a.B > (1 << 30)) return KVQ_ERR_UNSUPPORTED;   // workgroups of one launch
     a.ws_o = static_cast<float*>(ws);
     a.ws_ml = a.ws_o + (size_t)rows * a.n_splits * D;
     return hip_status(launch_prefill_attention(a, n_q, n_rb, causal, s));

@@ -140,7 +140,8 @@ hipError_t launch_decode_combine_f16(const uint16_t* ws_o, const float* ws_ml, f
                                      int ns, hipStream_t s);
 // Multi-query attention over the cache (DecodeArgs with T, splits and q as
 // [B][Hq][n_q][D]; out [B][Hq][n_q][D]).
-void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, int* n_rb, int* n_splits, int* split_len);
+bool prefill_factored(const DecodeArgs& a);
+void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, bool factored, int* n_rb, int* n_splits, int* split_len);
 int prefill_max_splits(int B, int Hkv, int Hq, int n_q, int T);
 hipError_t launch_prefill_attention(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s);
 // The fast decode: matrix-core kernels for 4-bit K (per-token affine,

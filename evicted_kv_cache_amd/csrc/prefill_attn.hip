@@ -40,8 +40,13 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPT = 64;          // tokens per tile
+constexpr int kXcds = 8;         // XCDs (L2 domains) of the device
 constexpr int kWaves = 8;        // waves per workgroup, 32 query rows each
 constexpr int kRows = 32 * kWaves;
+// Waves per workgroup of the factored-score kernel.  Four waves (two
+// workgroups of 128 rows per CU, with separate barriers) measured slower than
+// eight: each workgroup then unpacks every tile for half the rows.
+constexpr int kFactWaves = 8;
 constexpr int kPad = 8;          // halfs of padding per LDS row (bank spread)
 constexpr float kSlack = 8.0f;   // log2 headroom of the lazily moved softmax reference point
 
@@ -143,12 +148,16 @@ __device__ __forceinline__ void bload_codes(__amdgpu_buffer_rsrc_t r, uint32_t o
 // scales each group's sum by its token's s_g.  There is no key residual and
 // no second key product.
 template <int KK, int VK, int D, bool QX, bool C4, int FG>
-__global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
+__global__ __launch_bounds__((FG > 0 ? kFactWaves : kWaves) * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
     static_assert(!C4 || ((KK == KVQ_TOK_AFFINE || KK == KVQ_TOK_SYM4) && VK == KVQ_TOK_AFFINE),
                   "constant code widths: per-token layouts");
     static_assert(FG == 0 || (C4 && QX && KK == KVQ_TOK_AFFINE && D == 128 && FG <= 2),
                   "factored scores: 4-bit affine keys at head_dim 128, fp16/bf16 queries, 1 or 2 groups per row");
     constexpr bool kFact = FG > 0;
+    constexpr int NW = kFact ? kFactWaves : kWaves;      // waves per workgroup
+    constexpr int NT = NW * 64;
+    constexpr int RW = 32 * NW;                          // query rows per workgroup
     if constexpr (C4) {
         a.k_bits = 4;
         a.v_bits = 4;
@@ -156,9 +165,19 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     constexpr int NK = D / 16;               // K-steps of the score product
     constexpr int ND = D / 32;               // 32-row blocks of the output
     constexpr int C8 = D / 8;                // 8-channel chunks per row
-    const int split = blockIdx.x;
-    const int hk = blockIdx.y / n_rb, rb = blockIdx.y - hk * n_rb;
-    const int b = blockIdx.z;
+    // Workgroup x runs on XCD x % 8.  Work item p = (x % 8) * per_xcd + x / 8
+    // (split fastest, then row block, kv-head, batch) puts the splits of a row
+    // block, and the row blocks of a kv-head, on one XCD, where they share its
+    // L2 copy of the query rows and of the cache tiles; the grid is padded to
+    // a multiple of 8 and the padding exits.
+    const int per_xcd = (int)(gridDim.x / kXcds);
+    const int p = (int)(blockIdx.x % kXcds) * per_xcd + (int)(blockIdx.x / kXcds);
+    const int n_units = a.Hkv * n_rb;
+    if (p >= a.n_splits * n_units * a.B) return;
+    const int split = p % a.n_splits;
+    const int unit = p / a.n_splits;
+    const int b = unit / n_units;
+    const int hk = (unit - b * n_units) / n_rb, rb = unit - b * n_units - hk * n_rb;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int kh = lane >> 5, l32 = lane & 31;
     const int G = a.Hq / a.Hkv;
@@ -170,15 +189,18 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     // token-major) and the transposed value tile; after the last tile the
     // same space holds each wave's output block for a row-major write-out
     constexpr int kKeyHalfs = kPT * (D + kPad);
-    constexpr int kTileHalfs = 2 * kKeyHalfs + D * (kPT + kPad);
-    constexpr int kOutHalfs = kWaves * 32 * 33 * 2;          // [wave][32 rows][32 dims + pad] fp32
+    // factored: group scales [kPT] u32 and zero-point operands [kPT][2] uint4
+    // in place of the key residual
+    constexpr int kResHalfs = kFact ? 2 * kPT + kPT * 2 * 8 : kKeyHalfs;
+    constexpr int kTileHalfs = kKeyHalfs + kResHalfs + D * (kPT + kPad);
+    constexpr int kOutHalfs = NW * 32 * 33 * 2;              // [wave][32 rows][32 dims + pad] fp32
     __shared__ __align__(16) _Float16 lds[2 * kTileHalfs > kOutHalfs ? 2 * kTileHalfs : kOutHalfs];
     auto k_lds = [&](int buf) { return reinterpret_cast<_Float16 (*)[D + kPad]>(lds + buf * kTileHalfs); };
     auto kl_lds = [&](int buf) {
         return reinterpret_cast<_Float16 (*)[D + kPad]>(lds + buf * kTileHalfs + kKeyHalfs);
     };
     auto v_lds = [&](int buf) {
-        return reinterpret_cast<_Float16 (*)[kPT + kPad]>(lds + buf * kTileHalfs + 2 * kKeyHalfs);
+        return reinterpret_cast<_Float16 (*)[kPT + kPad]>(lds + buf * kTileHalfs + kKeyHalfs + kResHalfs);
     };
     // factored scores: the residual's space holds each token's group scales
     // (fp16 s_0 | s_1 << 16) and its zero-point operands ([token][group] 8 bf16)
@@ -188,7 +210,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     };
 
     // this lane's query row: fragments for every K-step
-    const int r = rb * kRows + wave * 32 + l32;
+    const int r = rb * RW + wave * 32 + l32;
     const bool row_ok = r < R;
     const int h = row_ok ? r / n_q : 0, i = row_ok ? r - (r / n_q) * n_q : 0;
     const int64_t grow = ((int64_t)b * a.Hq + hk * G + h) * n_q + i;     // global query row
@@ -284,23 +306,23 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     // t + 1 is unpacked into the other LDS buffer while tile t is computed,
     // and the codes and metadata of tile t + 2 are fetched into registers
     // behind it: one barrier per tile.
-    constexpr int kItems = (kPT * C8 + kWaves * 64 - 1) / (kWaves * 64);
+    constexpr int kItems = (kPT * C8 + NT - 1) / NT;
     dq::Pre8 pk[kItems], pv[kItems];
     // Per-token layouts put every item of a tile at a fixed byte offset from
     // the tile's first slot: each tile only rebuilds buffer resources (scalar
     // work) sized to its valid rows.
     constexpr bool kTokK = KK == KVQ_TOK_AFFINE || KK == KVQ_TOK_SYM4;
     constexpr bool kTokV = VK == KVQ_TOK_AFFINE;
-    // 4-bit affine keys and values at head_dim 128: a thread's two items are
-    // tokens 2p and 2p + 1 of one 8-channel chunk, whose transposed values
-    // sit in adjacent columns (one 32-bit LDS store per channel)
-    constexpr bool kPair = C4 && KK == KVQ_TOK_AFFINE && D == 128 && kItems == 2;
+    // 4-bit affine keys and values at head_dim 128: items 2p and 2p + 1 of a
+    // thread are tokens 2u and 2u + 1 of one 8-channel chunk, whose transposed
+    // values sit in adjacent columns (one 32-bit LDS store per channel)
+    constexpr bool kPair = C4 && KK == KVQ_TOK_AFFINE && D == 128 && kItems % 2 == 0 && kPT * C8 == kItems * NT;
     auto item_tc = [&](int j, int& t, int& c) {
         if constexpr (kPair) {
             c = tid % C8;
-            t = 2 * (tid / C8) + j;
+            t = 2 * (tid / C8 + (j >> 1) * (NT / C8)) + (j & 1);
         } else {
-            const int it = tid + j * kWaves * 64;
+            const int it = tid + j * NT;
             t = it / C8;
             c = it - t * C8;
         }
@@ -319,7 +341,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             const __amdgpu_buffer_rsrc_t rm = rsrc(static_cast<const uint8_t*>(a.k_meta) + slot0 * k_meta_b, nt * k_meta_b);
 #pragma unroll
             for (int j = 0; j < kItems; ++j) {
-                if (!kPair && tid + j * kWaves * 64 >= kPT * C8) break;
+                if (!kPair && tid + j * NT >= kPT * C8) break;
                 int t, c;
                 item_tc(j, t, c);
                 bload_codes(rk, (uint32_t)(t * k_row_b + c * kb), kb, pk[j]);
@@ -330,7 +352,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         } else {
 #pragma unroll
             for (int j = 0; j < kItems; ++j) {
-                const int it = tid + j * kWaves * 64;
+                const int it = tid + j * NT;
                 const int t = it / C8, c = it - t * C8;
                 if (it < kPT * C8 && tb + t < t_hi) dq::k_fetch8<KK>(a, bh, tb + t, c, pk[j]);
             }
@@ -340,7 +362,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
             const __amdgpu_buffer_rsrc_t rm = rsrc(static_cast<const uint8_t*>(a.v_meta) + slot0 * v_meta_b, nt * v_meta_b);
 #pragma unroll
             for (int j = 0; j < kItems; ++j) {
-                if (!kPair && tid + j * kWaves * 64 >= kPT * C8) break;
+                if (!kPair && tid + j * NT >= kPT * C8) break;
                 int t, c;
                 item_tc(j, t, c);
                 bload_codes(rv, (uint32_t)(t * v_row_b + c * a.v_bits), a.v_bits, pv[j]);
@@ -356,28 +378,31 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
         _Float16 (*vd)[kPT + kPad] = v_lds(buf);
         if constexpr (kPair) {
             // rows past the split were fetched as zero codes and metadata: zero keys and values
-            const int c = tid % C8, t0 = 2 * (tid / C8);
+#pragma unroll
+            for (int pp = 0; pp < kItems / 2; ++pp) {
+            const int c = tid % C8, t0 = 2 * (tid / C8 + pp * (NT / C8));
             float xv[2][8];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int jj2 = 0; jj2 < 2; ++jj2) {
+                const int j = 2 * pp + jj2;
                 float u[8];
                 if constexpr (kFact) {
                     // the code word under nibble masks: channels (0,4), (1,5)*16,
                     // (2,6), (3,7)*16 as fp16 subnormal pairs
                     const uint32_t w = pk[j].c0, w8 = w >> 8;
-                    *reinterpret_cast<uint4*>(&kd[t0 + j][8 * c]) =
+                    *reinterpret_cast<uint4*>(&kd[t0 + jj2][8 * c]) =
                         make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u);
                     constexpr int kCg = 128 / FG / 8;    // 8-channel chunks per group
                     if (c % kCg == 0) {
                         // first chunk of group g: the token's s_g, and z_g as an
                         // exact bf16 pair (zh keeps the top 8 significant bits)
                         const int g = c / kCg;
-                        reinterpret_cast<uint16_t*>(sc_lds(buf))[2 * (t0 + j) + g] = (uint16_t)(pk[j].meta & 0xFFFFu);
+                        reinterpret_cast<uint16_t*>(sc_lds(buf))[2 * (t0 + jj2) + g] = (uint16_t)(pk[j].meta & 0xFFFFu);
                         const float z = f16_bits_to_f32(pk[j].meta >> 16);
                         const uint32_t zhb = __float_as_uint(z) & 0xFFFF0000u;
                         const uint32_t zh = zhb >> 16, zl = __float_as_uint(z - __uint_as_float(zhb)) >> 16;
-                        zo_lds(buf)[t0 + j][g] = make_uint4(zh | (zh << 16), zh | (zl << 16), zl | (zl << 16), 0u);
-                        if (FG == 1) zo_lds(buf)[t0 + j][1] = make_uint4(0u, 0u, 0u, 0u);
+                        zo_lds(buf)[t0 + jj2][g] = make_uint4(zh | (zh << 16), zh | (zl << 16), zl | (zl << 16), 0u);
+                        if (FG == 1) zo_lds(buf)[t0 + jj2][1] = make_uint4(0u, 0u, 0u, 0u);
                     }
                 } else {
                     nib8(pk[j].c0, u);
@@ -389,13 +414,13 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
                         kh8[i] = (_Float16)x;
                         kl8[i] = (_Float16)(x - (float)kh8[i]);
                     }
-                    *reinterpret_cast<half8*>(&kd[t0 + j][8 * c]) = kh8;
-                    *reinterpret_cast<half8*>(&kld[t0 + j][8 * c]) = kl8;
+                    *reinterpret_cast<half8*>(&kd[t0 + jj2][8 * c]) = kh8;
+                    *reinterpret_cast<half8*>(&kld[t0 + jj2][8 * c]) = kl8;
                 }
                 nib8(pv[j].c0, u);
                 const float sv = f16_bits_to_f32(pv[j].meta & 0xFFFFu), zv = f16_bits_to_f32(pv[j].meta >> 16);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) xv[j][i] = fmaf(u[i], sv, zv);
+                for (int i = 0; i < 8; ++i) xv[jj2][i] = fmaf(u[i], sv, zv);
             }
             const int col = v_col(t0);                // even; token t0 + 1 is column col + 1
 #pragma unroll
@@ -404,11 +429,12 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
                 const h2 pr = {(_Float16)xv[0][jj], (_Float16)xv[1][jj]};
                 *reinterpret_cast<h2*>(&vd[8 * c + jj][vswz(8 * c + jj, col)]) = pr;
             }
+            }
             return;
         }
 #pragma unroll
         for (int j = 0; j < kItems; ++j) {
-            const int it = tid + j * kWaves * 64;
+            const int it = tid + j * NT;
             if (it >= kPT * C8) break;
             const int t = it / C8, c = it - t * C8;
             float xk[8] = {}, xv[8] = {};
@@ -580,7 +606,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
     const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
     float (*tr)[33] = reinterpret_cast<float (*)[33]>(lds) + wave * 32;      // [32 rows][32 dims + pad]
     const int wr = lane >> 1, wh = lane & 1;                                // row, 16-dim half it writes
-    const int r_w = rb * kRows + wave * 32 + wr;
+    const int r_w = rb * RW + wave * 32 + wr;
     int64_t grow_w = 0;
     if (r_w < R) {
         const int hw = r_w / n_q, iw = r_w - hw * n_q;
@@ -613,20 +639,22 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_attn_kernel(DecodeArgs a,
 
 template <int KK, int VK, bool QX, bool C4>
 hipError_t launch_prefill_kvq(const DecodeArgs& a, int n_q, int n_rb, int causal, hipStream_t s) {
-    dim3 grid((unsigned)a.n_splits, (unsigned)(a.Hkv * n_rb), (unsigned)a.B);
-    const dim3 blk(kWaves * 64);
+    const int64_t n_wg = (int64_t)a.n_splits * a.Hkv * n_rb * a.B;
+    const dim3 grid((unsigned)(((n_wg + kXcds - 1) / kXcds) * kXcds));
+    const dim3 blk(kWaves * 64), blk_f(kFactWaves * 64);
     switch (a.D) {
         case 32: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 32, QX, C4, 0>), grid, blk, 0, s, a, n_q, n_rb, causal); break;
         case 64: hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 64, QX, C4, 0>), grid, blk, 0, s, a, n_q, n_rb, causal); break;
         default:
             if constexpr (C4 && QX && KK == KVQ_TOK_AFFINE) {
-                // factored scores for key groups of 64 or 128 channels
+                // factored scores for key groups of 64 or 128 channels (the
+                // cases prefill_factored names)
                 if (a.k_group == 64) {
-                    hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4, 2>), grid, blk, 0, s, a, n_q, n_rb, causal);
+                    hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4, 2>), grid, blk_f, 0, s, a, n_q, n_rb, causal);
                     break;
                 }
                 if (a.k_group == 128) {
-                    hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4, 1>), grid, blk, 0, s, a, n_q, n_rb, causal);
+                    hipLaunchKernelGGL((prefill_attn_kernel<KK, VK, 128, QX, C4, 1>), grid, blk_f, 0, s, a, n_q, n_rb, causal);
                     break;
                 }
             }
@@ -676,11 +704,27 @@ int prefill_max_splits(int B, int Hkv, int Hq, int n_q, int T) {
     return (int)ns;
 }
 
-// Row blocks per kv-head and token splits (at most prefill_max_splits).
-void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, int* n_rb, int* n_splits, int* split_len) {
+// Whether a call takes the factored-score kernel (4-bit per-token affine keys
+// in groups of 64 or 128 and 4-bit affine values at head_dim 128, fp16 or
+// bf16 queries), which works on kFactWaves * 32 rows per workgroup.
+bool prefill_factored(const DecodeArgs& a) {
+    return a.D == 128 && a.k_kind == KVQ_TOK_AFFINE && a.k_bits == 4 && (a.k_group == 64 || a.k_group == 128) &&
+           a.v_kind == KVQ_TOK_AFFINE && a.v_bits == 4 && a.q_dtype != KVQ_F32;
+}
+
+// Row blocks per kv-head and token splits (at most prefill_max_splits).  The
+// plan aims at one round of workgroups: 256 of kWaves waves, or as many more
+// as the factored kernel's smaller workgroups allow.
+void prefill_plan(int B, int Hkv, int Hq, int n_q, int T, bool factored, int* n_rb, int* n_splits, int* split_len) {
     const int R = (Hq / Hkv) * n_q;
-    *n_rb = (R + kRows - 1) / kRows;
-    const int64_t ns = prefill_max_splits(B, Hkv, Hq, n_q, T);
+    const int rows = factored ? 32 * kFactWaves : kRows;
+    *n_rb = (R + rows - 1) / rows;
+    int64_t ns = prefill_max_splits(B, Hkv, Hq, n_q, T);
+    if (factored && kFactWaves < kWaves) {
+        const int64_t units = (int64_t)B * Hkv * *n_rb;
+        const int64_t want = (256 * (kWaves / kFactWaves) + units - 1) / units;
+        if (want < ns) ns = want;
+    }
     int len = (int)(((int64_t)T + ns - 1) / ns);
     len = ((len + kPT - 1) / kPT) * kPT;
     *split_len = len;
