@@ -220,23 +220,29 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
     float qc = 1.0f;                         // factor from score accumulators to base-2 logits
     auto prepare_query = [&]() {
         if constexpr (QX) {
-            // all of the row's loads first (16 bytes each, whatever the type), then the conversions
+            // All of the row's loads first (16 bytes each, whatever the
+            // type; a row past the group reads row 0 and is zeroed).  For
+            // finite fp16 and bf16 values |x| grows with the integer bits & 0x7FFF,
+            // so the row's largest magnitude is found on the bits.
             uint4 raw[NK];
+            const uint16_t* qrow = static_cast<const uint16_t*>(a.q) + (row_ok ? grow : 0) * D + kh * 8;
+#pragma unroll
+            for (int q = 0; q < NK; ++q) raw[q] = *reinterpret_cast<const uint4*>(qrow + q * 16);
+            uint32_t mbits = 0;
 #pragma unroll
             for (int q = 0; q < NK; ++q) {
-                raw[q] = make_uint4(0u, 0u, 0u, 0u);
-                if (row_ok) raw[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + grow * D + q * 16 + kh * 8);
-            }
-            const bool f16in = a.q_dtype == KVQ_F16;
-            auto elem = [&](uint32_t bits16) { return f16in ? f16_bits_to_f32(bits16) : bf16_bits_to_f32(bits16); };
-            float amax = 0.0f;
-#pragma unroll
-            for (int q = 0; q < NK; ++q) {
+                if (!row_ok) raw[q] = make_uint4(0u, 0u, 0u, 0u);
                 const uint32_t w[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    amax = fmaxf(amax, fmaxf(fabsf(elem(w[j] & 0xFFFFu)), fabsf(elem(w[j] >> 16))));
+                for (int j = 0; j < 4; ++j) mbits = max(mbits, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
             }
+            const bool f16in = a.q_dtype == KVQ_F16;
+            // both conversions, then a select: no branch per element
+            auto elem = [&](uint32_t b16) {
+                const float h = f16_bits_to_f32(b16), bf = bf16_bits_to_f32(b16);
+                return f16in ? h : bf;
+            };
+            float amax = elem(mbits);
             amax = fmaxf(amax, __shfl_xor(amax, 32));
             int ex = 0;
             if (amax > 0.0f) frexpf(amax, &ex);                  // amax in [2^(ex-1), 2^ex)
