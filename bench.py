@@ -237,6 +237,8 @@ def main():
                     help="untimed steps first (about 75 ms of decode: the clock has settled)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rows", default="ACDBE", help="extra rows to time (subset of ACDBE)")
+    ap.add_argument("--e-lengths", default="2048,32768",
+                    help="cache lengths of row E (comma-separated; one length gives its own counters)")
     ap.add_argument("--mode", default="full", choices=["full", "decode", "copy"],
                     help="decode: only the timed decode steps (for counter runs); "
                          "copy: a plain 2 GiB device copy (bandwidth probe / counter calibration)")
@@ -452,7 +454,7 @@ def main():
     if "E" in args.rows:
         we = synth.workload("affine4_g64")
         n_q = 128
-        for Te in (2048, 32768):
+        for Te in [int(x) for x in args.e_lengths.split(",")]:
             ke, ve, _ = synth.full(we, T=Te, batch=1, threads=max(1, min(16, os.cpu_count() or 1)))
             Le = K.Layout(**{**L.__dict__, "batch": 1, "capacity": Te})
             ce = K.Cache(Le)

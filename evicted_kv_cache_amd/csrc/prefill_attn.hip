@@ -338,7 +338,7 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
     const int k_meta_b = KK == KVQ_TOK_SYM4 ? (D / 32) * 2 : (kTokK ? (D / a.k_group) * 4 : 0);
     const int v_row_b = D * a.v_bits / 8;
     const int v_meta_b = kTokV ? (D / a.v_group) * 4 : 0;
-    auto fetch = [&](int tb) {
+    auto fetch = [&](int tb, dq::Pre8 (&pkd)[kItems], dq::Pre8 (&pvd)[kItems]) {
         // rows of the tile inside the split (0 past its end: every load then reads zero)
         const uint32_t nt = (uint32_t)__builtin_amdgcn_readfirstlane(max(0, min(kPT, t_hi - tb)));
         const int64_t slot0 = bh * a.cap + tb;
@@ -350,8 +350,8 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 if (!kPair && tid + j * NT >= kPT * C8) break;
                 int t, c;
                 item_tc(j, t, c);
-                bload_codes(rk, (uint32_t)(t * k_row_b + c * kb), kb, pk[j]);
-                pk[j].meta = KK == KVQ_TOK_SYM4
+                bload_codes(rk, (uint32_t)(t * k_row_b + c * kb), kb, pkd[j]);
+                pkd[j].meta = KK == KVQ_TOK_SYM4
                                  ? __builtin_amdgcn_raw_buffer_load_b16(rm, (t * (D / 32) + (8 * c) / 32) * 2, 0, 0)
                                  : __builtin_amdgcn_raw_buffer_load_b32(rm, (t * (D / a.k_group) + (8 * c) / a.k_group) * 4, 0, 0);
             }
@@ -360,7 +360,7 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
             for (int j = 0; j < kItems; ++j) {
                 const int it = tid + j * NT;
                 const int t = it / C8, c = it - t * C8;
-                if (it < kPT * C8 && tb + t < t_hi) dq::k_fetch8<KK>(a, bh, tb + t, c, pk[j]);
+                if (it < kPT * C8 && tb + t < t_hi) dq::k_fetch8<KK>(a, bh, tb + t, c, pkd[j]);
             }
         }
         if constexpr (kTokV) {
@@ -371,13 +371,13 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 if (!kPair && tid + j * NT >= kPT * C8) break;
                 int t, c;
                 item_tc(j, t, c);
-                bload_codes(rv, (uint32_t)(t * v_row_b + c * a.v_bits), a.v_bits, pv[j]);
-                pv[j].meta = __builtin_amdgcn_raw_buffer_load_b32(rm, (t * (D / a.v_group) + (8 * c) / a.v_group) * 4, 0, 0);
+                bload_codes(rv, (uint32_t)(t * v_row_b + c * a.v_bits), a.v_bits, pvd[j]);
+                pvd[j].meta = __builtin_amdgcn_raw_buffer_load_b32(rm, (t * (D / a.v_group) + (8 * c) / a.v_group) * 4, 0, 0);
             }
         }
     };
     // unpack the fetched tile at tb into buffer buf; rows past the split are zero
-    auto unpack = [&](int tb, int buf) {
+    auto unpack = [&](int tb, int buf, const dq::Pre8 (&pks)[kItems], const dq::Pre8 (&pvs)[kItems]) {
         const int nt = min(kPT, t_hi - tb);
         _Float16 (*kd)[D + kPad] = k_lds(buf);
         _Float16 (*kld)[D + kPad] = kl_lds(buf);
@@ -387,7 +387,6 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
 #pragma unroll
             for (int pp = 0; pp < kItems / 2; ++pp) {
             const int c = tid % C8, t0 = 2 * (tid / C8 + pp * (NT / C8));
-            float xv[2][8];
 #pragma unroll
             for (int jj2 = 0; jj2 < 2; ++jj2) {
                 const int j = 2 * pp + jj2;
@@ -395,7 +394,7 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 if constexpr (kFact) {
                     // the code word under nibble masks: channels (0,4), (1,5)*16,
                     // (2,6), (3,7)*16 as fp16 subnormal pairs
-                    const uint32_t w = pk[j].c0, w8 = w >> 8;
+                    const uint32_t w = pks[j].c0, w8 = w >> 8;
                     *reinterpret_cast<uint4*>(&kd[t0 + jj2][8 * c]) =
                         make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u);
                     constexpr int kCg = 128 / FG / 8;    // 8-channel chunks per group
@@ -403,16 +402,16 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                         // first chunk of group g: the token's s_g, and z_g as an
                         // exact bf16 pair (zh keeps the top 8 significant bits)
                         const int g = c / kCg;
-                        reinterpret_cast<uint16_t*>(sc_lds(buf))[2 * (t0 + jj2) + g] = (uint16_t)(pk[j].meta & 0xFFFFu);
-                        const float z = f16_bits_to_f32(pk[j].meta >> 16);
+                        reinterpret_cast<uint16_t*>(sc_lds(buf))[2 * (t0 + jj2) + g] = (uint16_t)(pks[j].meta & 0xFFFFu);
+                        const float z = f16_bits_to_f32(pks[j].meta >> 16);
                         const uint32_t zhb = __float_as_uint(z) & 0xFFFF0000u;
                         const uint32_t zh = zhb >> 16, zl = __float_as_uint(z - __uint_as_float(zhb)) >> 16;
                         zo_lds(buf)[t0 + jj2][g] = make_uint4(zh | (zh << 16), zh | (zl << 16), zl | (zl << 16), 0u);
                         if (FG == 1) zo_lds(buf)[t0 + jj2][1] = make_uint4(0u, 0u, 0u, 0u);
                     }
                 } else {
-                    nib8(pk[j].c0, u);
-                    const float sk = f16_bits_to_f32(pk[j].meta & 0xFFFFu), zk = f16_bits_to_f32(pk[j].meta >> 16);
+                    nib8(pks[j].c0, u);
+                    const float sk = f16_bits_to_f32(pks[j].meta & 0xFFFFu), zk = f16_bits_to_f32(pks[j].meta >> 16);
                     half8 kh8, kl8;
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
@@ -423,17 +422,27 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                     *reinterpret_cast<half8*>(&kd[t0 + jj2][8 * c]) = kh8;
                     *reinterpret_cast<half8*>(&kld[t0 + jj2][8 * c]) = kl8;
                 }
-                nib8(pv[j].c0, u);
-                const float sv = f16_bits_to_f32(pv[j].meta & 0xFFFFu), zv = f16_bits_to_f32(pv[j].meta >> 16);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) xv[jj2][i] = fmaf(u[i], sv, zv);
             }
+            // Values as (token t0, token t0 + 1) fp16 pairs, straight from the
+            // code bytes: byte i of both code words gives channels 2i (low
+            // nibbles) and 2i + 1 (high nibbles); 0x6400 | u is the fp16
+            // 1024 + u, so subtracting 1024 leaves u exactly, and one packed
+            // fp16 fma rounds u s + z once.
+            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+            const uint32_t w0 = pvs[2 * pp].c0, w1 = pvs[2 * pp + 1].c0;
+            const uint32_t m0 = pvs[2 * pp].meta, m1 = pvs[2 * pp + 1].meta;
+            const h2 s2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x05040100u));
+            const h2 z2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x07060302u));
+            const h2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
             const int col = v_col(t0);                // even; token t0 + 1 is column col + 1
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                const h2 pr = {(_Float16)xv[0][jj], (_Float16)xv[1][jj]};
-                *reinterpret_cast<h2*>(&vd[8 * c + jj][vswz(8 * c + jj, col)]) = pr;
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t x = __builtin_amdgcn_perm(w1, w0, (uint32_t)i | 0x0C000C00u | ((uint32_t)(4 + i) << 16));
+                const uint32_t e = (x & 0x000F000Fu) | 0x64006400u, od = ((x >> 4) & 0x000F000Fu) | 0x64006400u;
+                const h2 ve = __builtin_elementwise_fma(__builtin_bit_cast(h2, e) + m1024, s2, z2);
+                const h2 vo = __builtin_elementwise_fma(__builtin_bit_cast(h2, od) + m1024, s2, z2);
+                *reinterpret_cast<h2*>(&vd[8 * c + 2 * i][vswz(8 * c + 2 * i, col)]) = ve;
+                *reinterpret_cast<h2*>(&vd[8 * c + 2 * i + 1][vswz(8 * c + 2 * i + 1, col)]) = vo;
             }
             }
             return;
@@ -447,11 +456,11 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
             if (kTokK && kTokV) {
                 // rows past the split were fetched as zero codes and zero
                 // metadata, which dequantize to zero: no branch
-                dq::k_finish8<KK>(a, bh, tb + t, c, pk[j], xk);
-                dq::v_finish8<VK>(a, bh, tb + t, c, pv[j], xv);
+                dq::k_finish8<KK>(a, bh, tb + t, c, pks[j], xk);
+                dq::v_finish8<VK>(a, bh, tb + t, c, pvs[j], xv);
             } else if (t < nt) {
-                dq::k_finish8<KK>(a, bh, tb + t, c, pk[j], xk);
-                dq::v_finish8<VK>(a, bh, tb + t, c, pv[j], xv);
+                dq::k_finish8<KK>(a, bh, tb + t, c, pks[j], xk);
+                dq::v_finish8<VK>(a, bh, tb + t, c, pvs[j], xv);
             }
             half8 kh8, kl8;
             split_half8(xk, kh8, kl8);
@@ -462,25 +471,24 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
             for (int jj = 0; jj < 8; ++jj) vd[8 * c + jj][vswz(8 * c + jj, col)] = (_Float16)xv[jj];
         }
     };
-    if (t_lo < t_hi) fetch(t_lo);
-    prepare_query();
-    if (t_lo < t_hi) {
-        unpack(t_lo, 0);
-        if (t_lo + kPT < t_hi) fetch(t_lo + kPT);
+    // the first two tiles' codes are in flight while the query is prepared
+    {
+        dq::Pre8 pk0[kItems], pv0[kItems];
+        if (t_lo < t_hi) fetch(t_lo, pk0, pv0);
+        if (t_lo + kPT < t_hi) fetch(t_lo + kPT, pk, pv);
+        prepare_query();
+        if (t_lo < t_hi) unpack(t_lo, 0, pk0, pv0);
     }
     __syncthreads();
 
     const int lim_min = __builtin_amdgcn_readfirstlane(wave_min(row_ok ? lim : T - 1));
-    int buf = 0;
-    for (int t0 = t_lo; t0 < t_hi; t0 += kPT, buf ^= 1) {
-        _Float16 (*kd)[D + kPad] = k_lds(buf);
-        _Float16 (*kld)[D + kPad] = kl_lds(buf);
-        _Float16 (*vd)[kPT + kPad] = v_lds(buf);
-        // S^T for this wave's 32 rows: two 32-token blocks
-        floatx16 s[2];
+    // S^T for this wave's 32 rows over the tile in buffer bf: two 32-token blocks
+    floatx16 s[2];
+    auto scores = [&](int bf) {
+        _Float16 (*kd)[D + kPad] = k_lds(bf);
         if constexpr (kFact) {
-            const uint32_t* scl = sc_lds(buf);
-            uint4 (*zo)[2] = zo_lds(buf);
+            const uint32_t* scl = sc_lds(bf);
+            uint4 (*zo)[2] = zo_lds(bf);
 #pragma unroll
             for (int blk = 0; blk < 2; ++blk) {
                 const uint4 za = zo[blk * 32 + l32][kh];
@@ -512,31 +520,39 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 asm volatile("" : "+v"(s[blk]));
                 __builtin_amdgcn_sched_barrier(0);
             }
-        } else
+        } else {
+            _Float16 (*kld)[D + kPad] = kl_lds(bf);
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            s[blk] = floatx16{};
+            for (int blk = 0; blk < 2; ++blk) {
+                s[blk] = floatx16{};
 #pragma unroll
-            for (int q = 0; q < NK; ++q) {
-                const half8 ka = *reinterpret_cast<const half8*>(&kd[blk * 32 + l32][q * 16 + kh * 8]);
-                const half8 kl = *reinterpret_cast<const half8*>(&kld[blk * 32 + l32][q * 16 + kh * 8]);
-                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, qf[q], s[blk], 0, 0, 0);
-                if constexpr (!QX) s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qfl[q], s[blk], 0, 0, 0);
-                s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[q], s[blk], 0, 0, 0);
+                for (int q = 0; q < NK; ++q) {
+                    const half8 ka = *reinterpret_cast<const half8*>(&kd[blk * 32 + l32][q * 16 + kh * 8]);
+                    const half8 kl = *reinterpret_cast<const half8*>(&kld[blk * 32 + l32][q * 16 + kh * 8]);
+                    s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kl, qf[q], s[blk], 0, 0, 0);
+                    if constexpr (!QX) s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qfl[q], s[blk], 0, 0, 0);
+                    s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka, qf[q], s[blk], 0, 0, 0);
+                }
             }
         }
-        // the next tile goes into the other buffer while the products run
-        // (without a branch, so that the score products and the unpacking
-        // are one block the scheduler can interleave; past the split's end
-        // the unpack writes zero rows and the fetch reads zeros)
+    };
+    // the tile after t0 goes into buffer nb (without a branch for per-token
+    // layouts, so that the score products and the unpacking are one block the
+    // scheduler can interleave; past the split's end the unpack writes zero
+    // rows and the fetch reads zeros)
+    auto next_tile = [&](int t0, int nb) {
         if constexpr (kFact) __builtin_amdgcn_sched_barrier(0);
         if constexpr (kTokK && kTokV) {
-            unpack(t0 + kPT, buf ^ 1);
-            fetch(t0 + 2 * kPT);
+            unpack(t0 + kPT, nb, pk, pv);
+            fetch(t0 + 2 * kPT, pk, pv);
         } else if (t0 + kPT < t_hi) {
-            unpack(t0 + kPT, buf ^ 1);
-            if (t0 + 2 * kPT < t_hi) fetch(t0 + 2 * kPT);
+            unpack(t0 + kPT, nb, pk, pv);
+            if (t0 + 2 * kPT < t_hi) fetch(t0 + 2 * kPT, pk, pv);
         }
+    };
+    // softmax of the scores s of the tile at t0, and its values (buffer bf)
+    auto finish = [&](int t0, int bf) {
+        _Float16 (*vd)[kPT + kPad] = v_lds(bf);
         // mask (past the split or the row's last visible slot) -- only tiles
         // that reach either boundary for some row of the wave need it
         // (the row factor qc > 0 is applied to the max and inside the exponent)
@@ -601,7 +617,13 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 const half8 va = *reinterpret_cast<const half8*>(&vd[d * 32 + l32][vswz(d * 32 + l32, 16 * st + 8 * kh)]);
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[st], o[d], 0, 0, 0);
             }
-        __syncthreads();                     // this buffer is read, the other one written
+    };
+    int buf = 0;
+    for (int t0 = t_lo; t0 < t_hi; t0 += kPT, buf ^= 1) {
+        scores(buf);
+        next_tile(t0, buf ^ 1);
+        finish(t0, buf);
+        __syncthreads();                 // this buffer is read, the other one written
     }
 
     // partials of the split: o[dim] / l as fp16 and (m, l) of each row in
