@@ -628,8 +628,10 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
 
     // partials of the split: o[dim] / l as fp16 and (m, l) of each row in
     // fp32 (a row that saw no slot here has l = 0 and writes zeros).  The
-    // accumulators hold O^T (lane = row); each 32-dim block goes through LDS
-    // so that rows are written as contiguous 64-byte runs.
+    // accumulators hold O^T (lane = row); each 32-dim block goes through the
+    // wave's own LDS rows so that rows are written as contiguous 64-byte runs
+    // (only the wave's lanes exchange data there: wave-level syncs; the
+    // loop's last barrier has freed the tile buffers).
     const int ns = a.n_splits;
     const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
     float (*tr)[33] = reinterpret_cast<float (*)[33]>(lds) + wave * 32;      // [32 rows][32 dims + pad]
@@ -643,10 +645,10 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
     uint16_t* ws_h = reinterpret_cast<uint16_t*>(a.ws_o);
 #pragma unroll
     for (int d = 0; d < ND; ++d) {
-        if (d > 0) __syncthreads();          // previous block's reads are done (the loop ended in one)
+        if (d > 0) wave_lds_sync();          // the previous block's reads are done
 #pragma unroll
         for (int v = 0; v < 16; ++v) tr[l32][acc_row(v, kh)] = o[d][v] * inv_l;
-        __syncthreads();
+        wave_lds_sync();
         if (r_w < R) {
             uint32_t hw2[8];
 #pragma unroll
