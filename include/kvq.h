@@ -264,11 +264,15 @@ kvq_status kvq_decode_attention_noalloc(const kvq_layout* layout, const kvq_cach
  *   q    device [B][Hq][n_q][D] (q_dtype), before any position rotation
  *   out  device [B][Hq][n_q][D] fp32
  *   ws   at least kvq_prefill_workspace_bytes(layout, Hq, n_q) bytes
- * Keys and values are dequantized to fp16 per 64-token tile for the matrix
- * cores; scores, softmax and accumulation are fp32.  Errors as
- * kvq_decode_attention, plus KVQ_ERR_INVALID_ARG for n_q < 1, causal not
- * 0/1 or a causal chunk longer than the cache; KVQ_ERR_UNSUPPORTED for
- * B > 65535 or more than 65535 row blocks of 256 rows.                      */
+ * The products run on the matrix cores per 64-token tile: 4-bit per-token
+ * affine keys in groups of 64 or 128 channels (fp16 or bf16 queries) enter
+ * as their codes with the group scales and zero points applied to the sums;
+ * other keys are unpacked to an fp16 pair (rounded value and residual);
+ * values and probabilities enter as fp16; scores, softmax and accumulation
+ * are fp32.  Errors as kvq_decode_attention, plus KVQ_ERR_INVALID_ARG for
+ * n_q < 1, causal not 0/1 or a causal chunk longer than the cache;
+ * KVQ_ERR_UNSUPPORTED for B > 65535, Hkv * ceil(Hq / Hkv * n_q / 128) >
+ * 65535, or more than 2^30 workgroups in one launch.                        */
 size_t kvq_prefill_workspace_bytes(const kvq_layout* layout, int32_t n_q_heads, int32_t n_q);
 kvq_status kvq_prefill_attention(const kvq_layout* layout, const kvq_cache* cache, const void* q,
                                  int32_t q_dtype, int32_t n_q_heads, int32_t n_q, float sm_scale,

@@ -378,6 +378,9 @@ def test_prefill_attention_validation_without_gpu():
     assert call(q=MIS) == K.KVQ_ERR_ALIGNMENT
     assert call(Hq=30) == K.KVQ_ERR_INVALID_ARG
     assert call(Hq=80) == K.KVQ_ERR_UNSUPPORTED                 # more than 8 query heads per kv-head
+    # 8 kv-heads x ceil(4 * 262144 / 128) = 65536 row blocks of 128 rows
+    assert call(n_q=262144) == K.KVQ_ERR_UNSUPPORTED
+    assert call(n_q=262112, ws_bytes=0) == K.KVQ_ERR_WORKSPACE   # 65528 row blocks: past the limit check
 
 
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
