@@ -151,3 +151,31 @@ def test_prefill_factored_key_groups(kg, vg, dtype, stress):
     err = attn_err(got, ref)
     say(f"  error {err:.3e}")
     assert np.all(np.isfinite(got)) and err <= TOL, err
+
+
+@pytest.mark.parametrize("T,kg,dtype", [(1, 64, "bf16"), (63, 128, "f16"), (65, 64, "f16"), (200, 128, "bf16")])
+def test_prefill_factored_edges(T, kg, dtype):
+    """Factored scores on short caches (one slot, one partial tile, a tile
+    plus one slot) with some all-zero query rows (their logits are all zero:
+    the output is the mean of the visible values), causal and not."""
+    B, H, G, n_q = 1, 2, 4, 1 if T == 1 else min(T, 24)
+    w = synth.workload("affine4_g64", head_dim=128, seq_len=T, batch=B, n_kv_heads=H, n_q_heads=H * G,
+                       dtype=dtype, n_outlier_channels=6, outlier_scale=10.0)
+    k, v, _ = synth.full(w, threads=8)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind="tok_affine", k_bits=4,
+                     k_group=kg, v_kind="tok_affine", v_bits=4, v_group=64, in_dtype=dtype)
+    say("prefill factored edges", T, kg, dtype)
+    c, o = build_pair(pl, ol, k, v, dtype)
+    rng = np.random.default_rng([0, 702, T, kg])
+    qf = rng.standard_normal((B, H * G, n_q, 128), dtype=np.float32)
+    qf[:, 1] = 0.0                        # a whole query head of zero rows
+    qf[:, 4:, n_q // 2] = 0.0             # and one row in each later head
+    q = synth.cast(qf, dtype)
+    for causal in (False, True):
+        out = K.kvq_prefill_attention(pl, c, to_dev(q, dtype), causal=causal)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ref = prefill_attention(o, q, dtype, causal=causal)
+        err = attn_err(got, ref)
+        say(f"  causal={causal} error {err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= TOL, err
