@@ -101,6 +101,39 @@ __device__ __forceinline__ float q_elem(uint32_t bits16) {
 template <bool B>
 struct Flag { static constexpr bool value = B; };
 
+// Cross-lane sums without LDS (gfx950 lane swaps).  swap32_sum(a, b): lanes
+// 0..31 get a[l] + a[l + 32], lanes 32..63 get b[l - 32] + b[l].
+// swap16_sum(a, b): lanes of even 16-lane rows get a[l] + a[l + 16], lanes
+// of odd rows b[l - 16] + b[l].
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Maximum and sum over each 16-lane row, left in every lane of the row: DPP
+// butterflies (quad_perm [1,0,3,2], [2,3,0,1], half-row mirror, row mirror).
+__device__ __forceinline__ float dpp_f(float x, int ctrl) {
+    switch (ctrl) {
+        case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    }
+}
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x = fmaxf(x, dpp_f(x, c));
+    return x;
+}
+__device__ __forceinline__ float row16_sum(float x) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x += dpp_f(x, c);
+    return x;
+}
+
 // The four code-word nibble masks as the B operand of one 32-channel MFMA:
 // fp16 slots (c0, c4, c1, c5, c2, c6, c3, c7) of the word's eight channels,
 // odd channels 16x (their query slots carry 1/16).
@@ -350,8 +383,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
             float smax = 0.0f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) smax = fmaxf(smax, f16lo(mm[i]));
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) smax = fmaxf(smax, __shfl_xor(smax, off));
+            smax = row16_max(smax);
             int es = 0;
             frexpf(smax, &es);                    // |q s| < 2^(eq + es)
             const int E = 15 - eq - es;
@@ -370,8 +402,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
                                           pack_f16(hv[3], hv[7])};
             abuf[wave][1][hh][ci] = u32x4{pack_f16(lv[0], lv[4]), pack_f16(lv[1], lv[5]), pack_f16(lv[2], lv[6]),
                                           pack_f16(lv[3], lv[7])};
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) qzp += __shfl_xor(qzp, off);   // q . z of head hh
+            qzp = row16_sum(qzp);                 // q . z of head hh
             float qz[kGQ];
 #pragma unroll
             for (int h = 0; h < kGQ; ++h)
@@ -485,12 +516,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
             if constexpr (KF == kKKivi) {
                 xh = r == 0 ? y[p][0] : (r == 1 ? y[p][1] : (r == 2 ? y[p][2] : y[p][3]));   // head r
             } else {
-                // sum the quarters: rows r and r ^ 2 first (keeping the heads of
-                // this row pair), then r and r ^ 1 (keeping head r)
-                const bool hi = (r >> 1) != 0, odd = (r & 1) != 0;
-                const float z0 = (hi ? y[p][2] : y[p][0]) + __shfl_xor(hi ? y[p][0] : y[p][2], 32);
-                const float z1 = (hi ? y[p][3] : y[p][1]) + __shfl_xor(hi ? y[p][1] : y[p][3], 32);
-                xh = (odd ? z1 : z0) + __shfl_xor(odd ? z0 : z1, 16);
+                // sum the quarters: rows r and r ^ 2 first (keeping heads r & 1
+                // and (r & 1) + 2 of this row pair), then r and r ^ 1 (keeping head r)
+                const float z0 = swap32_sum(y[p][0], y[p][2]);
+                const float z1 = swap32_sum(y[p][1], y[p][3]);
+                xh = swap16_sum(z0, z1);
             }
             const float xl = xh * kCx;
             if constexpr (kTail) xs[p] = (tb + n + 16 * p < t_hi) ? xl : -INFINITY;
@@ -501,8 +531,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
         const bool grow = (xs[0] > m_lane) || (xs[1] > m_lane);
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             float mt = fmaxf(xs[0], xs[1]);
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
+            mt = row16_max(mt);
             const float m_new = fmaxf(m_lane, mt);
             const float alpha = __builtin_amdgcn_exp2f(m_lane - m_new);
             m_lane = m_new;
@@ -524,8 +553,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
 #pragma unroll
         for (int g = 0; g < NVG; ++g) sl = fmaxf(sl, fmaxf(f16lo(L.vm[0][g]), f16lo(L.vm[1][g])));
         if (__builtin_amdgcn_ballot_w64(sl > vsmax) != 0) {
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) sl = fmaxf(sl, __shfl_xor(sl, off));
+            sl = row16_max(sl);
             vsmax = fmaxf(vsmax, sl);
             int e;
             frexpf(vsmax, &e);                        // vsmax in [2^(e-1), 2^e)
