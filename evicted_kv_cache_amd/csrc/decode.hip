@@ -27,16 +27,8 @@ constexpr int kTile = 64;       // tokens per tile
 constexpr int kMaxGroup = 8;    // query heads per kv-head
 constexpr int kMaxD = 128;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
-    return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-    return v;
-}
+__device__ __forceinline__ float wave_max(float v) { return wave64_max(v); }
+__device__ __forceinline__ float wave_sum(float v) { return wave64_sum(v); }
 
 // Generic split-T decode for every layout (D <= 128, up to 8 query heads
 // per kv-head).  Per 64-token tile the block dequantizes K and V into LDS as
@@ -290,9 +282,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, 
     float mloc = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kCombineMaxSplits / 128; ++k) mloc = fmaxf(mloc, mlv[k].x);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 1)); mloc = fmaxf(mloc, __shfl_xor(mloc, 2));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 4)); mloc = fmaxf(mloc, __shfl_xor(mloc, 8));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16)); mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = wave64_max(mloc);
     if ((d & 63) == 0) red[0][d >> 6] = mloc;
     __syncthreads();
     const float M = fmaxf(red[0][0], red[0][1]);
@@ -306,8 +296,7 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(const float* ws_o, 
             dloc = fmaf(w, mlv[k].y, dloc);
         }
     }
-    dloc += __shfl_xor(dloc, 1); dloc += __shfl_xor(dloc, 2); dloc += __shfl_xor(dloc, 4);
-    dloc += __shfl_xor(dloc, 8); dloc += __shfl_xor(dloc, 16); dloc += __shfl_xor(dloc, 32);
+    dloc = wave64_sum(dloc);
     if ((d & 63) == 0) red[1][d >> 6] = dloc;
     if (d >= ns && d < kPre) w_s[d] = 0.0f;    // the padding of the prefetch
     __syncthreads();
@@ -355,9 +344,7 @@ __global__ __launch_bounds__(128) void combine_f16_kernel(const uint16_t* ws_o, 
     float mloc = -INFINITY;
 #pragma unroll
     for (int k = 0; k < kCombineMaxSplits / 128; ++k) mloc = fmaxf(mloc, mlv[k].x);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 1)); mloc = fmaxf(mloc, __shfl_xor(mloc, 2));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 4)); mloc = fmaxf(mloc, __shfl_xor(mloc, 8));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16)); mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = wave64_max(mloc);
     if ((t & 63) == 0) red[0][t >> 6] = mloc;
     __syncthreads();
     const float M = fmaxf(red[0][0], red[0][1]);
@@ -371,8 +358,7 @@ __global__ __launch_bounds__(128) void combine_f16_kernel(const uint16_t* ws_o, 
             dloc += wl;
         }
     }
-    dloc += __shfl_xor(dloc, 1); dloc += __shfl_xor(dloc, 2); dloc += __shfl_xor(dloc, 4);
-    dloc += __shfl_xor(dloc, 8); dloc += __shfl_xor(dloc, 16); dloc += __shfl_xor(dloc, 32);
+    dloc = wave64_sum(dloc);
     if ((t & 63) == 0) red[1][t >> 6] = dloc;
     __syncthreads();
     const float den = red[1][0] + red[1][1];

@@ -101,38 +101,6 @@ __device__ __forceinline__ float q_elem(uint32_t bits16) {
 template <bool B>
 struct Flag { static constexpr bool value = B; };
 
-// Cross-lane sums without LDS (gfx950 lane swaps).  swap32_sum(a, b): lanes
-// 0..31 get a[l] + a[l + 32], lanes 32..63 get b[l - 32] + b[l].
-// swap16_sum(a, b): lanes of even 16-lane rows get a[l] + a[l + 16], lanes
-// of odd rows b[l - 16] + b[l].
-__device__ __forceinline__ float swap32_sum(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-__device__ __forceinline__ float swap16_sum(float a, float b) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-// Maximum and sum over each 16-lane row, left in every lane of the row: DPP
-// butterflies (quad_perm [1,0,3,2], [2,3,0,1], half-row mirror, row mirror).
-__device__ __forceinline__ float dpp_f(float x, int ctrl) {
-    switch (ctrl) {
-        case 0: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
-        case 1: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
-        case 2: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
-        default: return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
-    }
-}
-__device__ __forceinline__ float row16_max(float x) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x = fmaxf(x, dpp_f(x, c));
-    return x;
-}
-__device__ __forceinline__ float row16_sum(float x) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) x += dpp_f(x, c);
-    return x;
-}
 
 // The four code-word nibble masks as the B operand of one 32-channel MFMA:
 // fp16 slots (c0, c4, c1, c5, c2, c6, c3, c7) of the word's eight channels,

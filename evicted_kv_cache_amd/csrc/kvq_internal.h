@@ -64,6 +64,77 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// ---------------------------------------------------------------- cross-lane
+// Exchanges and reductions within a wave without going through LDS: DPP row
+// operations for lane distances up to 8 (inside 16-lane rows) and the gfx950
+// lane swaps across rows (v_permlane16_swap: odd rows of the first operand
+// with even rows of the second; v_permlane32_swap: upper half of the first
+// with the lower half of the second).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
+}
+// The 32-bit value of lane l ^ M, M in {1, 2, 4, 8, 16, 32}.
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x) {
+    const int lane = threadIdx.x & 63;
+    if constexpr (M == 1) {
+        return dpp_u32<0xB1>(x);                 // quad_perm [1, 0, 3, 2]
+    } else if constexpr (M == 2) {
+        return dpp_u32<0x4E>(x);                 // quad_perm [2, 3, 0, 1]
+    } else if constexpr (M == 4) {
+        const uint32_t dn = dpp_u32<0x124>(x);   // row_ror:4  -> lane l - 4 (mod 16)
+        const uint32_t up = dpp_u32<0x12C>(x);   // row_ror:12 -> lane l + 4 (mod 16)
+        return (lane & 4) ? dn : up;
+    } else if constexpr (M == 8) {
+        return dpp_u32<0x128>(x);                // row_ror:8
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane & 16) ? r[0] : r[1];
+    } else {
+        static_assert(M == 32, "lane distance");
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane & 32) ? r[0] : r[1];
+    }
+}
+template <int M>
+__device__ __forceinline__ float lane_xor(float v) { return __uint_as_float(lane_xor_u32<M>(__float_as_uint(v))); }
+
+// op over each 16-lane row (Wide = false) or the whole wave (Wide = true),
+// left in every lane.  Each step combines the same two partial values in
+// every lane of a pair, so all lanes hold the identical result.
+template <bool Wide, typename T, typename Op>
+__device__ __forceinline__ T lane_reduce(T v, Op op) {
+    auto u = [](T x) { return __builtin_bit_cast(uint32_t, x); };
+    auto f = [](uint32_t x) { return __builtin_bit_cast(T, x); };
+    v = op(v, f(dpp_u32<0xB1>(u(v))));
+    v = op(v, f(dpp_u32<0x4E>(u(v))));
+    v = op(v, f(dpp_u32<0x141>(u(v))));          // row_half_mirror
+    v = op(v, f(dpp_u32<0x140>(u(v))));          // row_mirror
+    if constexpr (Wide) {
+        const auto r16 = __builtin_amdgcn_permlane16_swap(u(v), u(v), false, false);
+        v = op(f(r16[0]), f(r16[1]));
+        const auto r32 = __builtin_amdgcn_permlane32_swap(u(v), u(v), false, false);
+        v = op(f(r32[0]), f(r32[1]));
+    }
+    return v;
+}
+__device__ __forceinline__ float row16_max(float v) { return lane_reduce<false>(v, [](float a, float b) { return fmaxf(a, b); }); }
+__device__ __forceinline__ float row16_sum(float v) { return lane_reduce<false>(v, [](float a, float b) { return a + b; }); }
+__device__ __forceinline__ float wave64_max(float v) { return lane_reduce<true>(v, [](float a, float b) { return fmaxf(a, b); }); }
+__device__ __forceinline__ float wave64_sum(float v) { return lane_reduce<true>(v, [](float a, float b) { return a + b; }); }
+// x + (x of lane l ^ 32), and the same for 16 with a pair of operands:
+// swap32_sum(a, b): lanes 0..31 get a[l] + a[l + 32], lanes 32..63 b[l - 32] + b[l];
+// swap16_sum(a, b): lanes of even rows get a[l] + a[l + 16], of odd rows b[l - 16] + b[l].
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Quantization constants of the specification (kvq.h): eps = 1e-5.
 constexpr float kEps = 1e-5f;
 

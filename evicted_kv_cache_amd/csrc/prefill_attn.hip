@@ -68,11 +68,7 @@ __device__ __forceinline__ int v_col(int t) {
 // 16-byte operand reads of a row stay contiguous.
 __device__ __forceinline__ int vswz(int row, int col) { return col ^ (((row >> 4) & 7) << 3); }
 
-__device__ __forceinline__ int wave_min(int v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = min(v, __shfl_xor(v, off));
-    return v;
-}
+__device__ __forceinline__ int wave_min(int v) { return lane_reduce<true>(v, [](int x, int y) { return min(x, y); }); }
 
 __device__ __forceinline__ half8 to_half8(const float x[8]) {
     half8 h;
@@ -243,7 +239,7 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 return f16in ? h : bf;
             };
             float amax = elem(mbits);
-            amax = fmaxf(amax, __shfl_xor(amax, 32));
+            amax = fmaxf(amax, lane_xor<32>(amax));
             int ex = 0;
             if (amax > 0.0f) frexpf(amax, &ex);                  // amax in [2^(ex-1), 2^ex)
             const float up = ldexpf(1.0f, 15 - ex);              // largest |q| -> [2^14, 2^15)
@@ -277,7 +273,7 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 // half the whole row's (FG = 1); the partner lane holds the
                 // other half of every group's channels.
                 const float send = FG == 2 ? qsum[1 - kh] : qsum[0];
-                const float other = __shfl_xor(send, 32);
+                const float other = lane_xor<32>(send);
                 const float Q = (FG == 2 ? qsum[kh] : qsum[0]) + other;
                 // Q 2^-24 as an exact bf16 triple (truncating splits)
                 const float Qs = Q * 0x1p-24f;
@@ -578,7 +574,7 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
         // visible slot); only then are its output accumulators rescaled.  The
         // probabilities are then at most 2^kSlack, well inside fp16, and the
         // split's (m, l) stay consistent with its outputs.
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * qc;
+        mt = fmaxf(mt, lane_xor<32>(mt)) * qc;
         const float m_new = mt > m + kSlack ? mt : m;
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // nothing visible yet
         if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
@@ -607,7 +603,7 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 const half2v pr = {pf[st][2 * j], pf[st][2 * j + 1]};
                 ps = __builtin_amdgcn_fdot2(pr, one2, ps, false);
             }
-        ps += __shfl_xor(ps, 32);
+        ps = swap32_sum(ps, ps);
         l += ps;
         // O^T += V^T P^T
 #pragma unroll

@@ -105,13 +105,13 @@ __global__ __launch_bounds__(256) void snap_stats_kernel(SnapArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     if (key_base + acc_row(v, kh) < S) mx = fmaxf(mx, acc[v] * c);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = fmaxf(mx, lane_xor<32>(mx));
                 const float Mn = fmaxf(M[nt], mx);           // finite: key_base < S
                 float sum = 0.0f;
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     if (key_base + acc_row(v, kh) < S) sum += exp2f(acc[v] * c - Mn);
-                sum += __shfl_xor(sum, 32);
+                sum = swap32_sum(sum, sum);
                 L[nt] = (M[nt] == -INFINITY ? 0.0f : L[nt] * exp2f(M[nt] - Mn)) + sum;
                 M[nt] = Mn;
             }
@@ -197,12 +197,15 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
             if (ch0 >= a.n_stat) break;
             load_stats(ch0);
         }
-        for (int off = 1; off < tpr; off <<= 1) {
-            const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(L, off);
+        auto merge_pair = [&](float m2, float l2) {
             const float Mn = fmaxf(M, m2);
             L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
             M = Mn;
-        }
+        };
+        // lanes j = 0 .. tpr - 1 of a row (tpr in {2, 4, 8}) merge by lane distances 1, 2, 4
+        if (tpr > 1) { const float m2 = lane_xor<1>(M), l2 = lane_xor<1>(L); merge_pair(m2, l2); }
+        if (tpr > 2) { const float m2 = lane_xor<2>(M), l2 = lane_xor<2>(L); merge_pair(m2, l2); }
+        if (tpr > 4) { const float m2 = lane_xor<4>(M), l2 = lane_xor<4>(L); merge_pair(m2, l2); }
         if (r < wc && j == 0) {
             Mrow[r] = M;
             invL[r] = 1.0f / L;
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(256) void snap_scores_kernel(SnapArgs a) {
             if (i < wc) score += exp2f(acc[v] * c - Mrow[i]) * invL[i];
         }
     }
-    score += __shfl_xor(score, 32);
+    score = swap32_sum(score, score);
     if (kh == 0 && key < S)
         a.scores[((int64_t)b * a.H + h) * S + key] = score / (float)wc;
 }
@@ -318,13 +321,13 @@ __global__ __launch_bounds__(256) void snap_one_read_kernel(SnapArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     if (kb + acc_row(v, kh) < S) mx = fmaxf(mx, acc[f][nt][v] * c);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = fmaxf(mx, lane_xor<32>(mx));
                 const float Mn = fmaxf(M, mx);
                 float sum = 0.0f;
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
                     if (kb + acc_row(v, kh) < S) sum += exp2f(acc[f][nt][v] * c - Mn);
-                sum += __shfl_xor(sum, 32);
+                sum = swap32_sum(sum, sum);
                 L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + sum;
                 M = Mn;
             }
@@ -399,12 +402,15 @@ __global__ __launch_bounds__(256) void snap_one_read_kernel(SnapArgs a) {
                 M = mb;
             }
         }
-        for (int off = 1; off < tpr; off <<= 1) {
-            const float m2 = __shfl_xor(M, off), l2 = __shfl_xor(L, off);
+        auto merge_pair = [&](float m2, float l2) {
             const float Mn = fmaxf(M, m2);
             L = (M == -INFINITY ? 0.0f : L * exp2f(M - Mn)) + (m2 == -INFINITY ? 0.0f : l2 * exp2f(m2 - Mn));
             M = Mn;
-        }
+        };
+        // lanes j = 0 .. tpr - 1 of a row (tpr in {2, 4, 8}) merge by lane distances 1, 2, 4
+        if (tpr > 1) { const float m2 = lane_xor<1>(M), l2 = lane_xor<1>(L); merge_pair(m2, l2); }
+        if (tpr > 2) { const float m2 = lane_xor<2>(M), l2 = lane_xor<2>(L); merge_pair(m2, l2); }
+        if (tpr > 4) { const float m2 = lane_xor<4>(M), l2 = lane_xor<4>(L); merge_pair(m2, l2); }
         if (r < wc && j == 0) {
             Mrow[r] = M;
             invL[r] = 1.0f / L;
@@ -438,21 +444,21 @@ __global__ __launch_bounds__(256) void snap_one_read_kernel(SnapArgs a) {
         {
             const bool hi = (l32 & 8) != 0;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) x8[i] = (hi ? x[i + 8] : x[i]) + __shfl_xor(hi ? x[i] : x[i + 8], 8);
+            for (int i = 0; i < 8; ++i) x8[i] = (hi ? x[i + 8] : x[i]) + lane_xor<8>(hi ? x[i] : x[i + 8]);
         }
         {
             const bool hi = (l32 & 4) != 0;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x4[i] = (hi ? x8[i + 4] : x8[i]) + __shfl_xor(hi ? x8[i] : x8[i + 4], 4);
+            for (int i = 0; i < 4; ++i) x4[i] = (hi ? x8[i + 4] : x8[i]) + lane_xor<4>(hi ? x8[i] : x8[i + 4]);
         }
         {
             const bool hi = (l32 & 2) != 0;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) x2[i] = (hi ? x4[i + 2] : x4[i]) + __shfl_xor(hi ? x4[i] : x4[i + 2], 2);
+            for (int i = 0; i < 2; ++i) x2[i] = (hi ? x4[i + 2] : x4[i]) + lane_xor<2>(hi ? x4[i] : x4[i + 2]);
         }
         const bool hi = (l32 & 1) != 0;
-        float sc = (hi ? x2[1] : x2[0]) + __shfl_xor(hi ? x2[0] : x2[1], 1);
-        sc += __shfl_xor(sc, 16);
+        float sc = (hi ? x2[1] : x2[0]) + lane_xor<1>(hi ? x2[0] : x2[1]);
+        sc = swap16_sum(sc, sc);
         const int key = kb + acc_row(l32 & 15, kh);
         if (l32 < 16 && key < S) a.scores[bh * S + key] = sc / (float)wc;
     }
@@ -683,11 +689,8 @@ __device__ __forceinline__ void select_reg(const float* sc, int S, int n_sink, i
     uint4* h4 = reinterpret_cast<uint4*>(hist);
 #pragma unroll
     for (int q = 0; q < kSelPer / 4; ++q) h4[tid * (kSelPer / 4) + q] = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
-    }
+    kmin = lane_reduce<true>(kmin, [](uint32_t x, uint32_t y) { return min(x, y); });
+    kmax = lane_reduce<true>(kmax, [](uint32_t x, uint32_t y) { return max(x, y); });
     if (lane == 0) { tot16[0][wave] = kmin; tot16[1][wave] = kmax; }
     if (tid < 64) cand_rank[tid] = 0u;
     if (tid == 0) cand_n = 0u;
