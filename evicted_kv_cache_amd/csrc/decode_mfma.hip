@@ -181,8 +181,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
         qmax = fmaxf(qmax, fabsf(x[i]));
         qpart += x[i];
     }
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) qmax = fmaxf(qmax, __shfl_xor(qmax, off));
+    qmax = wave64_max(qmax);
     // scale so the largest |q| lands in [2^14, 2^15): exact fp16 for bf16/fp16 inputs
     int qexp = 0;
     if (qmax > 0.0f) { frexpf(qmax, &qexp); qexp -= 15; }
@@ -200,8 +199,11 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
     }
     // zero-point terms: sum of head h's query over quarter r (lane (r, h) holds it), / 2^(qexp + 24)
     float qsk[kGQ];
-#pragma unroll
-    for (int h = 0; h < kGQ; ++h) qsk[h] = ldexpf(__shfl(qpart, 16 * r + h), -(qexp + 24));
+    // lane (r, h) of this lane's row, by DPP row broadcasts
+    qsk[0] = ldexpf(__uint_as_float(dpp_u32<0x150>(__float_as_uint(qpart))), -(qexp + 24));
+    qsk[1] = ldexpf(__uint_as_float(dpp_u32<0x151>(__float_as_uint(qpart))), -(qexp + 24));
+    qsk[2] = ldexpf(__uint_as_float(dpp_u32<0x152>(__float_as_uint(qpart))), -(qexp + 24));
+    qsk[3] = ldexpf(__uint_as_float(dpp_u32<0x153>(__float_as_uint(qpart))), -(qexp + 24));
     // logit (base 2) = kC sum_quarters (s C + z qsk)
     const float kC = ldexpf(a.scale_log2, qexp + 24);
     const int kg = (32 * r) / GK;   // K group of this lane's quarter
@@ -441,8 +443,8 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
                 // the whole dot products: add the four quarters (lanes r = 0 .. 3 of the token)
 #pragma unroll
                 for (int h = 0; h < kGQ; ++h) {
-                    part[h] += __shfl_xor(part[h], 16);
-                    part[h] += __shfl_xor(part[h], 32);
+                    part[h] = swap16_sum(part[h], part[h]);
+                    part[h] = swap32_sum(part[h], part[h]);
                 }
                 if (cls[p] == 2) {
 #pragma unroll
@@ -627,12 +629,9 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
 
     // ---------------------------------------------------- wave-level reduction
     // head r sums over the row's tokens
+    l_lane = row16_sum(l_lane);
 #pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-        l_lane += __shfl_xor(l_lane, off);
-#pragma unroll
-        for (int g = 0; g < NVG; ++g) corr[g] += __shfl_xor(corr[g], off);
-    }
+    for (int g = 0; g < NVG; ++g) corr[g] = row16_sum(corr[g]);
     // undo the code scale 2^-24 and the weight scale 2^wexp (exact)
     const float unit = ldexpf(1.0f, 24 - wexp), unit16 = ldexpf(1.0f, 20 - wexp), unitc = ldexpf(1.0f, -wexp);
 #pragma unroll
@@ -641,7 +640,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void decode_mfma_kernel(D
         float cv = 0.0f;
 #pragma unroll
         for (int g = 0; g < NVG; ++g) {
-            const float cg = __shfl(corr[g], 16 * h);
+            const float cg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, corr[g]), 16 * h));
             cv = (g == r) ? cg : cv;
         }
         // a column is kept in the row of its own V group
