@@ -10,22 +10,24 @@
 //   S^T = K Q^T      (64 tokens x 32 query rows per wave, K-dim = head_dim)
 //   O^T += V^T P^T   (head_dim x 32 query rows per wave, K-dim = 64 tokens)
 //
-// with v_mfma_f32_32x32x16_f16.  The workgroup dequantizes each tile once into
-// LDS as fp16 (keys token-major, values transposed) for all its waves, into
-// one of two buffers, so the next tile is unpacked while the current one is
-// computed.  Keys are held as an fp16 pair (x_hi + x_lo, x_lo the rounding
-// residual); an fp16 or bf16 query row is scaled by a power of two into fp16
-// exactly, so the scores take K_hi Q + K_lo Q (an fp32 query is a pair as
-// well: K_hi Q_hi + K_lo Q_hi + K_hi Q_lo).  The logits are fp32-accurate
-// even where large keys (outlier channels) would make a single fp16
-// rounding move the softmax; values and probabilities enter the second
-// product as single fp16 (their rounding stays relative to the output).  The
-// online softmax runs in fp32 on the score accumulators, where each lane holds
-// one query column.  Tokens are handed to the second product in the order the
-// score accumulators hold them, and the value tile is stored in that order,
-// so probabilities go from registers to the matrix cores without a shuffle.
-// Splits over the tokens write unnormalized partials (m, l, o) that the
-// decode's log-sum-exp combine merges.
+// with v_mfma_f32_32x32x16_f16.  The workgroup unpacks each tile once into LDS
+// for all its waves, into one of two buffers, so the next tile is unpacked
+// while the current one is computed.  4-bit per-token affine keys in groups
+// of 64 or 128 channels (with fp16 or bf16 queries) enter the score product
+// as their codes, and the group scales and zero points are applied to the
+// sums (the factored scores below); other keys are held as an fp16 pair
+// (x_hi + x_lo, x_lo the rounding residual), with the fp16 or bf16 query row
+// scaled by a power of two into fp16 exactly, so the scores take
+// K_hi Q + K_lo Q (an fp32 query is a pair as well: K_hi Q_hi + K_lo Q_hi +
+// K_hi Q_lo).  Either way the logits are fp32-accurate even where large keys
+// (outlier channels) would make a single fp16 rounding move the softmax;
+// values and probabilities enter the second product as single fp16 (their
+// rounding stays relative to the output).  The online softmax runs in fp32 on
+// the score accumulators, where each lane holds one query column.  Tokens
+// are handed to the second product in the order the score accumulators hold
+// them, and the value tile is stored in that order, so probabilities go from
+// registers to the matrix cores without a shuffle.  Splits over the tokens
+// write partials (m, l, o / l in fp16) that a log-sum-exp combine merges.
 #include <math.h>
 
 #include "bufload.h"
@@ -381,65 +383,65 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
         if constexpr (kPair) {
             // rows past the split were fetched as zero codes and metadata: zero keys and values
 #pragma unroll
-            for (int pp = 0; pp < kItems / 2; ++pp) {
-            const int c = tid % C8, t0 = 2 * (tid / C8 + pp * (NT / C8));
+            for (int pp = 0; pp < kItems / 2; ++pp) {    // item pairs (2pp, 2pp + 1)
+                const int c = tid % C8, t0 = 2 * (tid / C8 + pp * (NT / C8));
 #pragma unroll
-            for (int jj2 = 0; jj2 < 2; ++jj2) {
-                const int j = 2 * pp + jj2;
-                float u[8];
-                if constexpr (kFact) {
-                    // the code word under nibble masks: channels (0,4), (1,5)*16,
-                    // (2,6), (3,7)*16 as fp16 subnormal pairs
-                    const uint32_t w = pks[j].c0, w8 = w >> 8;
-                    *reinterpret_cast<uint4*>(&kd[t0 + jj2][8 * c]) =
-                        make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u);
-                    constexpr int kCg = 128 / FG / 8;    // 8-channel chunks per group
-                    if (c % kCg == 0) {
-                        // first chunk of group g: the token's s_g, and z_g as an
-                        // exact bf16 pair (zh keeps the top 8 significant bits)
-                        const int g = c / kCg;
-                        reinterpret_cast<uint16_t*>(sc_lds(buf))[2 * (t0 + jj2) + g] = (uint16_t)(pks[j].meta & 0xFFFFu);
-                        const float z = f16_bits_to_f32(pks[j].meta >> 16);
-                        const uint32_t zhb = __float_as_uint(z) & 0xFFFF0000u;
-                        const uint32_t zh = zhb >> 16, zl = __float_as_uint(z - __uint_as_float(zhb)) >> 16;
-                        zo_lds(buf)[t0 + jj2][g] = make_uint4(zh | (zh << 16), zh | (zl << 16), zl | (zl << 16), 0u);
-                        if (FG == 1) zo_lds(buf)[t0 + jj2][1] = make_uint4(0u, 0u, 0u, 0u);
-                    }
-                } else {
-                    nib8(pks[j].c0, u);
-                    const float sk = f16_bits_to_f32(pks[j].meta & 0xFFFFu), zk = f16_bits_to_f32(pks[j].meta >> 16);
-                    half8 kh8, kl8;
+                for (int jj2 = 0; jj2 < 2; ++jj2) {
+                    const int j = 2 * pp + jj2;
+                    if constexpr (kFact) {
+                        // the code word under nibble masks: channels (0,4), (1,5)*16,
+                        // (2,6), (3,7)*16 as fp16 subnormal pairs
+                        const uint32_t w = pks[j].c0, w8 = w >> 8;
+                        *reinterpret_cast<uint4*>(&kd[t0 + jj2][8 * c]) =
+                            make_uint4(w & 0x000F000Fu, w & 0x00F000F0u, w8 & 0x000F000Fu, w8 & 0x00F000F0u);
+                        constexpr int kCg = 128 / FG / 8;    // 8-channel chunks per group
+                        if (c % kCg == 0) {
+                            // first chunk of group g: the token's s_g, and z_g as an
+                            // exact bf16 pair (zh keeps the top 8 significant bits)
+                            const int g = c / kCg;
+                            reinterpret_cast<uint16_t*>(sc_lds(buf))[2 * (t0 + jj2) + g] = (uint16_t)(pks[j].meta & 0xFFFFu);
+                            const float z = f16_bits_to_f32(pks[j].meta >> 16);
+                            const uint32_t zhb = __float_as_uint(z) & 0xFFFF0000u;
+                            const uint32_t zh = zhb >> 16, zl = __float_as_uint(z - __uint_as_float(zhb)) >> 16;
+                            zo_lds(buf)[t0 + jj2][g] = make_uint4(zh | (zh << 16), zh | (zl << 16), zl | (zl << 16), 0u);
+                            if (FG == 1) zo_lds(buf)[t0 + jj2][1] = make_uint4(0u, 0u, 0u, 0u);
+                        }
+                    } else {
+                        float u[8];
+                        nib8(pks[j].c0, u);
+                        const float sk = f16_bits_to_f32(pks[j].meta & 0xFFFFu), zk = f16_bits_to_f32(pks[j].meta >> 16);
+                        half8 kh8, kl8;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) {
-                        const float x = fmaf(u[i], sk, zk);
-                        kh8[i] = (_Float16)x;
-                        kl8[i] = (_Float16)(x - (float)kh8[i]);
+                        for (int i = 0; i < 8; ++i) {
+                            const float x = fmaf(u[i], sk, zk);
+                            kh8[i] = (_Float16)x;
+                            kl8[i] = (_Float16)(x - (float)kh8[i]);
+                        }
+                        *reinterpret_cast<half8*>(&kd[t0 + jj2][8 * c]) = kh8;
+                        *reinterpret_cast<half8*>(&kld[t0 + jj2][8 * c]) = kl8;
                     }
-                    *reinterpret_cast<half8*>(&kd[t0 + jj2][8 * c]) = kh8;
-                    *reinterpret_cast<half8*>(&kld[t0 + jj2][8 * c]) = kl8;
                 }
-            }
-            // Values as (token t0, token t0 + 1) fp16 pairs, straight from the
-            // code bytes: byte i of both code words gives channels 2i (low
-            // nibbles) and 2i + 1 (high nibbles); 0x6400 | u is the fp16
-            // 1024 + u, so subtracting 1024 leaves u exactly, and one packed
-            // fp16 fma rounds u s + z once.
-            typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-            const uint32_t w0 = pvs[2 * pp].c0, w1 = pvs[2 * pp + 1].c0;
-            const uint32_t m0 = pvs[2 * pp].meta, m1 = pvs[2 * pp + 1].meta;
-            const h2 s2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x05040100u));
-            const h2 z2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x07060302u));
-            const h2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-            const int col = v_col(t0);                // even; token t0 + 1 is column col + 1
+                // Values as (token t0, token t0 + 1) fp16 pairs, straight from the
+                // code bytes: byte i of both code words gives channels 2i (low
+                // nibbles) and 2i + 1 (high nibbles); 0x6400 | u is the fp16
+                // 1024 + u, so subtracting 1024 leaves u exactly, and one packed
+                // fp16 fma rounds u s + z once.
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                const uint32_t w0 = pvs[2 * pp].c0, w1 = pvs[2 * pp + 1].c0;
+                const uint32_t m0 = pvs[2 * pp].meta, m1 = pvs[2 * pp + 1].meta;
+                const h2 s2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x05040100u));
+                const h2 z2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x07060302u));
+                const h2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+                const int col = v_col(t0);                // even; token t0 + 1 is column col + 1
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = __builtin_amdgcn_perm(w1, w0, (uint32_t)i | 0x0C000C00u | ((uint32_t)(4 + i) << 16));
-                const uint32_t e = (x & 0x000F000Fu) | 0x64006400u, od = ((x >> 4) & 0x000F000Fu) | 0x64006400u;
-                const h2 ve = __builtin_elementwise_fma(__builtin_bit_cast(h2, e) + m1024, s2, z2);
-                const h2 vo = __builtin_elementwise_fma(__builtin_bit_cast(h2, od) + m1024, s2, z2);
-                *reinterpret_cast<h2*>(&vd[8 * c + 2 * i][vswz(8 * c + 2 * i, col)]) = ve;
-                *reinterpret_cast<h2*>(&vd[8 * c + 2 * i + 1][vswz(8 * c + 2 * i + 1, col)]) = vo;
-            }
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t x = __builtin_amdgcn_perm(w1, w0, (uint32_t)i | 0x0C000C00u | ((uint32_t)(4 + i) << 16));
+                    const uint32_t e = (x & 0x000F000Fu) | 0x64006400u, od = ((x >> 4) & 0x000F000Fu) | 0x64006400u;
+                    const h2 ve = __builtin_elementwise_fma(__builtin_bit_cast(h2, e) + m1024, s2, z2);
+                    const h2 vo = __builtin_elementwise_fma(__builtin_bit_cast(h2, od) + m1024, s2, z2);
+                    *reinterpret_cast<h2*>(&vd[8 * c + 2 * i][vswz(8 * c + 2 * i, col)]) = ve;
+                    *reinterpret_cast<h2*>(&vd[8 * c + 2 * i + 1][vswz(8 * c + 2 * i + 1, col)]) = vo;
+                }
             }
             return;
         }
