@@ -432,15 +432,17 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 const h2 s2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x05040100u));
                 const h2 z2 = __builtin_bit_cast(h2, __builtin_amdgcn_perm(m1, m0, 0x07060302u));
                 const h2 m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-                const int col = v_col(t0);                // even; token t0 + 1 is column col + 1
+                // rows 8c .. 8c + 7 share (row >> 4) & 7 = (c >> 1) & 7: one swizzled
+                // column for all eight stores (token t0 + 1 is the next column)
+                _Float16* vrow = &vd[8 * c][vswz(8 * c, v_col(t0))];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t x = __builtin_amdgcn_perm(w1, w0, (uint32_t)i | 0x0C000C00u | ((uint32_t)(4 + i) << 16));
                     const uint32_t e = (x & 0x000F000Fu) | 0x64006400u, od = ((x >> 4) & 0x000F000Fu) | 0x64006400u;
                     const h2 ve = __builtin_elementwise_fma(__builtin_bit_cast(h2, e) + m1024, s2, z2);
                     const h2 vo = __builtin_elementwise_fma(__builtin_bit_cast(h2, od) + m1024, s2, z2);
-                    *reinterpret_cast<h2*>(&vd[8 * c + 2 * i][vswz(8 * c + 2 * i, col)]) = ve;
-                    *reinterpret_cast<h2*>(&vd[8 * c + 2 * i + 1][vswz(8 * c + 2 * i + 1, col)]) = vo;
+                    *reinterpret_cast<h2*>(vrow + (2 * i) * (kPT + kPad)) = ve;
+                    *reinterpret_cast<h2*>(vrow + (2 * i + 1) * (kPT + kPad)) = vo;
                 }
             }
             return;
@@ -607,12 +609,15 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
             }
         ps = swap32_sum(ps, ps);
         l += ps;
-        // O^T += V^T P^T
+        // O^T += V^T P^T.  Row d * 32 + l32, 16-byte chunk 2 st + kh XORed with
+        // (row >> 4) & 7 = 2 d + (l32 >> 4) is chunk 2 (st ^ d) + (kh ^ (l32 >> 4)):
+        // a lane base plus a constant offset per (d, st).
+        const _Float16* vbase = &vd[l32][8 * (kh ^ (l32 >> 4))];
 #pragma unroll
         for (int d = 0; d < ND; ++d)
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                const half8 va = *reinterpret_cast<const half8*>(&vd[d * 32 + l32][vswz(d * 32 + l32, 16 * st + 8 * kh)]);
+                const half8 va = *reinterpret_cast<const half8*>(vbase + d * 32 * (kPT + kPad) + 16 * (st ^ (d & 3)));
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, pf[st], o[d], 0, 0, 0);
             }
     };
