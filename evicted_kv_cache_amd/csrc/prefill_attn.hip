@@ -659,9 +659,10 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
                 _Float16 lo = (_Float16)tr[wr][wh * 16 + 2 * k], hi = (_Float16)tr[wr][wh * 16 + 2 * k + 1];
                 hw2[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
             }
-            uint4* dst = reinterpret_cast<uint4*>(ws_h + (grow_w * ns + split) * D + d * 32 + wh * 16);
-            dst[0] = make_uint4(hw2[0], hw2[1], hw2[2], hw2[3]);
-            dst[1] = make_uint4(hw2[4], hw2[5], hw2[6], hw2[7]);
+            typedef uint32_t u32x4n __attribute__((ext_vector_type(4)));
+            u32x4n* dst = reinterpret_cast<u32x4n*>(ws_h + (grow_w * ns + split) * D + d * 32 + wh * 16);
+            __builtin_nontemporal_store(u32x4n{hw2[0], hw2[1], hw2[2], hw2[3]}, dst);
+            __builtin_nontemporal_store(u32x4n{hw2[4], hw2[5], hw2[6], hw2[7]}, dst + 1);
         }
     }
     if (row_ok && kh == 0) {
