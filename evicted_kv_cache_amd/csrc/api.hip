@@ -270,7 +270,7 @@ static DecodeArgs decode_args(const kvq_layout* L, const kvq_cache* c, const voi
     a.rope = rope; a.q_pos = q_pos;
     const float scale = sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)D);
     a.scale_log2 = scale * 1.4426950408889634f;
-    if (decode_fast_applies(a)) decode_fast_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
+    if (decode_fast_applies(a)) decode_fast_plan(a.B, a.Hkv, a.T, a.v_bits, &a.n_splits, &a.split_len);
     else decode_plan(a.B, a.Hkv, a.T, &a.n_splits, &a.split_len);
     return a;
 }

@@ -219,7 +219,7 @@ hipError_t launch_prefill_attention(const DecodeArgs& a, int n_q, int n_rb, int 
 // symmetric blocks or KIVI per-channel) and affine 4/8-bit V at head_dim
 // 128 with 1-4 query heads per kv-head (decode_mfma.hip).
 bool decode_fast_applies(const DecodeArgs& a);
-void decode_fast_plan(int B, int Hkv, int T, int* n_splits, int* split_len);
+void decode_fast_plan(int B, int Hkv, int T, int v_bits, int* n_splits, int* split_len);
 hipError_t launch_decode_fast(const DecodeArgs& a, hipStream_t s);
 bool decode_mfma_applies(const DecodeArgs& a);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
