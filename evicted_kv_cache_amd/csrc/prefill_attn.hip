@@ -51,6 +51,7 @@ constexpr int kRows = 32 * kWaves;
 constexpr int kFactWaves = 8;
 constexpr int kPad = 8;          // halfs of padding per LDS row (bank spread)
 constexpr float kSlack = 8.0f;   // log2 headroom of the lazily moved softmax reference point
+constexpr float kSlackP = 256.0f; // 2^kSlack
 
 // Row of the 32x32 block held by accumulator element v of lane half kh.
 __device__ __forceinline__ int acc_row(int v, int kh) { return 8 * (v >> 2) + 4 * kh + (v & 3); }
@@ -553,60 +554,81 @@ void prefill_attn_kernel(DecodeArgs a, int n_q, int n_rb, int causal) {
     // softmax of the scores s of the tile at t0, and its values (buffer bf)
     auto finish = [&](int t0, int bf) {
         _Float16 (*vd)[kPT + kPad] = v_lds(bf);
-        // mask (past the split or the row's last visible slot) -- only tiles
-        // that reach either boundary for some row of the wave need it
-        // (the row factor qc > 0 is applied to the max and inside the exponent)
-        float mt = -INFINITY;
-        if (t0 + kPT <= t_hi && t0 + kPT - 1 <= lim_min) {
+        // P^T fragments: K-step st takes accumulator elements 8 (st & 1) .. +7
+        // of block st >> 1 (v_exp_f32: results below 2^-126 flush to 0); the
+        // return value is this lane's sum of the fp16 probabilities the value
+        // product uses, two per instruction
+        half8 pf[4];
+        auto probs = [&](float mu) {
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+            for (int st = 0; st < 4; ++st)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[blk][v]);
-        } else {
+                for (int j = 0; j < 8; ++j)
+                    pf[st][j] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + j], qc, -mu));
+            typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+            const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            float sum = 0.0f;
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk)
+            for (int st = 0; st < 4; ++st)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int tok = t0 + blk * 32 + acc_row(v, kh);
-                    const float x = (tok < t_hi && tok <= lim) ? s[blk][v] : -INFINITY;
-                    s[blk][v] = x;
-                    mt = fmaxf(mt, x);
+                for (int j = 0; j < 4; ++j) {
+                    const half2v pr = {pf[st][2 * j], pf[st][2 * j + 1]};
+                    sum = __builtin_amdgcn_fdot2(pr, one2, sum, false);
                 }
-        }
+            return sum;
+        };
         // online softmax, base 2.  A row's reference point m moves only when
         // the row sees a logit more than kSlack above it (and on its first
         // visible slot); only then are its output accumulators rescaled.  The
         // probabilities are then at most 2^kSlack, well inside fp16, and the
-        // split's (m, l) stay consistent with its outputs.
-        mt = fmaxf(mt, lane_xor<32>(mt)) * qc;
-        const float m_new = mt > m + kSlack ? mt : m;
-        const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // nothing visible yet
-        if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
-            const float alpha = __builtin_amdgcn_exp2f(m - m_use);
-            l *= alpha;
-#pragma unroll
-            for (int d = 0; d < ND; ++d) o[d] *= alpha;
-        }
-        m = m_new;
-        // P^T fragments: K-step st takes accumulator elements 8 (st & 1) .. +7
-        // of block st >> 1 (v_exp_f32: results below 2^-126 flush to 0)
-        half8 pf[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                pf[st][j] = (_Float16)__builtin_amdgcn_exp2f(fmaf(s[st >> 1][8 * (st & 1) + j], qc, -m_use));
-        // the row sum takes the fp16 probabilities the value product uses, two per instruction
-        typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-        const half2v one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        // split's (m, l) stay consistent with its outputs.  A tile that needs
+        // no mask (every slot visible to every row of the wave) and a wave
+        // whose rows all have a reference point first take the probabilities
+        // against the current m: a lane sum below 2^kSlack bounds every one
+        // of them, so no logit is more than kSlack above m and m stays
+        // (the same decision as from the tile's maximum, which is then not
+        // needed); otherwise the tile takes the general path below.
+        const bool no_mask = t0 + kPT <= t_hi && t0 + kPT - 1 <= lim_min;
+        bool general = !no_mask || __builtin_amdgcn_ballot_w64(m == -INFINITY) != 0;
         float ps = 0.0f;
+        if (!general) {
+            ps = probs(m);
+            general = __builtin_amdgcn_ballot_w64(!(ps < kSlackP)) != 0;
+        }
+        if (general) {
+            // mask (past the split or the row's last visible slot) -- only
+            // tiles that reach either boundary for some row of the wave need
+            // it (the row factor qc > 0 is applied to the max and inside the
+            // exponent)
+            float mt = -INFINITY;
+            if (no_mask) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+                for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const half2v pr = {pf[st][2 * j], pf[st][2 * j + 1]};
-                ps = __builtin_amdgcn_fdot2(pr, one2, ps, false);
+                    for (int v = 0; v < 16; ++v) mt = fmaxf(mt, s[blk][v]);
+            } else {
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int tok = t0 + blk * 32 + acc_row(v, kh);
+                        const float x = (tok < t_hi && tok <= lim) ? s[blk][v] : -INFINITY;
+                        s[blk][v] = x;
+                        mt = fmaxf(mt, x);
+                    }
             }
+            mt = fmaxf(mt, lane_xor<32>(mt)) * qc;
+            const float m_new = mt > m + kSlack ? mt : m;
+            const float m_use = m_new == -INFINITY ? 0.0f : m_new;   // nothing visible yet
+            if (__builtin_amdgcn_ballot_w64(m_new > m) != 0) {
+                const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+                l *= alpha;
+#pragma unroll
+                for (int d = 0; d < ND; ++d) o[d] *= alpha;
+            }
+            m = m_new;
+            ps = probs(m_use);
+        }
         ps = swap32_sum(ps, ps);
         l += ps;
         // O^T += V^T P^T.  Row d * 32 + l32, 16-byte chunk 2 st + kh XORed with

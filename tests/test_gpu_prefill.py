@@ -179,3 +179,33 @@ def test_prefill_factored_edges(T, kg, dtype):
         err = attn_err(got, ref)
         say(f"  causal={causal} error {err:.3e}")
         assert np.all(np.isfinite(got)) and err <= TOL, err
+
+
+@pytest.mark.parametrize("kg,dtype", [(64, "bf16"), (128, "f16")])
+def test_prefill_reference_moves_inside_splits(kg, dtype):
+    """Key norms that grow along the cache in steps (x1 up to x9, plus single
+    spike tokens at x14): each row's largest logit keeps rising from tile to
+    tile inside a split, so the softmax reference point has to move (and the
+    output accumulators be rescaled) after the first tile, also on tiles that
+    need no mask.  Against the oracle, causal and not."""
+    B, H, G, T, n_q = 1, 2, 4, 3000, 24
+    rng = np.random.default_rng([0, 703, kg])
+    k = rng.standard_normal((B, H, T, 128), dtype=np.float32)
+    v = rng.standard_normal((B, H, T, 128), dtype=np.float32)
+    k *= (1.0 + np.floor(np.arange(T) / 375.0))[None, None, :, None].astype(np.float32)
+    spikes = rng.choice(T, size=12, replace=False)
+    k[:, :, spikes] *= 14.0 / (1.0 + np.floor(spikes / 375.0))[None, None, :, None]
+    k, v = synth.cast(k, dtype), synth.cast(v, dtype)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind="tok_affine", k_bits=4,
+                     k_group=kg, v_kind="tok_affine", v_bits=4, v_group=64, in_dtype=dtype)
+    say("prefill reference moves", kg, dtype)
+    c, o = build_pair(pl, ol, k, v, dtype)
+    q = synth.cast(rng.standard_normal((B, H * G, n_q, 128), dtype=np.float32), dtype)
+    for causal in (False, True):
+        out = K.kvq_prefill_attention(pl, c, to_dev(q, dtype), causal=causal)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        ref = prefill_attention(o, q, dtype, causal=causal)
+        err = attn_err(got, ref)
+        say(f"  causal={causal} error {err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= TOL, err
