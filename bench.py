@@ -76,6 +76,7 @@ def time_rotating(fns, reps, torch):
         for f in fns:
             f()
     ms = time_stream(g.replay, reps, 2, torch) / len(fns)
+    LAST_TRIALS[:] = [t / len(fns) for t in LAST_TRIALS]
     del g
     return ms
 
@@ -122,10 +123,15 @@ def sustain(fn, torch, ms_min=SUSTAIN_MS):
     return per
 
 
+TRIALS = 5
+LAST_TRIALS = []                   # ms per call of each trial of the last time_stream
+
+
 def time_stream(fn, steps, warmup, torch, sustain_ms=SUSTAIN_MS, min_timed_ms=MIN_TIMED_MS):
-    """Average ms per call of fn, with HIP events on the current stream: `warmup`
-    calls, then sustain_ms of device time untimed, then max(steps, as many as
-    fill min_timed_ms) timed calls."""
+    """Median over TRIALS trials of the average ms per call of fn, with HIP
+    events on the current stream: `warmup` calls, then sustain_ms of device
+    time untimed, then TRIALS trials of max(steps, as many as fill
+    min_timed_ms) timed calls each (the trials are kept in LAST_TRIALS)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -133,14 +139,23 @@ def time_stream(fn, steps, warmup, torch, sustain_ms=SUSTAIN_MS, min_timed_ms=MI
     if per > 0:
         steps = max(steps, math.ceil(min_timed_ms / per))
     s = torch.cuda.current_stream()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(s)
-    for _ in range(steps):
-        fn()
-    end.record(s)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    trials = []
+    for _ in range(TRIALS):
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(s)
+        for _ in range(steps):
+            fn()
+        end.record(s)
+        torch.cuda.synchronize()
+        trials.append(start.elapsed_time(end) / steps)
+    LAST_TRIALS[:] = trials
+    return sorted(trials)[TRIALS // 2]
+
+
+def trials_note(scale):
+    """The last time_stream's trials, times scale (e.g. 1e3 for us per call)."""
+    return [round(t * scale, 4) for t in LAST_TRIALS]
 
 
 def time_steps(fn, steps, warmup, torch):
@@ -292,8 +307,10 @@ def main():
             K.kvq_cache_reset(cache)               # host counters only: an empty cache
             K.kvq_quantize_append(L, cache, kd, vd)
         ms = time_stream(prefill, 1, 1, torch)
+        trials_a = trials_note(1.0)
         nbytes = 2 * kd.numel() * 2 + 2 * (cache.sizes.k_codes + cache.sizes.k_meta) + T * 4
         rows["A_quantize_prefill"] = {"workload": f"{w.name} prefill n_new={T}", "ms": round(ms, 4),
+                                      "trials_ms": trials_a,
                                       "GB/s": round(nbytes / ms / 1e6, 1),
                                       "frac_hbm": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
     else:
@@ -344,10 +361,12 @@ def main():
             st = K.kvq_evict_streaming(L, cache, dst, sink, window)
             assert st == K.KVQ_OK
         msc = time_stream(evict, 10, 2, torch)
+        trials_c = trials_note(1.0)
         row_bytes = 2 * (D * e["k_bits"] // 8 + (D // e["k_group"]) * 4)
         cbytes = 2 * B * Hkv * (sink + window) * row_bytes + 2 * (sink + window) * 4
         rows["C_evict"] = {"workload": f"{w.name} T={T} -> sink {sink} + window {window}",
-                           "ms": round(msc, 4), "GB/s": round(cbytes / msc / 1e6, 1),
+                           "ms": round(msc, 4), "trials_ms": trials_c,
+                           "GB/s": round(cbytes / msc / 1e6, 1),
                            "frac_hbm": round(cbytes / msc / 1e6 / PEAK_HBM_GBS, 4),
                            "algorithmic_bytes": cbytes,
                            "traffic": load_traffic(
@@ -377,11 +396,14 @@ def main():
         ncp = n_copies(ks.nbytes + vs.nbytes)
         copies = [(ksd.clone(), vsd.clone()) for _ in range(ncp)]
         msd = time_rotating([snap(a, b) for a, b in copies], 20, torch)
+        trials_d = trials_note(1e3)
         del copies
         sbytes = ks.nbytes + 2 * n_keep * Hs * Ds * 2 * 2 + sc.numel() * 4 + kept.numel() * 4
         rows["D_snapkv"] = {"workload": f"{ws_.name} S={Ss} w={ex['obs_window']} sink={ex['n_sink']} "
                                         f"budget={ex['budget']} Hkv={Hs} D={Ds}",
-                            "us": round(msd * 1e3, 2), "scores/s": round(Hs * Ss / (msd * 1e-3), 1),
+                            "us": round(msd * 1e3, 2), "trials_us": trials_d,
+                            "scores/s": round(Hs * Ss / (msd * 1e-3), 1),
+                            "logits/s": round(Bs * Hs * ex["obs_window"] * Ss / (msd * 1e-3), 1),
                             "algorithmic_bytes": sbytes,
                             "traffic": load_traffic(
                                 os.path.join(ROOT, "profiles", "snapkv_s8192_traffic.json"),
@@ -431,6 +453,7 @@ def main():
             del kdb, vdb
             usb = time_rotating([(lambda cc=cc: K.kvq_decode_attention(Lb, cc, qb, out=outb, ws=wsb))
                                  for cc in caches], 10, torch) * 1e3
+            trials_b = trials_note(1e3)
             del caches
             qo = Bb * Hqb * Db * (2 + 4)
             if eb["k_kind"] == "tok_sym4":     # codes + fp16 block scales; int8 V + (scale, zero)
@@ -441,7 +464,8 @@ def main():
             rows[f"B_decode_{wname}" + (f"_B{Bb}_T{Tb}" if over else "")] = {
                 "workload": f"{wname} B={Bb} Hq/Hkv={Hqb}/{Hb} D={Db} T={Tb} K {eb['k_kind']} "
                             f"{eb['k_bits']}-bit, V affine {eb['v_bits']}-bit",
-                "us": round(usb, 2), "algorithmic_bytes": nb, "GB/s": round(nb / usb / 1e3, 1),
+                "us": round(usb, 2), "trials_us": trials_b, "algorithmic_bytes": nb,
+                "GB/s": round(nb / usb / 1e3, 1),
                 "frac_hbm": round(nb / usb / 1e3 / PEAK_HBM_GBS, 4),
                 "timing": f"cold: graph replay over {ncp} identical caches ({ncp * cache_bytes >> 20} MiB)",
                 "us_warm": round(usw, 2), "GB/s_warm": round(nb / usw / 1e3, 1)}
@@ -465,11 +489,13 @@ def main():
             oe = torch.empty((1, Hq, n_q, D), dtype=torch.float32, device=dev)
             wse = torch.empty(max(K.kvq_prefill_workspace_bytes(Le, Hq, n_q), 16), dtype=torch.uint8, device=dev)
             mse = time_stream(lambda: K.kvq_prefill_attention(Le, ce, qe, causal=True, out=oe, ws=wse), 20, 3, torch)
+            trials_e = trials_note(1e3)
             flops = 4 * D * Hq * (n_q * (Te - n_q) + n_q * (n_q + 1) // 2)
             tf = flops / mse / 1e9
             rows[f"E_prefill_attention_T{Te}"] = {
                 "workload": f"{we.name} B=1 Hq/Hkv={Hq}/{Hkv} D={D} T={Te}, {n_q} causal queries per head",
-                "us": round(mse * 1e3, 2), "algorithmic_flops": flops, "TFLOP/s": round(tf, 1),
+                "us": round(mse * 1e3, 2), "trials_us": trials_e, "algorithmic_flops": flops,
+                "TFLOP/s": round(tf, 1),
                 "frac_mfma_fp16": round(tf / PEAK_MFMA_F16_TFLOPS, 4)}
             del ce, oe, wse
 
