@@ -204,6 +204,24 @@ def test_fast_decode_k_formats_and_8bit_v(k_kind, kg, vb, vg):
     check_decode(pl, c, o, synth.cast(synth.widen(q, "f16"), "bf16"), "bf16")
 
 
+@pytest.mark.parametrize("B,H", [(8, 8), (9, 7)])
+def test_8bit_value_decode_at_the_split_plan_boundary(B, H):
+    """Q4_0-style centered keys with 8-bit values: from 64 (batch, kv-head)
+    units the split plan aims at 256 workgroups instead of 512 (B=8 x 8
+    kv-heads: 4 splits of a ragged cache; 9 x 7 = 63 units: 6).  Every row
+    against the oracle."""
+    w = synth.workload("q4_0_centered")
+    T = 1500
+    k, v, q = gen(w, B, H, T, Hq=4 * H)
+    bias = np.stack([synth.head_params(w, h)[0] for h in range(H)]).astype(np.float32)
+    pl, ol = layouts(batch=B, n_kv_heads=H, head_dim=128, capacity=T, k_kind="tok_sym4", k_bits=4,
+                     k_group=32, v_kind="tok_affine", v_bits=8, v_group=32, in_dtype="f16",
+                     flags=K.KVQ_CENTER_K)
+    say("8-bit value decode, split plan boundary", B, H)
+    c, o = build_pair(pl, ol, k, v, "f16", k_bias=bias)
+    check_decode(pl, c, o, q, "f16")
+
+
 @pytest.mark.parametrize("k_kind,kg,vb,vg,dt", [
     ("tok_affine", 32, 4, 128, "bf16"), ("tok_affine", 64, 4, 64, "f16"), ("tok_sym4", 32, 8, 64, "f16"),
 ])
