@@ -14,11 +14,15 @@ workloads and reported under "rows":
   B  decode on the other cache formats: Q4_0-style centered K + int8 V
      (batch 16, T = 16384), a KIVI int4 Llama-3.2-3B layer (T = 8192) and
      the same layer shape at batch 16, T = 16384
+  E  multi-query (prefill-chunk) attention: 128 causal queries per head,
+     32 / 8 heads x 128, T = 2048 and 32768 (matrix-core bound)
 Inputs are seeded synthetic data (synth) already resident in HBM when the
 timed region starts.  Times come from HIP events on the stream the kernels
-run on.  The CPU oracle is timed on a bounded sample as the CPU baseline.
+run on; every row other than the step is the median of five trials.  The
+CPU oracle is timed on a bounded sample as the CPU baseline.
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps 300] [--warmup 200] [--no-cpu-baseline]
+                       [--rows ACDBE] [--e-lengths 2048,32768]
 """
 from __future__ import annotations
 
